@@ -1,0 +1,248 @@
+"""Benchmark: one decode step of compressed-KV attention on one MI355X.
+
+A step is one pass of the whole hot path over one layer of the LLaMA-7B-shaped
+workload (B=1, 32 query/KV heads, D=128, 8192 tokens, INT8 per-token cache,
+H2O keep 0.3 = 4 sinks + 1024 recent + 1429 heavy hitters):
+
+  1. quantize-append the new token's K and V          (kvc_quant_append)
+  2. attention over all 8192 tokens + H2O accumulation (kvc_decode_attn)
+  3. keep-set selection down to 2457 slots             (kvc_h2o_select)
+  4. compaction of the kept slots into the other buffer (kvc_compact)
+
+Steps rotate over 32 distinct layer caches (2.1 GiB, like the 32 layers of the
+model), so every launch streams its 66 MiB from HBM rather than from the
+256 MB Infinity Cache. Inputs are resident in HBM before timing starts.
+
+The timed region replays HIP graphs, one per phase of a 32-layer block:
+[rewind lengths + 32 appends] [32 attentions] [32 x (select + compact)].
+HIP events around the attention phase give the attention kernels' average
+duration, from which the roofline fraction is computed.
+
+Prints one JSON line. Run ``python bench.py --help`` for options.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV GB/s & tokens/s (fraction of HBM peak), INT8, L=8192, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+LAYERS = 32
+
+
+def step_bytes(B, Hq, H, D, bits, L, budget):
+    """Algorithmic bytes of one step, by part (what the method must move)."""
+    rb = D * bits // 8
+    kv = B * H * L * 2 * (rb + 4)                        # codes + fp32 scales, K and V
+    parts = {
+        "append": B * H * (2 * D * 2 + 2 * (rb + 4) + 4 + 4),   # fp16 in; codes, scales, position, score out
+        "attention": kv + B * Hq * D * 2 + B * Hq * D * 4,      # KV + q (fp16) + out (fp32)
+        "h2o": 2 * B * H * L * 4,                                # score read-modify-write
+        "select": B * H * L * 4 + B * H * L,                     # scores in, mask out
+        "compact": B * H * L + 2 * B * H * budget * (2 * (rb + 4) + 8),  # mask; kept rows in and out
+    }
+    return parts, kv + B * Hq * D * 2   # attention kernel's own algorithmic bytes (KV + q)
+
+
+def cpu_baseline(w, d, budget_s=12.0):
+    """Time the fp64 oracle (unchanged) on the host for one full step of the
+    same workload, repeated until about ``budget_s`` seconds have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    B, H, D, L = w.batch, w.num_kv_heads, w.head_dim, w.context
+    ref = oracle.RefCache(B, H, D, L, w.bits)
+    ref.append(d["k"][:, :, :L - 1], d["v"][:, :, :L - 1])
+    snap = (ref.k_codes.copy(), ref.v_codes.copy(), ref.k_scale.copy(), ref.v_scale.copy(),
+            ref.positions.copy(), ref.lengths.copy(), ref.num_seen.copy())
+    times = []
+    t_total = time.perf_counter()
+    while True:
+        (ref.k_codes[:], ref.v_codes[:], ref.k_scale[:], ref.v_scale[:], ref.positions[:],
+         ref.lengths[:], ref.num_seen[:]) = snap
+        ref.score[:] = 0
+        t0 = time.perf_counter()
+        ref.step(d["q"], d["k"][:, :, L - 1:], d["v"][:, :, L - 1:], budget=w.budget, n_sink=w.n_sink,
+                 n_recent=w.n_recent)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_total > budget_s or len(times) >= 20:
+            break
+    return min(times), len(times), cores
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024, help="timed steps (rounded up to a multiple of 32)")
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence and KV head with no communication; see DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import compressed_kv_cache_kvc_amd as kvc
+    from workloads import draw, get
+
+    torch.cuda.set_device(0)
+    w = get("llama7b_8k")
+    d = draw(w)
+    B, Hq, H, D, L, bits = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.context, w.bits
+    budget, S, R = w.budget, w.n_sink, w.n_recent
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    # ---- device state: 32 layer caches, shared lengths so one fill rewinds all ----
+    lengths_all = torch.zeros((LAYERS, B), dtype=torch.int32, device="cuda")
+    seen_all = torch.zeros((LAYERS, B), dtype=torch.int32, device="cuda")
+    caches, scores, masks = [], [], []
+    k_pre, v_pre = dev(d["k"][:, :, :L - 1]), dev(d["v"][:, :, :L - 1])
+    for i in range(LAYERS):
+        c = kvc.KVCache(B, H, D, L, bits)
+        c.lengths, c.num_seen = lengths_all[i], seen_all[i]
+        c.desc = c._make_desc()
+        kvc.kvc_quant_append(c, k_pre, v_pre, max_len_hint=0)
+        caches.append(c)
+        scores.append(c.score_buffer())
+        masks.append(torch.zeros((B, H, L), dtype=torch.uint8, device="cuda"))
+    del k_pre, v_pre
+    dst = kvc.KVCache(B, H, D, L, bits)
+    dst_score = dst.score_buffer()
+    k_new, v_new, q = dev(d["k"][:, :, L - 1:]), dev(d["v"][:, :, L - 1:]), dev(d["q"])
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    ws_attn = torch.empty(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, L, True), dtype=torch.uint8,
+                          device="cuda")
+    ws_comp = torch.empty(kvc.kvc_compact_workspace_bytes(caches[0], L), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def phase_append():
+        lengths_all.fill_(L - 1)
+        for i in range(LAYERS):
+            kvc.kvc_quant_append(caches[i], k_new, v_new, h2o_score=scores[i], max_len_hint=L - 1)
+
+    def phase_attn():
+        for i in range(LAYERS):
+            kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L, workspace=ws_attn)
+
+    def phase_evict():
+        for i in range(LAYERS):
+            kvc.kvc_h2o_select(caches[i], scores[i], budget, S, R, masks[i], max_len_hint=L)
+            kvc.kvc_compact(caches[i], scores[i], masks[i], dst, dst_score, max_len_hint=L, workspace=ws_comp)
+
+    # ---- eager pass, then capture each phase as a graph ----
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        phase_append(); phase_attn(); phase_evict()
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    eager_len = dst.lengths.clone()
+    graphs = []
+    for fn in (phase_append, phase_attn, phase_evict):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    blocks_w = max(1, (args.warmup + LAYERS - 1) // LAYERS)
+    blocks = max(1, (args.steps + LAYERS - 1) // LAYERS)
+    steps = blocks * LAYERS
+    with torch.cuda.stream(stream):
+        for _ in range(blocks_w):
+            for g in graphs:
+                g.replay()
+    torch.cuda.synchronize()
+    # The replayed graph must reproduce the eager result.
+    assert torch.equal(out, eager_out), "graph replay differs from the eager attention output"
+    assert torch.equal(dst.lengths, eager_len)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(blocks)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        wall0 = time.perf_counter()
+        for bi in range(blocks):
+            graphs[0].replay()
+            ev[bi][0].record(stream)
+            graphs[1].replay()
+            ev[bi][1].record(stream)
+            graphs[2].replay()
+        t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev)
+
+    parts, attn_alg = step_bytes(B, Hq, H, D, bits, L, budget)
+    step_alg = sum(parts.values())
+    ms_per_step = total_ms / steps
+    attn_us = attn_ms * 1e3 / steps
+    value = step_alg / (ms_per_step * 1e-3) / 1e9
+    attn_gbps = attn_alg / (attn_us * 1e-6) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": blocks_w * LAYERS,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 codes, fp32 math",
+        "data": "synthetic (seeded N(0,1) fp16 K/V with 4 outlier channels per head x10)",
+        "config": {"workload": "llama7b_8k", "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": D,
+                   "context": L, "bits": bits, "budget": budget, "n_sink": S, "n_recent": R,
+                   "layer_buffers_rotated": LAYERS},
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "step_bytes": step_alg,
+        "step_fraction_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "attention_us": round(attn_us, 3),
+        "attention_kv_gbps": round(attn_gbps, 1),
+        "wall_s": round(wall, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode attention (attn_split_kernel + attn_combine_kernel)",
+            "achieved": round(attn_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        t_cpu, n_cpu, cores = cpu_baseline(w, d, args.cpu_seconds)
+        rec["cpu_baseline"] = {
+            "value": round(step_alg / t_cpu / 1e9, 4),
+            "unit": "GB/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": f"best of {n_cpu} full oracle steps (append, attention+H2O, select, compact) "
+                      f"of the same 8192-token layer; {t_cpu * 1e3:.1f} ms per step, "
+                      f"{B / t_cpu:.2f} tokens/s",
+        }
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

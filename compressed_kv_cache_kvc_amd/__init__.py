@@ -1,0 +1,322 @@
+"""Compressed-KV decode attention for AMD MI355X: Python binding of libkvc.
+
+Argument marshalling only. Every step of the path runs in the HIP kernels of
+``libkvc.so``; this module turns torch tensors into device pointers, calls the
+C ABI declared in ``include/kvc.h`` through ctypes, and raises
+:class:`KvcError` on a non-OK status. There is no CPU fallback: importing the
+package fails loudly when the library has not been built.
+
+Function names match the C entry points (``kvc_quant_append``,
+``kvc_decode_attn``, ``kvc_h2o_select``, ``kvc_compact`` and the
+``kvc_pool_*`` calls). :class:`KVCache` owns the device buffers one cache
+descriptor points to; :class:`BlockPool` wraps the host block pool.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "KvcError", "KVCache", "BlockPool", "lib", "LIB_PATH",
+    "kvc_abi_version", "kvc_status_str", "kvc_last_error",
+    "kvc_quant_append", "kvc_decode_attn", "kvc_decode_attn_workspace_bytes",
+    "kvc_h2o_select", "kvc_h2o_select_workspace_bytes", "kvc_compact", "kvc_compact_workspace_bytes",
+    "row_bytes",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so")
+
+KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_CAPACITY, KVC_ERR_UNSUPPORTED, KVC_ERR_DEVICE = range(5)
+
+
+class KvcCacheDesc(ctypes.Structure):
+    """ctypes mirror of ``kvc_cache_t``."""
+    _fields_ = [
+        ("bits", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("lengths", ctypes.c_void_p), ("num_seen", ctypes.c_void_p),
+        ("positions", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    # torch brings its own HIP runtime (libamdhip64.so, soname libamdhip64.so.7).
+    # Loading torch first lets libkvc.so bind to that same runtime by soname;
+    # otherwise the process would hold two HIP runtimes and the second finds no device.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m compressed_kv_cache_kvc_amd.build` "
+            "(or __graft_entry__.build()). There is no fallback implementation.")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_uint64
+    D = ctypes.POINTER(KvcCacheDesc)
+    sig = {
+        "kvc_abi_version": (I32, []),
+        "kvc_status_str": (ctypes.c_char_p, [I32]),
+        "kvc_last_error": (ctypes.c_char_p, []),
+        "kvc_quant_append": (I32, [D, P, P, I32, P, I32, P]),
+        "kvc_decode_attn_workspace_bytes": (SZ, [D, I32, I32, I32]),
+        "kvc_decode_attn": (I32, [D, P, I32, P, P, I32, P, SZ, P]),
+        "kvc_h2o_select_workspace_bytes": (SZ, [D, I32]),
+        "kvc_h2o_select": (I32, [D, P, I32, I32, I32, P, I32, P, SZ, P]),
+        "kvc_compact_workspace_bytes": (SZ, [D, I32]),
+        "kvc_compact": (I32, [D, P, P, D, P, I32, P, SZ, P]),
+        "kvc_pool_create": (P, [I32, I32, U64]),
+        "kvc_pool_destroy": (None, [P]),
+        "kvc_pool_reserve": (I32, [P, I32, I32]),
+        "kvc_pool_free": (I32, [P, I32]),
+        "kvc_pool_num_free": (I32, [P]),
+        "kvc_pool_num_blocks": (I32, [P, I32]),
+        "kvc_pool_block_table": (I32, [P, P, I32, I32, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.kvc_last_error().decode()
+        super().__init__(f"{where}: {lib.kvc_status_str(status).decode()}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != KVC_OK:
+        raise KvcError(status, where)
+
+
+def kvc_abi_version() -> int:
+    return lib.kvc_abi_version()
+
+
+def kvc_status_str(status: int) -> str:
+    return lib.kvc_status_str(status).decode()
+
+
+def kvc_last_error() -> str:
+    return lib.kvc_last_error().decode()
+
+
+def row_bytes(head_dim: int, bits: int) -> int:
+    """Bytes of one token row of one KV head (codes only)."""
+    return head_dim * bits // 8
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _need(t, dtype, name, numel=None):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+
+
+class KVCache:
+    """Device buffers of one compressed cache (one layer) and its descriptor.
+
+    Contiguous layout (``block_size=0``): codes ``[B][Hkv][capacity][RB]`` uint8,
+    scales ``[B][Hkv][capacity]`` fp32, positions int32 of the same shape.
+    Paged layout (``block_size=16``): codes ``[num_blocks][Hkv][16][RB]``,
+    scales ``[num_blocks][Hkv][16]``, a ``[B][max_blocks]`` int32 block table,
+    and no positions. ``lengths`` and ``num_seen`` are ``[B]`` int32.
+    """
+
+    def __init__(self, batch: int, num_kv_heads: int, head_dim: int, capacity: int, bits: int = 8,
+                 device="cuda", block_size: int = 0, num_blocks: int = 0, max_blocks_per_seq: int = 0,
+                 positions: bool = True):
+        import torch
+        self.batch, self.num_kv_heads, self.head_dim, self.bits = batch, num_kv_heads, head_dim, bits
+        self.block_size = block_size
+        rb = row_bytes(head_dim, bits)
+        if block_size:
+            self.capacity = max_blocks_per_seq * block_size
+            rows = (num_blocks, num_kv_heads, block_size)
+            self.block_table = torch.full((batch, max_blocks_per_seq), -1, dtype=torch.int32, device=device)
+            self.positions = None
+        else:
+            self.capacity = capacity
+            rows = (batch, num_kv_heads, capacity)
+            self.block_table = None
+            self.positions = torch.zeros(rows, dtype=torch.int32, device=device) if positions else None
+        self.num_blocks, self.max_blocks_per_seq = num_blocks, max_blocks_per_seq
+        self.k_codes = torch.zeros(rows + (rb,), dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros(rows + (rb,), dtype=torch.uint8, device=device)
+        self.k_scale = torch.zeros(rows, dtype=torch.float32, device=device)
+        self.v_scale = torch.zeros(rows, dtype=torch.float32, device=device)
+        self.lengths = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.num_seen = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.max_len = 0   # host-side upper bound of the device lengths
+        self.desc = self._make_desc()
+
+    def _make_desc(self) -> KvcCacheDesc:
+        d = KvcCacheDesc()
+        d.bits, d.batch, d.num_kv_heads, d.head_dim = self.bits, self.batch, self.num_kv_heads, self.head_dim
+        d.capacity, d.block_size = self.capacity, self.block_size
+        d.max_blocks_per_seq, d.num_blocks = self.max_blocks_per_seq, self.num_blocks
+        d.k_codes, d.v_codes = _ptr(self.k_codes), _ptr(self.v_codes)
+        d.k_scale, d.v_scale = _ptr(self.k_scale), _ptr(self.v_scale)
+        d.lengths, d.num_seen = _ptr(self.lengths), _ptr(self.num_seen)
+        d.positions = _ptr(self.positions)
+        d.block_table = _ptr(self.block_table)
+        return d
+
+    def score_buffer(self):
+        """A zeroed fp32 H2O score array ``[B][Hkv][capacity]``."""
+        import torch
+        return torch.zeros((self.batch, self.num_kv_heads, self.capacity), dtype=torch.float32,
+                           device=self.k_codes.device)
+
+
+def _desc(cache) -> KvcCacheDesc:
+    return cache.desc if isinstance(cache, KVCache) else cache
+
+
+def kvc_quant_append(cache, k_new, v_new, h2o_score=None, max_len_hint: Optional[int] = None, stream=None):
+    """Quantize ``k_new``/``v_new`` fp16 ``[B][Hkv][n][D]`` into the cache (see kvc.h)."""
+    import torch
+    d = _desc(cache)
+    n_new = k_new.shape[2]
+    _need(k_new, torch.float16, "k_new", d.batch * d.num_kv_heads * n_new * d.head_dim)
+    _need(v_new, torch.float16, "v_new", d.batch * d.num_kv_heads * n_new * d.head_dim)
+    _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    _check(lib.kvc_quant_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), n_new, _ptr(h2o_score),
+                                max_len_hint, _stream(stream)), "kvc_quant_append")
+    if isinstance(cache, KVCache):
+        cache.max_len = max_len_hint + n_new
+
+
+def kvc_decode_attn_workspace_bytes(cache, num_q_heads: int, max_len_hint: int, with_h2o: bool) -> int:
+    return lib.kvc_decode_attn_workspace_bytes(ctypes.byref(_desc(cache)), num_q_heads, max_len_hint,
+                                               int(bool(with_h2o)))
+
+
+def kvc_decode_attn(cache, q, out, h2o_score=None, max_len_hint: Optional[int] = None, workspace=None,
+                    stream=None):
+    """Decode attention; ``q`` fp16 ``[B][Hq][D]``, ``out`` fp32 ``[B][Hq][D]`` (see kvc.h)."""
+    import torch
+    d = _desc(cache)
+    Hq = q.shape[1]
+    _need(q, torch.float16, "q", d.batch * Hq * d.head_dim)
+    _need(out, torch.float32, "out", d.batch * Hq * d.head_dim)
+    _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    if workspace is None:
+        n = kvc_decode_attn_workspace_bytes(d, Hq, max_len_hint, h2o_score is not None)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.kvc_decode_attn(ctypes.byref(d), _ptr(q), Hq, _ptr(out), _ptr(h2o_score), max_len_hint,
+                               _ptr(workspace), workspace.numel(), _stream(stream)), "kvc_decode_attn")
+
+
+def kvc_h2o_select_workspace_bytes(cache, max_len_hint: int) -> int:
+    return lib.kvc_h2o_select_workspace_bytes(ctypes.byref(_desc(cache)), max_len_hint)
+
+
+def kvc_h2o_select(cache, h2o_score, budget: int, n_sink: int, n_recent: int, keep_mask,
+                   max_len_hint: Optional[int] = None, workspace=None, stream=None):
+    """Keep mask uint8 ``[B][Hkv][capacity]``: sinks + recent + top-k by score (see kvc.h)."""
+    import torch
+    d = _desc(cache)
+    _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
+    _need(keep_mask, torch.uint8, "keep_mask", d.batch * d.num_kv_heads * d.capacity)
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(lib.kvc_h2o_select(ctypes.byref(d), _ptr(h2o_score), budget, n_sink, n_recent, _ptr(keep_mask),
+                              max_len_hint, _ptr(workspace), nbytes, _stream(stream)), "kvc_h2o_select")
+
+
+def kvc_compact_workspace_bytes(cache, max_len_hint: int) -> int:
+    return lib.kvc_compact_workspace_bytes(ctypes.byref(_desc(cache)), max_len_hint)
+
+
+def kvc_compact(src, src_score, keep_mask, dst, dst_score=None, max_len_hint: Optional[int] = None,
+                workspace=None, stream=None):
+    """Stable out-of-place compaction of the kept slots from ``src`` to ``dst`` (see kvc.h)."""
+    import torch
+    ds, dd = _desc(src), _desc(dst)
+    _need(src_score, torch.float32, "src_score", ds.batch * ds.num_kv_heads * ds.capacity)
+    _need(dst_score, torch.float32, "dst_score", dd.batch * dd.num_kv_heads * dd.capacity)
+    _need(keep_mask, torch.uint8, "keep_mask", ds.batch * ds.num_kv_heads * ds.capacity)
+    if max_len_hint is None:
+        max_len_hint = src.max_len
+    if workspace is None:
+        n = kvc_compact_workspace_bytes(ds, max_len_hint)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=keep_mask.device)
+    _check(lib.kvc_compact(ctypes.byref(ds), _ptr(src_score), _ptr(keep_mask), ctypes.byref(dd), _ptr(dst_score),
+                           max_len_hint, _ptr(workspace), workspace.numel(), _stream(stream)), "kvc_compact")
+    if isinstance(dst, KVCache) and isinstance(src, KVCache):
+        dst.max_len = src.max_len
+
+
+class BlockPool:
+    """Host block pool (``kvc_pool_*``): seeded block placement and block tables."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, shuffle_seed: int = 0):
+        self._p = lib.kvc_pool_create(num_blocks, block_size, shuffle_seed)
+        if not self._p:
+            raise KvcError(KVC_ERR_INVALID_ARG, "kvc_pool_create")
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self):
+        if self._p:
+            lib.kvc_pool_destroy(self._p)
+            self._p = None
+
+    __del__ = close
+
+    def reserve(self, seq_id: int, num_tokens: int) -> None:
+        _check(lib.kvc_pool_reserve(self._p, seq_id, num_tokens), "kvc_pool_reserve")
+
+    def free(self, seq_id: int) -> None:
+        _check(lib.kvc_pool_free(self._p, seq_id), "kvc_pool_free")
+
+    @property
+    def num_free(self) -> int:
+        return lib.kvc_pool_num_free(self._p)
+
+    def num_blocks_of(self, seq_id: int) -> int:
+        return lib.kvc_pool_num_blocks(self._p, seq_id)
+
+    def block_table(self, seq_ids: Sequence[int], max_blocks: int):
+        """``[len(seq_ids)][max_blocks]`` int32 host table (a numpy array)."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int32))
+        table = np.empty((len(ids), max_blocks), dtype=np.int32)
+        _check(lib.kvc_pool_block_table(self._p, ids.ctypes.data, len(ids), max_blocks, table.ctypes.data),
+               "kvc_pool_block_table")
+        return table

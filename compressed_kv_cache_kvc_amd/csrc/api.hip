@@ -1,0 +1,255 @@
+// libkvc entry points: host-side validation, workspace sizing and launches.
+//
+// Every entry point checks its arguments before touching the GPU, so each
+// error status is returned with nothing enqueued. No entry point allocates
+// device memory or synchronizes.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+namespace {
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int32_t device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVC_OK;
+  return fail(KVC_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape and pointer checks shared by every device call.
+int32_t check_cache(const kvc_cache_t* c, const char* name) {
+  if (!c) return fail(KVC_ERR_INVALID_ARG, "%s is NULL", name);
+  if (c->bits != 8 && c->bits != 4) return fail(KVC_ERR_INVALID_ARG, "%s: bits must be 8 or 4 (got %d)", name, c->bits);
+  if (c->batch < 1 || c->num_kv_heads < 1)
+    return fail(KVC_ERR_INVALID_ARG, "%s: batch and num_kv_heads must be >= 1", name);
+  if (c->head_dim != 64 && c->head_dim != 128) {
+    if (c->head_dim > 0 && c->head_dim % 16 == 0 && c->head_dim <= 256)
+      return fail(KVC_ERR_UNSUPPORTED, "%s: head_dim %d is not built (64 and 128 are)", name, c->head_dim);
+    return fail(KVC_ERR_INVALID_ARG, "%s: head_dim must be a multiple of 16 in [16, 256]", name);
+  }
+  if (c->capacity < 1) return fail(KVC_ERR_INVALID_ARG, "%s: capacity must be >= 1", name);
+  if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale || !c->lengths || !c->num_seen)
+    return fail(KVC_ERR_INVALID_ARG, "%s: NULL buffer in the descriptor", name);
+  if (c->block_size == 0) {
+    if (c->block_table) return fail(KVC_ERR_INVALID_ARG, "%s: contiguous cache with a block table", name);
+    if ((long long)c->batch * c->num_kv_heads * c->capacity > (1LL << 40))
+      return fail(KVC_ERR_INVALID_ARG, "%s: cache too large", name);
+  } else if (c->block_size == 16) {
+    if (!c->block_table || c->max_blocks_per_seq < 1 || c->num_blocks < 1)
+      return fail(KVC_ERR_INVALID_ARG, "%s: paged cache needs a block table, max_blocks_per_seq and num_blocks", name);
+    if ((long long)c->max_blocks_per_seq * c->block_size != c->capacity)
+      return fail(KVC_ERR_INVALID_ARG, "%s: paged capacity must equal max_blocks_per_seq * block_size", name);
+    if (c->positions) return fail(KVC_ERR_INVALID_ARG, "%s: paged caches keep no positions", name);
+  } else {
+    return fail(KVC_ERR_UNSUPPORTED, "%s: block_size must be 0 (contiguous) or 16 (got %d)", name, c->block_size);
+  }
+  return KVC_OK;
+}
+
+struct AttnGeom {
+  int splits;
+  size_t off_ml, off_pexp, total;
+};
+
+int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t with_h2o, AttnGeom* g) {
+  int32_t st = check_cache(c, "cache");
+  if (st) return st;
+  if (Hq < 1 || Hq % c->num_kv_heads) return fail(KVC_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int G = Hq / c->num_kv_heads;
+  if (G > 16) return fail(KVC_ERR_INVALID_ARG, "more than 16 query heads per KV head");
+  if (hint < 1) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 1");
+  if (hint > c->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint %d exceeds capacity %d", hint, c->capacity);
+  const int S = (hint + kSplitTokens - 1) / kSplitTokens;
+  if ((long long)S * G > 8192) return fail(KVC_ERR_UNSUPPORTED, "too many splits for one KV head (%d x %d)", S, G);
+  const size_t BH = (size_t)c->batch * Hq;
+  const size_t part_o = align256(BH * S * c->head_dim * sizeof(float));
+  const size_t part_ml = align256(BH * S * 2 * sizeof(float));
+  const size_t pexp = with_h2o ? align256(BH * S * kSplitTokens * sizeof(float)) : 0;
+  g->splits = S;
+  g->off_ml = part_o;
+  g->off_pexp = part_o + part_ml;
+  g->total = part_o + part_ml + pexp;
+  return KVC_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_str(int32_t s) {
+  switch (s) {
+    case KVC_OK: return "KVC_OK";
+    case KVC_ERR_INVALID_ARG: return "KVC_ERR_INVALID_ARG";
+    case KVC_ERR_CAPACITY: return "KVC_ERR_CAPACITY";
+    case KVC_ERR_UNSUPPORTED: return "KVC_ERR_UNSUPPORTED";
+    case KVC_ERR_DEVICE: return "KVC_ERR_DEVICE";
+    default: return "KVC_UNKNOWN";
+  }
+}
+
+const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kvc_quant_append(const kvc_cache_t* cache, const void* k_new, const void* v_new, int32_t n_new,
+                         float* h2o_score, int32_t max_len_hint, void* stream) {
+  clear_error();
+  int32_t st = check_cache(cache, "cache");
+  if (st) return st;
+  if (!k_new || !v_new) return fail(KVC_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+  if (n_new < 1) return fail(KVC_ERR_INVALID_ARG, "n_new must be >= 1");
+  if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
+  if ((long long)max_len_hint + n_new > cache->capacity)
+    return fail(KVC_ERR_CAPACITY, "max_len_hint %d + n_new %d exceeds capacity %d", max_len_hint, n_new,
+                cache->capacity);
+  return device_status(launch_quant_append(*cache, static_cast<const __half*>(k_new),
+                                           static_cast<const __half*>(v_new), n_new, h2o_score,
+                                           static_cast<hipStream_t>(stream)),
+                       "kvc_quant_append launch");
+}
+
+size_t kvc_decode_attn_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_heads, int32_t max_len_hint,
+                                       int32_t with_h2o) {
+  AttnGeom g;
+  if (attn_geometry(cache, num_q_heads, max_len_hint, with_h2o, &g)) return 0;
+  return g.total;
+}
+
+int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_heads, float* out, float* h2o_score,
+                        int32_t max_len_hint, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  AttnGeom g;
+  int32_t st = attn_geometry(cache, num_q_heads, max_len_hint, h2o_score != nullptr, &g);
+  if (st) return st;
+  if (!q || !out) return fail(KVC_ERR_INVALID_ARG, "q and out must not be NULL");
+  if (!workspace || workspace_bytes < g.total)
+    return fail(KVC_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", g.total, workspace ? workspace_bytes : 0);
+  if ((uintptr_t)workspace % 256) return fail(KVC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  AttnLaunch a;
+  a.c = *cache;
+  a.q = static_cast<const __half*>(q);
+  a.out = out;
+  a.score = h2o_score;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + g.off_ml);
+  a.pexp = h2o_score ? reinterpret_cast<float*>(ws + g.off_pexp) : nullptr;
+  a.num_q_heads = num_q_heads;
+  a.splits = g.splits;
+  a.qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
+  return device_status(launch_decode_attn(a, static_cast<hipStream_t>(stream)), "kvc_decode_attn launch");
+}
+
+size_t kvc_h2o_select_workspace_bytes(const kvc_cache_t* cache, int32_t max_len_hint) {
+  (void)cache;
+  (void)max_len_hint;
+  return 0;
+}
+
+int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t budget, int32_t n_sink,
+                       int32_t n_recent, uint8_t* keep_mask, int32_t max_len_hint, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  clear_error();
+  (void)workspace;
+  (void)workspace_bytes;
+  int32_t st = check_cache(cache, "cache");
+  if (st) return st;
+  if (!h2o_score || !keep_mask) return fail(KVC_ERR_INVALID_ARG, "h2o_score and keep_mask must not be NULL");
+  if (budget < 1) return fail(KVC_ERR_INVALID_ARG, "budget must be >= 1");
+  if (n_sink < 0 || n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
+  if ((long long)n_sink + n_recent > budget) return fail(KVC_ERR_INVALID_ARG, "n_sink + n_recent exceeds budget");
+  if (budget > cache->capacity) return fail(KVC_ERR_CAPACITY, "budget exceeds capacity");
+  if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
+  if (max_len_hint > cache->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
+  return device_status(launch_select(*cache, h2o_score, budget, n_sink, n_recent, keep_mask, cache->capacity,
+                                     static_cast<hipStream_t>(stream)),
+                       "kvc_h2o_select launch");
+}
+
+size_t kvc_compact_workspace_bytes(const kvc_cache_t* src, int32_t max_len_hint) {
+  if (check_cache(src, "src") || max_len_hint < 0 || max_len_hint > src->capacity) return 0;
+  const int chunks = max_len_hint > 0 ? (max_len_hint + kCompactChunk - 1) / kCompactChunk : 1;
+  return align256((size_t)src->batch * src->num_kv_heads * chunks * sizeof(int32_t));
+}
+
+int32_t kvc_compact(const kvc_cache_t* src, const float* src_score, const uint8_t* keep_mask, const kvc_cache_t* dst,
+                    float* dst_score, int32_t max_len_hint, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int32_t st = check_cache(src, "src");
+  if (st) return st;
+  if ((st = check_cache(dst, "dst"))) return st;
+  if (src->block_size || dst->block_size) return fail(KVC_ERR_UNSUPPORTED, "compaction of paged caches is not built");
+  if (src->bits != dst->bits || src->batch != dst->batch || src->num_kv_heads != dst->num_kv_heads ||
+      src->head_dim != dst->head_dim || src->capacity != dst->capacity)
+    return fail(KVC_ERR_INVALID_ARG, "src and dst geometries differ");
+  if (!keep_mask) return fail(KVC_ERR_INVALID_ARG, "keep_mask must not be NULL");
+  if ((src_score == nullptr) != (dst_score == nullptr))
+    return fail(KVC_ERR_INVALID_ARG, "pass both src_score and dst_score, or neither");
+  if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
+  if (max_len_hint > src->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
+  const size_t need = kvc_compact_workspace_bytes(src, max_len_hint);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVC_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+  // Out-of-place: no destination buffer may overlap any source buffer.
+  const size_t rows = (size_t)src->batch * src->num_kv_heads * src->capacity;
+  const size_t RB = (size_t)src->head_dim * src->bits / 8;
+  const void* s_bufs[] = {src->k_codes, src->v_codes, src->k_scale, src->v_scale, src->positions, src_score,
+                          keep_mask, src->lengths, src->num_seen};
+  const size_t s_len[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, rows, (size_t)src->batch * 4,
+                          (size_t)src->batch * 4};
+  const void* d_bufs[] = {dst->k_codes, dst->v_codes, dst->k_scale, dst->v_scale, dst->positions, dst_score,
+                          dst->lengths, dst->num_seen, workspace};
+  const size_t d_len[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, (size_t)src->batch * 4,
+                          (size_t)src->batch * 4, need};
+  for (int i = 0; i < 9; ++i)
+    for (int j = 0; j < 9; ++j)
+      if (overlap(s_bufs[i], s_len[i], d_bufs[j], d_len[j]))
+        return fail(KVC_ERR_INVALID_ARG, "dst buffer %d overlaps src buffer %d (compaction is out of place)", j, i);
+  // Kernels read at most `chunks` * kCompactChunk slots per row.
+  const int chunks = max_len_hint > 0 ? (max_len_hint + kCompactChunk - 1) / kCompactChunk : 1;
+  return device_status(launch_compact(*src, src_score, keep_mask, *dst, dst_score, static_cast<int32_t*>(workspace),
+                                      chunks, static_cast<hipStream_t>(stream)),
+                       "kvc_compact launch");
+}
+
+}  // extern "C"

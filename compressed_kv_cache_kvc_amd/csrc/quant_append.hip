@@ -1,0 +1,151 @@
+// Quantize-on-write of new K/V tokens into the compressed cache.
+//
+// Per-token symmetric quantization ("KV Cache optimization techniques"
+// tutorial, section 1.2; INT4 constants from section 1.1; "KV Cache
+// Compression Report", section 3.2): one fp32 scale per (sequence, KV head,
+// token) = max-abs over head_dim / qmax, codes = round-half-even(x / scale)
+// clamped to the code range. Both divisions are correctly rounded fp32
+// divisions and the rounding is v_rndne (half to even), so the codes and
+// scales are reproducible bit for bit.
+//
+// One wave quantizes one row (head_dim fp16 values = D*2 bytes): each lane
+// holds one or two fp16 pairs, the max-abs is a wave reduction, and each lane
+// writes its pair's two codes (2 bytes for INT8, 1 byte for INT4).
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+template <int BITS>
+__device__ __forceinline__ int encode(float x, float s) {
+  constexpr float kMax = BITS == 8 ? 127.f : 7.f;
+  constexpr float kMin = BITS == 8 ? -127.f : -8.f;
+  if (s == 0.f) return 0;
+  float t = rintf(__fdiv_rn(x, s));
+  t = fminf(fmaxf(t, kMin), kMax);
+  return (int)t;
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_pair(uint8_t* codes, int p, int c0, int c1) {
+  if (BITS == 8) {
+    const unsigned short w = (unsigned short)((c0 & 0xFF) | ((c1 & 0xFF) << 8));
+    reinterpret_cast<unsigned short*>(codes)[p] = w;
+  } else {
+    codes[p] = (uint8_t)((c0 & 0xF) | ((c1 & 0xF) << 4));
+  }
+}
+
+// Quantize one row of D <= 256 fp16 values with the calling wave.
+template <int BITS>
+__device__ __forceinline__ void quant_row(const __half* __restrict__ x, uint8_t* __restrict__ codes,
+                                          float* __restrict__ scale_out, int D, int lane) {
+  constexpr float kQmax = BITS == 8 ? 127.f : 7.f;
+  const int P = D >> 1;
+  const __half2* x2 = reinterpret_cast<const __half2*>(x);
+  const bool h0 = lane < P, h1 = lane + 64 < P;
+  float2 v0 = make_float2(0.f, 0.f), v1 = make_float2(0.f, 0.f);
+  if (h0) v0 = __half22float2(x2[lane]);
+  if (h1) v1 = __half22float2(x2[lane + 64]);
+  float a = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v1.x), fabsf(v1.y)));
+  a = wave_max(a);
+  const float s = __fdiv_rn(a, kQmax);
+  if (lane == 0) *scale_out = s;
+  if (h0) store_pair<BITS>(codes, lane, encode<BITS>(v0.x, s), encode<BITS>(v0.y, s));
+  if (h1) store_pair<BITS>(codes, lane + 64, encode<BITS>(v1.x, s), encode<BITS>(v1.y, s));
+}
+
+// Decode-sized appends: one workgroup per sequence does every row of that
+// sequence and then advances its length, so a single launch suffices.
+template <int BITS>
+__global__ __launch_bounds__(1024) void quant_append_seq_kernel(kvc_cache_t c, const __half* __restrict__ kn,
+                                                                const __half* __restrict__ vn, int n_new,
+                                                                float* __restrict__ score) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int L0 = c.lengths[b];
+  const int seen = c.num_seen[b];
+  const int H = c.num_kv_heads, D = c.head_dim, RB = D * BITS / 8;
+  const int rows = H * n_new * 2;
+  for (int r = wave; r < rows; r += 16) {
+    const int kv = r & 1, ht = r >> 1, h = ht / n_new, t = ht - h * n_new;
+    const long long row = cache_row(c, b, h, L0 + t);
+    if (row < 0) continue;
+    const __half* src = (kv ? vn : kn) + (((long long)b * H + h) * n_new + t) * D;
+    uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * RB;
+    quant_row<BITS>(src, dst, (kv ? c.v_scale : c.k_scale) + row, D, lane);
+    if (kv == 0 && lane == 0) {
+      if (c.positions) c.positions[row] = seen + t;
+      if (score) score[((long long)b * H + h) * c.capacity + L0 + t] = 0.f;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    c.lengths[b] = L0 + n_new;
+    c.num_seen[b] = seen + n_new;
+  }
+}
+
+// Prefill-sized appends: four rows per workgroup over the whole grid; the
+// lengths advance in a second launch once every row has read them.
+template <int BITS>
+__global__ __launch_bounds__(256) void quant_append_rows_kernel(kvc_cache_t c, const __half* __restrict__ kn,
+                                                                const __half* __restrict__ vn, int n_new,
+                                                                float* __restrict__ score, long long total) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= total) return;
+  const int H = c.num_kv_heads, D = c.head_dim, RB = D * BITS / 8;
+  const int kv = (int)(r & 1);
+  const long long rest = r >> 1;
+  const int t = (int)(rest % n_new);
+  const long long bh = rest / n_new;
+  const int h = (int)(bh % H), b = (int)(bh / H);
+  const int L0 = c.lengths[b];
+  const long long row = cache_row(c, b, h, L0 + t);
+  if (row < 0) return;
+  const __half* src = (kv ? vn : kn) + rest * D;
+  uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * RB;
+  quant_row<BITS>(src, dst, (kv ? c.v_scale : c.k_scale) + row, D, lane);
+  if (kv == 0 && lane == 0) {
+    if (c.positions) c.positions[row] = c.num_seen[b] + t;
+    if (score) score[bh * c.capacity + L0 + t] = 0.f;
+  }
+}
+
+__global__ void advance_lengths_kernel(int32_t* lengths, int32_t* num_seen, int B, int n) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) {
+    lengths[b] += n;
+    num_seen[b] += n;
+  }
+}
+
+template <int BITS>
+hipError_t launch_bits(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new, float* score,
+                       hipStream_t st) {
+  const long long rows_per_seq = (long long)c.num_kv_heads * n_new * 2;
+  if (rows_per_seq <= 256) {
+    hipLaunchKernelGGL(quant_append_seq_kernel<BITS>, dim3(c.batch), dim3(1024), 0, st, c, kn, vn, n_new,
+                       score);
+    return hipGetLastError();
+  }
+  const long long total = rows_per_seq * c.batch;
+  const long long blocks = (total + 3) / 4;
+  hipLaunchKernelGGL(quant_append_rows_kernel<BITS>, dim3((unsigned)blocks), dim3(256), 0, st, c, kn, vn,
+                     n_new, score, total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(advance_lengths_kernel, dim3((c.batch + 255) / 256), dim3(256), 0, st, c.lengths,
+                     c.num_seen, c.batch, n_new);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_append(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new,
+                               float* score, hipStream_t st) {
+  return c.bits == 8 ? launch_bits<8>(c, kn, vn, n_new, score, st) : launch_bits<4>(c, kn, vn, n_new, score, st);
+}
+
+}  // namespace kvc

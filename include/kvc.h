@@ -1,0 +1,267 @@
+/*
+ * kvc.h - C ABI of libkvc: compressed-KV single-query decode attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * A decode step over a compressed KV cache has four parts, each one call:
+ *   kvc_quant_append  per-token symmetric INT8/INT4 quantize-on-write of K, V
+ *   kvc_decode_attn   softmax(q K^T / sqrt(D)) V with dequantization fused in,
+ *                     plus optional H2O accumulation of attention mass
+ *   kvc_h2o_select    sink + recent-window + top-k heavy-hitter keep mask
+ *   kvc_compact       stable out-of-place compaction of the kept slots
+ * and a host-side paged block pool (kvc_pool_*) that yields block tables.
+ *
+ * Conventions shared by every call:
+ *  - Plain C types only. Device pointers are raw addresses of device memory
+ *    the caller allocated (e.g. from torch tensors); host pointers are named
+ *    "_host". `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *  - The library never allocates or frees device memory, keeps no pointer
+ *    after a call returns, and never synchronizes: a device call validates its
+ *    arguments on the host, enqueues kernels on `stream` and returns. KVC_OK
+ *    means "validated and enqueued". A fault inside a kernel surfaces at the
+ *    caller's next synchronization.
+ *  - Errors are status codes; nothing throws or exits across the ABI.
+ *    kvc_last_error() returns a message for the calling thread's last failure.
+ *    On any error status nothing was enqueued.
+ *  - `max_len_hint` is the caller's upper bound on the cache lengths the call
+ *    will see (device lengths are not read on the host). It sizes the launch
+ *    grid and the workspace and is checked against the capacity. Kernels also
+ *    clamp every device length to the capacity, so a wrong hint cannot make
+ *    them access memory out of bounds; it can only make results wrong.
+ *  - Calls on one stream run in order; calls that write the same buffers must
+ *    not overlap on different streams.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = 1,  /* bad pointer, size, shape or aliasing */
+  KVC_ERR_CAPACITY = 2,     /* not enough cache slots or pool blocks */
+  KVC_ERR_UNSUPPORTED = 3,  /* valid request outside what this build implements */
+  KVC_ERR_DEVICE = 4        /* a HIP runtime call failed; see kvc_last_error() */
+} kvc_status;
+
+/*
+ * Descriptor of one compressed cache (one layer). Plain old data; the caller
+ * owns every buffer it points to.
+ *
+ * Layout (row = one token of one KV head, RB = head_dim * bits / 8 bytes):
+ *  contiguous (block_size == 0):
+ *    k_codes, v_codes  uint8 [batch][num_kv_heads][capacity][RB]
+ *    k_scale, v_scale  fp32  [batch][num_kv_heads][capacity]
+ *    positions         int32 [batch][num_kv_heads][capacity] or NULL
+ *  paged (block_size == 16):
+ *    k_codes, v_codes  uint8 [num_blocks][num_kv_heads][block_size][RB]
+ *    k_scale, v_scale  fp32  [num_blocks][num_kv_heads][block_size]
+ *    block_table       int32 [batch][max_blocks_per_seq], -1 = no block;
+ *                      logical token t of sequence b lives in slot
+ *                      t % block_size of block block_table[b][t / block_size]
+ *    positions         must be NULL; capacity = max_blocks_per_seq * block_size
+ *  both:
+ *    lengths   int32 [batch]  tokens currently held per sequence (all KV heads
+ *                             of a sequence hold the same count)
+ *    num_seen  int32 [batch]  tokens ever appended per sequence
+ *
+ * INT8 codes are two's-complement bytes in [-127, 127]. INT4 codes are
+ * two's-complement nibbles in [-7, 7], element 2j in the low nibble of byte j
+ * and element 2j+1 in the high nibble. A token's value is code * scale.
+ */
+typedef struct kvc_cache {
+  int32_t bits;                /* 8 or 4 */
+  int32_t batch;               /* sequences, >= 1 */
+  int32_t num_kv_heads;        /* >= 1 */
+  int32_t head_dim;            /* 64, 128 or 256 */
+  int32_t capacity;            /* slots per (sequence, KV head) */
+  int32_t block_size;          /* 0 = contiguous, 16 = paged */
+  int32_t max_blocks_per_seq;  /* paged only */
+  int32_t num_blocks;          /* paged only: blocks in the pool arrays */
+  void* k_codes;
+  void* v_codes;
+  float* k_scale;
+  float* v_scale;
+  int32_t* lengths;
+  int32_t* num_seen;
+  int32_t* positions;
+  const int32_t* block_table;
+} kvc_cache_t;
+
+/* ABI version compiled into the library (KVC_ABI_VERSION). */
+int32_t kvc_abi_version(void);
+
+/* Static name of a status code ("KVC_OK", ...); "KVC_UNKNOWN" otherwise. */
+const char* kvc_status_str(int32_t status);
+
+/* Message of the calling thread's last failed call ("" if none). The pointer
+ * stays valid until the thread's next libkvc call. */
+const char* kvc_last_error(void);
+
+/*
+ * Quantize-on-write (per-token symmetric quantization).
+ * Sources: "KV Cache optimization techniques" tutorial, section 1.2 (one scale
+ * per token over head_dim, max-abs / 127) and section 1.1 (INT4: / 7, clamp
+ * [-8, 7]); "KV Cache Compression Report", section 3.2 (quantize K and V when
+ * they are written, never recompute).
+ *
+ * For each sequence b, KV head h and new token t < n_new, with x = the fp16 row
+ * k_new[b][h][t][:] (and likewise v_new):
+ *   scale = amax_d |x_d| / qmax   (qmax 127 or 7; correctly rounded fp32 division)
+ *   code_d = round-half-even(x_d / scale)  (correctly rounded fp32 division),
+ *            clamped to [-127, 127] or [-8, 7]; an all-zero row gets scale 0
+ *            and codes 0.
+ * The row is written at slot lengths[b] + t; positions (if not NULL) get
+ * num_seen[b] + t; h2o_score (if not NULL, [batch][num_kv_heads][capacity]
+ * fp32) is set to 0 at the new slots. lengths[b] and num_seen[b] then advance
+ * by n_new, on the device, in stream order.
+ *
+ * k_new, v_new: device fp16 [batch][num_kv_heads][n_new][head_dim].
+ * Errors: INVALID_ARG for a bad descriptor, NULL inputs or n_new < 1 or
+ * max_len_hint < 0; CAPACITY if max_len_hint + n_new > capacity. Paged: the
+ * blocks for the new slots must already be in the table; slots whose block is
+ * missing are skipped by the kernel.
+ */
+int32_t kvc_quant_append(const kvc_cache_t* cache, const void* k_new, const void* v_new,
+                         int32_t n_new, float* h2o_score, int32_t max_len_hint,
+                         void* stream);
+
+/*
+ * Workspace bytes kvc_decode_attn needs for this cache, head count and length
+ * bound (with_h2o != 0 when an H2O score array will be passed). 0 on invalid
+ * arguments.
+ */
+size_t kvc_decode_attn_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_heads,
+                                       int32_t max_len_hint, int32_t with_h2o);
+
+/*
+ * Decode attention over the compressed cache, dequantization fused.
+ * Sources: "KV Cache Compression Report", section 1.1 (attention =
+ * softmax(Q K^T / sqrt(d)) V) and section 3.2 (the attention kernel reads
+ * K_q * scale_k and V_q * scale_v, dequantizing inside the kernel); section 3.4
+ * (H2O: accumulated attention per token); eviction-and-reuse survey, section
+ * 3.3 (a token's score is the attention it receives from later tokens) and
+ * section 6 (GQA: query heads share KV heads).
+ *
+ * For sequence b and query head h, with G = num_q_heads / num_kv_heads, KV head
+ * g = h / G and L = lengths[b]:
+ *   s_i = (q[b][h] . code^K_i) * scale^K_i / sqrt(head_dim),   i < L
+ *   p_i = exp(s_i - max_j s_j) / sum_j exp(s_j - max_j s_j)
+ *   out[b][h][:] = sum_i p_i * scale^V_i * code^V_i
+ * If h2o_score is not NULL ([batch][num_kv_heads][capacity] fp32):
+ *   h2o_score[b][g][i] += sum over the G query heads of g of p_i.
+ *
+ * q: device fp16 [batch][num_q_heads][head_dim]; out: device fp32
+ * [batch][num_q_heads][head_dim]. workspace: device memory of at least
+ * kvc_decode_attn_workspace_bytes(...) bytes, 256-byte aligned, owned by the
+ * caller; its contents on entry do not matter.
+ * Errors: INVALID_ARG for a bad descriptor, NULL q/out, num_q_heads not a
+ * multiple of num_kv_heads, G > 16, max_len_hint < 1 or a workspace that is
+ * NULL or too small; CAPACITY if max_len_hint > capacity.
+ */
+int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_heads,
+                        float* out, float* h2o_score, int32_t max_len_hint,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kvc_h2o_select needs (may be 0). */
+size_t kvc_h2o_select_workspace_bytes(const kvc_cache_t* cache, int32_t max_len_hint);
+
+/*
+ * Keep-set selection: attention sinks + recent window + heavy hitters.
+ * Sources: "KV Cache Compression Report", section 3.3 (the first 4 tokens
+ * are permanent attention sinks, a window keeps the most recent tokens) and
+ * section 3.4 (keep the top-scoring tokens plus the recent ones, kept indices
+ * sorted); "KV Cache optimization techniques" tutorial, sections 2.2 and 2.4.
+ *
+ * For each (b, g) row with L = lengths[b]:
+ *   L <= budget: keep every slot < L.
+ *   otherwise:   keep slots [0, n_sink) and [L - n_recent, L), plus the
+ *                k = budget - n_sink - n_recent slots of [n_sink, L - n_recent)
+ *                with the largest h2o_score; equal scores go to the lower slot.
+ * keep_mask: device uint8 [batch][num_kv_heads][capacity]; slots < L get 1 or 0,
+ * slots >= L are left untouched. h2o_score must hold non-negative, non-NaN
+ * values (attention mass always is).
+ * Errors: INVALID_ARG for a bad descriptor, NULL pointers, budget < 1,
+ * n_sink < 0, n_recent < 0, n_sink + n_recent > budget, or a workspace
+ * smaller than required; CAPACITY if budget or max_len_hint > capacity.
+ */
+int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t budget,
+                       int32_t n_sink, int32_t n_recent, uint8_t* keep_mask,
+                       int32_t max_len_hint, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Workspace bytes kvc_compact needs. */
+size_t kvc_compact_workspace_bytes(const kvc_cache_t* src, int32_t max_len_hint);
+
+/*
+ * Stable out-of-place compaction of the kept slots.
+ * Sources: "KV Cache optimization techniques" tutorial, section 2.2 (kept
+ * indices sorted, and the attention scores move with the kept K/V); "KV Cache
+ * Compression Report", section 3.4 (the kept list is sorted).
+ *
+ * For each (b, g) row, the slots i < lengths[b] with keep_mask[b][g][i] != 0
+ * are copied, in ascending order, to slots 0, 1, ... of dst: K and V codes and
+ * scales, positions (when both src and dst have them) and h2o scores (when
+ * src_score and dst_score are both given). dst->lengths[b] is set to the count
+ * kept by KV head 0 (every head of a sequence must keep the same count, as
+ * kvc_h2o_select guarantees) and dst->num_seen[b] to src->num_seen[b].
+ * Slots of dst at or beyond the new length are left untouched.
+ *
+ * src and dst must be contiguous caches with the same bits, batch,
+ * num_kv_heads, head_dim and capacity; no dst buffer may overlap a src buffer,
+ * the mask or the src scores (INVALID_ARG otherwise); paged caches give
+ * UNSUPPORTED. workspace: device memory of kvc_compact_workspace_bytes(...).
+ */
+int32_t kvc_compact(const kvc_cache_t* src, const float* src_score, const uint8_t* keep_mask,
+                    const kvc_cache_t* dst, float* dst_score, int32_t max_len_hint,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged block pool (host only; no device memory is touched).
+ * Source: "KV Cache optimization techniques" tutorial, section 3.2
+ * (PagedAttention): fixed-size blocks, a per-sequence block list, a reference
+ * count per block and a free set; allocation fails without side effects when
+ * blocks run short; freeing an unknown sequence does nothing; an unknown
+ * sequence is an error when its blocks are asked for.
+ *
+ * The free list is shuffled with `shuffle_seed` (0 = identity order), so block
+ * placement is a seeded permutation of the pool. Pools are not thread-safe.
+ */
+typedef struct kvc_pool kvc_pool_t;
+
+/* NULL on num_blocks < 1, block_size < 1 or allocation failure. */
+kvc_pool_t* kvc_pool_create(int32_t num_blocks, int32_t block_size, uint64_t shuffle_seed);
+void kvc_pool_destroy(kvc_pool_t* pool);
+
+/* Make sequence seq_id (>= 0) hold at least num_tokens tokens, growing an
+ * existing reservation. All or nothing: CAPACITY and no change if free blocks
+ * are short; INVALID_ARG for seq_id < 0 or num_tokens < 0. */
+int32_t kvc_pool_reserve(kvc_pool_t* pool, int32_t seq_id, int32_t num_tokens);
+
+/* Drop the sequence's reference on each of its blocks; blocks whose count
+ * reaches 0 return to the free list. OK (no-op) for an unknown seq_id. */
+int32_t kvc_pool_free(kvc_pool_t* pool, int32_t seq_id);
+
+/* Blocks on the free list (-1 for a NULL pool). */
+int32_t kvc_pool_num_free(const kvc_pool_t* pool);
+
+/* Blocks held by seq_id, or -1 if it is unknown. */
+int32_t kvc_pool_num_blocks(const kvc_pool_t* pool, int32_t seq_id);
+
+/* Fill table_host [batch][max_blocks] with each listed sequence's blocks in
+ * logical order, padded with -1. INVALID_ARG for an unknown seq_id, NULL
+ * pointers or batch < 1; CAPACITY if a sequence holds more than max_blocks. */
+int32_t kvc_pool_block_table(const kvc_pool_t* pool, const int32_t* seq_ids_host,
+                             int32_t batch, int32_t max_blocks, int32_t* table_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

@@ -1,0 +1,210 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load on a machine without a GPU, export every function that
+include/kvc.h declares, and reject bad arguments on the host with the
+documented status before any kernel launch. The block pool is pure host code
+and is tested fully here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+kvc = pytest.importorskip("compressed_kv_cache_kvc_amd")
+lib = kvc.lib
+
+OK, INVALID, CAPACITY, UNSUPPORTED = 0, 1, 2, 3
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_exports_match_binding_names():
+    for n in declared_functions():
+        if not n.startswith("kvc_pool_"):
+            assert hasattr(kvc, n), f"binding lacks {n}"
+
+
+def test_version_and_status_strings():
+    assert kvc.kvc_abi_version() == 1
+    assert kvc.kvc_status_str(0) == "KVC_OK"
+    assert kvc.kvc_status_str(2) == "KVC_ERR_CAPACITY"
+    assert kvc.kvc_status_str(99) == "KVC_UNKNOWN"
+
+
+def desc(**kw):
+    d = kvc.KvcCacheDesc()
+    d.bits, d.batch, d.num_kv_heads, d.head_dim, d.capacity = 8, 1, 4, 64, 512
+    d.block_size = d.max_blocks_per_seq = d.num_blocks = 0
+    d.k_codes = d.v_codes = d.k_scale = d.v_scale = d.lengths = d.num_seen = FAKE
+    d.positions = FAKE
+    d.block_table = None
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def append(d, k=FAKE, v=FAKE, n=1, hint=0):
+    return lib.kvc_quant_append(ctypes.byref(d), k, v, n, None, hint, None)
+
+
+def attn(d, hq=4, hint=16, ws=FAKE * 256, nbytes=1 << 30, q=FAKE, out=FAKE, score=None):
+    return lib.kvc_decode_attn(ctypes.byref(d), q, hq, out, score, hint, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("bits", 3, INVALID), ("bits", 16, INVALID), ("batch", 0, INVALID), ("num_kv_heads", 0, INVALID),
+    ("head_dim", 96, UNSUPPORTED), ("head_dim", 100, INVALID), ("capacity", 0, INVALID),
+    ("k_codes", None, INVALID), ("lengths", None, INVALID), ("block_size", 8, UNSUPPORTED),
+])
+def test_descriptor_validation(field, value, status):
+    d = desc(**{field: value})
+    assert append(d) == status
+    assert kvc.kvc_last_error() != ""
+    assert attn(d) == status
+
+
+def test_paged_descriptor_rules():
+    d = desc(block_size=16, max_blocks_per_seq=4, num_blocks=8, capacity=64, positions=None)
+    assert append(d) == INVALID                       # no block table
+    d.block_table = FAKE
+    d.capacity = 60
+    assert append(d) == INVALID                       # capacity != blocks * 16
+    d.capacity = 64
+    d.positions = FAKE
+    assert append(d) == INVALID                       # paged keeps no positions
+
+
+def test_append_validation():
+    d = desc()
+    assert append(d, k=None) == INVALID
+    assert append(d, n=0) == INVALID
+    assert append(d, hint=-1) == INVALID
+    assert append(d, hint=512) == CAPACITY
+    assert append(d, hint=500, n=13) == CAPACITY
+
+
+def test_decode_attn_validation():
+    d = desc()
+    assert attn(d, hq=6) == INVALID                   # not a multiple of 4 KV heads
+    assert attn(d, hq=4 * 17) == INVALID              # more than 16 q heads per KV head
+    assert attn(d, hint=0) == INVALID
+    assert attn(d, hint=513) == CAPACITY
+    assert attn(d, q=None) == INVALID
+    assert attn(d, ws=None) == INVALID
+    need = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), 4, 16, 0)
+    assert need > 0
+    assert attn(d, nbytes=need - 1) == INVALID
+    assert attn(d, ws=FAKE * 256 + 4) == INVALID      # misaligned workspace
+    assert lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), 4, 16, 1) > need
+    assert lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), 6, 16, 0) == 0
+
+
+def test_select_validation():
+    d = desc()
+    sel = lambda budget, s, r, hint=16, score=FAKE, mask=FAKE: lib.kvc_h2o_select(
+        ctypes.byref(d), score, budget, s, r, mask, hint, None, 0, None)
+    assert sel(0, 0, 0) == INVALID
+    assert sel(8, 5, 4) == INVALID
+    assert sel(8, -1, 0) == INVALID
+    assert sel(513, 4, 4) == CAPACITY
+    assert sel(8, 2, 2, score=None) == INVALID
+    assert sel(8, 2, 2, hint=600) == CAPACITY
+
+
+def test_compact_validation():
+    src = desc(k_codes=0x100000, v_codes=0x200000, k_scale=0x300000, v_scale=0x400000,
+               positions=0x500000, lengths=0x600000, num_seen=0x600100)
+    dst = desc(k_codes=0x1100000, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
+               positions=0x1500000, lengths=0x1600000, num_seen=0x1600100)
+    mask, ws = 0x2000000, 0x3000000
+    call = lambda s, d, ss=None, dsc=None, hint=16, w=ws, n=1 << 20: lib.kvc_compact(
+        ctypes.byref(s), ss, mask, ctypes.byref(d), dsc, hint, w, n, None)
+    bad = desc(k_codes=0x1100000, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
+               positions=0x1500000, lengths=0x1600000, num_seen=0x600100)   # aliases src.num_seen
+    assert call(src, bad) == INVALID
+    alias = desc(k_codes=0x100000 + 64, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
+                 positions=0x1500000, lengths=0x1600000, num_seen=0x1600100)
+    assert call(src, alias) == INVALID
+    other = desc(k_codes=0x1100000, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
+                 positions=0x1500000, lengths=0x1600000, num_seen=0x1600100, capacity=256)
+    assert call(src, other) == INVALID
+    assert call(src, dst, ss=0x4000000) == INVALID    # one score array without the other
+    assert call(src, dst, w=None) == INVALID
+    assert call(src, dst, hint=513) == CAPACITY
+    paged = desc(block_size=16, max_blocks_per_seq=32, num_blocks=8, positions=None, block_table=FAKE)
+    assert call(paged, dst) == UNSUPPORTED
+    assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 512) >= 4 * 1 * 4
+    assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 2048) == 0   # beyond capacity
+
+
+# -- block pool -----------------------------------------------------------------
+
+def test_pool_all_or_nothing_and_free():
+    p = kvc.BlockPool(10, 16, shuffle_seed=0)
+    assert p.num_free == 10
+    p.reserve(1, 33)                     # 3 blocks
+    assert p.num_free == 7 and p.num_blocks_of(1) == 3
+    with pytest.raises(kvc.KvcError) as e:
+        p.reserve(2, 16 * 8)             # needs 8, 7 free
+    assert e.value.status == CAPACITY
+    assert p.num_free == 7 and p.num_blocks_of(2) == -1
+    p.reserve(1, 48)                     # still 3 blocks: no change
+    assert p.num_free == 7
+    p.reserve(1, 49)                     # grows by one
+    assert p.num_blocks_of(1) == 4 and p.num_free == 6
+    p.free(1)
+    assert p.num_free == 10
+    p.free(12345)                        # unknown: no-op
+    assert p.num_free == 10
+
+
+def test_pool_block_table():
+    p = kvc.BlockPool(8, 16, shuffle_seed=0)
+    p.reserve(5, 20)
+    p.reserve(9, 1)
+    t = p.block_table([5, 9], 4)
+    assert t.tolist() == [[0, 1, -1, -1], [2, -1, -1, -1]]
+    with pytest.raises(kvc.KvcError):
+        p.block_table([5, 77], 4)        # unknown sequence
+    with pytest.raises(kvc.KvcError) as e:
+        p.block_table([5], 1)            # holds 2 > 1
+    assert e.value.status == CAPACITY
+
+
+def test_pool_seeded_permutation():
+    p = kvc.BlockPool(64, 16, shuffle_seed=1234)
+    p.reserve(0, 64 * 16)
+    t = p.block_table([0], 64)[0]
+    assert sorted(t.tolist()) == list(range(64))
+    assert t.tolist() != list(range(64))
+    q = kvc.BlockPool(64, 16, shuffle_seed=1234)
+    q.reserve(0, 64 * 16)
+    assert np.array_equal(q.block_table([0], 64)[0], t)
+    assert p.num_free == 0
+    with pytest.raises(kvc.KvcError):
+        p.reserve(1, 1)
+
+
+def test_pool_bad_args():
+    assert lib.kvc_pool_create(0, 16, 0) is None
+    assert lib.kvc_pool_num_free(None) == -1
+    p = kvc.BlockPool(4, 16)
+    with pytest.raises(kvc.KvcError):
+        p.reserve(-1, 5)

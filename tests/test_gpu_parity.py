@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs are the seeded workload arrays; both sides get the same fp16 bits.
+Sizes span several 256-token splits with a ragged tail; the LLaMA-7B-shaped
+8192-token layer runs at full size in the launch configuration the benchmark
+times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import draw, get
+
+from kvc_testlib import (assert_codes_equal, assert_keep_equivalent, assert_out_close, assert_scores_close, dev,
+                         host, make_gpu_cache, prefill_both)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+kvc = pytest.importorskip("compressed_kv_cache_kvc_amd")
+
+
+def _attend_both(gc, ref, q16, score):
+    out = torch.empty((q16.shape[0], q16.shape[1], gc.head_dim), dtype=torch.float32, device="cuda")
+    kvc.kvc_decode_attn(gc, dev(q16), out, h2o_score=score)
+    ro, _ = ref.attend(q16, h2o=score is not None)
+    torch.cuda.synchronize()
+    return host(out), ro
+
+
+# ---------------------------------------------------------------- quantize ---
+
+@pytest.mark.parametrize("name,bits,L", [
+    ("tiny_mha", 8, 512), ("tiny_mha", 4, 512), ("tiny_mha", 8, 1), ("tiny_mha", 8, 300),
+    ("llama7b_8k", 8, 8192), ("llama70b_int4", 4, 1100), ("qwen_gqa_stream", 8, 777),
+])
+def test_quant_append_bit_exact(name, bits, L):
+    w = get(name).scaled(context=L, batch=min(get(name).batch, 2))
+    print(f"[quant] {name} bits={bits} L={L}", flush=True)
+    d = draw(w)
+    gc, ref, _ = prefill_both(w, d, bits=bits)
+    torch.cuda.synchronize()
+    assert_codes_equal(gc, ref)
+    assert host(gc.num_seen).tolist() == [L] * w.batch
+
+
+def test_quant_zero_rows_and_halfway_cases():
+    """All-zero rows give scale 0 and code 0; amax = 127 rows hit exact halves."""
+    w = get("tiny_mha").scaled(context=4)
+    k = np.zeros((1, 4, 4, 64), np.float16)
+    k[0, 1, :, 0] = 127.0
+    k[0, 1, :, 1:12] = np.array([2.5, 3.5, -2.5, -3.5, 126.5, 0.5, -0.5, 1.5, 6.5, -6.5, 100.5], np.float16)
+    v = -k
+    d = {"k": k, "v": v}
+    for bits in (8, 4):
+        gc, ref, _ = prefill_both(w, d, capacity=8, bits=bits)
+        torch.cuda.synchronize()
+        assert_codes_equal(gc, ref)
+
+
+# ---------------------------------------------------------------- attention --
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("L", [1, 255, 256, 257, 512, 1000])
+def test_decode_attn_tiny(bits, L):
+    w = get("tiny_mha").scaled(context=L)
+    print(f"[attn] tiny bits={bits} L={L}", flush=True)
+    d = draw(w)
+    gc, ref, score = prefill_both(w, d, bits=bits)
+    out, ro = _attend_both(gc, ref, d["q"], score)
+    assert_out_close(out, ro)
+    assert_scores_close(host(score), ref.score, ref.lengths)
+
+
+@pytest.mark.parametrize("hq,hkv,bits,D", [(8, 2, 8, 128), (28, 4, 8, 128), (16, 2, 4, 128), (12, 4, 8, 64),
+                                           (6, 3, 4, 64), (64, 8, 4, 128)])
+def test_decode_attn_gqa(hq, hkv, bits, D):
+    w = get("qwen_gqa_stream").scaled(num_q_heads=hq, num_kv_heads=hkv, head_dim=D, bits=bits, batch=2,
+                                      context=1333)
+    print(f"[attn] gqa hq={hq} hkv={hkv} bits={bits} D={D}", flush=True)
+    d = draw(w)
+    gc, ref, score = prefill_both(w, d)
+    out, ro = _attend_both(gc, ref, d["q"], score)
+    assert_out_close(out, ro)
+    assert_scores_close(host(score), ref.score, ref.lengths)
+
+
+def test_decode_attn_is_deterministic():
+    w = get("tiny_mha").scaled(context=700, num_q_heads=8, num_kv_heads=2)
+    d = draw(w)
+    gc, _, _ = prefill_both(w, d)
+    outs = []
+    for _ in range(2):
+        o = torch.empty((1, 8, 64), dtype=torch.float32, device="cuda")
+        s = gc.score_buffer()
+        kvc.kvc_decode_attn(gc, dev(d["q"]), o, h2o_score=s)
+        outs.append((host(o), host(s)))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
+
+def test_empty_sequence_gives_zero_output():
+    gc = kvc.KVCache(2, 2, 64, 64, 8)
+    w = get("tiny_mha").scaled(context=5, num_q_heads=2, num_kv_heads=2, batch=1)
+    d = draw(w)
+    # Sequence 0 gets 5 tokens, sequence 1 stays empty (length 0).
+    k = np.concatenate([d["k"], np.zeros_like(d["k"])])
+    kvc.kvc_quant_append(gc, dev(k), dev(k))
+    gc.lengths[1] = 0
+    out = torch.full((2, 2, 64), 7.0, dtype=torch.float32, device="cuda")
+    kvc.kvc_decode_attn(gc, dev(np.concatenate([d["q"], d["q"]])), out, max_len_hint=5)
+    o = host(out)
+    assert np.all(o[1] == 0) and np.all(np.isfinite(o[0]))
+
+
+# ---------------------------------------------------------- select/compact --
+
+@pytest.mark.parametrize("L,budget,S,R", [(512, 128, 4, 64), (3000, 1000, 4, 100), (9000, 2457, 4, 1024),
+                                          (100, 100, 4, 10), (99, 100, 4, 10), (300, 20, 10, 10),
+                                          (5000, 5000 - 1, 4, 2048)])
+def test_select_bit_exact_on_shared_scores(L, budget, S, R):
+    """Same fp32 scores on both sides: the keep masks must be identical,
+    including ties (broken toward the lower slot)."""
+    rng = np.random.default_rng(L + budget)
+    B, H = 2, 3
+    sc = rng.random((B, H, L)).astype(np.float32) * 3
+    sc[:, :, ::7] = np.float32(0.5)          # large tie classes
+    sc[:, 1, :] = np.float32(1.0)            # one row of all-equal scores
+    sc[:, 2, ::3] = 0.0
+    cap = max(L, budget)
+    gc = kvc.KVCache(B, H, 64, cap, 8)
+    gc.lengths.fill_(L)
+    score = dev(np.pad(sc, ((0, 0), (0, 0), (0, cap - L))))
+    mask = torch.full((B, H, cap), 9, dtype=torch.uint8, device="cuda")
+    kvc.kvc_h2o_select(gc, score, budget, S, R, mask, max_len_hint=L)
+    m = host(mask)
+    assert np.all(m[:, :, L:] == 9)          # slots past the length are untouched
+    m = m[:, :, :L].astype(bool)
+    for b in range(B):
+        for g in range(H):
+            ref = oracle.select_keep(sc[b, g].astype(np.float64), L, budget, S, R)
+            assert np.array_equal(m[b, g], ref), (b, g)
+
+
+@pytest.mark.parametrize("bits,D", [(8, 128), (4, 128), (8, 64)])
+def test_compact_bit_exact(bits, D):
+    rng = np.random.default_rng(7 + bits + D)
+    B, H, L, cap, keep_n = 2, 3, 2500, 2600, 900
+    w = get("tiny_mha").scaled(context=L, batch=B, num_q_heads=H, num_kv_heads=H, head_dim=D, bits=bits)
+    d = draw(w)
+    gc, ref, score = prefill_both(w, d, capacity=cap)
+    sc = rng.random((B, H, cap)).astype(np.float32)
+    score.copy_(dev(sc))
+    mask = np.zeros((B, H, cap), np.uint8)
+    for b in range(B):
+        for g in range(H):
+            mask[b, g, rng.choice(L, keep_n, replace=False)] = 1
+    dst = make_gpu_cache(w, cap, bits)
+    dst_score = dst.score_buffer()
+    kvc.kvc_compact(gc, score, dev(mask), dst, dst_score)
+    torch.cuda.synchronize()
+    ref.score[:] = sc
+    ref.compact(mask.astype(bool))
+    assert_codes_equal(dst, ref)
+    assert np.array_equal(host(dst_score)[:, :, :keep_n], sc[np.nonzero(mask)].reshape(B, H, keep_n))
+    assert host(dst.num_seen).tolist() == [L] * B
+
+
+# ------------------------------------------------------- whole decode step --
+
+def _full_step(w, d, prior=()):
+    gc, ref, score = prefill_both(w, d)
+    for pq in prior:
+        _attend_both(gc, ref, pq, score)
+    out, ro = _attend_both(gc, ref, d["q"], score)
+    err = assert_out_close(out, ro)
+    rel = assert_scores_close(host(score), ref.score, ref.lengths)
+    mask = torch.zeros((w.batch, w.num_kv_heads, gc.capacity), dtype=torch.uint8, device="cuda")
+    kvc.kvc_h2o_select(gc, score, w.budget, w.n_sink, w.n_recent, mask)
+    torch.cuda.synchronize()
+    amb = assert_keep_equivalent(host(mask), ref.score, ref.lengths, w.budget, w.n_sink, w.n_recent)
+    # Compact on the GPU with the oracle's mask so that both caches keep the
+    # same tokens, then compare the compacted caches bit for bit.
+    keep_ref = ref.select(w.budget, w.n_sink, w.n_recent)
+    dst = make_gpu_cache(w, gc.capacity)
+    dst_score = dst.score_buffer()
+    kvc.kvc_compact(gc, score, dev(keep_ref.astype(np.uint8)), dst, dst_score)
+    torch.cuda.synchronize()
+    ref.compact(keep_ref)
+    assert_codes_equal(dst, ref)
+    print(f"max-abs out err {err:.2e}, worst score rel err {rel:.2e}, ambiguous {amb}", flush=True)
+    return dst, ref
+
+
+def test_tiny_mha_full_schedule():
+    w = get("tiny_mha")
+    d = draw(w)
+    _full_step(w, d, prior=list(d["prior_q"]))
+
+
+def test_llama7b_8k_full_size():
+    """The benchmarked workload at full size: 32 heads, D=128, 8192 tokens,
+    outlier channels, keep 2457 = 4 + 1024 + 1429."""
+    w = get("llama7b_8k")
+    print("[step] llama7b_8k full size", flush=True)
+    d = draw(w)
+    _full_step(w, d)
+
+
+def test_int4_70b_shape_reduced():
+    w = get("llama70b_int4").scaled(context=6000, batch=1, budget=1200, n_recent=256)
+    print("[step] 70B-shaped INT4, L=6000", flush=True)
+    d = draw(w)
+    _full_step(w, d)
+
+
+# ------------------------------------------------------------------ paged ---
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_paged_decode_reduced(bits):
+    w = get("paged_b32").scaled(batch=4, num_q_heads=8, num_kv_heads=4, bits=bits, len_lo=100, len_hi=700)
+    print(f"[paged] bits={bits}", flush=True)
+    d = draw(w)
+    B, H, D, bs = w.batch, w.num_kv_heads, w.head_dim, w.paged_block
+    table = d["block_table"]
+    nb = int(d["num_blocks"])
+    lengths = d["lengths"]
+    gc = kvc.KVCache(B, H, D, 0, bits, block_size=bs, num_blocks=nb, max_blocks_per_seq=table.shape[1])
+    gc.block_table.copy_(dev(table))
+    # Append each sequence's tokens in two pieces of a common count, padding the
+    # short sequences' second piece is not possible with one call, so append
+    # per sequence with a one-sequence view of the same pool.
+    rb = D * bits // 8
+    kp = np.zeros((nb, H, bs, D), np.int8)
+    vp = np.zeros((nb, H, bs, D), np.int8)
+    ksp = np.zeros((nb, H, bs), np.float32)
+    vsp = np.zeros((nb, H, bs), np.float32)
+    for b in range(B):
+        one = kvc.KvcCacheDesc.from_buffer_copy(gc.desc)
+        one.batch = 1
+        one.block_table = gc.block_table[b].data_ptr()
+        one.lengths = gc.lengths[b:b + 1].data_ptr()
+        one.num_seen = gc.num_seen[b:b + 1].data_ptr()
+        L = int(lengths[b])
+        kvc.kvc_quant_append(one, dev(d["k_seq"][b][None]), dev(d["v_seq"][b][None]), max_len_hint=0)
+        lens = np.zeros(1, np.int64)
+        oracle.paged_append(kp, ksp, vp, vsp, table[b:b + 1], lens, d["k_seq"][b][None], d["v_seq"][b][None],
+                            bits, bs)
+    torch.cuda.synchronize()
+    assert host(gc.lengths).tolist() == lengths.tolist()
+    used = table[table >= 0]
+    kc = host(gc.k_codes)[used]
+    want = kp[used].view(np.uint8) if bits == 8 else oracle.pack_int4(kp[used])
+    # Slots past a sequence's length inside its last block hold zeros on both sides.
+    assert np.array_equal(kc, want)
+    assert np.array_equal(host(gc.k_scale)[used].view(np.uint32), ksp[used].view(np.uint32))
+    out = torch.empty((B, w.num_q_heads, D), dtype=torch.float32, device="cuda")
+    kvc.kvc_decode_attn(gc, dev(d["q"]), out, max_len_hint=int(lengths.max()))
+    ro = oracle.paged_decode_attention(d["q"], kp, ksp, vp, vsp, table, lengths, bs)
+    torch.cuda.synchronize()
+    assert_out_close(host(out), ro)
+    assert rb == kc.shape[-1]
