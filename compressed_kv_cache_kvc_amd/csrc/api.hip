@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "kvc_internal.h"
@@ -78,10 +79,14 @@ int32_t check_cache(const kvc_cache_t* c, const char* name) {
 }
 
 struct AttnGeom {
-  int splits;
-  size_t off_ml, off_pexp, total;
+  int splits, tiles;
+  size_t off_ml, off_logits, total;
 };
 
+// Launch geometry of the decode-attention kernels. A split covers `tiles`
+// 256-token tiles; tiles are grouped so that the grid still has about 1024
+// workgroups (4 per CU on 256 CUs), which keeps the cross-split merge short
+// for long contexts.
 int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t with_h2o, AttnGeom* g) {
   int32_t st = check_cache(c, "cache");
   if (st) return st;
@@ -90,16 +95,28 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
   if (G > 16) return fail(KVC_ERR_INVALID_ARG, "more than 16 query heads per KV head");
   if (hint < 1) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 1");
   if (hint > c->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint %d exceeds capacity %d", hint, c->capacity);
-  const int S = (hint + kSplitTokens - 1) / kSplitTokens;
-  if ((long long)S * G > 8192) return fail(KVC_ERR_UNSUPPORTED, "too many splits for one KV head (%d x %d)", S, G);
+  const long long rb = (long long)c->head_dim * c->bits / 8;
+  if ((long long)c->capacity * rb >= (1LL << 32) - 4096)
+    return fail(KVC_ERR_UNSUPPORTED, "one (sequence, KV head) row must stay below 4 GiB");
+  if (c->block_size && (long long)c->num_blocks * c->num_kv_heads * c->block_size * rb >= (1LL << 32))
+    return fail(KVC_ERR_UNSUPPORTED, "paged pools must stay below 4 GiB of codes");
+  const long long tiles_total = (hint + kSplitTokens - 1) / kSplitTokens;
+  long long nt = 1;
+  if (G <= attn_heads_per_pass(G)) {
+    const long long rows = (long long)c->batch * c->num_kv_heads;
+    nt = std::max(1LL, tiles_total * rows / 1024);
+  }
+  const long long S = (tiles_total + nt - 1) / nt;
+  if (S * (G + 2) > 16384) return fail(KVC_ERR_UNSUPPORTED, "too many splits for one KV head (%lld x %d)", S, G);
   const size_t BH = (size_t)c->batch * Hq;
   const size_t part_o = align256(BH * S * c->head_dim * sizeof(float));
   const size_t part_ml = align256(BH * S * 2 * sizeof(float));
-  const size_t pexp = with_h2o ? align256(BH * S * kSplitTokens * sizeof(float)) : 0;
-  g->splits = S;
+  const size_t logits = with_h2o ? align256(BH * S * nt * kSplitTokens * sizeof(float)) : 0;
+  g->splits = (int)S;
+  g->tiles = (int)nt;
   g->off_ml = part_o;
-  g->off_pexp = part_o + part_ml;
-  g->total = part_o + part_ml + pexp;
+  g->off_logits = part_o + part_ml;
+  g->total = part_o + part_ml + logits;
   return KVC_OK;
 }
 
@@ -173,9 +190,10 @@ int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_h
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.part_o = reinterpret_cast<float*>(ws);
   a.part_ml = reinterpret_cast<float*>(ws + g.off_ml);
-  a.pexp = h2o_score ? reinterpret_cast<float*>(ws + g.off_pexp) : nullptr;
+  a.logits = h2o_score ? reinterpret_cast<float*>(ws + g.off_logits) : nullptr;
   a.num_q_heads = num_q_heads;
   a.splits = g.splits;
+  a.tiles = g.tiles;
   a.qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
   return device_status(launch_decode_attn(a, static_cast<hipStream_t>(stream)), "kvc_decode_attn launch");
 }
@@ -201,7 +219,8 @@ int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t
   if (budget > cache->capacity) return fail(KVC_ERR_CAPACITY, "budget exceeds capacity");
   if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
   if (max_len_hint > cache->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
-  return device_status(launch_select(*cache, h2o_score, budget, n_sink, n_recent, keep_mask, cache->capacity,
+  // The kernel reads at most max_len_hint slots per row.
+  return device_status(launch_select(*cache, h2o_score, budget, n_sink, n_recent, keep_mask, max_len_hint,
                                      static_cast<hipStream_t>(stream)),
                        "kvc_h2o_select launch");
 }

@@ -2,71 +2,76 @@
 //
 // The kept slots keep their relative (ascending) order and carry their scores
 // with them ("KV Cache optimization techniques" tutorial, section 2.2; "KV
-// Cache Compression Report", section 3.4). The destination slot of a kept
-// slot is the number of kept slots before it: an exclusive prefix sum of the
-// mask. Two launches: per-chunk counts, then each chunk adds the counts of
-// the chunks before it, scans its own 1024 slots and moves the kept rows.
-// Reading src and writing dst, which may not overlap, removes every race.
+// Cache Compression Report", section 3.4). The destination of a kept slot is
+// the number of kept slots before it: an exclusive prefix sum of the mask.
+//
+// A 256-thread workgroup owns a 256-slot chunk of one (sequence, KV head) row,
+// one slot per thread. Its offset is the count of kept slots in the chunks
+// before it: for rows of up to 64 chunks the workgroup counts them straight
+// from the mask (one launch); longer rows get a first launch that writes
+// per-chunk counts. A block scan of the chunk's flags gives each kept slot its
+// destination and lists the kept slots in LDS; the rows are then copied
+// cooperatively, RB/16 lanes per row with 16-byte accesses, and every load of
+// the chunk is issued before the first store so that the copy is bound by
+// bandwidth rather than latency. Reading src and writing dst, which may not
+// overlap, removes every race.
 #include "kvc_internal.h"
 
 namespace kvc {
 namespace {
 
 constexpr int CH = kCompactChunk;
-constexpr int NT = 256;
-constexpr int PER = CH / NT;
+constexpr int NT = CH;  // one slot per thread
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int block_sum(int v, int* tmp) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
   __syncthreads();
-  const int r = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) r += tmp[w];
   __syncthreads();
   return r;
+}
+
+// Number of nonzero bytes in a 32-bit word.
+__device__ __forceinline__ int nonzero_bytes(unsigned x) {
+  return __popc((((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u);
+}
+
+__device__ __forceinline__ int row_length(const kvc_cache_t& c, int b, int chunks) {
+  return __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), chunks * CH));
 }
 
 __global__ __launch_bounds__(NT) void compact_count_kernel(kvc_cache_t src, const uint8_t* __restrict__ mask,
                                                            int32_t* __restrict__ counts, int chunks) {
   const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int L = min(min(src.lengths[b], src.capacity), chunks * CH);
+  const int L = row_length(src, b, chunks);
   const uint8_t* m = mask + ((long long)b * src.num_kv_heads + g) * src.capacity;
-  int n = 0;
-  for (int q = 0; q < PER; ++q) {
-    const int i = ch * CH + q * NT + threadIdx.x;
-    if (i < L) n += m[i] != 0;
-  }
-  __shared__ int tmp[4];
-  n = block_sum(n, tmp);
+  const int i = ch * CH + threadIdx.x;
+  __shared__ int tmp[NT / 64];
+  const int n = block_sum(i < L && m[i] != 0, tmp);
   if (threadIdx.x == 0) counts[((long long)b * src.num_kv_heads + g) * chunks + ch] = n;
 }
 
-template <int RB>
-__device__ __forceinline__ void copy_row(const uint8_t* __restrict__ s, uint8_t* __restrict__ d) {
-  if (RB % 16 == 0) {
-#pragma unroll
-    for (int i = 0; i < RB / 16; ++i) reinterpret_cast<uint4*>(d)[i] = reinterpret_cast<const uint4*>(s)[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < RB / 8; ++i) reinterpret_cast<uint2*>(d)[i] = reinterpret_cast<const uint2*>(s)[i];
-  }
-}
-
-template <int RB>
+template <int RB, bool RECOUNT>
 __global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const float* __restrict__ src_score,
                                                           const uint8_t* __restrict__ mask, kvc_cache_t dst,
                                                           float* __restrict__ dst_score,
                                                           const int32_t* __restrict__ counts, int chunks) {
+  constexpr int LPR = RB / 16;        // lanes per row
+  constexpr int RPP = NT / LPR;       // rows per pass
   const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int H = src.num_kv_heads;
-  const int L = min(min(src.lengths[b], src.capacity), chunks * CH);
+  const int L = row_length(src, b, chunks);
   const long long rowoff = ((long long)b * H + g) * src.capacity;
-  __shared__ int tmp[16];
-  // Offset of this chunk: kept slots in the chunks before it.
-  int off = 0;
-  const int32_t* cr = counts + ((long long)b * H + g) * chunks;
-  for (int q = tid; q < ch; q += NT) off += cr[q];
-  off = block_sum(off, tmp);
+  const uint8_t* mrow = mask + rowoff;
+  __shared__ int tmp[2 * (NT / 64)];
+  __shared__ int list[CH];
+
   if (ch * CH >= L) {
     if (ch == 0 && g == 0 && tid == 0) {
       dst.lengths[b] = 0;
@@ -74,57 +79,129 @@ __global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const
     }
     return;
   }
-  // Each thread scans PER consecutive slots.
-  const int i0 = ch * CH + tid * PER;
-  int flags = 0, n = 0;
+  const int i = ch * CH + tid;
+  const int f = (i < L) & (mrow[min(i, L - 1)] != 0);  // L >= 1 here
+  // Kept slots in the chunks before this one: `pre` is this thread's share.
+  int pre = 0;
+  if (RECOUNT) {
+    if (ch > 0) {
+      if (rowoff % 16 == 0) {
+        // 16 mask bytes per load, at most four loads per thread, all issued
+        // together (clamped index, masked count).
+        const int words = ch * (CH / 16);
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int i = i0 + q;
-    const int f = (i < L) && mask[rowoff + i] != 0;
-    flags |= f << q;
-    n += f;
+        for (int q = 0; q < kCompactRecountChunks * (CH / 16) / NT; ++q) {
+          const int w = tid + q * NT;
+          const uint4 v = reinterpret_cast<const uint4*>(mrow)[min(w, words - 1)];
+          const int nzb = nonzero_bytes(v.x) + nonzero_bytes(v.y) + nonzero_bytes(v.z) + nonzero_bytes(v.w);
+          pre += w < words ? nzb : 0;
+        }
+      } else {
+#pragma unroll 8
+        for (int q = 0; q < ch; ++q) pre += mrow[tid + q * NT] != 0;
+      }
+    }
+  } else {
+    const int32_t* cr = counts + ((long long)b * H + g) * chunks;
+    for (int q = tid; q < ch; q += NT) pre += cr[q];
   }
-  // Inclusive scan of n over the workgroup.
+
+  // One block scan gives both the chunk's rank of each kept slot (low 16 bits:
+  // the flags) and, from its total, the offset (high bits: the earlier counts;
+  // at most 16384 with RECOUNT). Long rows sum their offset separately.
   const int lane = tid & 63, wave = tid >> 6;
-  int incl = n;
+  int incl = RECOUNT ? (pre << 16) | f : f;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int t = __shfl_up(incl, o);
     if (lane >= o) incl += t;
   }
-  if (lane == 63) tmp[8 + wave] = incl;
+  int* wt = tmp + NT / 64;
+  if (lane == 63) wt[wave] = incl;
+  int off;
+  if (!RECOUNT) off = block_sum(pre, tmp);  // barriers inside also publish wt
   __syncthreads();
-  for (int w = 0; w < wave; ++w) incl += tmp[8 + w];
-  int d = off + incl - n;
-  const uint8_t* sk = static_cast<const uint8_t*>(src.k_codes);
-  const uint8_t* sv = static_cast<const uint8_t*>(src.v_codes);
-  uint8_t* dk = static_cast<uint8_t*>(dst.k_codes);
-  uint8_t* dv = static_cast<uint8_t*>(dst.v_codes);
+  int total = 0;
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    if (flags & (1 << q)) {
-      const long long si = rowoff + i0 + q, di = rowoff + d;
-      copy_row<RB>(sk + si * RB, dk + di * RB);
-      copy_row<RB>(sv + si * RB, dv + di * RB);
-      dst.k_scale[di] = src.k_scale[si];
-      dst.v_scale[di] = src.v_scale[si];
-      if (src.positions && dst.positions) dst.positions[di] = src.positions[si];
-      if (src_score && dst_score) dst_score[di] = src_score[si];
-      ++d;
+  for (int w = 0; w < NT / 64; ++w) {
+    if (w < wave) incl += wt[w];
+    total += wt[w];
+  }
+  if (RECOUNT) {
+    off = total >> 16;
+    total &= 0xFFFF;
+    incl &= 0xFFFF;
+  }
+  if (f) list[incl - 1] = i;
+  __syncthreads();
+
+  // Cooperative row copies: lane `part` of each LPR-lane group moves bytes
+  // [16 * part, 16 * part + 16) of a K row and the matching V row.
+  const uint8_t* sk = static_cast<const uint8_t*>(src.k_codes) + rowoff * RB;
+  const uint8_t* sv = static_cast<const uint8_t*>(src.v_codes) + rowoff * RB;
+  uint8_t* dk = static_cast<uint8_t*>(dst.k_codes) + rowoff * RB;
+  uint8_t* dv = static_cast<uint8_t*>(dst.v_codes) + rowoff * RB;
+  const int part = tid % LPR, r0 = tid / LPR;
+  // Batches of BATCH passes: every load of a batch is issued before its
+  // stores. Lanes past the last kept row reload that row (a cache hit) rather
+  // than branch, and only their stores are skipped.
+  constexpr int BATCH = 4;
+  const bool mine = tid < total;
+  const long long si = rowoff + list[mine ? tid : 0], di = rowoff + off + tid;
+  float ksv = 0.f, vsv = 0.f, scv = 0.f;
+  int pos = 0;
+  if (mine) {
+    ksv = src.k_scale[si];
+    vsv = src.v_scale[si];
+    if (src.positions && dst.positions) pos = src.positions[si];
+    if (src_score && dst_score) scv = src_score[si];
+  }
+  const int npass = (total + RPP - 1) / RPP;
+  for (int p0 = 0; p0 < npass; p0 += BATCH) {
+    u32x4 kx[BATCH], vx[BATCH];
+#pragma unroll
+    for (int p = 0; p < BATCH; ++p) {
+      const long long s_row = list[min(r0 + (p0 + p) * RPP, total - 1)];
+      kx[p] = *reinterpret_cast<const u32x4*>(sk + s_row * RB + part * 16);
+      vx[p] = *reinterpret_cast<const u32x4*>(sv + s_row * RB + part * 16);
+    }
+#pragma unroll
+    for (int p = 0; p < BATCH; ++p) {
+      const int q = r0 + (p0 + p) * RPP;
+      if (q < total) {
+        const long long d = off + q;
+        *reinterpret_cast<u32x4*>(dk + d * RB + part * 16) = kx[p];
+        *reinterpret_cast<u32x4*>(dv + d * RB + part * 16) = vx[p];
+      }
     }
   }
+  if (mine) {
+    dst.k_scale[di] = ksv;
+    dst.v_scale[di] = vsv;
+    if (src.positions && dst.positions) dst.positions[di] = pos;
+    if (src_score && dst_score) dst_score[di] = scv;
+  }
   // The chunk holding the row's last slot knows the row's total.
-  if (g == 0 && ch == (L - 1) / CH && tid == NT - 1) {
-    dst.lengths[b] = d;
+  if (g == 0 && ch == (L - 1) / CH && tid == 0) {
+    dst.lengths[b] = off + total;
     dst.num_seen[b] = src.num_seen[b];
   }
 }
 
 template <int RB>
-hipError_t launch_move(const kvc_cache_t& src, const float* ss, const uint8_t* mask, const kvc_cache_t& dst,
-                       float* ds, const int32_t* counts, int chunks, hipStream_t st) {
-  hipLaunchKernelGGL(compact_move_kernel<RB>, dim3(chunks, src.num_kv_heads, src.batch), dim3(NT), 0, st, src, ss,
-                     mask, dst, ds, counts, chunks);
+hipError_t launch_rb(const kvc_cache_t& src, const float* ss, const uint8_t* mask, const kvc_cache_t& dst,
+                     float* ds, int32_t* counts, int chunks, hipStream_t st) {
+  const dim3 grid(chunks, src.num_kv_heads, src.batch);
+  if (chunks <= kCompactRecountChunks) {
+    hipLaunchKernelGGL((compact_move_kernel<RB, true>), grid, dim3(NT), 0, st, src, ss, mask, dst, ds, counts,
+                       chunks);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(compact_count_kernel, grid, dim3(NT), 0, st, src, mask, counts, chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((compact_move_kernel<RB, false>), grid, dim3(NT), 0, st, src, ss, mask, dst, ds, counts,
+                     chunks);
   return hipGetLastError();
 }
 
@@ -132,15 +209,10 @@ hipError_t launch_move(const kvc_cache_t& src, const float* ss, const uint8_t* m
 
 hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const uint8_t* mask,
                           const kvc_cache_t& dst, float* dst_score, int32_t* counts, int chunks, hipStream_t st) {
-  hipLaunchKernelGGL(compact_count_kernel, dim3(chunks, src.num_kv_heads, src.batch), dim3(NT), 0, st, src, mask,
-                     counts, chunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int RB = src.head_dim * src.bits / 8;
-  switch (RB) {
-    case 32: return launch_move<32>(src, src_score, mask, dst, dst_score, counts, chunks, st);
-    case 64: return launch_move<64>(src, src_score, mask, dst, dst_score, counts, chunks, st);
-    case 128: return launch_move<128>(src, src_score, mask, dst, dst_score, counts, chunks, st);
+  switch (src.head_dim * src.bits / 8) {
+    case 32: return launch_rb<32>(src, src_score, mask, dst, dst_score, counts, chunks, st);
+    case 64: return launch_rb<64>(src, src_score, mask, dst, dst_score, counts, chunks, st);
+    case 128: return launch_rb<128>(src, src_score, mask, dst, dst_score, counts, chunks, st);
     default: return hipErrorInvalidValue;
   }
 }

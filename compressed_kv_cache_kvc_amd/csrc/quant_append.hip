@@ -9,8 +9,10 @@
 // scales are reproducible bit for bit.
 //
 // One wave quantizes one row (head_dim fp16 values = D*2 bytes): each lane
-// holds one or two fp16 pairs, the max-abs is a wave reduction, and each lane
-// writes its pair's two codes (2 bytes for INT8, 1 byte for INT4).
+// holds one fp16 pair (two for D = 256), the max-abs is a DPP wave reduction,
+// and each lane writes its pair's two codes (2 bytes for INT8, 1 byte for INT4).
+// Loads are unconditional (clamped addresses, masked values), so a wave's
+// rows are all in flight at once.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -36,47 +38,89 @@ __device__ __forceinline__ void store_pair(uint8_t* codes, int p, int c0, int c1
   }
 }
 
-// Quantize one row of D <= 256 fp16 values with the calling wave.
-template <int BITS>
-__device__ __forceinline__ void quant_row(const __half* __restrict__ x, uint8_t* __restrict__ codes,
-                                          float* __restrict__ scale_out, int D, int lane) {
-  constexpr float kQmax = BITS == 8 ? 127.f : 7.f;
-  const int P = D >> 1;
+// The fp16 pair(s) of one row a lane owns: pair `lane` (and `lane + 64` when
+// D = 256); lanes past the row's D/2 pairs hold zeros.
+template <int D>
+struct RowVals {
+  float2 v[D > 128 ? 2 : 1];
+};
+
+template <int D>
+__device__ __forceinline__ RowVals<D> load_row(const __half* __restrict__ x, int lane) {
+  constexpr int P = D / 2;
   const __half2* x2 = reinterpret_cast<const __half2*>(x);
-  const bool h0 = lane < P, h1 = lane + 64 < P;
-  float2 v0 = make_float2(0.f, 0.f), v1 = make_float2(0.f, 0.f);
-  if (h0) v0 = __half22float2(x2[lane]);
-  if (h1) v1 = __half22float2(x2[lane + 64]);
-  float a = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v1.x), fabsf(v1.y)));
+  RowVals<D> r;
+#pragma unroll
+  for (int k = 0; k < (D > 128 ? 2 : 1); ++k) {
+    const int p = lane + 64 * k;
+    const float2 f = __half22float2(x2[min(p, P - 1)]);
+    r.v[k] = p < P ? f : make_float2(0.f, 0.f);
+  }
+  return r;
+}
+
+// Quantize a loaded row: wave-wide max-abs, the scale, then each lane's codes.
+template <int BITS, int D>
+__device__ __forceinline__ void quant_vals(const RowVals<D>& r, uint8_t* __restrict__ codes,
+                                           float* __restrict__ scale_out, int lane) {
+  constexpr float kQmax = BITS == 8 ? 127.f : 7.f;
+  constexpr int P = D / 2;
+  constexpr int K = D > 128 ? 2 : 1;
+  float a = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) a = fmaxf(a, fmaxf(fabsf(r.v[k].x), fabsf(r.v[k].y)));
   a = wave_max(a);
   const float s = __fdiv_rn(a, kQmax);
   if (lane == 0) *scale_out = s;
-  if (h0) store_pair<BITS>(codes, lane, encode<BITS>(v0.x, s), encode<BITS>(v0.y, s));
-  if (h1) store_pair<BITS>(codes, lane + 64, encode<BITS>(v1.x, s), encode<BITS>(v1.y, s));
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int p = lane + 64 * k;
+    if (p < P) store_pair<BITS>(codes, p, encode<BITS>(r.v[k].x, s), encode<BITS>(r.v[k].y, s));
+  }
 }
 
 // Decode-sized appends: one workgroup per sequence does every row of that
-// sequence and then advances its length, so a single launch suffices.
-template <int BITS>
+// sequence and then advances its length, so a single launch suffices. Each
+// wave loads R rows (row indices clamped, so the loads are unconditional)
+// before reducing any of them; the first batch is issued before the lengths
+// are read, so one memory latency covers both.
+template <int BITS, int D>
 __global__ __launch_bounds__(1024) void quant_append_seq_kernel(kvc_cache_t c, const __half* __restrict__ kn,
                                                                 const __half* __restrict__ vn, int n_new,
                                                                 float* __restrict__ score) {
+  constexpr int R = 4;
+  constexpr int RB = D * BITS / 8;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int L0 = c.lengths[b];
-  const int seen = c.num_seen[b];
-  const int H = c.num_kv_heads, D = c.head_dim, RB = D * BITS / 8;
+  const int H = c.num_kv_heads;
   const int rows = H * n_new * 2;
-  for (int r = wave; r < rows; r += 16) {
-    const int kv = r & 1, ht = r >> 1, h = ht / n_new, t = ht - h * n_new;
-    const long long row = cache_row(c, b, h, L0 + t);
-    if (row < 0) continue;
-    const __half* src = (kv ? vn : kn) + (((long long)b * H + h) * n_new + t) * D;
-    uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * RB;
-    quant_row<BITS>(src, dst, (kv ? c.v_scale : c.k_scale) + row, D, lane);
-    if (kv == 0 && lane == 0) {
-      if (c.positions) c.positions[row] = seen + t;
-      if (score) score[((long long)b * H + h) * c.capacity + L0 + t] = 0.f;
+  RowVals<D> vals[R];
+  auto load_batch = [&](int r0) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int r = min(r0 + 16 * q, rows - 1);
+      const int kv = r & 1, ht = r >> 1, h = ht / n_new, t = ht - h * n_new;
+      vals[q] = load_row<D>((kv ? vn : kn) + (((long long)b * H + h) * n_new + t) * D, lane);
+    }
+  };
+  load_batch(wave);
+  const int L0 = __builtin_amdgcn_readfirstlane(c.lengths[b]);
+  const int seen = __builtin_amdgcn_readfirstlane(c.num_seen[b]);
+  for (int r0 = wave; r0 < rows; r0 += 16 * R) {
+    if (r0 != wave) load_batch(r0);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int r = r0 + 16 * q;
+      if (r >= rows) continue;
+      const int kv = r & 1, ht = r >> 1, h = ht / n_new, t = ht - h * n_new;
+      const long long row = cache_row(c, b, h, L0 + t);
+      if (row < 0) continue;
+      uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * RB;
+      quant_vals<BITS, D>(vals[q], dst, (kv ? c.v_scale : c.k_scale) + row, lane);
+      if (kv == 0 && lane == 0) {
+        if (c.positions) c.positions[row] = seen + t;
+        if (score) score[((long long)b * H + h) * c.capacity + L0 + t] = 0.f;
+      }
     }
   }
   __syncthreads();
@@ -88,25 +132,26 @@ __global__ __launch_bounds__(1024) void quant_append_seq_kernel(kvc_cache_t c, c
 
 // Prefill-sized appends: four rows per workgroup over the whole grid; the
 // lengths advance in a second launch once every row has read them.
-template <int BITS>
+template <int BITS, int D>
 __global__ __launch_bounds__(256) void quant_append_rows_kernel(kvc_cache_t c, const __half* __restrict__ kn,
                                                                 const __half* __restrict__ vn, int n_new,
                                                                 float* __restrict__ score, long long total) {
+  constexpr int RB = D * BITS / 8;
   const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= total) return;
-  const int H = c.num_kv_heads, D = c.head_dim, RB = D * BITS / 8;
+  const int H = c.num_kv_heads;
   const int kv = (int)(r & 1);
   const long long rest = r >> 1;
   const int t = (int)(rest % n_new);
   const long long bh = rest / n_new;
   const int h = (int)(bh % H), b = (int)(bh / H);
+  const RowVals<D> vals = load_row<D>((kv ? vn : kn) + rest * D, lane);
   const int L0 = c.lengths[b];
   const long long row = cache_row(c, b, h, L0 + t);
   if (row < 0) return;
-  const __half* src = (kv ? vn : kn) + rest * D;
   uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * RB;
-  quant_row<BITS>(src, dst, (kv ? c.v_scale : c.k_scale) + row, D, lane);
+  quant_vals<BITS, D>(vals, dst, (kv ? c.v_scale : c.k_scale) + row, lane);
   if (kv == 0 && lane == 0) {
     if (c.positions) c.positions[row] = c.num_seen[b] + t;
     if (score) score[bh * c.capacity + L0 + t] = 0.f;
@@ -121,18 +166,18 @@ __global__ void advance_lengths_kernel(int32_t* lengths, int32_t* num_seen, int 
   }
 }
 
-template <int BITS>
+template <int BITS, int D>
 hipError_t launch_bits(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new, float* score,
                        hipStream_t st) {
   const long long rows_per_seq = (long long)c.num_kv_heads * n_new * 2;
   if (rows_per_seq <= 256) {
-    hipLaunchKernelGGL(quant_append_seq_kernel<BITS>, dim3(c.batch), dim3(1024), 0, st, c, kn, vn, n_new,
+    hipLaunchKernelGGL((quant_append_seq_kernel<BITS, D>), dim3(c.batch), dim3(1024), 0, st, c, kn, vn, n_new,
                        score);
     return hipGetLastError();
   }
   const long long total = rows_per_seq * c.batch;
   const long long blocks = (total + 3) / 4;
-  hipLaunchKernelGGL(quant_append_rows_kernel<BITS>, dim3((unsigned)blocks), dim3(256), 0, st, c, kn, vn,
+  hipLaunchKernelGGL((quant_append_rows_kernel<BITS, D>), dim3((unsigned)blocks), dim3(256), 0, st, c, kn, vn,
                      n_new, score, total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -141,11 +186,18 @@ hipError_t launch_bits(const kvc_cache_t& c, const __half* kn, const __half* vn,
   return hipGetLastError();
 }
 
+template <int BITS>
+hipError_t launch_dim(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new, float* score,
+                      hipStream_t st) {
+  return c.head_dim == 64 ? launch_bits<BITS, 64>(c, kn, vn, n_new, score, st)
+                          : launch_bits<BITS, 128>(c, kn, vn, n_new, score, st);
+}
+
 }  // namespace
 
 hipError_t launch_quant_append(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new,
                                float* score, hipStream_t st) {
-  return c.bits == 8 ? launch_bits<8>(c, kn, vn, n_new, score, st) : launch_bits<4>(c, kn, vn, n_new, score, st);
+  return c.bits == 8 ? launch_dim<8>(c, kn, vn, n_new, score, st) : launch_dim<4>(c, kn, vn, n_new, score, st);
 }
 
 }  // namespace kvc

@@ -87,6 +87,19 @@ def test_decode_attn_gqa(hq, hkv, bits, D):
     assert_scores_close(host(score), ref.score, ref.lengths)
 
 
+@pytest.mark.parametrize("hq,hkv,bits", [(8, 8, 8), (16, 8, 8), (8, 8, 4)])
+def test_decode_attn_multi_tile_splits(hq, hkv, bits):
+    """Long rows: each split walks several 256-token tiles with an online
+    softmax (70001 tokens x 8 KV heads gives 2 tiles per split)."""
+    w = get("tiny_mha").scaled(num_q_heads=hq, num_kv_heads=hkv, head_dim=128, bits=bits, context=70001)
+    print(f"[attn] multi-tile hq={hq} hkv={hkv} bits={bits}", flush=True)
+    d = draw(w)
+    gc, ref, score = prefill_both(w, d)
+    out, ro = _attend_both(gc, ref, d["q"], score)
+    assert_out_close(out, ro)
+    assert_scores_close(host(score), ref.score, ref.lengths)
+
+
 def test_decode_attn_is_deterministic():
     w = get("tiny_mha").scaled(context=700, num_q_heads=8, num_kv_heads=2)
     d = draw(w)
@@ -119,7 +132,7 @@ def test_empty_sequence_gives_zero_output():
 
 @pytest.mark.parametrize("L,budget,S,R", [(512, 128, 4, 64), (3000, 1000, 4, 100), (9000, 2457, 4, 1024),
                                           (100, 100, 4, 10), (99, 100, 4, 10), (300, 20, 10, 10),
-                                          (5000, 5000 - 1, 4, 2048)])
+                                          (5000, 5000 - 1, 4, 2048), (20000, 5000, 4, 256)])
 def test_select_bit_exact_on_shared_scores(L, budget, S, R):
     """Same fp32 scores on both sides: the keep masks must be identical,
     including ties (broken toward the lower slot)."""
@@ -144,10 +157,13 @@ def test_select_bit_exact_on_shared_scores(L, budget, S, R):
             assert np.array_equal(m[b, g], ref), (b, g)
 
 
-@pytest.mark.parametrize("bits,D", [(8, 128), (4, 128), (8, 64)])
-def test_compact_bit_exact(bits, D):
+@pytest.mark.parametrize("bits,D,L,keep_n", [(8, 128, 2500, 900), (4, 128, 2500, 900), (8, 64, 2500, 900),
+                                             (8, 128, 40000, 12000)])
+def test_compact_bit_exact(bits, D, L, keep_n):
+    """Short rows take the one-launch path; 40000 slots (40 chunks) take the
+    count-then-move path."""
     rng = np.random.default_rng(7 + bits + D)
-    B, H, L, cap, keep_n = 2, 3, 2500, 2600, 900
+    B, H, cap = 2, 3, L + 100
     w = get("tiny_mha").scaled(context=L, batch=B, num_q_heads=H, num_kv_heads=H, head_dim=D, bits=bits)
     d = draw(w)
     gc, ref, score = prefill_both(w, d, capacity=cap)
