@@ -6,8 +6,9 @@ H2O keep 0.3 = 4 sinks + 1024 recent + 1429 heavy hitters):
 
   1. quantize-append the new token's K and V          (kvc_quant_append)
   2. attention over all 8192 tokens + H2O accumulation (kvc_decode_attn)
-  3. keep-set selection down to 2457 slots             (kvc_h2o_select)
-  4. compaction of the kept slots into the other buffer (kvc_compact)
+  3. keep-set selection down to 2457 slots, as a mask and
+     an ascending keep list                            (kvc_h2o_select)
+  4. compaction of the kept slots into the other buffer (kvc_compact_gather)
 
 Steps rotate over 32 distinct layer caches (2.1 GiB, like the 32 layers of the
 model), so every launch streams its 66 MiB from HBM rather than from the
@@ -47,8 +48,8 @@ def step_bytes(B, Hq, H, D, bits, L, budget):
         "append": B * H * (2 * D * 2 + 2 * (rb + 4) + 4 + 4),   # fp16 in; codes, scales, position, score out
         "attention": kv + B * Hq * D * 2 + B * Hq * D * 4,      # KV + q (fp16) + out (fp32)
         "h2o": 2 * B * H * L * 4,                                # score read-modify-write
-        "select": B * H * L * 4 + B * H * L,                     # scores in, mask out
-        "compact": B * H * L + 2 * B * H * budget * (2 * (rb + 4) + 8),  # mask; kept rows in and out
+        "select": B * H * L * 4 + B * H * L + B * H * budget * 4,  # scores in; mask and keep list out
+        "compact": B * H * budget * 4 + 2 * B * H * budget * (2 * (rb + 4) + 8),  # list; kept rows in and out
     }
     return parts, kv + B * Hq * D * 2   # attention kernel's own algorithmic bytes (KV + q)
 
@@ -111,7 +112,7 @@ def main(argv=None):
     # ---- device state: 32 layer caches, shared lengths so one fill rewinds all ----
     lengths_all = torch.zeros((LAYERS, B), dtype=torch.int32, device="cuda")
     seen_all = torch.zeros((LAYERS, B), dtype=torch.int32, device="cuda")
-    caches, scores, masks = [], [], []
+    caches, scores, masks, keep_lists = [], [], [], []
     k_pre, v_pre = dev(d["k"][:, :, :L - 1]), dev(d["v"][:, :, :L - 1])
     for i in range(LAYERS):
         c = kvc.KVCache(B, H, D, L, bits)
@@ -121,6 +122,7 @@ def main(argv=None):
         caches.append(c)
         scores.append(c.score_buffer())
         masks.append(torch.zeros((B, H, L), dtype=torch.uint8, device="cuda"))
+        keep_lists.append(torch.zeros((B, H, budget), dtype=torch.int32, device="cuda"))
     del k_pre, v_pre
     dst = kvc.KVCache(B, H, D, L, bits)
     dst_score = dst.score_buffer()
@@ -128,7 +130,6 @@ def main(argv=None):
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     ws_attn = torch.empty(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, L, True), dtype=torch.uint8,
                           device="cuda")
-    ws_comp = torch.empty(kvc.kvc_compact_workspace_bytes(caches[0], L), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
     def phase_append():
@@ -142,8 +143,9 @@ def main(argv=None):
 
     def phase_evict():
         for i in range(LAYERS):
-            kvc.kvc_h2o_select(caches[i], scores[i], budget, S, R, masks[i], max_len_hint=L)
-            kvc.kvc_compact(caches[i], scores[i], masks[i], dst, dst_score, max_len_hint=L, workspace=ws_comp)
+            kvc.kvc_h2o_select(caches[i], scores[i], budget, S, R, masks[i], keep_index=keep_lists[i],
+                               max_len_hint=L)
+            kvc.kvc_compact_gather(caches[i], scores[i], keep_lists[i], budget, dst, dst_score)
 
     # ---- eager pass, then capture each phase as a graph ----
     stream = torch.cuda.Stream()

@@ -21,7 +21,7 @@ __all__ = [
     "KvcError", "KVCache", "BlockPool", "lib", "LIB_PATH",
     "kvc_abi_version", "kvc_status_str", "kvc_last_error",
     "kvc_quant_append", "kvc_decode_attn", "kvc_decode_attn_workspace_bytes",
-    "kvc_h2o_select", "kvc_h2o_select_workspace_bytes", "kvc_compact", "kvc_compact_workspace_bytes",
+    "kvc_h2o_select", "kvc_compact", "kvc_compact_workspace_bytes", "kvc_compact_gather",
     "row_bytes",
 ]
 
@@ -50,7 +50,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m compressed_kv_cache_kvc_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python compressed_kv_cache_kvc_amd/build.py` "
             "(or __graft_entry__.build()). There is no fallback implementation.")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, SZ, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_uint64
@@ -62,10 +62,10 @@ def _load():
         "kvc_quant_append": (I32, [D, P, P, I32, P, I32, P]),
         "kvc_decode_attn_workspace_bytes": (SZ, [D, I32, I32, I32]),
         "kvc_decode_attn": (I32, [D, P, I32, P, P, I32, P, SZ, P]),
-        "kvc_h2o_select_workspace_bytes": (SZ, [D, I32]),
-        "kvc_h2o_select": (I32, [D, P, I32, I32, I32, P, I32, P, SZ, P]),
+        "kvc_h2o_select": (I32, [D, P, I32, I32, I32, P, P, I32, P]),
         "kvc_compact_workspace_bytes": (SZ, [D, I32]),
         "kvc_compact": (I32, [D, P, P, D, P, I32, P, SZ, P]),
+        "kvc_compact_gather": (I32, [D, P, P, I32, D, P, P]),
         "kvc_pool_create": (P, [I32, I32, U64]),
         "kvc_pool_destroy": (None, [P]),
         "kvc_pool_reserve": (I32, [P, I32, I32]),
@@ -242,22 +242,19 @@ def kvc_decode_attn(cache, q, out, h2o_score=None, max_len_hint: Optional[int] =
                                _ptr(workspace), workspace.numel(), _stream(stream)), "kvc_decode_attn")
 
 
-def kvc_h2o_select_workspace_bytes(cache, max_len_hint: int) -> int:
-    return lib.kvc_h2o_select_workspace_bytes(ctypes.byref(_desc(cache)), max_len_hint)
-
-
-def kvc_h2o_select(cache, h2o_score, budget: int, n_sink: int, n_recent: int, keep_mask,
-                   max_len_hint: Optional[int] = None, workspace=None, stream=None):
-    """Keep mask uint8 ``[B][Hkv][capacity]``: sinks + recent + top-k by score (see kvc.h)."""
+def kvc_h2o_select(cache, h2o_score, budget: int, n_sink: int, n_recent: int, keep_mask, keep_index=None,
+                   max_len_hint: Optional[int] = None, stream=None):
+    """Keep mask uint8 ``[B][Hkv][capacity]`` (and optionally the ascending keep
+    list int32 ``[B][Hkv][budget]``): sinks + recent + top-k by score (see kvc.h)."""
     import torch
     d = _desc(cache)
     _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
     _need(keep_mask, torch.uint8, "keep_mask", d.batch * d.num_kv_heads * d.capacity)
+    _need(keep_index, torch.int32, "keep_index", d.batch * d.num_kv_heads * budget)
     if max_len_hint is None:
         max_len_hint = cache.max_len
-    nbytes = 0 if workspace is None else workspace.numel()
     _check(lib.kvc_h2o_select(ctypes.byref(d), _ptr(h2o_score), budget, n_sink, n_recent, _ptr(keep_mask),
-                              max_len_hint, _ptr(workspace), nbytes, _stream(stream)), "kvc_h2o_select")
+                              _ptr(keep_index), max_len_hint, _stream(stream)), "kvc_h2o_select")
 
 
 def kvc_compact_workspace_bytes(cache, max_len_hint: int) -> int:
@@ -281,6 +278,19 @@ def kvc_compact(src, src_score, keep_mask, dst, dst_score=None, max_len_hint: Op
                            max_len_hint, _ptr(workspace), workspace.numel(), _stream(stream)), "kvc_compact")
     if isinstance(dst, KVCache) and isinstance(src, KVCache):
         dst.max_len = src.max_len
+
+
+def kvc_compact_gather(src, src_score, keep_index, n_keep: int, dst, dst_score=None, stream=None):
+    """Compaction from the ascending keep list ``[B][Hkv][n_keep]`` (see kvc.h)."""
+    import torch
+    ds, dd = _desc(src), _desc(dst)
+    _need(src_score, torch.float32, "src_score", ds.batch * ds.num_kv_heads * ds.capacity)
+    _need(dst_score, torch.float32, "dst_score", dd.batch * dd.num_kv_heads * dd.capacity)
+    _need(keep_index, torch.int32, "keep_index", ds.batch * ds.num_kv_heads * n_keep)
+    _check(lib.kvc_compact_gather(ctypes.byref(ds), _ptr(src_score), _ptr(keep_index), n_keep, ctypes.byref(dd),
+                                  _ptr(dst_score), _stream(stream)), "kvc_compact_gather")
+    if isinstance(dst, KVCache) and isinstance(src, KVCache):
+        dst.max_len = min(src.max_len, n_keep)
 
 
 class BlockPool:

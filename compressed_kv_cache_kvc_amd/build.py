@@ -1,6 +1,6 @@
 """Build libkvc.so (HIP kernels + C ABI) in-tree for gfx950.
 
-    python -m compressed_kv_cache_kvc_amd.build
+    python compressed_kv_cache_kvc_amd/build.py
 
 Compiles every source under csrc/ with hipcc (host-only C++ with g++) into
 ``_build/`` and links ``compressed_kv_cache_kvc_amd/libkvc.so``. No fast-math:

@@ -126,6 +126,42 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Compaction is out of place: no destination buffer (nor the workspace) may
+// overlap any source buffer, the keep mask or list, or the source scores.
+int32_t check_out_of_place(const kvc_cache_t* src, const float* src_score, const void* keep, size_t keep_bytes,
+                           const kvc_cache_t* dst, const float* dst_score, const void* workspace, size_t ws_bytes) {
+  const size_t rows = (size_t)src->batch * src->num_kv_heads * src->capacity;
+  const size_t RB = (size_t)src->head_dim * src->bits / 8;
+  const void* s_bufs[] = {src->k_codes, src->v_codes, src->k_scale, src->v_scale, src->positions, src_score,
+                          keep, src->lengths, src->num_seen};
+  const size_t s_len[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, keep_bytes,
+                          (size_t)src->batch * 4, (size_t)src->batch * 4};
+  const void* d_bufs[] = {dst->k_codes, dst->v_codes, dst->k_scale, dst->v_scale, dst->positions, dst_score,
+                          dst->lengths, dst->num_seen, workspace};
+  const size_t d_len[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, (size_t)src->batch * 4,
+                          (size_t)src->batch * 4, ws_bytes};
+  for (int i = 0; i < 9; ++i)
+    for (int j = 0; j < 9; ++j)
+      if (overlap(s_bufs[i], s_len[i], d_bufs[j], d_len[j]))
+        return fail(KVC_ERR_INVALID_ARG, "dst buffer %d overlaps src buffer %d (compaction is out of place)", j, i);
+  return KVC_OK;
+}
+
+// Shared checks of both compaction entry points.
+int32_t check_compact_pair(const kvc_cache_t* src, const kvc_cache_t* dst, const float* src_score,
+                           const float* dst_score) {
+  int32_t st = check_cache(src, "src");
+  if (st) return st;
+  if ((st = check_cache(dst, "dst"))) return st;
+  if (src->block_size || dst->block_size) return fail(KVC_ERR_UNSUPPORTED, "compaction of paged caches is not built");
+  if (src->bits != dst->bits || src->batch != dst->batch || src->num_kv_heads != dst->num_kv_heads ||
+      src->head_dim != dst->head_dim || src->capacity != dst->capacity)
+    return fail(KVC_ERR_INVALID_ARG, "src and dst geometries differ");
+  if ((src_score == nullptr) != (dst_score == nullptr))
+    return fail(KVC_ERR_INVALID_ARG, "pass both src_score and dst_score, or neither");
+  return KVC_OK;
+}
+
 }  // namespace
 }  // namespace kvc
 
@@ -198,18 +234,10 @@ int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_h
   return device_status(launch_decode_attn(a, static_cast<hipStream_t>(stream)), "kvc_decode_attn launch");
 }
 
-size_t kvc_h2o_select_workspace_bytes(const kvc_cache_t* cache, int32_t max_len_hint) {
-  (void)cache;
-  (void)max_len_hint;
-  return 0;
-}
-
 int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t budget, int32_t n_sink,
-                       int32_t n_recent, uint8_t* keep_mask, int32_t max_len_hint, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, int32_t max_len_hint,
+                       void* stream) {
   clear_error();
-  (void)workspace;
-  (void)workspace_bytes;
   int32_t st = check_cache(cache, "cache");
   if (st) return st;
   if (!h2o_score || !keep_mask) return fail(KVC_ERR_INVALID_ARG, "h2o_score and keep_mask must not be NULL");
@@ -220,8 +248,8 @@ int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t
   if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
   if (max_len_hint > cache->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
   // The kernel reads at most max_len_hint slots per row.
-  return device_status(launch_select(*cache, h2o_score, budget, n_sink, n_recent, keep_mask, max_len_hint,
-                                     static_cast<hipStream_t>(stream)),
+  return device_status(launch_select(*cache, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index,
+                                     max_len_hint, static_cast<hipStream_t>(stream)),
                        "kvc_h2o_select launch");
 }
 
@@ -234,41 +262,39 @@ size_t kvc_compact_workspace_bytes(const kvc_cache_t* src, int32_t max_len_hint)
 int32_t kvc_compact(const kvc_cache_t* src, const float* src_score, const uint8_t* keep_mask, const kvc_cache_t* dst,
                     float* dst_score, int32_t max_len_hint, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  int32_t st = check_cache(src, "src");
+  int32_t st = check_compact_pair(src, dst, src_score, dst_score);
   if (st) return st;
-  if ((st = check_cache(dst, "dst"))) return st;
-  if (src->block_size || dst->block_size) return fail(KVC_ERR_UNSUPPORTED, "compaction of paged caches is not built");
-  if (src->bits != dst->bits || src->batch != dst->batch || src->num_kv_heads != dst->num_kv_heads ||
-      src->head_dim != dst->head_dim || src->capacity != dst->capacity)
-    return fail(KVC_ERR_INVALID_ARG, "src and dst geometries differ");
   if (!keep_mask) return fail(KVC_ERR_INVALID_ARG, "keep_mask must not be NULL");
-  if ((src_score == nullptr) != (dst_score == nullptr))
-    return fail(KVC_ERR_INVALID_ARG, "pass both src_score and dst_score, or neither");
   if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
   if (max_len_hint > src->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
   const size_t need = kvc_compact_workspace_bytes(src, max_len_hint);
   if (!workspace || workspace_bytes < need)
     return fail(KVC_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : 0);
-  // Out-of-place: no destination buffer may overlap any source buffer.
-  const size_t rows = (size_t)src->batch * src->num_kv_heads * src->capacity;
-  const size_t RB = (size_t)src->head_dim * src->bits / 8;
-  const void* s_bufs[] = {src->k_codes, src->v_codes, src->k_scale, src->v_scale, src->positions, src_score,
-                          keep_mask, src->lengths, src->num_seen};
-  const size_t s_len[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, rows, (size_t)src->batch * 4,
-                          (size_t)src->batch * 4};
-  const void* d_bufs[] = {dst->k_codes, dst->v_codes, dst->k_scale, dst->v_scale, dst->positions, dst_score,
-                          dst->lengths, dst->num_seen, workspace};
-  const size_t d_len[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, (size_t)src->batch * 4,
-                          (size_t)src->batch * 4, need};
-  for (int i = 0; i < 9; ++i)
-    for (int j = 0; j < 9; ++j)
-      if (overlap(s_bufs[i], s_len[i], d_bufs[j], d_len[j]))
-        return fail(KVC_ERR_INVALID_ARG, "dst buffer %d overlaps src buffer %d (compaction is out of place)", j, i);
+  if ((st = check_out_of_place(src, src_score, keep_mask, (size_t)src->batch * src->num_kv_heads * src->capacity,
+                                dst, dst_score, workspace, need)))
+    return st;
   // Kernels read at most `chunks` * kCompactChunk slots per row.
   const int chunks = max_len_hint > 0 ? (max_len_hint + kCompactChunk - 1) / kCompactChunk : 1;
   return device_status(launch_compact(*src, src_score, keep_mask, *dst, dst_score, static_cast<int32_t*>(workspace),
                                       chunks, static_cast<hipStream_t>(stream)),
                        "kvc_compact launch");
+}
+
+int32_t kvc_compact_gather(const kvc_cache_t* src, const float* src_score, const int32_t* keep_index,
+                           int32_t n_keep, const kvc_cache_t* dst, float* dst_score, void* stream) {
+  clear_error();
+  int32_t st = check_compact_pair(src, dst, src_score, dst_score);
+  if (st) return st;
+  if (!keep_index) return fail(KVC_ERR_INVALID_ARG, "keep_index must not be NULL");
+  if (n_keep < 1) return fail(KVC_ERR_INVALID_ARG, "n_keep must be >= 1");
+  if (n_keep > src->capacity) return fail(KVC_ERR_CAPACITY, "n_keep exceeds capacity");
+  if ((st = check_out_of_place(src, src_score, keep_index,
+                               (size_t)src->batch * src->num_kv_heads * n_keep * sizeof(int32_t), dst, dst_score,
+                               nullptr, 0)))
+    return st;
+  return device_status(launch_compact_gather(*src, src_score, keep_index, n_keep, *dst, dst_score,
+                                             static_cast<hipStream_t>(stream)),
+                       "kvc_compact_gather launch");
 }
 
 }  // extern "C"

@@ -26,8 +26,7 @@ constexpr int NT = CH;  // one slot per thread
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int block_sum(int v, int* tmp) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v = wave_sum_i(v);
   if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
   __syncthreads();
   int r = 0;
@@ -57,95 +56,25 @@ __global__ __launch_bounds__(NT) void compact_count_kernel(kvc_cache_t src, cons
   if (threadIdx.x == 0) counts[((long long)b * src.num_kv_heads + g) * chunks + ch] = n;
 }
 
-template <int RB, bool RECOUNT>
-__global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const float* __restrict__ src_score,
-                                                          const uint8_t* __restrict__ mask, kvc_cache_t dst,
-                                                          float* __restrict__ dst_score,
-                                                          const int32_t* __restrict__ counts, int chunks) {
+// Copy `total` kept rows of one (sequence, KV head) row: kept row q (source
+// slot list[q], in LDS) goes to destination slot off + q. K and V rows move
+// cooperatively, RB/16 lanes per row with 16-byte accesses; every load of a
+// batch is issued before its stores. Lanes past the last kept row reload that
+// row (a cache hit) rather than branch, and only their stores are skipped.
+// Thread t also moves the scales, position and score of kept row t.
+template <int RB, int NT>
+__device__ __forceinline__ void copy_rows(const kvc_cache_t& src, const float* __restrict__ src_score,
+                                          const kvc_cache_t& dst, float* __restrict__ dst_score, long long rowoff,
+                                          const int* list, int total, int off) {
   constexpr int LPR = RB / 16;        // lanes per row
   constexpr int RPP = NT / LPR;       // rows per pass
-  const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int H = src.num_kv_heads;
-  const int L = row_length(src, b, chunks);
-  const long long rowoff = ((long long)b * H + g) * src.capacity;
-  const uint8_t* mrow = mask + rowoff;
-  __shared__ int tmp[2 * (NT / 64)];
-  __shared__ int list[CH];
-
-  if (ch * CH >= L) {
-    if (ch == 0 && g == 0 && tid == 0) {
-      dst.lengths[b] = 0;
-      dst.num_seen[b] = src.num_seen[b];
-    }
-    return;
-  }
-  const int i = ch * CH + tid;
-  const int f = (i < L) & (mrow[min(i, L - 1)] != 0);  // L >= 1 here
-  // Kept slots in the chunks before this one: `pre` is this thread's share.
-  int pre = 0;
-  if (RECOUNT) {
-    if (ch > 0) {
-      if (rowoff % 16 == 0) {
-        // 16 mask bytes per load, at most four loads per thread, all issued
-        // together (clamped index, masked count).
-        const int words = ch * (CH / 16);
-#pragma unroll
-        for (int q = 0; q < kCompactRecountChunks * (CH / 16) / NT; ++q) {
-          const int w = tid + q * NT;
-          const uint4 v = reinterpret_cast<const uint4*>(mrow)[min(w, words - 1)];
-          const int nzb = nonzero_bytes(v.x) + nonzero_bytes(v.y) + nonzero_bytes(v.z) + nonzero_bytes(v.w);
-          pre += w < words ? nzb : 0;
-        }
-      } else {
-#pragma unroll 8
-        for (int q = 0; q < ch; ++q) pre += mrow[tid + q * NT] != 0;
-      }
-    }
-  } else {
-    const int32_t* cr = counts + ((long long)b * H + g) * chunks;
-    for (int q = tid; q < ch; q += NT) pre += cr[q];
-  }
-
-  // One block scan gives both the chunk's rank of each kept slot (low 16 bits:
-  // the flags) and, from its total, the offset (high bits: the earlier counts;
-  // at most 16384 with RECOUNT). Long rows sum their offset separately.
-  const int lane = tid & 63, wave = tid >> 6;
-  int incl = RECOUNT ? (pre << 16) | f : f;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  int* wt = tmp + NT / 64;
-  if (lane == 63) wt[wave] = incl;
-  int off;
-  if (!RECOUNT) off = block_sum(pre, tmp);  // barriers inside also publish wt
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    if (w < wave) incl += wt[w];
-    total += wt[w];
-  }
-  if (RECOUNT) {
-    off = total >> 16;
-    total &= 0xFFFF;
-    incl &= 0xFFFF;
-  }
-  if (f) list[incl - 1] = i;
-  __syncthreads();
-
-  // Cooperative row copies: lane `part` of each LPR-lane group moves bytes
-  // [16 * part, 16 * part + 16) of a K row and the matching V row.
+  constexpr int BATCH = 4;
+  const int tid = threadIdx.x;
   const uint8_t* sk = static_cast<const uint8_t*>(src.k_codes) + rowoff * RB;
   const uint8_t* sv = static_cast<const uint8_t*>(src.v_codes) + rowoff * RB;
   uint8_t* dk = static_cast<uint8_t*>(dst.k_codes) + rowoff * RB;
   uint8_t* dv = static_cast<uint8_t*>(dst.v_codes) + rowoff * RB;
   const int part = tid % LPR, r0 = tid / LPR;
-  // Batches of BATCH passes: every load of a batch is issued before its
-  // stores. Lanes past the last kept row reload that row (a cache hit) rather
-  // than branch, and only their stores are skipped.
-  constexpr int BATCH = 4;
   const bool mine = tid < total;
   const long long si = rowoff + list[mine ? tid : 0], di = rowoff + off + tid;
   float ksv = 0.f, vsv = 0.f, scv = 0.f;
@@ -181,11 +110,115 @@ __global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const
     if (src.positions && dst.positions) dst.positions[di] = pos;
     if (src_score && dst_score) dst_score[di] = scv;
   }
+}
+
+template <int RB, bool RECOUNT>
+__global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const float* __restrict__ src_score,
+                                                          const uint8_t* __restrict__ mask, kvc_cache_t dst,
+                                                          float* __restrict__ dst_score,
+                                                          const int32_t* __restrict__ counts, int chunks) {
+  const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int H = src.num_kv_heads;
+  const int L = row_length(src, b, chunks);
+  const long long rowoff = ((long long)b * H + g) * src.capacity;
+  const uint8_t* mrow = mask + rowoff;
+  __shared__ int tmp[2 * (NT / 64)];
+  __shared__ int list[CH];
+
+  if (ch * CH >= L) {
+    if (ch == 0 && g == 0 && tid == 0) {
+      dst.lengths[b] = 0;
+      dst.num_seen[b] = src.num_seen[b];
+    }
+    return;
+  }
+  const int i = ch * CH + tid;
+  // Clamped to the capacity (a kernel argument), not to L, so that this load
+  // does not wait for the length.
+  const int f = (i < L) & (mrow[min(i, src.capacity - 1)] != 0);
+  // Kept slots in the chunks before this one: `pre` is this thread's share.
+  int pre = 0;
+  if (RECOUNT) {
+    if (ch > 0) {
+      if (rowoff % 16 == 0) {
+        // 16 mask bytes per load, at most four loads per thread, all issued
+        // together (clamped index, masked count).
+        const int words = ch * (CH / 16);
+#pragma unroll
+        for (int q = 0; q < kCompactRecountChunks * (CH / 16) / NT; ++q) {
+          const int w = tid + q * NT;
+          const uint4 v = reinterpret_cast<const uint4*>(mrow)[min(w, words - 1)];
+          const int nzb = nonzero_bytes(v.x) + nonzero_bytes(v.y) + nonzero_bytes(v.z) + nonzero_bytes(v.w);
+          pre += w < words ? nzb : 0;
+        }
+      } else {
+#pragma unroll 8
+        for (int q = 0; q < ch; ++q) pre += mrow[tid + q * NT] != 0;
+      }
+    }
+  } else {
+    const int32_t* cr = counts + ((long long)b * H + g) * chunks;
+    for (int q = tid; q < ch; q += NT) pre += cr[q];
+  }
+
+  // One block scan gives both the chunk's rank of each kept slot (low 16 bits:
+  // the flags) and, from its total, the offset (high bits: the earlier counts;
+  // at most 16384 with RECOUNT). Long rows sum their offset separately.
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = wave_inclusive_scan(RECOUNT ? (pre << 16) | f : f);
+  int* wt = tmp + NT / 64;
+  if (lane == 63) wt[wave] = incl;
+  int off;
+  if (!RECOUNT) off = block_sum(pre, tmp);  // barriers inside also publish wt
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    if (w < wave) incl += wt[w];
+    total += wt[w];
+  }
+  if (RECOUNT) {
+    off = total >> 16;
+    total &= 0xFFFF;
+    incl &= 0xFFFF;
+  }
+  if (f) list[incl - 1] = i;
+  __syncthreads();
+
+  copy_rows<RB, NT>(src, src_score, dst, dst_score, rowoff, list, total, off);
   // The chunk holding the row's last slot knows the row's total.
   if (g == 0 && ch == (L - 1) / CH && tid == 0) {
     dst.lengths[b] = off + total;
     dst.num_seen[b] = src.num_seen[b];
   }
+}
+
+
+// Compaction from a sorted gather list (the kept slots of each row in
+// ascending order, as kvc_h2o_select emits): destination slot j takes source
+// slot keep_index[b][g][j] for j < min(length, n_keep). No scan is needed, so
+// a workgroup's 256 destination slots start copying after one index load.
+template <int RB>
+__global__ __launch_bounds__(NT) void compact_gather_kernel(kvc_cache_t src, const float* __restrict__ src_score,
+                                                            const int32_t* __restrict__ keep_index, int n_keep,
+                                                            kvc_cache_t dst, float* __restrict__ dst_score) {
+  const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int H = src.num_kv_heads;
+  __shared__ int list[CH];
+  const int32_t* krow = keep_index + ((long long)b * H + g) * n_keep;
+  // The index load does not wait for the length: clamped to n_keep instead.
+  const int j = ch * CH + tid;
+  const int idx = krow[min(j, n_keep - 1)];
+  const int count = __builtin_amdgcn_readfirstlane(min(min(src.lengths[b], src.capacity), n_keep));
+  if (ch == 0 && g == 0 && tid == 0) {
+    dst.lengths[b] = count;
+    dst.num_seen[b] = src.num_seen[b];
+  }
+  if (ch * CH >= count) return;
+  const int total = min(CH, count - ch * CH);
+  list[tid] = min(max(idx, 0), src.capacity - 1);  // a bad index cannot leave the row
+  __syncthreads();
+  copy_rows<RB, NT>(src, src_score, dst, dst_score, ((long long)b * H + g) * src.capacity, list, total, ch * CH);
 }
 
 template <int RB>
@@ -205,7 +238,25 @@ hipError_t launch_rb(const kvc_cache_t& src, const float* ss, const uint8_t* mas
   return hipGetLastError();
 }
 
+template <int RB>
+hipError_t launch_gather_rb(const kvc_cache_t& src, const float* ss, const int32_t* keep_index, int n_keep,
+                            const kvc_cache_t& dst, float* ds, hipStream_t st) {
+  const dim3 grid((n_keep + CH - 1) / CH, src.num_kv_heads, src.batch);
+  hipLaunchKernelGGL((compact_gather_kernel<RB>), grid, dim3(NT), 0, st, src, ss, keep_index, n_keep, dst, ds);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_compact_gather(const kvc_cache_t& src, const float* src_score, const int32_t* keep_index,
+                                 int n_keep, const kvc_cache_t& dst, float* dst_score, hipStream_t st) {
+  switch (src.head_dim * src.bits / 8) {
+    case 32: return launch_gather_rb<32>(src, src_score, keep_index, n_keep, dst, dst_score, st);
+    case 64: return launch_gather_rb<64>(src, src_score, keep_index, n_keep, dst, dst_score, st);
+    case 128: return launch_gather_rb<128>(src, src_score, keep_index, n_keep, dst, dst_score, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const uint8_t* mask,
                           const kvc_cache_t& dst, float* dst_score, int32_t* counts, int chunks, hipStream_t st) {

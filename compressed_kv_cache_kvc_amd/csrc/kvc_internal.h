@@ -24,8 +24,6 @@ constexpr int kCompactChunk = 256;
 // Rows of at most this many chunks are compacted in one launch (each
 // workgroup recounts the kept slots before its chunk from the mask).
 constexpr int kCompactRecountChunks = 64;
-// Candidate keys the selection kernel stages in LDS (48 KiB).
-constexpr int kSelectResidentKeys = 12288;
 
 // ---- launchers (defined in the .hip files; return the first HIP error) ----
 hipError_t launch_quant_append(const kvc_cache_t& c, const __half* k_new, const __half* v_new,
@@ -50,11 +48,13 @@ hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st);
 int attn_heads_per_pass(int G);
 
 hipError_t launch_select(const kvc_cache_t& c, const float* score, int budget, int n_sink,
-                         int n_recent, uint8_t* mask, int max_len, hipStream_t st);
+                         int n_recent, uint8_t* mask, int32_t* keep_index, int max_len, hipStream_t st);
 
 hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const uint8_t* mask,
                           const kvc_cache_t& dst, float* dst_score, int32_t* counts, int chunks,
                           hipStream_t st);
+hipError_t launch_compact_gather(const kvc_cache_t& src, const float* src_score, const int32_t* keep_index,
+                                 int n_keep, const kvc_cache_t& dst, float* dst_score, hipStream_t st);
 
 // ---- device helpers ----
 template <int CTRL, int ROW_MASK = 0xF>
@@ -75,6 +75,62 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<0x142, 0xA>(v, v));
   v = fmaxf(v, dpp_f<0x143, 0xC>(v, v));
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, BOUND_ZERO);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP (no LDS):
+// three row shifts build 4-lane sums inside each 16-lane row, shifts by 4 and
+// 8 on the upper banks complete the row, and two row broadcasts carry row
+// totals forward. Lanes whose DPP source is masked off receive 0.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int v0 = v;
+  v += dpp_i<0x111, 0xF, 0xF, true>(v0);  // row_shr:1
+  v += dpp_i<0x112, 0xF, 0xF, true>(v0);  // row_shr:2
+  v += dpp_i<0x113, 0xF, 0xF, true>(v0);  // row_shr:3
+  v += dpp_i<0x114, 0xF, 0xE>(v);         // row_shr:4 into lanes 4..15 of each row
+  v += dpp_i<0x118, 0xF, 0xC>(v);         // row_shr:8 into lanes 8..15
+  v += dpp_i<0x142, 0xA>(v);              // row_bcast:15 into rows 1 and 3
+  v += dpp_i<0x143, 0xC>(v);              // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Sum over the wave, returned in every lane (DPP, then a read of lane 63).
+__device__ __forceinline__ int wave_sum_i(int v) {
+  return __builtin_amdgcn_readlane(wave_inclusive_scan(v), 63);
+}
+
+// Unsigned min / max over the wave, returned in every lane.
+template <bool MAX>
+__device__ __forceinline__ unsigned wave_minmax_u(unsigned v) {
+  auto op = [](unsigned x, unsigned y) { return MAX ? (x > y ? x : y) : (x < y ? x : y); };
+  // Masked-off lanes of the broadcasts read 0, a no-op only for max; the
+  // row-broadcast steps therefore pass the value itself as the fallback.
+  v = op(v, (unsigned)dpp_i<0xB1>((int)v));
+  v = op(v, (unsigned)dpp_i<0x4E>((int)v));
+  v = op(v, (unsigned)dpp_i<0x141>((int)v));
+  v = op(v, (unsigned)dpp_i<0x140>((int)v));
+  v = op(v, (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = op(v, (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum over a workgroup of NT threads. `tmp` is NT/64 ints of
+// LDS; two barriers.
+template <int NT>
+__device__ __forceinline__ int block_inclusive_scan(int v, int* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_inclusive_scan(v);
+  if (lane == 63) tmp[wave] = v;
+  __syncthreads();
+  int add = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) add += (w < wave) ? tmp[w] : 0;
+  __syncthreads();
+  return v + add;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

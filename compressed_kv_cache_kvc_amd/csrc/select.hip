@@ -6,260 +6,256 @@
 // report; "KV Cache optimization techniques" tutorial, section 2.2). Equal
 // scores go to the lower slot, so the result is unique.
 //
-// One 1024-thread workgroup per (sequence, KV head) row; scores become
-// order-preserving unsigned keys. The threshold T is the k-th largest key:
-//  * T is found by an MSB-first radix select: four passes of 8-bit digits,
-//    each a histogram of the keys that still match the digits chosen so far,
-//    then a wave-wide suffix scan that picks the digit holding the k-th key;
-//  * rows of up to 16 candidates per thread keep their keys in registers and
-//    give every wave its own LDS histogram (two barriers per pass);
-//  * longer rows read their keys from memory on every pass and share eight
-//    sub-histograms.
-// Keys above T are kept; of the keys equal to T, the first (k - count above T)
-// in slot order are kept, ranked by a block-wide prefix count over
-// thread-contiguous slot ranges.
+// One workgroup per (sequence, KV head) row; scores become order-preserving
+// unsigned keys and the threshold T is the k-th largest key, found by an
+// MSB-first radix select:
+//  * the bits shared by the row's smallest and largest key are known at once
+//    (one block reduction), so digits start at the first bit that varies;
+//  * digits are up to 11 bits wide (2048-bin LDS histogram, at most three
+//    passes). Wide digits that start where keys differ spread each wave's
+//    histogram increments over many bins (LDS atomics that collide on one
+//    address within a wave instruction serialize; scores are probability mass
+//    and mostly share a few binary exponents);
+//  * the bin holding the k-th key comes from a block-wide suffix scan.
+// Rows of up to 8192 candidates use 256 threads holding up to 32 keys each in
+// registers: few waves keep the per-pass fixed cost (scans, barriers) low,
+// since every instruction runs once per wave. Longer rows use 1024 threads and
+// re-read their keys from memory on every pass. Keys above T are kept; of the
+// keys equal to T, the first (k - count above T) in slot order are kept,
+// ranked by a block-wide prefix count over thread-contiguous slot ranges.
+//
+// Besides the mask, the kernel can emit the sorted list of kept slots (the
+// gather list of the compaction that follows).
 #include "kvc_internal.h"
 
 namespace kvc {
 namespace {
 
-constexpr int NT = 1024;
-constexpr int NSUB = 8;
-constexpr int kRegKeys = 16;  // keys per thread in the register path
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
 
 __device__ __forceinline__ unsigned order_key(float f) {
   const unsigned u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum over the workgroup; `tmp` holds 16 ints of LDS.
-__device__ __forceinline__ int block_inclusive_scan(int v, int* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(v, o);
-    if (lane >= o) v += n;
+// Block-wide min and max of unsigned keys (every thread gets both): DPP wave
+// reductions, then the wave results through LDS.
+template <int NT>
+__device__ __forceinline__ void block_minmax(unsigned& lo, unsigned& hi, unsigned* tmp) {
+  lo = wave_minmax_u<false>(lo);
+  hi = wave_minmax_u<true>(hi);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    tmp[wave] = lo;
+    tmp[16 + wave] = hi;
   }
-  if (lane == 63) tmp[wave] = v;
   __syncthreads();
-  int add = 0;
-  for (int w = 0; w < wave; ++w) add += tmp[w];
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    lo = min(lo, tmp[w]);
+    hi = max(hi, tmp[16 + w]);
+  }
   __syncthreads();
-  return v + add;
 }
 
-// Write the mask of one row given the threshold key T and the number of
-// T-equal candidates to keep. `key_at(i)` returns the key of candidate slot i.
-template <typename KeyAt>
-__device__ __forceinline__ void write_mask(uint8_t* m, int L, int lo, int hi, bool any_heavy, unsigned T,
-                                           int need, KeyAt key_at, int* scan_tmp) {
+// Radix select over the candidates. `for_keys(f)` calls f(key) for each of the
+// calling thread's candidate keys. On return, T is the k-th largest key and
+// `k` the number of keys equal to T that are kept.
+template <int NT, typename ForKeys>
+__device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, int* hist, int* scan_tmp,
+                                                    unsigned* mm_tmp, int* sel) {
+  constexpr int BPT = kBins / NT;  // bins per thread in the digit search
   const int tid = threadIdx.x;
-  for (int i = tid; i < lo; i += NT) m[i] = 1;
-  for (int i = hi + tid; i < L; i += NT) m[i] = 1;
-  const int n = hi - lo;
-  const int per = (n + NT - 1) / NT;
-  const int i0 = lo + min(tid * per, n), i1 = lo + min(tid * per + per, n);
-  int ties = 0;
-  if (any_heavy)
-    for (int i = i0; i < i1; ++i) ties += key_at(i) == T;
-  int rank = block_inclusive_scan(ties, scan_tmp) - ties;
-  for (int i = i0; i < i1; ++i) {
-    uint8_t keep = 0;
-    if (any_heavy) {
-      const unsigned u = key_at(i);
-      if (u > T) {
-        keep = 1;
-      } else if (u == T) {
-        keep = rank < need;
-        ++rank;
-      }
-    }
-    m[i] = keep;
-  }
-}
-
-__global__ __launch_bounds__(NT) void select_reg_kernel(kvc_cache_t c, const float* __restrict__ score, int budget,
-                                                        int n_sink, int n_recent, uint8_t* __restrict__ mask,
-                                                        int max_len) {
-  constexpr int NWAVE = NT / 64;
-  __shared__ int hist[NWAVE][256];  // one histogram per wave: no cross-wave contention
-  __shared__ int sel_digit, sel_k;
-  __shared__ int scan_tmp[16];
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), max_len));
-  const long long rowoff = ((long long)b * c.num_kv_heads + g) * c.capacity;
-  const float* row = score + rowoff;
-  uint8_t* m = mask + rowoff;
-  if (L <= budget) {
-    for (int i = tid; i < L; i += NT) m[i] = 1;
-    return;
-  }
-  const int lo = n_sink, hi = L - n_recent, n = hi - lo;
-  int k = budget - n_sink - n_recent;
-  // Thread t holds candidates [lo + t*per, lo + t*per + per) (per <= kRegKeys;
-  // the host routes longer rows to the radix kernel). Unconditional loads from
-  // clamped slots keep all of them in flight at once.
-  const int per = (n + NT - 1) / NT;
-  const int i0 = lo + min(tid * per, n), cnt = min(tid * per + per, n) - min(tid * per, n);
-  unsigned key[kRegKeys];
-#pragma unroll
-  for (int q = 0; q < kRegKeys; ++q) key[q] = order_key(row[lo + min(i0 - lo + q, n - 1)]);
-
-  unsigned T = 0, pmask = 0;
-  const bool any_heavy = k > 0;
-  if (any_heavy) {
-    for (int i = tid; i < NWAVE * 256; i += NT) (&hist[0][0])[i] = 0;
+  unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
+  for_keys([&](unsigned u) {
+    kmin = min(kmin, u);
+    kmax = max(kmax, u);
+  });
+  block_minmax<NT>(kmin, kmax, mm_tmp);
+  const unsigned diff = kmin ^ kmax;
+  if (diff == 0) return kmin;  // every candidate equal: keep the lowest k slots
+  int remaining = 32 - __clz(diff);  // low bits still undecided
+  const unsigned low = (remaining == 32) ? 0xFFFFFFFFu : ((1u << remaining) - 1u);
+  unsigned T = kmin & ~low, pmask = ~low;
+  for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+  __syncthreads();
+  while (remaining > 0) {
+    const int width = min(kDigitBits, remaining);
+    const int shift = remaining - width;
+    const unsigned dmask = (1u << width) - 1u;
+    for_keys([&](unsigned u) {
+      if ((u & pmask) == T) atomicAdd(&hist[(u >> shift) & dmask], 1);
+    });
     __syncthreads();
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    // Thread t owns the BPT bins just below kBins - BPT*t, so the inclusive
+    // scan over threads counts keys from the largest digit down; each bin is
+    // cleared once read.
+    const int top = kBins - BPT * tid - 1;
+    int c[BPT], tot = 0;
 #pragma unroll
-      for (int q = 0; q < kRegKeys; ++q)
-        if (q < cnt && (key[q] & pmask) == T) atomicAdd(&hist[wave][(key[q] >> shift) & 255u], 1);
-      __syncthreads();
-      if (wave == 0) {
-        // Lane l owns digits 4l .. 4l+3: sum them over the per-wave
-        // histograms (and clear those for the next pass), then a suffix scan
-        // from the largest digit finds the one holding the k-th largest key.
-        int cnt4[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) {
-          int4* hp = reinterpret_cast<int4*>(&hist[w][4 * lane]);
-          const int4 h4 = *hp;
-          cnt4[0] += h4.x;
-          cnt4[1] += h4.y;
-          cnt4[2] += h4.z;
-          cnt4[3] += h4.w;
-          *hp = make_int4(0, 0, 0, 0);
-        }
-        const int tot = cnt4[0] + cnt4[1] + cnt4[2] + cnt4[3];
-        // Inclusive scan from the top: lanes 63 .. lane.
-        int suf = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int nb = __shfl_down(suf, o);
-          if (lane + o < 64) suf += nb;
-        }
-        int above = suf - tot;  // keys whose digit is larger than this lane's four
-#pragma unroll
-        for (int q = 3; q >= 0; --q) {
-          if (above < k && k <= above + cnt4[q]) {
-            sel_digit = 4 * lane + q;
-            sel_k = k - above;
-          }
-          above += cnt4[q];
-        }
-      }
-      __syncthreads();
-      T |= (unsigned)sel_digit << shift;
-      pmask |= 255u << shift;
-      k = sel_k;
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = hist[top - j];
+      hist[top - j] = 0;
+      tot += c[j];
     }
-  }
-  // T is the threshold key and k the number of T-equal candidates to keep,
-  // lowest slots first.
-  for (int i = tid; i < lo; i += NT) m[i] = 1;
-  for (int i = hi + tid; i < L; i += NT) m[i] = 1;
-  int ties = 0;
+    const int incl = block_inclusive_scan<NT>(tot, scan_tmp);
+    int before = incl - tot;  // keys with a digit above this thread's bins
 #pragma unroll
-  for (int q = 0; q < kRegKeys; ++q) ties += any_heavy & (q < cnt) & (key[q] == T);
-  int rank = block_inclusive_scan(ties, scan_tmp) - ties;
-#pragma unroll
-  for (int q = 0; q < kRegKeys; ++q) {
-    if (q < cnt) {
-      uint8_t keep = 0;
-      if (any_heavy) {
-        if (key[q] > T) {
-          keep = 1;
-        } else if (key[q] == T) {
-          keep = rank < k;
-          ++rank;
-        }
+    for (int j = 0; j < BPT; ++j) {
+      if (before < k && k <= before + c[j]) {
+        sel[0] = top - j;
+        sel[1] = k - before;
       }
-      m[i0 + q] = keep;
+      before += c[j];
     }
+    __syncthreads();
+    T |= (unsigned)sel[0] << shift;
+    pmask |= dmask << shift;
+    k = sel[1];
+    remaining = shift;
   }
+  return T;
 }
 
-__global__ __launch_bounds__(NT) void select_radix_kernel(kvc_cache_t c, const float* __restrict__ score,
-                                                          int budget, int n_sink, int n_recent,
-                                                          uint8_t* __restrict__ mask, int max_len) {
-  __shared__ int hist[NSUB][256];
-  __shared__ int sel_digit, sel_k;
+// NT threads; REG: each thread holds KPT consecutive candidates in registers.
+template <int NT, int KPT, bool REG>
+__global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* __restrict__ score, int budget,
+                                                    int n_sink, int n_recent, uint8_t* __restrict__ mask,
+                                                    int32_t* __restrict__ keep_index, int max_len) {
+  __shared__ int hist[kBins];
   __shared__ int scan_tmp[16];
-
+  __shared__ unsigned mm_tmp[32];
+  __shared__ int sel[2];
+  __shared__ __align__(16) unsigned stage_lds[REG ? NT * KPT : 1];
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int L = __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), max_len));
   const long long rowoff = ((long long)b * c.num_kv_heads + g) * c.capacity;
   const float* row = score + rowoff;
   uint8_t* m = mask + rowoff;
+  int32_t* kidx = keep_index ? keep_index + ((long long)b * c.num_kv_heads + g) * budget : nullptr;
   if (L <= budget) {
-    for (int i = tid; i < L; i += NT) m[i] = 1;
+    for (int i = tid; i < L; i += NT) {
+      m[i] = 1;
+      if (kidx) kidx[i] = i;
+    }
     return;
   }
-  const int lo = n_sink, hi = L - n_recent;
-  const int k_heavy = budget - n_sink - n_recent;
-  auto key_at = [&](int i) -> unsigned { return order_key(row[i]); };
-
-  unsigned prefix = 0, pmask = 0;
-  int k = k_heavy;
-  if (k > 0) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      for (int i = tid; i < NSUB * 256; i += NT) (&hist[0][0])[i] = 0;
-      __syncthreads();
-      int* h = hist[(tid >> 6) & (NSUB - 1)];
-      for (int i = lo + tid; i < hi; i += NT) {
-        const unsigned u = key_at(i);
-        if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l owns digits 255-4l .. 252-4l (descending order)
-        int cnt[4], tot = 0;
+  const int lo = n_sink, hi = L - n_recent, n = hi - lo;
+  int k = budget - n_sink - n_recent;
+  // Thread t holds candidates [lo + t*per, lo + t*per + per); per is a
+  // multiple of 4, so that its range starts on a 16-byte boundary of the
+  // staging buffer.
+  const int per = ((n + NT - 1) / NT + 3) & ~3;
+  const int i0 = lo + min(tid * per, n), cnt = min(tid * per + per, n) - min(tid * per, n);
+  unsigned key[REG ? KPT : 1];
+  if (REG) {
+    // Coalesced loads (slot lo + tid + j*NT, clamped, all in flight) into LDS,
+    // then each thread reads its contiguous range back with 16-byte LDS reads
+    // (its range starts at a multiple of 4 words).
+    unsigned* stage = reinterpret_cast<unsigned*>(stage_lds);
+    unsigned v[KPT];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int s = 0;
+    for (int j = 0; j < KPT; ++j) v[j] = order_key(row[lo + min(tid + j * NT, n - 1)]);
 #pragma unroll
-          for (int sub = 0; sub < NSUB; ++sub) s += hist[sub][255 - 4 * tid - q];
-          cnt[q] = s;
-          tot += s;
-        }
-        int incl = tot;
+    for (int j = 0; j < KPT; ++j) stage[tid + j * NT] = v[j];
+    __syncthreads();
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int n = __shfl_up(incl, o);
-          if (tid >= o) incl += n;
-        }
-        int before = incl - tot;  // keys with a larger digit than this lane's first
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (before < k && k <= before + cnt[q]) {
-            sel_digit = 255 - 4 * tid - q;
-            sel_k = k - before;
-          }
-          before += cnt[q];
-        }
-      }
-      __syncthreads();
-      prefix |= (unsigned)sel_digit << shift;
-      pmask |= 255u << shift;
-      k = sel_k;
+    for (int q = 0; q < KPT; q += 4) {
+      const uint4 w = *reinterpret_cast<const uint4*>(stage + min(tid * per + q, NT * KPT - 4));
+      key[q] = w.x;
+      key[q + 1] = w.y;
+      key[q + 2] = w.z;
+      key[q + 3] = w.w;
     }
   }
-  write_mask(m, L, lo, hi, k_heavy > 0, prefix, k, key_at, scan_tmp);
+  // Every candidate once, in any order (the histogram passes). Register path:
+  // the thread's own keys. Memory path: slots strided over the workgroup
+  // (coalesced), KPT unconditional loads from clamped slots in flight at a time.
+  auto for_keys = [&](auto f) {
+    if (REG) {
+#pragma unroll
+      for (int q = 0; q < KPT; ++q)
+        if (q < cnt) f(key[q]);
+    } else {
+      for (int base = lo + tid; base < hi; base += KPT * NT) {
+        unsigned kk[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) kk[j] = order_key(row[min(base + j * NT, hi - 1)]);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (base + j * NT < hi) f(kk[j]);
+      }
+    }
+  };
+  // The thread's contiguous candidates in slot order: f(slot, key).
+  auto for_own = [&](auto f) {
+    if (REG) {
+#pragma unroll
+      for (int q = 0; q < KPT; ++q)
+        if (q < cnt) f(i0 + q, key[q]);
+    } else {
+      for (int q0 = 0; q0 < cnt; q0 += KPT) {
+        unsigned kk[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) kk[j] = order_key(row[i0 + min(q0 + j, cnt - 1)]);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (q0 + j < cnt) f(i0 + q0 + j, kk[j]);
+      }
+    }
+  };
+  const bool any_heavy = k > 0;
+  unsigned T = 0;
+  if (any_heavy) T = radix_threshold<NT>(for_keys, k, hist, scan_tmp, mm_tmp, sel);
+
+  // Sinks and the recent window are always kept.
+  const int n_heavy = budget - n_sink - n_recent;
+  for (int i = tid; i < lo; i += NT) {
+    m[i] = 1;
+    if (kidx) kidx[i] = i;
+  }
+  for (int i = hi + tid; i < L; i += NT) {
+    m[i] = 1;
+    if (kidx) kidx[lo + n_heavy + (i - hi)] = i;
+  }
+  // Candidates: rank the threshold ties in slot order; with a gather list,
+  // also count the candidates above T before this thread.
+  int ties = 0, above = 0;
+  for_own([&](int, unsigned u) {
+    ties += any_heavy & (u == T);
+    above += any_heavy & (u > T);
+  });
+  int tie_rank = block_inclusive_scan<NT>(ties, scan_tmp) - ties;
+  // Kept before this thread = candidates above T before it + ties kept before it.
+  int out = kidx ? block_inclusive_scan<NT>(above, scan_tmp) - above + min(tie_rank, k) : 0;
+  for_own([&](int i, unsigned u) {
+    uint8_t keepb = 0;
+    if (any_heavy) {
+      if (u > T) {
+        keepb = 1;
+      } else if (u == T) {
+        keepb = tie_rank < k;
+        ++tie_rank;
+      }
+    }
+    m[i] = keepb;
+    if (kidx && keepb) kidx[lo + out++] = i;
+  });
 }
 
 }  // namespace
 
 hipError_t launch_select(const kvc_cache_t& c, const float* score, int budget, int n_sink, int n_recent,
-                         uint8_t* mask, int max_len, hipStream_t st) {
+                         uint8_t* mask, int32_t* keep_index, int max_len, hipStream_t st) {
   const long long cand = (long long)max_len - n_sink - n_recent;
-  if (cand <= (long long)NT * kRegKeys)
-    hipLaunchKernelGGL(select_reg_kernel, dim3(c.num_kv_heads, c.batch), dim3(NT), 0, st, c, score, budget, n_sink,
-                       n_recent, mask, max_len);
+  const dim3 grid(c.num_kv_heads, c.batch);
+  if (cand <= 256 * 32)
+    hipLaunchKernelGGL((select_kernel<256, 32, true>), grid, dim3(256), 0, st, c, score, budget, n_sink, n_recent,
+                       mask, keep_index, max_len);
   else
-    hipLaunchKernelGGL(select_radix_kernel, dim3(c.num_kv_heads, c.batch), dim3(NT), 0, st, c, score, budget,
-                       n_sink, n_recent, mask, max_len);
+    hipLaunchKernelGGL((select_kernel<1024, 8, false>), grid, dim3(1024), 0, st, c, score, budget, n_sink,
+                       n_recent, mask, keep_index, max_len);
   return hipGetLastError();
 }
 

@@ -169,9 +169,6 @@ int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_h
                         float* out, float* h2o_score, int32_t max_len_hint,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes kvc_h2o_select needs (may be 0). */
-size_t kvc_h2o_select_workspace_bytes(const kvc_cache_t* cache, int32_t max_len_hint);
-
 /*
  * Keep-set selection: attention sinks + recent window + heavy hitters.
  * Sources: "KV Cache Compression Report", section 3.3 (the first 4 tokens
@@ -185,16 +182,18 @@ size_t kvc_h2o_select_workspace_bytes(const kvc_cache_t* cache, int32_t max_len_
  *                k = budget - n_sink - n_recent slots of [n_sink, L - n_recent)
  *                with the largest h2o_score; equal scores go to the lower slot.
  * keep_mask: device uint8 [batch][num_kv_heads][capacity]; slots < L get 1 or 0,
- * slots >= L are left untouched. h2o_score must hold non-negative, non-NaN
- * values (attention mass always is).
- * Errors: INVALID_ARG for a bad descriptor, NULL pointers, budget < 1,
- * n_sink < 0, n_recent < 0, n_sink + n_recent > budget, or a workspace
- * smaller than required; CAPACITY if budget or max_len_hint > capacity.
+ * slots >= L are left untouched. keep_index (may be NULL): device int32
+ * [batch][num_kv_heads][budget]; entries j < min(L, budget) receive the kept
+ * slots in ascending order (the gather list kvc_compact_gather takes); later
+ * entries are left untouched. h2o_score must hold non-negative, non-NaN values
+ * (attention mass always is).
+ * Errors: INVALID_ARG for a bad descriptor, NULL score or mask, budget < 1,
+ * n_sink < 0, n_recent < 0 or n_sink + n_recent > budget; CAPACITY if budget
+ * or max_len_hint > capacity.
  */
 int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t budget,
-                       int32_t n_sink, int32_t n_recent, uint8_t* keep_mask,
-                       int32_t max_len_hint, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       int32_t n_sink, int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index,
+                       int32_t max_len_hint, void* stream);
 
 /* Workspace bytes kvc_compact needs. */
 size_t kvc_compact_workspace_bytes(const kvc_cache_t* src, int32_t max_len_hint);
@@ -221,6 +220,22 @@ size_t kvc_compact_workspace_bytes(const kvc_cache_t* src, int32_t max_len_hint)
 int32_t kvc_compact(const kvc_cache_t* src, const float* src_score, const uint8_t* keep_mask,
                     const kvc_cache_t* dst, float* dst_score, int32_t max_len_hint,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Compaction from a gather list, the form kvc_h2o_select emits in keep_index.
+ * Same result and sources as kvc_compact: for each (b, g) row, destination
+ * slot j takes source slot keep_index[b][g][j] (K and V codes and scales,
+ * positions when both caches have them, scores when both score arrays are
+ * given) for j < min(lengths[b], n_keep); dst->lengths[b] is set to that count
+ * and dst->num_seen[b] to src->num_seen[b]. keep_index: device int32
+ * [batch][num_kv_heads][n_keep], ascending within a row; an index outside
+ * [0, capacity) is clamped into it (no out-of-bounds access, a wrong result).
+ * No workspace and no scan: one launch that starts copying at once.
+ * Errors: as kvc_compact, plus INVALID_ARG for a NULL list or n_keep < 1 and
+ * CAPACITY for n_keep > capacity.
+ */
+int32_t kvc_compact_gather(const kvc_cache_t* src, const float* src_score, const int32_t* keep_index,
+                           int32_t n_keep, const kvc_cache_t* dst, float* dst_score, void* stream);
 
 /*
  * Paged block pool (host only; no device memory is touched).

@@ -119,7 +119,7 @@ def test_decode_attn_validation():
 def test_select_validation():
     d = desc()
     sel = lambda budget, s, r, hint=16, score=FAKE, mask=FAKE: lib.kvc_h2o_select(
-        ctypes.byref(d), score, budget, s, r, mask, hint, None, 0, None)
+        ctypes.byref(d), score, budget, s, r, mask, None, hint, None)
     assert sel(0, 0, 0) == INVALID
     assert sel(8, 5, 4) == INVALID
     assert sel(8, -1, 0) == INVALID
@@ -150,6 +150,14 @@ def test_compact_validation():
     assert call(src, dst, hint=513) == CAPACITY
     paged = desc(block_size=16, max_blocks_per_seq=32, num_blocks=8, positions=None, block_table=FAKE)
     assert call(paged, dst) == UNSUPPORTED
+    gather = lambda s_, d_, idx=0x5000000, n=16: lib.kvc_compact_gather(ctypes.byref(s_), None, idx, n,
+                                                                        ctypes.byref(d_), None, None)
+    assert gather(src, bad) == INVALID
+    assert gather(src, dst, idx=None) == INVALID
+    assert gather(src, dst, n=0) == INVALID
+    assert gather(src, dst, n=513) == CAPACITY
+    assert gather(src, dst, idx=0x1100000) == INVALID   # list overlaps dst codes
+    assert gather(paged, dst) == UNSUPPORTED
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 512) >= 4 * 1 * 4
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 2048) == 0   # beyond capacity
 

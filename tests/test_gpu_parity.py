@@ -147,14 +147,19 @@ def test_select_bit_exact_on_shared_scores(L, budget, S, R):
     gc.lengths.fill_(L)
     score = dev(np.pad(sc, ((0, 0), (0, 0), (0, cap - L))))
     mask = torch.full((B, H, cap), 9, dtype=torch.uint8, device="cuda")
-    kvc.kvc_h2o_select(gc, score, budget, S, R, mask, max_len_hint=L)
+    kidx = torch.full((B, H, budget), -7, dtype=torch.int32, device="cuda")
+    kvc.kvc_h2o_select(gc, score, budget, S, R, mask, keep_index=kidx, max_len_hint=L)
     m = host(mask)
     assert np.all(m[:, :, L:] == 9)          # slots past the length are untouched
     m = m[:, :, :L].astype(bool)
+    ki = host(kidx)
+    n_keep = min(L, budget)
+    assert np.all(ki[:, :, n_keep:] == -7)
     for b in range(B):
         for g in range(H):
             ref = oracle.select_keep(sc[b, g].astype(np.float64), L, budget, S, R)
             assert np.array_equal(m[b, g], ref), (b, g)
+            assert np.array_equal(ki[b, g, :n_keep], np.nonzero(ref)[0]), (b, g)
 
 
 @pytest.mark.parametrize("bits,D,L,keep_n", [(8, 128, 2500, 900), (4, 128, 2500, 900), (8, 64, 2500, 900),
@@ -176,12 +181,18 @@ def test_compact_bit_exact(bits, D, L, keep_n):
     dst = make_gpu_cache(w, cap, bits)
     dst_score = dst.score_buffer()
     kvc.kvc_compact(gc, score, dev(mask), dst, dst_score)
+    # The same compaction from the ascending keep list.
+    kidx = np.stack([np.stack([np.nonzero(mask[b, g])[0] for g in range(H)]) for b in range(B)]).astype(np.int32)
+    dst2 = make_gpu_cache(w, cap, bits)
+    dst2_score = dst2.score_buffer()
+    kvc.kvc_compact_gather(gc, score, dev(kidx), keep_n, dst2, dst2_score)
     torch.cuda.synchronize()
     ref.score[:] = sc
     ref.compact(mask.astype(bool))
-    assert_codes_equal(dst, ref)
-    assert np.array_equal(host(dst_score)[:, :, :keep_n], sc[np.nonzero(mask)].reshape(B, H, keep_n))
-    assert host(dst.num_seen).tolist() == [L] * B
+    for out, out_score in ((dst, dst_score), (dst2, dst2_score)):
+        assert_codes_equal(out, ref)
+        assert np.array_equal(host(out_score)[:, :, :keep_n], sc[np.nonzero(mask)].reshape(B, H, keep_n))
+        assert host(out.num_seen).tolist() == [L] * B
 
 
 # ------------------------------------------------------- whole decode step --
@@ -194,15 +205,26 @@ def _full_step(w, d, prior=()):
     err = assert_out_close(out, ro)
     rel = assert_scores_close(host(score), ref.score, ref.lengths)
     mask = torch.zeros((w.batch, w.num_kv_heads, gc.capacity), dtype=torch.uint8, device="cuda")
-    kvc.kvc_h2o_select(gc, score, w.budget, w.n_sink, w.n_recent, mask)
+    kidx = torch.zeros((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device="cuda")
+    kvc.kvc_h2o_select(gc, score, w.budget, w.n_sink, w.n_recent, mask, keep_index=kidx)
     torch.cuda.synchronize()
     amb = assert_keep_equivalent(host(mask), ref.score, ref.lengths, w.budget, w.n_sink, w.n_recent)
-    # Compact on the GPU with the oracle's mask so that both caches keep the
-    # same tokens, then compare the compacted caches bit for bit.
+    m, ki = host(mask), host(kidx)
+    for b in range(w.batch):   # the keep list is the mask's kept slots, ascending
+        L = int(ref.lengths[b])
+        for g in range(w.num_kv_heads):
+            assert np.array_equal(ki[b, g, :min(L, w.budget)], np.nonzero(m[b, g, :L])[0])
+    # Compact on the GPU with the oracle's keep list so that both caches keep
+    # the same tokens, then compare the compacted caches bit for bit.
     keep_ref = ref.select(w.budget, w.n_sink, w.n_recent)
+    ref_list = np.zeros((w.batch, w.num_kv_heads, w.budget), np.int32)
+    for b in range(w.batch):
+        for g in range(w.num_kv_heads):
+            idx = np.nonzero(keep_ref[b, g])[0]
+            ref_list[b, g, :len(idx)] = idx
     dst = make_gpu_cache(w, gc.capacity)
     dst_score = dst.score_buffer()
-    kvc.kvc_compact(gc, score, dev(keep_ref.astype(np.uint8)), dst, dst_score)
+    kvc.kvc_compact_gather(gc, score, dev(ref_list), w.budget, dst, dst_score)
     torch.cuda.synchronize()
     ref.compact(keep_ref)
     assert_codes_equal(dst, ref)
