@@ -36,6 +36,25 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn KV GB/s & tokens/s (fraction of HBM peak), INT8, L=8192, 1 GPU"
+
+# HBM bytes one decode-attention launch (split + combine) moves on this
+# workload, from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by the same
+# counters on a plain 64 MiB device copy. The figure holds only for the
+# attention sources it was taken on; any change to them reports null.
+TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
+                   "compressed_kv_cache_kvc_amd/csrc/kvc_internal.h",
+                   "compressed_kv_cache_kvc_amd/csrc/api.hip")
+TRAFFIC_SHA256 = "28d30a89ae24b083e688d9a3dd5771b597930ac96609d0754f01fb9df2747921"
+TRAFFIC_BYTES = 76404443
+
+
+def attention_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return TRAFFIC_BYTES if h.hexdigest() == TRAFFIC_SHA256 else None
 HBM_PEAK_GBPS = 8000.0
 LAYERS = 32
 
@@ -83,6 +102,27 @@ def cpu_baseline(w, d, budget_s=12.0):
     return min(times), len(times), cores
 
 
+def copy_calibration(torch, mib):
+    """Eight copies of ``mib`` MiB between two device buffers: each launch
+    reads and writes exactly ``mib`` MiB, so per-dispatch FETCH_SIZE and
+    WRITE_SIZE of this kernel give the counters' scale in bytes."""
+    torch.cuda.set_device(0)
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(8):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / 8
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "us_per_copy": round(us, 2),
+                      "gbps_read_plus_write": round(2 * n / (us * 1e-6) / 1e9, 1)}))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +130,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the benchmark, run 8 plain device-to-device copies of this many MiB "
+                         "(the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -99,6 +142,8 @@ def main(argv=None):
         return 2
 
     import torch
+    if args.copy_mib:
+        return copy_calibration(torch, args.copy_mib)
     import compressed_kv_cache_kvc_amd as kvc
     from workloads import draw, get
 
@@ -228,7 +273,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": attention_traffic(),
         },
     }
     if not args.no_cpu_baseline:
