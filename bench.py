@@ -173,7 +173,7 @@ def main(argv=None):
     dst_score = dst.score_buffer()
     k_new, v_new, q = dev(d["k"][:, :, L - 1:]), dev(d["v"][:, :, L - 1:]), dev(d["q"])
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
-    ws_attn = torch.empty(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, L, True), dtype=torch.uint8,
+    ws_attn = torch.zeros(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, L, True), dtype=torch.uint8,
                           device="cuda")
     torch.cuda.synchronize()
 

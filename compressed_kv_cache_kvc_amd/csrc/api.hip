@@ -84,9 +84,9 @@ struct AttnGeom {
 };
 
 // Launch geometry of the decode-attention kernels. A split covers `tiles`
-// 256-token tiles; tiles are grouped so that the grid still has about 1024
-// workgroups (4 per CU on 256 CUs), which keeps the cross-split merge short
-// for long contexts.
+// 256-token tiles (one 64-token block per wave per tile); tiles are grouped so
+// that the grid has about 512 workgroups (2 per CU on 256 CUs, all resident);
+// longer contexts loop over tiles.
 int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t with_h2o, AttnGeom* g) {
   int32_t st = check_cache(c, "cache");
   if (st) return st;
@@ -101,11 +101,8 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
   if (c->block_size && (long long)c->num_blocks * c->num_kv_heads * c->block_size * rb >= (1LL << 32))
     return fail(KVC_ERR_UNSUPPORTED, "paged pools must stay below 4 GiB of codes");
   const long long tiles_total = (hint + kSplitTokens - 1) / kSplitTokens;
-  long long nt = 1;
-  if (G <= attn_heads_per_pass(G)) {
-    const long long rows = (long long)c->batch * c->num_kv_heads;
-    nt = std::max(1LL, tiles_total * rows / 1024);
-  }
+  const long long rows = (long long)c->batch * c->num_kv_heads;
+  const long long nt = std::max(1LL, tiles_total * rows / 512);
   const long long S = (tiles_total + nt - 1) / nt;
   if (S * (G + 2) > 16384) return fail(KVC_ERR_UNSUPPORTED, "too many splits for one KV head (%lld x %d)", S, G);
   const size_t BH = (size_t)c->batch * Hq;

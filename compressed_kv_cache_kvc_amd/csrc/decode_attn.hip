@@ -1,126 +1,139 @@
 // Single-query decode attention over an INT8/INT4 KV cache, dequantization fused.
 //
 // Computes softmax(q K^T / sqrt(D)) V ("KV Cache Compression Report", section
-// 1.1) reading the quantized cache directly; a key or value is code * scale
-// (section 3.2 of the report), and the scale is applied once per token
-// instead of per element: s_i = (q . code_i) * scale_i / sqrt(D) and
-// o = sum_i (p_i * scale_i) * code_i.
+// 1.1) straight from the quantized cache. A key or value is code * scale
+// (section 3.2 of the report), and the scale is applied once per token rather
+// than per element: s_i = (q . code_i) * kscale_i / sqrt(D) and
+// o = sum_i (p_i * vscale_i) * code_i.
+//
+// Both contractions run on the int8 matrix cores (v_mfma_i32_16x16x64_i8),
+// with the cache codes as one operand, unconverted:
+//  * q . code: q (fp16) is split per head into four int8 limbs,
+//    q = 2^-E (a0 + a1/2^7 + a2/2^14 + a3/2^21), exact to 2^-27 of max|q|.
+//    Rows of the A operand are (head, limb) pairs, the B operand is 16 tokens
+//    x 64 codes read straight from HBM, and the integer sums are exact, so
+//    the only roundings are the final combination of the four limb sums;
+//  * p . V: the weights w_i = p_i * vscale_i of a 64-token block are split the
+//    same way (exponent from the block maximum), and V, staged in LDS, is read
+//    transposed (ds_read_b64_tr_b8) so that each lane holds 16 tokens of one
+//    channel, the layout of the B operand.
+// INT4 codes are widened to bytes holding code + 8; the +8 is taken out of
+// the integer sums (q side) or as 8 * sum(w) (V side).
 //
 // Split-K (flash-decoding) layout for gfx950:
-//  * grid (splits, KV heads, sequences); a 256-thread workgroup (4 waves of 64)
-//    owns `tiles` consecutive 256-token tiles of one (sequence, KV head) and
-//    serves the query heads that read that KV head (GQA), HC at a time;
-//  * a token row (RB = D*bits/8 bytes) is read by LPT lanes, 16 bytes each for
-//    INT8 and 8 bytes each for INT4 (16 elements per lane either way); a lane
-//    group owns IT consecutive tokens of a tile, so each load is a full row
-//    segment;
-//  * loads are raw buffer loads: K and V share one 32-bit lane offset, the
-//    bases sit in scalar registers, and reads past the sequence length return
-//    zeros, so the ragged tail needs no branches;
-//  * all K and V loads of a tile are issued before any arithmetic (64 KB in
-//    flight per workgroup), and the kernel is shaped to keep 4 workgroups per
-//    CU resident for the single-head case;
-//  * q.k uses v_dot2_f32_f16 on codes turned into fp16 exactly (byte | 0x6400
-//    is 1024 + byte; subtracting 1024 + the code bias recovers the code), so
-//    the products are exact and only the fp32 sums round;
-//  * each wave keeps its own online softmax (running max, sum, output) over
-//    its tokens of every tile, so the tile loop has no barrier; the four waves
-//    merge once at the end and the split writes (max, sum, o[D]);
-//  * a second kernel merges the splits in a fixed order (deterministic).
+//  * grid (splits, KV heads, sequences); a 256-thread workgroup owns `tiles`
+//    256-token tiles of one (sequence, KV head) row and serves every query
+//    head of that KV head (GQA), up to 8 per pass;
+//  * each wave owns one 64-token block of every tile. It issues the block's
+//    loads at once, raw buffer loads bounded by the cache capacity: scales,
+//    then K codes (registers, in the B-operand layout), then V codes, which
+//    INT8 caches move straight into the wave's LDS staging area (LDS DMA).
+//    The first block's loads go out before the sequence length is known;
+//    tokens past it are masked by selects;
+//  * V rows are staged token-major with their 16-byte chunks XOR-swizzled per
+//    row, so that every transposed read touches each LDS bank exactly twice;
+//  * the online softmax keeps one token per lane, so exp2 runs once per
+//    (head, token);
+//  * the four waves merge once at the end and the split writes (max, sum,
+//    o[D]); a second kernel merges the splits in a fixed order (deterministic).
 // Logits are kept in log2 units (scaled by log2(e)) and exponentiated with exp2.
 //
 // H2O (report section 3.4; eviction-and-reuse survey section 3.3): with a
 // score array, the split kernel also spills each logit; the merge kernel turns
 // it into p_i = exp2(s_i - m) / l with the global (m, l) of its query head and
 // adds the sum over the group's query heads to score[b][g][i].
+#include <type_traits>
+
 #include "kvc_internal.h"
 
 namespace kvc {
 namespace {
 
-constexpr int TS = kSplitTokens;
+constexpr int TS = kSplitTokens;  // tokens per tile: 4 waves x 64
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-template <int BITS>
-struct Chunk;
-template <>
-struct Chunk<8> {
-  using T = u32x4;  // 16 bytes = 16 INT8 codes
-};
-template <>
-struct Chunk<4> {
-  using T = u32x2;  // 8 bytes = 16 INT4 codes
-};
-
-__device__ __forceinline__ half2_t as_h2(unsigned w) { return __builtin_bit_cast(half2_t, w); }
-
-// 4 INT8 codes (one dword) -> two fp16 pairs holding the exact code values,
-// element order (0,1) and (2,3).
-__device__ __forceinline__ void i8x4_to_h2(unsigned w, half2_t& a, half2_t& b) {
-  const unsigned u = w ^ 0x80808080u;  // code + 128 in each byte
-  const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  a = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias;
-  b = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias;
-}
-
-// 8 INT4 codes (one dword) -> four fp16 pairs, element order (0,4) (1,5) (2,6) (3,7).
-__device__ __forceinline__ void i4x8_to_h2(unsigned w, half2_t* o) {
-  const unsigned u = w ^ 0x88888888u;  // code + 8 in each nibble
-  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) o[k] = as_h2(((u >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - bias;
-}
-
-template <int BITS>
-__device__ __forceinline__ float code_at(const unsigned* w, int e) {
-  if (BITS == 8) return (float)(signed char)(w[e >> 2] >> (8 * (e & 3)));
-  return (float)((int)(w[e >> 3] << (28 - 4 * (e & 7))) >> 28);  // sign-extended nibble
-}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit dword format).
 constexpr int kBufferFlags = 0x00020000;
 
-template <typename CT>
-__device__ __forceinline__ CT load_chunk(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  if constexpr (sizeof(CT) == 16)
-    return __builtin_bit_cast(CT, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  else
-    return __builtin_bit_cast(CT, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+__device__ __forceinline__ i32x4 load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-
+__device__ __forceinline__ i32x2 load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ i32x4 mfma(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Sum over an aligned group of LPT consecutive lanes (LPT = 2, 4, 8 or 16), with
-// DPP lane permutes: xor 1, xor 2, then the half-row and row mirrors.
-template <int LPT>
-__device__ __forceinline__ float group_sum(float v) {
-  if (LPT >= 2) v += dpp<0xB1>(v);
-  if (LPT >= 4) v += dpp<0x4E>(v);
-  if (LPT >= 8) v += dpp<0x141>(v);
-  if (LPT >= 16) v += dpp<0x140>(v);
-  return v;
+// 16 INT4 codes (8 bytes, element 2j in the low nibble of byte j) -> 16 bytes
+// holding code + 8 (0..15). Byte i of the result holds element
+// int4_elem(i): bytes 0-3 elements 0,2,4,6; 4-7 1,3,5,7; 8-11 8,10,12,14;
+// 12-15 9,11,13,15.
+__device__ __forceinline__ i32x4 widen_int4(i32x2 w) {
+  const unsigned u0 = (unsigned)w[0] ^ 0x88888888u, u1 = (unsigned)w[1] ^ 0x88888888u;
+  return i32x4{(int)(u0 & 0x0F0F0F0Fu), (int)((u0 >> 4) & 0x0F0F0F0Fu), (int)(u1 & 0x0F0F0F0Fu),
+               (int)((u1 >> 4) & 0x0F0F0F0Fu)};
+}
+__device__ __forceinline__ int int4_elem(int i) { return (i & 8) | ((i & 3) << 1) | ((i >> 2) & 1); }
+__device__ __forceinline__ int int4_byte(int e) { return (e & 8) | ((e & 1) << 2) | ((e >> 1) & 3); }
+
+// a0 + a1 / 2^7 + a2 / 2^14 + a3 / 2^21 for the four limb sums of one MFMA
+// output row group (each below 2^24 in magnitude, so exact in fp32).
+__device__ __forceinline__ float limb_sum(i32x4 c) {
+  float t = (float)c[3] * 0x1p-21f;
+  t = fmaf((float)c[2], 0x1p-14f, t);
+  t = fmaf((float)c[1], 0x1p-7f, t);
+  return t + (float)c[0];
 }
 
-// Sum (or max) over the lanes of a wave that share lane % LPT: DPP row
-// rotations inside each 16-lane row, then cross-row exchanges.
-template <int LPT, bool MAX>
-__device__ __forceinline__ float stride_reduce(float v) {
-  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
-  if (LPT <= 2) v = op(v, dpp<0x122>(v));
-  if (LPT <= 4) v = op(v, dpp<0x124>(v));
-  if (LPT <= 8) v = op(v, dpp<0x128>(v));
-  v = op(v, __shfl_xor(v, 16));
-  v = op(v, __shfl_xor(v, 32));
+// Split y (|y| < 64) into four limbs: y = a0 + a1/2^7 + a2/2^14 + a3/2^21 + r,
+// |r| <= 2^-22, each |a| <= 64. Every step is exact in fp32.
+__device__ __forceinline__ void to_limbs(float y, int* l) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = rintf(y);
+    l[k] = (int)a;
+    y = (y - a) * 128.f;
+  }
+}
+
+// Exponent E with max * 2^E in [32, 64): then every scaled value is below 64
+// in magnitude and its leading limb fits the int8 range. 0 for max == 0.
+__device__ __forceinline__ int limb_exponent(float mx) {
+  int ex = 0;
+  frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+  return mx > 0.f ? 6 - ex : 0;
+}
+
+template <bool MAX>
+__device__ __forceinline__ float op2(float a, float b) {
+  return MAX ? fmaxf(a, b) : a + b;
+}
+
+// Reduction over the lanes that hold one query head in the logit layout:
+// all 64 lanes (GP = 1), lane rows r and r ^ 2 (GP = 2) or one 16-lane row
+// (GP >= 4). Every lane receives the result of its head.
+template <int GP, bool MAX>
+__device__ __forceinline__ float head_reduce(float v) {
+  v = op2<MAX>(v, dpp_f<0xB1>(v, v));
+  v = op2<MAX>(v, dpp_f<0x4E>(v, v));
+  v = op2<MAX>(v, dpp_f<0x141>(v, v));
+  v = op2<MAX>(v, dpp_f<0x140>(v, v));
+  if (GP == 1) {
+    const float id = MAX ? v : 0.f;  // what the masked-off rows of a broadcast combine with
+    v = op2<MAX>(v, dpp_f<0x142, 0xA>(id, v));
+    v = op2<MAX>(v, dpp_f<0x143, 0xC>(id, v));
+    v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  } else if (GP == 2) {
+    v = op2<MAX>(v, __shfl_xor(v, 32));
+  }
   return v;
 }
 
@@ -135,37 +148,61 @@ __device__ __forceinline__ float part_weight(float m_part, float m_total) {
   return m_part == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_part - m_total);
 }
 
-template <int BITS, int D, int HC, bool PAGED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HC == 1 ? 4 : 2)))
-void attn_split_kernel(AttnLaunch a) {
-  using CT = typename Chunk<BITS>::T;
-  constexpr int RB = D * BITS / 8;
-  constexpr int CB = (int)sizeof(CT);
-  constexpr int EPL = 16;
-  constexpr int NW = CB / 4;          // dwords per lane chunk
-  constexpr int LPT = RB / CB;        // lanes per token
-  constexpr int TPI = 64 / LPT;       // lane groups per wave
-  constexpr int IT = 64 / TPI;        // tokens per lane group per tile
-  static_assert(RB % CB == 0 && 64 % LPT == 0 && IT >= 1 && 16 % IT == 0, "layout");
+__device__ __forceinline__ unsigned sel4(const unsigned* v, int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+// GP: query heads served per pass, padded to 1, 2, 4 or 8.
+//
+// Logit layout of a 64-token block: NC = GP accumulators; lane l of
+// accumulator c holds (head, token) = (j % GP, 16 * (j / GP) + l % 16) with
+// j = 4c + l / 16, i.e. one token per lane for GP = 1 and one head per 16-lane
+// row for GP >= 4. The PV output of row set rs holds head 4 rs + l / 16 (the
+// same head as the lane's logits) and channel 16 m + l % 16 of block m.
+template <int BITS, int D, int GP, bool PAGED>
+__global__ __launch_bounds__(256) void attn_split_kernel(AttnLaunch a) {
+  constexpr int RB = D * BITS / 8;          // bytes per token row in HBM
+  constexpr int KB = BITS == 8 ? 16 : 8;    // HBM bytes per lane per load (16 elements)
+  constexpr int NDH = D / 64;               // 64-element halves of a row (QK k = 64)
+  constexpr int NCB = D / 16;               // 16-channel blocks (PV n = 16) = lanes per V row
+  constexpr int TPV = 64 / NCB;             // tokens per V load instruction
+  constexpr int NC = GP;                    // logit accumulators per block
+  constexpr int NRS = GP > 4 ? GP / 4 : 1;  // PV row sets (4 heads each)
+  constexpr int NQ = GP > 4 ? GP / 4 : 1;   // q limb rows held per lane (one per row set)
+  constexpr int NSC = GP >= 4 ? 4 : GP;     // scale loads per block
+  constexpr int VROW = D;                   // staged V row stride in LDS (chunks XOR-swizzled, see vchunk)
+  static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "GP");
+  // LDS chunk (16 bytes) of staged token row t that holds V chunk m: the XOR
+  // makes the 64 lanes of a transposed read (tokens 16 q + 0..7 or 8..15 of
+  // one chunk, q = 0..3) touch every LDS bank exactly twice.
+  auto vchunk = [](int t, int m) -> int {
+    return NCB == 8 ? (m ^ (((t >> 1) ^ ((t >> 4) << 2)) & 7)) : (m ^ (((t >> 2) ^ (t >> 4)) & 3));
+  };
 
   const kvc_cache_t& c = a.c;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = lane / LPT, sub = lane - grp * LPT;
+  const int quad = lane >> 4, col = lane & 15;
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits, NT = a.tiles;
   const long long span = (long long)S * NT * TS;  // logit slots per query head
   // Uniform by construction; readfirstlane keeps it (and the buffer resources
   // built from it) in scalar registers.
   const int L = __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), (int)span));
 
-  __shared__ float red_m[4][HC];
-  __shared__ float red_l[4][HC];
-  __shared__ float red_o[4][HC][D];
+  __shared__ __align__(16) uint8_t v_stage[4][64 * VROW];
+  __shared__ __align__(16) int8_t w_limb[4][NRS][16][64];
+  __shared__ __align__(16) int8_t q_limb[GP][4][D];
+  __shared__ float q_fac[GP], q_off[GP];
+  __shared__ float red_m[4][GP], red_l[4][GP];
+  float* red_o = reinterpret_cast<float*>(&v_stage[0][0]);  // [4][GP][D], used after the block loop
+  static_assert(4 * GP * D * 4 <= 4 * 64 * VROW, "merge buffer fits the staging area");
 
-  // Contiguous: one resource per (sequence, KV head) row limited to L tokens.
-  // Paged: one resource over the whole pool (the host checks it is below
-  // 4 GiB) and a block lookup per lane group; IT divides the block size, so a
-  // group's IT tokens of a tile sit in one block.
+  // Contiguous: one resource per (sequence, KV head) row of `capacity` tokens;
+  // rows past the capacity read 0. Paged: one resource over the whole pool
+  // (the host checks it is below 4 GiB); a 16-token page of a missing block
+  // maps past the end and reads 0. Neither depends on the sequence length, so
+  // the first loads go out before it is known; slots in [L, capacity) hold
+  // stale but finite codes, and every token past L is masked by selects.
   __amdgpu_buffer_rsrc_t rk, rv, rks, rvs;
   unsigned pool_rows = 0;
   if (PAGED) {
@@ -176,189 +213,329 @@ void attn_split_kernel(AttnLaunch a) {
     rvs = __builtin_amdgcn_make_buffer_rsrc(c.v_scale, 0, pool_rows * 4, kBufferFlags);
   } else {
     const long long base = ((long long)b * H + g) * c.capacity;
-    const unsigned valid = (unsigned)max(L, 0);
+    const unsigned valid = (unsigned)c.capacity;
     rk = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(c.k_codes) + base * RB, 0, valid * RB, kBufferFlags);
     rv = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(c.v_codes) + base * RB, 0, valid * RB, kBufferFlags);
     rks = __builtin_amdgcn_make_buffer_rsrc(c.k_scale + base, 0, valid * 4, kBufferFlags);
     rvs = __builtin_amdgcn_make_buffer_rsrc(c.v_scale + base, 0, valid * 4, kBufferFlags);
   }
-  const float qk_scale = a.qk_log2;
 
-  for (int hc = 0; hc < G; hc += HC) {
-    // ---- q slice for this lane's 16 elements, as fp16 pairs in code order ----
-    half2_t qv[HC][8];
+  // This wave's blocks: block `it` starts at token t0(it) and holds tokens
+  // below L only for it < nb.
+  auto block_t0 = [&](int it) { return ((s * NT + it) * 4 + wave) * 64; };
+  const int nb = max(0, min(NT, (L - ((s * NT) * 4 + wave) * 64 + 255) / 256));
+
+  // Registers of one block's loads; two sets keep two blocks in flight.
+  using KT = typename std::conditional<BITS == 8, i32x4, i32x2>::type;
+  struct Regs {
+    KT kq[4][NDH], vq[BITS == 8 ? 1 : NCB];
+    float ksv[NSC], vsv[NSC];
+  };
+  // Issue every load of block `it`: K and V scales, then K codes into `r`,
+  // then V codes (INT8: straight into this wave's LDS staging area, swizzled;
+  // INT4: into `r`). Waiting for the scales and K (loads return in order)
+  // does not wait for V. Rows of contiguous caches are tokens; paged rows come
+  // from the block's four 16-token pages.
+  auto issue = [&](Regs& r, int it) {
+    unsigned pb[4];
+    const int t0 = block_t0(it);
+    if (PAGED) {
 #pragma unroll
-    for (int i = 0; i < HC; ++i) {
-      if (hc + i < G) {
-        const __half* qh = a.q + ((long long)b * Hq + g * G + hc + i) * D + sub * EPL;
-        const uint4 q0 = reinterpret_cast<const uint4*>(qh)[0];
-        const uint4 q1 = reinterpret_cast<const uint4*>(qh)[1];
-        const unsigned qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        if (BITS == 8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qv[i][e] = as_h2(qw[e]);
-        } else {
-          // INT4 pairs are (k, k+4) within each group of 8 elements.
-#pragma unroll
-          for (int w8 = 0; w8 < 2; ++w8)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const unsigned lo = (qw[w8 * 4 + (k >> 1)] >> (16 * (k & 1))) & 0xFFFFu;
-              const unsigned hi = (qw[w8 * 4 + 2 + (k >> 1)] >> (16 * (k & 1))) & 0xFFFFu;
-              qv[i][w8 * 4 + k] = as_h2(lo | (hi << 16));
-            }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[i][e] = half2_t{};
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * i;
+        const int blk = t < c.capacity ? c.block_table[(long long)b * c.max_blocks_per_seq + t / 16] : -1;
+        pb[i] = __builtin_amdgcn_readfirstlane((unsigned)blk < (unsigned)c.num_blocks ? (unsigned)((blk * H + g) * 16)
+                                                                                     : pool_rows);
       }
     }
+    auto row_static = [&](int page, int t) -> unsigned {  // page known at compile time
+      return PAGED ? pb[page] + (unsigned)(t & 15) : (unsigned)(t0 + t);
+    };
+#pragma unroll
+    for (int si = 0; si < NSC; ++si) {
+      const int t = GP >= 8 ? 16 * si + col : 16 * ((4 * si + quad) / GP) + col;
+      const unsigned row = PAGED ? sel4(pb, t >> 4) + (unsigned)(t & 15) : (unsigned)(t0 + t);
+      r.ksv[si] = load_f32(rks, row * 4);
+      r.vsv[si] = load_f32(rvs, row * 4);
+    }
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+      for (int dh = 0; dh < NDH; ++dh) {
+        const unsigned off = row_static(tg, 16 * tg + col) * RB + dh * (RB / NDH) + quad * KB;
+        if constexpr (BITS == 8) r.kq[tg][dh] = load16(rk, off); else r.kq[tg][dh] = load8(rk, off);
+      }
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      // Lane l fills LDS chunk l % NCB of token row TPV j + l / NCB (DMA
+      // writes lane l at 16 l), so it fetches the V chunk that belongs there.
+      const int t = TPV * j + lane / NCB;
+      if constexpr (BITS == 8) {
+        const unsigned off = row_static((TPV * j) >> 4, t) * RB + vchunk(t, lane % NCB) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)&v_stage[wave][j * 1024], 16, off, 0, 0, 0);
+      } else {
+        const unsigned off = row_static((TPV * j) >> 4, t) * RB + (lane % NCB) * KB;
+        r.vq[j] = load8(rv, off);
+      }
+    }
+  };
 
-    float m_run[HC], l_run[HC], acc[HC][EPL];
+  for (int hp = 0; hp < G; hp += GP) {
+    const int gh = min(GP, G - hp);  // real heads in this pass
+    // ---- q as int8 limbs, per head: wave w takes heads w and w + 4 ----
+    // q is read first and the first block's loads go out right after it, so
+    // the q setup overlaps them and waiting for q (loads return in order)
+    // does not wait for the cache reads.
+    constexpr int EPL = D / 64, HPW = GP > 4 ? 2 : 1;
+    float xq[HPW][EPL];
 #pragma unroll
-    for (int i = 0; i < HC; ++i) {
-      m_run[i] = -INFINITY;
-      l_run[i] = 0.f;
+    for (int hi = 0; hi < HPW; ++hi)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
+      for (int e = 0; e < EPL; ++e) {
+        const int h = wave + 4 * hi;
+        xq[hi][e] = h < gh ? __half2float(a.q[((long long)b * Hq + g * G + hp + h) * D + lane * EPL + e]) : 0.f;
+      }
+    Regs ra;
+    issue(ra, 0);
+#pragma unroll
+    for (int hi = 0; hi < HPW; ++hi) {
+      const int h = wave + 4 * hi;
+      if (h >= GP) break;
+      const float* x = xq[hi];
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) mx = fmaxf(mx, fabsf(x[e]));
+      mx = wave_max(mx);
+      const int E = limb_exponent(mx);
+      int lsum[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int d = lane * EPL + e;
+        int lm[4];
+        to_limbs(ldexpf(x[e], E), lm);
+        const int pos = BITS == 8 ? d : ((d & ~15) | int4_byte(d & 15));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          q_limb[h][k][pos] = (int8_t)lm[k];
+          lsum[k] += lm[k];
+        }
+      }
+      if (BITS == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lsum[k] = wave_sum_i(lsum[k]);
+      }
+      if (lane == 0) {
+        q_fac[h] = mx > 0.f ? ldexpf(a.qk_log2, -E) : 0.f;
+        // INT4: the codes enter as code + 8, so each limb sum carries 8 * sum(limb).
+        q_off[h] = BITS == 4 ? 8.f * ((float)lsum[0] + (float)lsum[1] * 0x1p-7f + (float)lsum[2] * 0x1p-14f +
+                                      (float)lsum[3] * 0x1p-21f)
+                             : 0.f;
+      }
+    }
+    if (GP < 4) {  // limb rows of heads that do not exist stay zero
+      int* z = reinterpret_cast<int*>(&w_limb[wave][0][4 * GP][0]);
+      for (int i = lane; i < (16 - 4 * GP) * 16; i += 64) z[i] = 0;
+    }
+    __syncthreads();
+
+    // ---- QK A operands: lane row 4 * slot + r holds limb r of one head ----
+    // GP <= 4: the MFMA of token group tg uses slots tg % (4 / GP) * GP ...
+    // + GP - 1 (head = slot % GP), the others are zero; GP = 8: row set rs
+    // holds heads 4 rs + slot.
+    const int slot = col >> 2;
+    i32x4 qrow[NQ][NDH];
+#pragma unroll
+    for (int v = 0; v < NQ; ++v) {
+      const int h = GP > 4 ? 4 * v + slot : slot % GP;
+#pragma unroll
+      for (int dh = 0; dh < NDH; ++dh)
+        qrow[v][dh] = *reinterpret_cast<const i32x4*>(&q_limb[h][col & 3][dh * 64 + quad * 16]);
+    }
+    auto a_operand = [&](int tg, int v, int dh) -> i32x4 {
+      if (GP >= 4) return qrow[v][dh];
+      constexpr int NVAR = GP < 4 ? 4 / GP : 1;  // variants of the masked operand
+      const bool on = slot / GP == tg % NVAR;
+      i32x4 q = qrow[0][dh];
+      asm volatile("" : "+v"(q));  // rebuilt per use: hoisting all of them would cost 32 registers
+      return i32x4{on ? q[0] : 0, on ? q[1] : 0, on ? q[2] : 0, on ? q[3] : 0};
+    };
+    float qf[NC], qo[NC];
+    bool hv[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const int h = (4 * cc + quad) % GP;
+      qf[cc] = q_fac[h];
+      qo[cc] = q_off[h];
+      hv[cc] = h < gh;
     }
 
-    for (int tile = 0; tile < NT; ++tile) {
-      const int tb = (s * NT + tile) * TS + wave * 64 + grp * IT;  // first token of this lane group
-      const int nvalid = max(0, min(IT, L - tb));
-      unsigned row;
-      if (PAGED) {
-        const long long r = nvalid > 0 ? cache_row(c, b, g, tb) : -1;
-        row = r < 0 ? pool_rows : (unsigned)r;  // no block: every read returns zero
-      } else {
-        row = (unsigned)tb;
-      }
+    float m_run[NRS], l_part[NRS], w_part[NRS], o_acc[NRS][NCB];
+#pragma unroll
+    for (int rs = 0; rs < NRS; ++rs) {
+      m_run[rs] = -INFINITY;
+      l_part[rs] = 0.f;
+      w_part[rs] = 0.f;
+#pragma unroll
+      for (int m = 0; m < NCB; ++m) o_acc[rs][m] = 0.f;
+    }
 
-      // ---- issue every load of the tile ----
-      CT kr[IT], vr[IT];
-      float ks[IT], vs[IT];
-      const unsigned off = row * RB + sub * CB;
-#pragma unroll
-      for (int j = 0; j < IT; ++j) kr[j] = load_chunk<CT>(rk, off + j * RB);
-#pragma unroll
-      for (int j = 0; j < IT; ++j) vr[j] = load_chunk<CT>(rv, off + j * RB);
-      // One dword per scale: each read is bounds-checked on its own.
-#pragma unroll
-      for (int j = 0; j < IT; ++j) {
-        ks[j] = load_f32(rks, (row + j) * 4);
-        vs[j] = load_f32(rvs, (row + j) * 4);
-      }
+    // One 64-token block: logits, online softmax, weights, P.V.
+    auto process = [&](Regs& r, int it) {
+      const int t0 = block_t0(it);
 
-      // ---- logits ----
-      float sl[HC][IT];
+      // ---- logits: int8 MFMA on raw K codes ----
+      i32x4 acc[NC];
 #pragma unroll
-      for (int j = 0; j < IT; ++j) {
-        const unsigned* w = reinterpret_cast<const unsigned*>(&kr[j]);
-        half2_t kh[8];
-        if (BITS == 8) {
+      for (int cc = 0; cc < NC; ++cc) acc[cc] = i32x4{0, 0, 0, 0};
 #pragma unroll
-          for (int d = 0; d < NW; ++d) i8x4_to_h2(w[d], kh[2 * d], kh[2 * d + 1]);
-        } else {
+      for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
-          for (int d = 0; d < NW; ++d) i4x8_to_h2(w[d], kh + 4 * d);
-        }
+        for (int dh = 0; dh < NDH; ++dh) {
+          i32x4 kb;
+          if constexpr (BITS == 8) kb = r.kq[tg][dh]; else kb = widen_int4(r.kq[tg][dh]);
+          if (GP <= 4) {
+            const int cc = tg * GP / 4;
+            acc[cc] = mfma(a_operand(tg, 0, dh), kb, acc[cc]);
+          } else {
 #pragma unroll
-        for (int i = 0; i < HC; ++i) {
-          float dot = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dot = __builtin_amdgcn_fdot2(kh[e], qv[i][e], dot, false);
-          sl[i][j] = dot;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < HC; ++i)
-#pragma unroll
-        for (int j = 0; j < IT; ++j) {
-          const float v = group_sum<LPT>(sl[i][j]);
-          sl[i][j] = (j < nvalid) ? v * (ks[j] * qk_scale) : -INFINITY;
-        }
-
-      // ---- H2O: spill the logits ----
-      if (a.logits != nullptr && sub == 0) {
-#pragma unroll
-        for (int i = 0; i < HC; ++i) {
-          if (hc + i < G) {
-            float* dst = a.logits + ((long long)b * Hq + g * G + hc + i) * span + tb;
-#pragma unroll
-            for (int j = 0; j < IT; ++j) dst[j] = sl[i][j];
+            for (int rs = 0; rs < NRS; ++rs) acc[tg * NRS + rs] = mfma(a_operand(tg, rs, dh), kb, acc[tg * NRS + rs]);
           }
         }
+      float sv[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const int j = 4 * cc + quad, tok = 16 * (j / GP) + col;
+        float x = (limb_sum(acc[cc]) - qo[cc]) * qf[cc] * r.ksv[GP >= 8 ? cc / 2 : cc];
+        if (t0 + tok >= L || !hv[cc]) x = -INFINITY;
+        sv[cc] = x;
+        if (a.logits != nullptr && hv[cc])  // H2O: spill the logit
+          a.logits[((long long)b * Hq + g * G + hp + j % GP) * span + t0 + tok] = x;
       }
 
-      // ---- online softmax, one running state per wave ----
+      // ---- online softmax, one running state per (wave, head) ----
+      float corr[NRS], wscale[NRS];
 #pragma unroll
-      for (int i = 0; i < HC; ++i) {
-        float mt = sl[i][0];
+      for (int rs = 0; rs < NRS; ++rs) {
+        float mb = -INFINITY;
 #pragma unroll
-        for (int j = 1; j < IT; ++j) mt = fmaxf(mt, sl[i][j]);
-        mt = stride_reduce<LPT, true>(mt);
-        const float m_new = fmaxf(m_run[i], mt);
-        const float corr = (m_new == -INFINITY) ? 1.f : exp2_or_zero(m_run[i] - m_new);
-        m_run[i] = m_new;
-        l_run[i] *= corr;
+        for (int cc = 0; cc < NC; ++cc)
+          if ((GP >= 8 ? cc % NRS : 0) == rs) mb = fmaxf(mb, sv[cc]);
+        mb = head_reduce<GP, true>(mb);
+        const float mn = fmaxf(m_run[rs], mb);
+        corr[rs] = m_run[rs] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rs] - mn);
+        m_run[rs] = mn;
+        l_part[rs] *= corr[rs];
+        w_part[rs] *= corr[rs];
+      }
+      float wv[NC];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[i][e] *= corr;
-#pragma unroll
-        for (int j = 0; j < IT; ++j) {
-          const float p = (m_new == -INFINITY) ? 0.f : exp2_or_zero(sl[i][j] - m_new);
-          sl[i][j] = p;
-          l_run[i] += p;
-        }
+      for (int cc = 0; cc < NC; ++cc) {
+        const int rs = GP >= 8 ? cc % NRS : 0;
+        const float p = sv[cc] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[cc] - m_run[rs]);
+        l_part[rs] += p;
+        wv[cc] = sv[cc] == -INFINITY ? 0.f : p * r.vsv[GP >= 8 ? cc / 2 : cc];  // a masked slot's scale may be stale
+        w_part[rs] += wv[cc];
       }
 
-      // ---- P.V over this lane's 16 elements ----
+      // ---- weights as int8 limbs, rows (head, limb) x 64 tokens, in LDS ----
 #pragma unroll
-      for (int j = 0; j < IT; ++j) {
-        const unsigned* w = reinterpret_cast<const unsigned*>(&vr[j]);
-        float wt[HC];
+      for (int rs = 0; rs < NRS; ++rs) {
+        float wm = 0.f;
 #pragma unroll
-        for (int i = 0; i < HC; ++i) wt[i] = sl[i][j] * vs[j];
+        for (int cc = 0; cc < NC; ++cc)
+          if ((GP >= 8 ? cc % NRS : 0) == rs) wm = fmaxf(wm, wv[cc]);
+        wm = head_reduce<GP, true>(wm);
+        const int E = limb_exponent(wm);
+        wscale[rs] = ldexpf(1.f, -E);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float v = code_at<BITS>(w, e);
+        for (int cc = 0; cc < NC; ++cc) {
+          if ((GP >= 8 ? cc % NRS : 0) != rs) continue;
+          const int j = 4 * cc + quad, h = j % GP, tok = 16 * (j / GP) + col;
+          int lm[4];
+          to_limbs(ldexpf(wv[cc], E), lm);
 #pragma unroll
-          for (int i = 0; i < HC; ++i) acc[i][e] = fmaf(wt[i], v, acc[i][e]);
+          for (int k = 0; k < 4; ++k) w_limb[wave][rs][4 * (h & 3) + k][tok] = (int8_t)lm[k];
         }
       }
+      // ---- V rows in LDS: INT8 came by DMA; INT4 is widened here ----
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) {
+          const int t = TPV * j + lane / NCB;
+          const i32x4 val = widen_int4(r.vq[j]);
+          i32x2* dst = reinterpret_cast<i32x2*>(&v_stage[wave][t * VROW + vchunk(t, lane % NCB) * 16]);
+          dst[0] = i32x2{val[0], val[1]};
+          dst[1] = i32x2{val[2], val[3]};
+        }
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the V DMA of this block has landed
+      }
+      asm volatile("" ::: "memory");
+
+      // ---- p . V: A = weight limbs, B = V transposed by ds_read_b64_tr_b8 ----
+      // Within each 16-lane group, source lane 2b + h reads token 16 quad + b
+      // (+ 8), channels 8h..8h+7 of the block; lane col then holds channel col
+      // of those 8 tokens.
+      const int tr_row = quad * 16 + (col >> 1), tr_col = (col & 1) * 8;
+#pragma unroll
+      for (int rs = 0; rs < NRS; ++rs) {
+        const i32x4 aw = *reinterpret_cast<const i32x4*>(&w_limb[wave][rs][col][quad * 16]);
+#pragma unroll
+        for (int m = 0; m < NCB; ++m) {
+          uint8_t* p0 = &v_stage[wave][tr_row * VROW + vchunk(tr_row, m) * 16 + tr_col];
+          uint8_t* p1 = &v_stage[wave][(tr_row + 8) * VROW + vchunk(tr_row + 8, m) * 16 + tr_col];
+          const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p0);
+          const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p1);
+          const i32x4 pv = mfma(aw, i32x4{lo[0], lo[1], hi[0], hi[1]}, i32x4{0, 0, 0, 0});
+          o_acc[rs][m] = fmaf(o_acc[rs][m], corr[rs], wscale[rs] * limb_sum(pv));
+        }
+      }
+      asm volatile("" ::: "memory");
+    };
+    for (int it = 0; it < nb; ++it) {
+      if (it > 0) issue(ra, it);
+      process(ra, it);
     }
 
-    // ---- merge the lane groups of each wave, then the four waves ----
+    // ---- merge the four waves ----
+    float l_tot[NRS], w_tot[NRS];
 #pragma unroll
-    for (int i = 0; i < HC; ++i) {
-      const float l = stride_reduce<LPT, false>(l_run[i]);
+    for (int rs = 0; rs < NRS; ++rs) {
+      l_tot[rs] = head_reduce<GP, false>(l_part[rs]);
+      w_tot[rs] = BITS == 4 ? head_reduce<GP, false>(w_part[rs]) : 0.f;
+    }
+    __syncthreads();  // every wave is done with v_stage, which red_o reuses
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] = stride_reduce<LPT, false>(acc[i][e]);
-      if (lane == 0) {
-        red_m[wave][i] = m_run[i];
-        red_l[wave][i] = l;
-      }
-      if (grp == 0) {
+    for (int rs = 0; rs < NRS; ++rs) {
+      const int hh = (GP >= 8 ? 4 * rs : 0) + quad;  // head of this lane's PV rows
+      if (quad < (GP < 4 ? GP : 4) && hh < gh) {
+        if (col == 0) {
+          red_m[wave][hh] = m_run[rs];
+          red_l[wave][hh] = l_tot[rs];
+        }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) red_o[wave][i][sub * EPL + e] = acc[i][e];
+        for (int m = 0; m < NCB; ++m) {
+          const int ch = m * 16 + (BITS == 8 ? col : int4_elem(col));
+          red_o[(wave * GP + hh) * D + ch] = o_acc[rs][m] - 8.f * w_tot[rs];
+        }
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < HC * D; idx += 256) {
+    for (int idx = tid; idx < gh * D; idx += 256) {
       const int i = idx / D, d = idx - i * D;
-      if (hc + i < G) {
-        const float M = fmaxf(fmaxf(red_m[0][i], red_m[1][i]), fmaxf(red_m[2][i], red_m[3][i]));
-        float o = 0.f;
+      const float M = fmaxf(fmaxf(red_m[0][i], red_m[1][i]), fmaxf(red_m[2][i], red_m[3][i]));
+      float o = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) o = fmaf(red_o[w][i][d], part_weight(red_m[w][i], M), o);
-        a.part_o[(((long long)b * Hq + g * G + hc + i) * S + s) * D + d] = o;
-        if (d == 0) {
-          float l = 0.f;
+      for (int w = 0; w < 4; ++w) o = fmaf(red_o[(w * GP + i) * D + d], part_weight(red_m[w][i], M), o);
+      const long long hq = (long long)b * Hq + g * G + hp + i;
+      a.part_o[(hq * S + s) * D + d] = o;
+      if (d == 0) {
+        float l = 0.f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) l = fmaf(red_l[w][i], part_weight(red_m[w][i], M), l);
-          float* ml = a.part_ml + (((long long)b * Hq + g * G + hc + i) * S + s) * 2;
-          ml[0] = M;
-          ml[1] = l;
-        }
+        for (int w = 0; w < 4; ++w) l = fmaf(red_l[w][i], part_weight(red_m[w][i], M), l);
+        a.part_ml[(hq * S + s) * 2] = M;
+        a.part_ml[(hq * S + s) * 2 + 1] = l;
       }
     }
     __syncthreads();
@@ -377,6 +554,8 @@ constexpr int kH2oChunk = 1024;
 template <int D, int GMAX>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   constexpr int kPrefetchHeads = GMAX;
+  constexpr int PARTS = 256 / D;  // threads per output element
+  constexpr int kPre = 8;         // split partials per thread read before the statistics
   extern __shared__ float fac[];  // [heads][S] split weights, then [heads] m and 1/l
   const kvc_cache_t& c = a.c;
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -388,23 +567,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int h_lo = out_block ? x : 0, nh = out_block ? 1 : G;
   float* minv = fac + nh * S;  // [nh][2]: m, 1/l
 
-  // H2O blocks: fetch the score slots and the first heads' logits before the
-  // split statistics, so both memory round trips overlap.
+  // Every read below comes from a clamped, always valid address and does not
+  // wait for the sequence length or the statistics, so all of them are in
+  // flight together; values past L are never used.
+  const int tl = (int)min(span, (long long)c.capacity) - 1;
   const int t0 = (x - G) * kH2oChunk + tid * 4;
   float sc[4] = {0.f, 0.f, 0.f, 0.f};
   float lg[kPrefetchHeads][4];
   float* srow = a.score ? a.score + ((long long)b * H + g) * c.capacity : nullptr;
   const float* lrow = a.logits + ((long long)b * Hq + g * G) * span;
   if (!out_block && srow) {
-    // Unconditional loads from clamped slots, so that they are all in flight
-    // together; slot 0 always exists, and values past L are never used.
-    const int tl = max(L - 1, 0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) sc[k] = srow[min(t0 + k, tl)];
 #pragma unroll
     for (int i = 0; i < kPrefetchHeads; ++i)
 #pragma unroll
       for (int k = 0; k < 4; ++k) lg[i][k] = lrow[min(i, G - 1) * span + min(t0 + k, tl)];
+  }
+  const int d = tid % D, pi = tid / D;
+  const float* po = a.part_o + ((long long)b * Hq + g * G + h_lo) * S * D + d;
+  float pre[kPre];
+  if (out_block) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) pre[k] = po[(long long)min(pi + k * PARTS, S - 1) * D];
   }
 
   // Split statistics: one wave per head, lanes over the splits.
@@ -430,22 +615,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   __syncthreads();
 
   if (out_block) {
-    // 256 / D threads per output element, each over every (256 / D)-th split.
-    constexpr int PARTS = 256 / D;
+    // PARTS threads per output element, each over every PARTS-th split.
     __shared__ float part[PARTS][D];
-    const int d = tid % D, pi = tid / D;
-    const int h = g * G + x;
-    const float* po = a.part_o + ((long long)b * Hq + h) * S * D + d;
     float o = 0.f;
-#pragma unroll 8
-    for (int sp = pi; sp < S; sp += PARTS) o = fmaf(po[(long long)sp * D], fac[sp], o);
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+      if (pi + k * PARTS < S) o = fmaf(pre[k], fac[pi + k * PARTS], o);
+    for (int sp = pi + kPre * PARTS; sp < S; sp += PARTS) o = fmaf(po[(long long)sp * D], fac[sp], o);
     part[pi][d] = o;
     __syncthreads();
     if (pi == 0) {
       float r = part[0][d];
 #pragma unroll
       for (int p = 1; p < PARTS; ++p) r += part[p][d];
-      a.out[((long long)b * Hq + h) * D + d] = r;
+      a.out[((long long)b * Hq + g * G + x) * D + d] = r;
     }
     return;
   }
@@ -465,28 +648,27 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   }
 }
 
-template <int BITS, int D, int HC, bool PAGED>
+template <int BITS, int D, int GP, bool PAGED>
 hipError_t launch_split(const AttnLaunch& a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_split_kernel<BITS, D, HC, PAGED>), dim3(a.splits, a.c.num_kv_heads, a.c.batch),
+  hipLaunchKernelGGL((attn_split_kernel<BITS, D, GP, PAGED>), dim3(a.splits, a.c.num_kv_heads, a.c.batch),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <int BITS, int D, bool PAGED>
-hipError_t launch_hc(const AttnLaunch& a, int G, hipStream_t st) {
+hipError_t launch_gp(const AttnLaunch& a, int G, hipStream_t st) {
   if (G == 1) return launch_split<BITS, D, 1, PAGED>(a, st);
   if (G == 2) return launch_split<BITS, D, 2, PAGED>(a, st);
-  return launch_split<BITS, D, 4, PAGED>(a, st);
+  if (G <= 4) return launch_split<BITS, D, 4, PAGED>(a, st);
+  return launch_split<BITS, D, 8, PAGED>(a, st);  // more than 8: passes of 8
 }
 
 template <int BITS, int D>
 hipError_t launch_paged(const AttnLaunch& a, int G, hipStream_t st) {
-  return a.c.block_size ? launch_hc<BITS, D, true>(a, G, st) : launch_hc<BITS, D, false>(a, G, st);
+  return a.c.block_size ? launch_gp<BITS, D, true>(a, G, st) : launch_gp<BITS, D, false>(a, G, st);
 }
 
 }  // namespace
-
-int attn_heads_per_pass(int G) { return G == 1 ? 1 : G == 2 ? 2 : 4; }
 
 hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st) {
   const int G = a.num_q_heads / a.c.num_kv_heads;

@@ -43,9 +43,6 @@ struct AttnLaunch {
   float qk_log2;     // log2(e) / sqrt(head_dim)
 };
 hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st);
-// Query heads one split-kernel pass serves; with more heads per KV head than
-// this, a split holds a single tile.
-int attn_heads_per_pass(int G);
 
 hipError_t launch_select(const kvc_cache_t& c, const float* score, int budget, int n_sink,
                          int n_recent, uint8_t* mask, int32_t* keep_index, int max_len, hipStream_t st);

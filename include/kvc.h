@@ -160,7 +160,8 @@ size_t kvc_decode_attn_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_h
  * q: device fp16 [batch][num_q_heads][head_dim]; out: device fp32
  * [batch][num_q_heads][head_dim]. workspace: device memory of at least
  * kvc_decode_attn_workspace_bytes(...) bytes, 256-byte aligned, owned by the
- * caller; its contents on entry do not matter.
+ * caller; its contents on entry do not matter. One workspace serves one call
+ * at a time.
  * Errors: INVALID_ARG for a bad descriptor, NULL q/out, num_q_heads not a
  * multiple of num_kv_heads, G > 16, max_len_hint < 1 or a workspace that is
  * NULL or too small; CAPACITY if max_len_hint > capacity.

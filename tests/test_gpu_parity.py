@@ -114,6 +114,27 @@ def test_decode_attn_is_deterministic():
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
 
+def test_workspace_reused_across_calls():
+    """One workspace serves consecutive calls of different shapes (head
+    counts, lengths and split counts); nothing from one call leaks into the
+    next."""
+    ws = None
+    for hq, hkv, L in [(4, 4, 700), (4, 4, 3000), (8, 2, 1500), (2, 2, 9000), (8, 4, 700), (4, 4, 700)]:
+        w = get("tiny_mha").scaled(num_q_heads=hq, num_kv_heads=hkv, context=L, batch=2)
+        print(f"[attn] workspace reuse hq={hq} hkv={hkv} L={L}", flush=True)
+        d = draw(w)
+        gc, ref, score = prefill_both(w, d)
+        if ws is None:
+            ws = torch.full((1 << 22,), 0xA5, dtype=torch.uint8, device="cuda")
+        assert kvc.kvc_decode_attn_workspace_bytes(gc, hq, L, True) <= ws.numel()
+        out = torch.empty((2, hq, 64), dtype=torch.float32, device="cuda")
+        kvc.kvc_decode_attn(gc, dev(d["q"]), out, h2o_score=score, workspace=ws)
+        ro, _ = ref.attend(d["q"], h2o=True)
+        torch.cuda.synchronize()
+        assert_out_close(host(out), ro)
+        assert_scores_close(host(score), ref.score, ref.lengths)
+
+
 def test_empty_sequence_gives_zero_output():
     gc = kvc.KVCache(2, 2, 64, 64, 8)
     w = get("tiny_mha").scaled(context=5, num_q_heads=2, num_kv_heads=2, batch=1)
