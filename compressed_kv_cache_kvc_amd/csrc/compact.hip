@@ -68,7 +68,7 @@ __device__ __forceinline__ void copy_rows(const kvc_cache_t& src, const float* _
                                           const int* list, int total, int off) {
   constexpr int LPR = RB / 16;        // lanes per row
   constexpr int RPP = NT / LPR;       // rows per pass
-  constexpr int BATCH = 4;
+  constexpr int BATCH = 8;  // every pass of a 256-row chunk in flight at once (RB <= 128)
   const int tid = threadIdx.x;
   const uint8_t* sk = static_cast<const uint8_t*>(src.k_codes) + rowoff * RB;
   const uint8_t* sv = static_cast<const uint8_t*>(src.v_codes) + rowoff * RB;
@@ -99,8 +99,10 @@ __device__ __forceinline__ void copy_rows(const kvc_cache_t& src, const float* _
       const int q = r0 + (p0 + p) * RPP;
       if (q < total) {
         const long long d = off + q;
-        *reinterpret_cast<u32x4*>(dk + d * RB + part * 16) = kx[p];
-        *reinterpret_cast<u32x4*>(dv + d * RB + part * 16) = vx[p];
+        // Streaming stores: the compacted rows are not read again by this
+        // launch, so they should not sit dirty in L2 until the kernel ends.
+        __builtin_nontemporal_store(kx[p], reinterpret_cast<u32x4*>(dk + d * RB + part * 16));
+        __builtin_nontemporal_store(vx[p], reinterpret_cast<u32x4*>(dv + d * RB + part * 16));
       }
     }
   }

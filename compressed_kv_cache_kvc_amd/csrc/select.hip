@@ -16,7 +16,10 @@
 //    histogram increments over many bins (LDS atomics that collide on one
 //    address within a wave instruction serialize; scores are probability mass
 //    and mostly share a few binary exponents);
-//  * the bin holding the k-th key comes from a block-wide suffix scan.
+//  * the bin holding the k-th key comes from a block-wide suffix scan; once
+//    that bin holds at most 64 keys, they are gathered into LDS and one wave
+//    ranks them directly (each lane counts the keys above and equal to its
+//    own), which ends the search without further passes.
 // Rows of up to 8192 candidates use 256 threads holding up to 32 keys each in
 // registers: few waves keep the per-pass fixed cost (scans, barriers) low,
 // since every instruction runs once per wave. Longer rows use 1024 threads and
@@ -64,7 +67,7 @@ __device__ __forceinline__ void block_minmax(unsigned& lo, unsigned& hi, unsigne
 // `k` the number of keys equal to T that are kept.
 template <int NT, typename ForKeys>
 __device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, int* hist, int* scan_tmp,
-                                                    unsigned* mm_tmp, int* sel) {
+                                                    unsigned* mm_tmp, int* sel, unsigned* small) {
   constexpr int BPT = kBins / NT;  // bins per thread in the digit search
   const int tid = threadIdx.x;
   unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -79,6 +82,7 @@ __device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, in
   const unsigned low = (remaining == 32) ? 0xFFFFFFFFu : ((1u << remaining) - 1u);
   unsigned T = kmin & ~low, pmask = ~low;
   for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+  if (tid == 0) sel[3] = 0;  // keys gathered into `small`
   __syncthreads();
   while (remaining > 0) {
     const int width = min(kDigitBits, remaining);
@@ -106,6 +110,7 @@ __device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, in
       if (before < k && k <= before + c[j]) {
         sel[0] = top - j;
         sel[1] = k - before;
+        sel[2] = c[j];
       }
       before += c[j];
     }
@@ -114,6 +119,32 @@ __device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, in
     pmask |= dmask << shift;
     k = sel[1];
     remaining = shift;
+    if (remaining > 0 && sel[2] <= 64) {
+      // Few keys share the prefix found so far: gather them and rank them in
+      // one wave. The k-th largest key u has g keys above it and e equal,
+      // with g < k <= g + e.
+      for_keys([&](unsigned u) {
+        if ((u & pmask) == T) small[atomicAdd(&sel[3], 1)] = u;
+      });
+      __syncthreads();
+      const int n_small = sel[2];
+      if (tid < 64) {
+        const unsigned u = small[min(tid, n_small - 1)];
+        int gt = 0, eq = 0;
+        for (int j = 0; j < n_small; ++j) {
+          const unsigned w = small[j];
+          gt += w > u;
+          eq += w == u;
+        }
+        if (tid < n_small && gt < k && k <= gt + eq) {
+          sel[0] = (int)u;
+          sel[1] = k - gt;
+        }
+      }
+      __syncthreads();
+      k = sel[1];
+      return (unsigned)sel[0];
+    }
   }
   return T;
 }
@@ -126,12 +157,20 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
   __shared__ int hist[kBins];
   __shared__ int scan_tmp[16];
   __shared__ unsigned mm_tmp[32];
-  __shared__ int sel[2];
+  __shared__ int sel[4];
+  __shared__ unsigned small[64];
   __shared__ __align__(16) unsigned stage_lds[REG ? NT * KPT : 1];
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int L = __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), max_len));
   const long long rowoff = ((long long)b * c.num_kv_heads + g) * c.capacity;
   const float* row = score + rowoff;
+  // The register path's coalesced loads cover slots n_sink .. n_sink + NT*KPT
+  // - 1 (clamped to the row) and do not wait for the sequence length.
+  unsigned v[REG ? KPT : 1];
+  if (REG) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) v[j] = order_key(row[min(n_sink + tid + j * NT, c.capacity - 1)]);
+  }
+  const int L = __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), max_len));
   uint8_t* m = mask + rowoff;
   int32_t* kidx = keep_index ? keep_index + ((long long)b * c.num_kv_heads + g) * budget : nullptr;
   if (L <= budget) {
@@ -150,13 +189,10 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
   const int i0 = lo + min(tid * per, n), cnt = min(tid * per + per, n) - min(tid * per, n);
   unsigned key[REG ? KPT : 1];
   if (REG) {
-    // Coalesced loads (slot lo + tid + j*NT, clamped, all in flight) into LDS,
-    // then each thread reads its contiguous range back with 16-byte LDS reads
-    // (its range starts at a multiple of 4 words).
+    // The coalesced loads (slot lo + tid + j*NT) go to LDS, then each thread
+    // reads its contiguous range back with 16-byte LDS reads (its range starts
+    // at a multiple of 4 words); staged slots past the candidates are unused.
     unsigned* stage = reinterpret_cast<unsigned*>(stage_lds);
-    unsigned v[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) v[j] = order_key(row[lo + min(tid + j * NT, n - 1)]);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) stage[tid + j * NT] = v[j];
     __syncthreads();
@@ -207,7 +243,7 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
   };
   const bool any_heavy = k > 0;
   unsigned T = 0;
-  if (any_heavy) T = radix_threshold<NT>(for_keys, k, hist, scan_tmp, mm_tmp, sel);
+  if (any_heavy) T = radix_threshold<NT>(for_keys, k, hist, scan_tmp, mm_tmp, sel, small);
 
   // Sinks and the recent window are always kept.
   const int n_heavy = budget - n_sink - n_recent;
@@ -226,9 +262,20 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
     ties += any_heavy & (u == T);
     above += any_heavy & (u > T);
   });
-  int tie_rank = block_inclusive_scan<NT>(ties, scan_tmp) - ties;
+  // Both prefix counts at once when every count fits 16 bits (ties in the
+  // low half); longer rows scan them separately.
+  int tie_rank, above_before;
+  if (n < 65536) {
+    const int packed = ties | (above << 16);
+    const int before = block_inclusive_scan<NT>(packed, scan_tmp) - packed;
+    tie_rank = before & 0xFFFF;
+    above_before = before >> 16;
+  } else {
+    tie_rank = block_inclusive_scan<NT>(ties, scan_tmp) - ties;
+    above_before = block_inclusive_scan<NT>(above, scan_tmp) - above;
+  }
   // Kept before this thread = candidates above T before it + ties kept before it.
-  int out = kidx ? block_inclusive_scan<NT>(above, scan_tmp) - above + min(tie_rank, k) : 0;
+  int out = above_before + min(tie_rank, k);
   for_own([&](int i, unsigned u) {
     uint8_t keepb = 0;
     if (any_heavy) {
