@@ -321,3 +321,142 @@ def test_paged_decode_reduced(bits):
     torch.cuda.synchronize()
     assert_out_close(host(out), ro)
     assert rb == kc.shape[-1]
+
+
+# ------------------------------------------------ full-size configurations --
+# The larger workloads run at full size on the GPU, in the launch configuration
+# the library picks for them; the oracle checks sampled sequences or rows
+# (it computes each sampled row from the fp16 inputs on its own).
+
+def _row_check(gpu_codes, gpu_scale, codes_ref, scale_ref, bits):
+    want = codes_ref.view(np.uint8) if bits == 8 else oracle.pack_int4(codes_ref)
+    assert np.array_equal(gpu_codes, want)
+    assert np.array_equal(gpu_scale.view(np.uint32), scale_ref.astype(np.float32).view(np.uint32))
+
+
+def test_paged_b32_full_size():
+    """32 sequences of 1024..4096 tokens in 16-token INT8 blocks placed by a
+    seeded permutation; all 32 appended and attended on the GPU, 4 sampled
+    sequences checked in full (codes, scales, every query head's output)."""
+    w = get("paged_b32")
+    print("[paged] full size B=32", flush=True)
+    d = draw(w)
+    B, Hq, H, D, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.paged_block
+    table, nb, lengths = d["block_table"], int(d["num_blocks"]), d["lengths"]
+    gc = kvc.KVCache(B, H, D, 0, 8, block_size=bs, num_blocks=nb, max_blocks_per_seq=table.shape[1])
+    gc.block_table.copy_(dev(table))
+    for b in range(B):
+        one = kvc.KvcCacheDesc.from_buffer_copy(gc.desc)
+        one.batch = 1
+        one.block_table = gc.block_table[b].data_ptr()
+        one.lengths = gc.lengths[b:b + 1].data_ptr()
+        one.num_seen = gc.num_seen[b:b + 1].data_ptr()
+        kvc.kvc_quant_append(one, dev(d["k_seq"][b][None]), dev(d["v_seq"][b][None]), max_len_hint=0)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    kvc.kvc_decode_attn(gc, dev(d["q"]), out, max_len_hint=int(lengths.max()))
+    torch.cuda.synchronize()
+    assert host(gc.lengths).tolist() == lengths.tolist()
+    kc_all, ks_all, o = host(gc.k_codes), host(gc.k_scale), host(out)
+    for b in np.random.default_rng(33).choice(B, 4, replace=False):
+        L, nbk = int(lengths[b]), (int(lengths[b]) + bs - 1) // bs
+        blocks = table[b, :nbk]
+        local = np.arange(nbk, dtype=np.int32)[None]          # the sequence's blocks, renumbered
+        kp = np.zeros((nbk, H, bs, D), np.int8); vp = np.zeros_like(kp)
+        ksp = np.zeros((nbk, H, bs), np.float32); vsp = np.zeros_like(ksp)
+        oracle.paged_append(kp, ksp, vp, vsp, local, np.zeros(1, np.int64), d["k_seq"][b][None],
+                            d["v_seq"][b][None], 8, bs)
+        assert np.array_equal(kc_all[blocks], kp.view(np.uint8)), b
+        assert np.array_equal(ks_all[blocks].view(np.uint32), ksp.view(np.uint32)), b
+        ro = oracle.paged_decode_attention(d["q"][b:b + 1], kp, ksp, vp, vsp, local, lengths[b:b + 1], bs)
+        assert_out_close(o[b:b + 1], ro)
+
+
+def test_qwen_gqa_stream_full_size():
+    """8 sequences x 32768 tokens, 28 query / 4 KV heads: 64 decode steps of
+    append, attention with H2O, keep-set selection (checked against the
+    oracle's) and compaction back to 8192, all at full size. Both sides
+    compact with the oracle's keep list so that they stay on the same tokens."""
+    w = get("qwen_gqa_stream")
+    print("[stream] full size, 64 steps", flush=True)
+    d = draw(w)
+    B, Hq, H, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.context
+    gc, ref, score = prefill_both(w, d)
+    other = make_gpu_cache(w, L)
+    other_score = other.score_buffer()
+    worst_err, ambiguous = 0.0, 0
+    for s in range(w.steps):
+        if s > 0:
+            kvc.kvc_quant_append(gc, dev(d["step_k"][s]), dev(d["step_v"][s]), h2o_score=score)
+            ref.append(d["step_k"][s], d["step_v"][s])
+        out, ro = _attend_both(gc, ref, d["step_q"][s], score)
+        worst_err = max(worst_err, assert_out_close(out, ro))
+        assert_scores_close(host(score), ref.score, ref.lengths)
+        if int(ref.lengths.max()) <= w.budget:
+            continue
+        mask = torch.zeros((B, H, gc.capacity), dtype=torch.uint8, device="cuda")
+        kidx = torch.zeros((B, H, w.budget), dtype=torch.int32, device="cuda")
+        kvc.kvc_h2o_select(gc, score, w.budget, w.n_sink, w.n_recent, mask, keep_index=kidx)
+        torch.cuda.synchronize()
+        ambiguous += assert_keep_equivalent(host(mask), ref.score, ref.lengths, w.budget, w.n_sink, w.n_recent)
+        keep_ref = ref.select(w.budget, w.n_sink, w.n_recent)
+        ref_list = np.stack([np.stack([np.nonzero(keep_ref[b, g])[0] for g in range(H)])
+                             for b in range(B)]).astype(np.int32)
+        kvc.kvc_compact_gather(gc, score, dev(ref_list), w.budget, other, other_score)
+        ref.compact(keep_ref)
+        gc, other, score, other_score = other, gc, other_score, score
+    torch.cuda.synchronize()
+    assert_codes_equal(gc, ref)
+    assert host(gc.lengths).tolist() == [w.budget] * B
+    print(f"64 steps: worst max-abs out err {worst_err:.2e}, ambiguous keep slots {ambiguous}", flush=True)
+
+
+def test_llama70b_int4_full_size():
+    """4 sequences x 131072 tokens, INT4, 64 query / 8 KV heads, 1% outlier
+    tokens x8: prefill, append, attention with H2O, selection and compaction
+    at full size on the GPU; two sampled (sequence, KV head) rows checked end
+    to end (codes, scales, the 8 query heads' outputs, H2O scores, keep-set,
+    compacted row)."""
+    w = get("llama70b_int4")
+    print("[70b] full size INT4", flush=True)
+    d = draw(w)
+    B, Hq, H, D, L, G = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.context, w.group
+    gc = make_gpu_cache(w, L)
+    score = gc.score_buffer()
+    k16, v16 = dev(d["k"]), dev(d["v"])
+    kvc.kvc_quant_append(gc, k16[:, :, :L - 1].contiguous(), v16[:, :, :L - 1].contiguous(), h2o_score=score)
+    kvc.kvc_quant_append(gc, k16[:, :, L - 1:].contiguous(), v16[:, :, L - 1:].contiguous(), h2o_score=score)
+    del k16, v16
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    kvc.kvc_decode_attn(gc, dev(d["q"]), out, h2o_score=score)
+    mask = torch.zeros((B, H, L), dtype=torch.uint8, device="cuda")
+    kidx = torch.zeros((B, H, w.budget), dtype=torch.int32, device="cuda")
+    kvc.kvc_h2o_select(gc, score, w.budget, w.n_sink, w.n_recent, mask, keep_index=kidx)
+    torch.cuda.synchronize()
+    samples = [(0, 3), (2, 6)]
+    lists = host(kidx).copy()
+    refs = {}
+    for b, g in samples:
+        kc, ks = oracle.quantize_rows(d["k"][b, g], 4)
+        vc, vs = oracle.quantize_rows(d["v"][b, g], 4)
+        _row_check(host(gc.k_codes[b, g]), host(gc.k_scale[b, g]), kc, ks, 4)
+        _row_check(host(gc.v_codes[b, g]), host(gc.v_scale[b, g]), vc, vs, 4)
+        ro, p = oracle.attend_head_group(d["q"][b, g * G:(g + 1) * G], kc, ks, vc, vs)
+        assert_out_close(host(out[b, g * G:(g + 1) * G]), ro)
+        sref = oracle.h2o_accumulate(np.zeros(L), p)
+        assert_scores_close(host(score[b, g])[None, None], sref[None, None], np.array([L]))
+        assert_keep_equivalent(host(mask[b, g])[None, None], sref[None, None], np.array([L]), w.budget,
+                               w.n_sink, w.n_recent)
+        keep = oracle.select_keep(sref, L, w.budget, w.n_sink, w.n_recent)
+        lists[b, g] = np.nonzero(keep)[0]
+        refs[(b, g)] = oracle.compact_row(keep, kc, vc, ks, vs, np.arange(L), sref)
+    dst = make_gpu_cache(w, L)
+    dst_score = dst.score_buffer()
+    kvc.kvc_compact_gather(gc, score, dev(lists), w.budget, dst, dst_score)
+    torch.cuda.synchronize()
+    assert host(dst.lengths).tolist() == [w.budget] * B
+    for (b, g), (kc, vc, ks, vs, pos, sc) in refs.items():
+        _row_check(host(dst.k_codes[b, g, :w.budget]), host(dst.k_scale[b, g, :w.budget]), kc, ks, 4)
+        _row_check(host(dst.v_codes[b, g, :w.budget]), host(dst.v_scale[b, g, :w.budget]), vc, vs, 4)
+        assert np.array_equal(host(dst.positions[b, g, :w.budget]), pos)
+        gpu_sc = host(dst_score[b, g, :w.budget]).astype(np.float64)
+        assert np.all(np.abs(gpu_sc - sc) <= 1e-5 * np.abs(sc) + 1e-30)

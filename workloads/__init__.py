@@ -88,15 +88,32 @@ def get(name: str) -> Workload:
     return WORKLOADS[name]
 
 
+def _to_f16(x: np.ndarray) -> np.ndarray:
+    """float32 -> float16, round to nearest even (IEEE). torch's conversion is
+    the same rounding and runs on every core; numpy's is the fallback."""
+    try:
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float16).numpy()
+    except ImportError:
+        return x.astype(np.float16)
+
+
 def _normal16(rng: np.random.Generator, shape) -> np.ndarray:
-    return rng.standard_normal(size=shape, dtype=np.float32).astype(np.float16)
+    return _to_f16(rng.standard_normal(size=shape, dtype=np.float32))
 
 
-def _kv_chunk(rng, shape, scale_mask: Optional[np.ndarray], scale: float) -> np.ndarray:
+def _kv_chunk(rng, shape, chans: Optional[np.ndarray], toks: Optional[np.ndarray], scale: float) -> np.ndarray:
+    """One sequence's K or V, [Hkv][L][D]: N(0, 1), with the outlier channels
+    (per KV head) or outlier token positions multiplied by `scale` in float32
+    before the cast."""
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    if scale_mask is not None:
-        x = np.where(scale_mask, x * np.float32(scale), x)
-    return x.astype(np.float16)
+    s = np.float32(scale)
+    if chans is not None:
+        for g in range(shape[0]):
+            x[g][:, chans[g]] *= s
+    if toks is not None:
+        x[:, toks, :] *= s
+    return _to_f16(x)
 
 
 def draw(w: Workload) -> Dict[str, np.ndarray]:
@@ -146,36 +163,24 @@ def draw(w: Workload) -> Dict[str, np.ndarray]:
     # Structure is drawn from a child generator so that K and V chunks can be
     # produced in one pass with the outlier mask already known.
     srng = np.random.default_rng([w.seed, 2])
-    chan_mask = None
+    chans = None
     if w.outlier_channels:
-        chan_mask = np.zeros((Hkv, 1, D), dtype=bool)
-        for g in range(Hkv):
-            chan_mask[g, 0, srng.choice(D, size=w.outlier_channels, replace=False)] = True
-        out["outlier_channels"] = np.stack(
-            [np.nonzero(chan_mask[g, 0])[0] for g in range(Hkv)]).astype(np.int32)
-    tok_masks = None
+        # per KV head, distinct channels in ascending order
+        chans = np.stack([np.sort(srng.choice(D, size=w.outlier_channels, replace=False))
+                          for _ in range(Hkv)]).astype(np.int32)
+        out["outlier_channels"] = chans
+    toks = None
     if w.outlier_token_frac:
         n_out = int(round(w.outlier_token_frac * L))
-        tok_masks = []
-        for b in range(B):
-            m = np.zeros((1, L, 1), dtype=bool)
-            m[0, srng.choice(L, size=n_out, replace=False), 0] = True
-            tok_masks.append(m)
-        out["outlier_tokens"] = np.stack([np.nonzero(m[0, :, 0])[0] for m in tok_masks]).astype(np.int32)
-
-    def mask_for(b):
-        if chan_mask is not None:
-            return chan_mask
-        if tok_masks is not None:
-            return tok_masks[b]
-        return None
+        toks = np.stack([np.sort(srng.choice(L, size=n_out, replace=False)) for _ in range(B)]).astype(np.int32)
+        out["outlier_tokens"] = toks
 
     k = np.empty((B, Hkv, L, D), dtype=np.float16)
     v = np.empty((B, Hkv, L, D), dtype=np.float16)
     for b in range(B):
-        k[b] = _kv_chunk(rng, (Hkv, L, D), mask_for(b), w.outlier_scale)
+        k[b] = _kv_chunk(rng, (Hkv, L, D), chans, None if toks is None else toks[b], w.outlier_scale)
     for b in range(B):
-        v[b] = _kv_chunk(rng, (Hkv, L, D), mask_for(b), w.outlier_scale)
+        v[b] = _kv_chunk(rng, (Hkv, L, D), chans, None if toks is None else toks[b], w.outlier_scale)
     out["k"], out["v"] = k, v
     out["lengths"] = np.full(B, L, dtype=np.int32)
 
