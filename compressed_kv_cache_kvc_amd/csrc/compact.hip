@@ -197,30 +197,82 @@ __global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const
 
 
 // Compaction from a sorted gather list (the kept slots of each row in
-// ascending order, as kvc_h2o_select emits): destination slot j takes source
-// slot keep_index[b][g][j] for j < min(length, n_keep). No scan is needed, so
-// a workgroup's 256 destination slots start copying after one index load.
+// ascending order, as kvc_h2o_select emits): destination slot j of row (b, g)
+// takes source slot keep_index[b][g][j] for j < min(length, n_keep). No scan
+// is needed. The flat list [B][Hkv][n_keep] is split evenly over the grid, so
+// every CU moves the same number of rows: a workgroup takes `per_wg` (at most
+// NT) consecutive entries, one entry per thread for the index, scales,
+// position and score, and LPR lanes per entry for the codes, with every load
+// in flight before the first store.
 template <int RB>
 __global__ __launch_bounds__(NT) void compact_gather_kernel(kvc_cache_t src, const float* __restrict__ src_score,
                                                             const int32_t* __restrict__ keep_index, int n_keep,
-                                                            kvc_cache_t dst, float* __restrict__ dst_score) {
-  const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int H = src.num_kv_heads;
-  __shared__ int list[CH];
-  const int32_t* krow = keep_index + ((long long)b * H + g) * n_keep;
-  // The index load does not wait for the length: clamped to n_keep instead.
-  const int j = ch * CH + tid;
-  const int idx = krow[min(j, n_keep - 1)];
-  const int count = __builtin_amdgcn_readfirstlane(min(min(src.lengths[b], src.capacity), n_keep));
-  if (ch == 0 && g == 0 && tid == 0) {
-    dst.lengths[b] = count;
-    dst.num_seen[b] = src.num_seen[b];
+                                                            kvc_cache_t dst, float* __restrict__ dst_score,
+                                                            long long entries, int per_wg) {
+  constexpr int LPR = RB / 16;        // lanes per row
+  constexpr int RPP = NT / LPR;       // rows per pass
+  constexpr int NPASS = NT / RPP;     // passes for NT rows
+  const int tid = threadIdx.x, H = src.num_kv_heads;
+  const long long cap = src.capacity;
+  __shared__ long long s_row[NT], d_row[NT];  // source / destination row of each entry; -1: not copied
+  const long long e = (long long)blockIdx.x * per_wg + tid;
+  const bool mine = tid < per_wg && e < entries;
+  long long si = -1, di = 0;
+  if (mine) {
+    const long long bg = e / n_keep;
+    const int j = (int)(e - bg * n_keep), b = (int)(bg / H);
+    const int idx = keep_index[e];
+    const int count = min(min(src.lengths[b], src.capacity), n_keep);
+    if (j < count) {
+      si = bg * cap + min(max(idx, 0), src.capacity - 1);  // a bad index cannot leave the row
+      di = bg * cap + j;
+    }
   }
-  if (ch * CH >= count) return;
-  const int total = min(CH, count - ch * CH);
-  list[tid] = min(max(idx, 0), src.capacity - 1);  // a bad index cannot leave the row
+  s_row[tid] = si;
+  d_row[tid] = di;
+  float ksv = 0.f, vsv = 0.f, scv = 0.f;
+  int pos = 0;
+  if (si >= 0) {
+    ksv = src.k_scale[si];
+    vsv = src.v_scale[si];
+    if (src.positions && dst.positions) pos = src.positions[si];
+    if (src_score && dst_score) scv = src_score[si];
+  }
+  if (blockIdx.x == 0) {
+    for (int b = tid; b < src.batch; b += NT) {
+      dst.lengths[b] = min(min(src.lengths[b], src.capacity), n_keep);
+      dst.num_seen[b] = src.num_seen[b];
+    }
+  }
   __syncthreads();
-  copy_rows<RB, NT>(src, src_score, dst, dst_score, ((long long)b * H + g) * src.capacity, list, total, ch * CH);
+  const uint8_t* sk = static_cast<const uint8_t*>(src.k_codes);
+  const uint8_t* sv = static_cast<const uint8_t*>(src.v_codes);
+  uint8_t* dk = static_cast<uint8_t*>(dst.k_codes);
+  uint8_t* dv = static_cast<uint8_t*>(dst.v_codes);
+  const int part = tid % LPR, r0 = tid / LPR;
+  u32x4 kx[NPASS], vx[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const long long r = s_row[r0 + p * RPP];
+    const long long row = r < 0 ? 0 : r;  // every load valid; unused rows are not stored
+    kx[p] = *reinterpret_cast<const u32x4*>(sk + row * RB + part * 16);
+    vx[p] = *reinterpret_cast<const u32x4*>(sv + row * RB + part * 16);
+  }
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int q = r0 + p * RPP;
+    if (s_row[q] >= 0) {
+      // Streaming stores: the compacted rows are not read again by this launch.
+      __builtin_nontemporal_store(kx[p], reinterpret_cast<u32x4*>(dk + d_row[q] * RB + part * 16));
+      __builtin_nontemporal_store(vx[p], reinterpret_cast<u32x4*>(dv + d_row[q] * RB + part * 16));
+    }
+  }
+  if (si >= 0) {
+    dst.k_scale[di] = ksv;
+    dst.v_scale[di] = vsv;
+    if (src.positions && dst.positions) dst.positions[di] = pos;
+    if (src_score && dst_score) dst_score[di] = scv;
+  }
 }
 
 template <int RB>
@@ -243,8 +295,13 @@ hipError_t launch_rb(const kvc_cache_t& src, const float* ss, const uint8_t* mas
 template <int RB>
 hipError_t launch_gather_rb(const kvc_cache_t& src, const float* ss, const int32_t* keep_index, int n_keep,
                             const kvc_cache_t& dst, float* ds, hipStream_t st) {
-  const dim3 grid((n_keep + CH - 1) / CH, src.num_kv_heads, src.batch);
-  hipLaunchKernelGGL((compact_gather_kernel<RB>), grid, dim3(NT), 0, st, src, ss, keep_index, n_keep, dst, ds);
+  // About 512 workgroups (2 per CU) for the flat list, at most NT entries each.
+  const long long entries = (long long)src.batch * src.num_kv_heads * n_keep;
+  const int per_wg = (int)std::min<long long>(NT, std::max<long long>(1, (entries + 511) / 512));
+  const long long wgs = (entries + per_wg - 1) / per_wg;
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((compact_gather_kernel<RB>), dim3((unsigned)wgs), dim3(NT), 0, st, src, ss, keep_index, n_keep,
+                     dst, ds, entries, per_wg);
   return hipGetLastError();
 }
 

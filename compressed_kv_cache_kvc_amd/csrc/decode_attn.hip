@@ -160,7 +160,8 @@ __device__ __forceinline__ unsigned sel4(const unsigned* v, int i) {
 // row for GP >= 4. The PV output of row set rs holds head 4 rs + l / 16 (the
 // same head as the lane's logits) and channel 16 m + l % 16 of block m.
 template <int BITS, int D, int GP, bool PAGED>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnLaunch a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3 : 2))) void attn_split_kernel(
+    AttnLaunch a) {
   constexpr int RB = D * BITS / 8;          // bytes per token row in HBM
   constexpr int KB = BITS == 8 ? 16 : 8;    // HBM bytes per lane per load (16 elements)
   constexpr int NDH = D / 64;               // 64-element halves of a row (QK k = 64)

@@ -184,7 +184,7 @@ def test_select_bit_exact_on_shared_scores(L, budget, S, R):
 
 
 @pytest.mark.parametrize("bits,D,L,keep_n", [(8, 128, 2500, 900), (4, 128, 2500, 900), (8, 64, 2500, 900),
-                                             (8, 128, 40000, 12000)])
+                                             (4, 64, 2500, 900), (8, 128, 40000, 12000)])
 def test_compact_bit_exact(bits, D, L, keep_n):
     """Short rows take the one-launch path; 40000 slots (40 chunks) take the
     count-then-move path."""
