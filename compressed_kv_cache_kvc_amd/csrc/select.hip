@@ -71,8 +71,8 @@ __device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, in
   constexpr int BPT = kBins / NT;  // bins per thread in the digit search
   const int tid = threadIdx.x;
   unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
-  for_keys([&](unsigned u) {
-    kmin = min(kmin, u);
+  for_keys([&](unsigned u) {  // key 0 marks an unused register slot
+    kmin = min(kmin, u == 0u ? 0xFFFFFFFFu : u);
     kmax = max(kmax, u);
   });
   block_minmax<NT>(kmin, kmax, mm_tmp);
@@ -84,13 +84,21 @@ __device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, in
   for (int i = tid; i < kBins; i += NT) hist[i] = 0;
   if (tid == 0) sel[3] = 0;  // keys gathered into `small`
   __syncthreads();
+  bool first = true;
   while (remaining > 0) {
     const int width = min(kDigitBits, remaining);
     const int shift = remaining - width;
     const unsigned dmask = (1u << width) - 1u;
-    for_keys([&](unsigned u) {
-      if ((u & pmask) == T) atomicAdd(&hist[(u >> shift) & dmask], 1);
-    });
+    if (first) {
+      // Every real key shares the prefix T of the first pass: add the match
+      // flag instead of branching per key.
+      for_keys([&](unsigned u) { atomicAdd(&hist[(u >> shift) & dmask], (int)((u & pmask) == T)); });
+    } else {
+      for_keys([&](unsigned u) {
+        if ((u & pmask) == T) atomicAdd(&hist[(u >> shift) & dmask], 1);
+      });
+    }
+    first = false;
     __syncthreads();
     // Thread t owns the BPT bins just below kBins - BPT*t, so the inclusive
     // scan over threads counts keys from the largest digit down; each bin is
@@ -204,6 +212,11 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
       key[q + 2] = w.z;
       key[q + 3] = w.w;
     }
+    // Slots past the thread's candidates hold key 0, below every real key
+    // (scores are non-negative, so real keys have the top bit set): loops over
+    // the keys then need no per-key branch.
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) key[q] = q < cnt ? key[q] : 0u;
   }
   // Every candidate once, in any order (the histogram passes). Register path:
   // the thread's own keys. Memory path: slots strided over the workgroup
@@ -211,8 +224,7 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
   auto for_keys = [&](auto f) {
     if (REG) {
 #pragma unroll
-      for (int q = 0; q < KPT; ++q)
-        if (q < cnt) f(key[q]);
+      for (int q = 0; q < KPT; ++q) f(key[q]);  // key 0 in unused slots
     } else {
       for (int base = lo + tid; base < hi; base += KPT * NT) {
         unsigned kk[KPT];
@@ -258,10 +270,19 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
   // Candidates: rank the threshold ties in slot order; with a gather list,
   // also count the candidates above T before this thread.
   int ties = 0, above = 0;
-  for_own([&](int, unsigned u) {
-    ties += any_heavy & (u == T);
-    above += any_heavy & (u > T);
-  });
+  if (REG) {
+    // Unused slots hold key 0, never equal to or above T.
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      ties += any_heavy & (key[q] == T);
+      above += any_heavy & (key[q] > T);
+    }
+  } else {
+    for_own([&](int, unsigned u) {
+      ties += any_heavy & (u == T);
+      above += any_heavy & (u > T);
+    });
+  }
   // Both prefix counts at once when every count fits 16 bits (ties in the
   // low half); longer rows scan them separately.
   int tie_rank, above_before;
