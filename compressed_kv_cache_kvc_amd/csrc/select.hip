@@ -20,10 +20,11 @@
 //    that bin holds at most 64 keys, they are gathered into LDS and one wave
 //    ranks them directly (each lane counts the keys above and equal to its
 //    own), which ends the search without further passes.
-// Rows of up to 8192 candidates use 256 threads holding up to 32 keys each in
-// registers: few waves keep the per-pass fixed cost (scans, barriers) low,
-// since every instruction runs once per wave. Longer rows use 1024 threads and
-// re-read their keys from memory on every pass. Keys above T are kept; of the
+// Rows of up to 8192 candidates use 1024 threads holding up to 8 keys each in
+// registers, with no per-key branches (unused slots hold key 0); with a single
+// workgroup per row the kernel is latency-bound, and 16 waves per CU hide each
+// other's latency. Longer rows use 1024 threads that re-read their keys from
+// memory on every pass. Keys above T are kept; of the
 // keys equal to T, the first (k - count above T) in slot order are kept,
 // ranked by a block-wide prefix count over thread-contiguous slot ranges.
 //
@@ -318,8 +319,8 @@ hipError_t launch_select(const kvc_cache_t& c, const float* score, int budget, i
                          uint8_t* mask, int32_t* keep_index, int max_len, hipStream_t st) {
   const long long cand = (long long)max_len - n_sink - n_recent;
   const dim3 grid(c.num_kv_heads, c.batch);
-  if (cand <= 256 * 32)
-    hipLaunchKernelGGL((select_kernel<256, 32, true>), grid, dim3(256), 0, st, c, score, budget, n_sink, n_recent,
+  if (cand <= 1024 * 8)
+    hipLaunchKernelGGL((select_kernel<1024, 8, true>), grid, dim3(1024), 0, st, c, score, budget, n_sink, n_recent,
                        mask, keep_index, max_len);
   else
     hipLaunchKernelGGL((select_kernel<1024, 8, false>), grid, dim3(1024), 0, st, c, score, budget, n_sink,
