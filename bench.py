@@ -44,8 +44,8 @@ METRIC = "decode-attn KV GB/s & tokens/s (fraction of HBM peak), INT8, L=8192, 1
 TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/kvc_internal.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "28d30a89ae24b083e688d9a3dd5771b597930ac96609d0754f01fb9df2747921"
-TRAFFIC_BYTES = 76404443
+TRAFFIC_SHA256 = "10b759f36d648dd9aaacd995294479b9be9bc93a7408d51ed35f1f85013cd168"
+TRAFFIC_BYTES = 74294381
 
 
 def attention_traffic():
