@@ -123,6 +123,90 @@ def copy_calibration(torch, mib):
     return 0
 
 
+def secondary_attention(kvc, torch, reps=16):
+    """Decode-attention throughput of the other workloads at full size, as KV
+    GB/s of algorithmic bytes (codes + scales + q) and the fraction of the
+    8 TB/s peak. Cache contents are random device data quantized by the library
+    (timing does not depend on the values); the paged lengths follow the
+    paged workload's seeded lengths, its block table a seeded permutation.
+    Caches that fit the 256 MB Infinity Cache are rotated."""
+    from workloads import get
+    res = {}
+
+    def timed(launch, n_bufs):
+        for i in range(3):
+            launch(i % n_bufs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            launch(i % n_bufs)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def report(name, w, kv_bytes, us, extra):
+        gbps = kv_bytes / (us * 1e-6) / 1e9
+        res[name] = {"workload": name, "us_per_launch": round(us, 2), "kv_bytes": int(kv_bytes),
+                     "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), **extra}
+
+    # Paged batch: 32 sequences, 16-token INT8 blocks, no H2O.
+    w = get("paged_b32")
+    B, H, D, bs = w.batch, w.num_kv_heads, w.head_dim, w.paged_block
+    lengths = np.random.default_rng([w.seed, 1]).integers(w.len_lo, w.len_hi, endpoint=True, size=B)
+    nblk = [(int(n) + bs - 1) // bs for n in lengths]
+    perm = np.random.default_rng(w.seed).permutation(sum(nblk)).astype(np.int32)
+    table = np.full((B, max(nblk)), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+    gc = kvc.KVCache(B, H, D, 0, 8, block_size=bs, num_blocks=int(sum(nblk)), max_blocks_per_seq=table.shape[1])
+    gc.block_table.copy_(torch.from_numpy(table).cuda())
+    for b in range(B):
+        one = kvc.KvcCacheDesc.from_buffer_copy(gc.desc)
+        one.batch = 1
+        one.block_table = gc.block_table[b].data_ptr()
+        one.lengths = gc.lengths[b:b + 1].data_ptr()
+        one.num_seen = gc.num_seen[b:b + 1].data_ptr()
+        kv = torch.randn((2, 1, H, int(lengths[b]), D), device="cuda").half()
+        kvc.kvc_quant_append(one, kv[0], kv[1], max_len_hint=0)
+    q = torch.randn((B, w.num_q_heads, D), device="cuda").half()
+    out = torch.empty((B, w.num_q_heads, D), dtype=torch.float32, device="cuda")
+    hint = int(lengths.max())
+    ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(gc, w.num_q_heads, hint, False), dtype=torch.uint8,
+                     device="cuda")
+    us = timed(lambda i: kvc.kvc_decode_attn(gc, q, out, max_len_hint=hint, workspace=ws), 1)
+    report("paged_b32", w, int(lengths.sum()) * H * 2 * (D + 4) + q.numel() * 2, us,
+           {"tokens": int(lengths.sum()), "h2o": False})
+    del gc, ws
+    torch.cuda.empty_cache()
+
+    # GQA steady state (8193 tokens, 28/4 heads) and the 70B INT4 layer, H2O on.
+    for name, L, n_bufs in (("qwen_gqa_stream", 8193, 8), ("llama70b_int4", 131072, 1)):
+        w = get(name)
+        B, Hq, H, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+        caches, scores = [], []
+        for i in range(n_bufs):
+            c = kvc.KVCache(B, H, D, L, w.bits)
+            kv = torch.randn((2, B, H, L, D), device="cuda").half()
+            kvc.kvc_quant_append(c, kv[0], kv[1], max_len_hint=0)
+            del kv
+            caches.append(c)
+            scores.append(c.score_buffer())
+        q = torch.randn((B, Hq, D), device="cuda").half()
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, L, True), dtype=torch.uint8,
+                         device="cuda")
+        us = timed(lambda i: kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L,
+                                                 workspace=ws), n_bufs)
+        report(name, w, B * H * L * 2 * (D * w.bits // 8 + 4) + q.numel() * 2, us,
+               {"tokens": B * L, "h2o": True, "bits": w.bits, "q_heads": Hq, "kv_heads": H})
+        del caches, scores, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +214,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the attention-only measurements of the paged, GQA and INT4 workloads")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the benchmark, run 8 plain device-to-device copies of this many MiB "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -276,6 +362,8 @@ def main(argv=None):
             "traffic": attention_traffic(),
         },
     }
+    if not args.no_secondary:
+        rec["secondary_attention"] = secondary_attention(kvc, torch)
     if not args.no_cpu_baseline:
         t_cpu, n_cpu, cores = cpu_baseline(w, d, args.cpu_seconds)
         rec["cpu_baseline"] = {
