@@ -14,10 +14,13 @@ Steps rotate over 32 distinct layer caches (2.1 GiB, like the 32 layers of the
 model), so every launch streams its 66 MiB from HBM rather than from the
 256 MB Infinity Cache. Inputs are resident in HBM before timing starts.
 
-The timed region replays HIP graphs, one per phase of a 32-layer block:
-[rewind lengths + 32 appends] [32 attentions] [32 x (select + compact)].
-HIP events around the attention phase give the attention kernels' average
-duration, from which the roofline fraction is computed.
+The timed region replays one HIP graph per 32-layer block in decode order:
+rewind the lengths, then for each layer append, attention, select, compact.
+`value` and `ms_per_step` come from it. The same steps then run again as
+four graphs per block, one per phase ([rewind + 32 appends] [32 attentions]
+[32 selects] [32 compactions]), with HIP events between the phases: they give
+each phase's time ("phases") and the attention kernels' average duration, from
+which the roofline fraction is computed.
 
 Prints one JSON line. Run ``python bench.py --help`` for options.
 """
@@ -71,6 +74,23 @@ def step_bytes(B, Hq, H, D, bits, L, budget):
         "compact": B * H * budget * 4 + 2 * B * H * budget * (2 * (rb + 4) + 8),  # list; kept rows in and out
     }
     return parts, kv + B * Hq * D * 2   # attention kernel's own algorithmic bytes (KV + q)
+
+
+def phase_table(phase_ms, steps, parts, attn_alg):
+    """Per-phase time and HBM roofline fraction of one step. Each phase is one
+    replayed graph (one launch per layer buffer, or two for attention) timed
+    with events on the replay stream; bytes are the phase's algorithmic bytes:
+    attention counts the KV stream and q as in the roofline entry, plus the
+    H2O score read-modify-write its merge kernel does."""
+    names = ("append", "attention", "select", "compact")
+    alg = (parts["append"], attn_alg + parts["h2o"], parts["select"], parts["compact"])
+    table = {}
+    for name, ms, b in zip(names, phase_ms, alg):
+        us = ms * 1e3 / steps
+        gbps = b / (us * 1e-6) / 1e9
+        table[name] = {"us": round(us, 3), "bytes": int(b), "gbps": round(gbps, 1),
+                       "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    return table
 
 
 def cpu_baseline(w, d, budget_s=12.0):
@@ -272,56 +292,93 @@ def main(argv=None):
         for i in range(LAYERS):
             kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L, workspace=ws_attn)
 
-    def phase_evict():
+    def phase_select():
         for i in range(LAYERS):
+            kvc.kvc_h2o_select(caches[i], scores[i], budget, S, R, masks[i], keep_index=keep_lists[i],
+                               max_len_hint=L)
+
+    def phase_compact():
+        for i in range(LAYERS):
+            kvc.kvc_compact_gather(caches[i], scores[i], keep_lists[i], budget, dst, dst_score)
+
+    def whole_block():
+        # Decode order: each layer's append, attention and eviction in turn.
+        lengths_all.fill_(L - 1)
+        for i in range(LAYERS):
+            kvc.kvc_quant_append(caches[i], k_new, v_new, h2o_score=scores[i], max_len_hint=L - 1)
+            kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L, workspace=ws_attn)
             kvc.kvc_h2o_select(caches[i], scores[i], budget, S, R, masks[i], keep_index=keep_lists[i],
                                max_len_hint=L)
             kvc.kvc_compact_gather(caches[i], scores[i], keep_lists[i], budget, dst, dst_score)
 
-    # ---- eager pass, then capture each phase as a graph ----
+    # ---- eager pass, then capture the whole block and each phase as graphs ----
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        phase_append(); phase_attn(); phase_evict()
+        whole_block()
     torch.cuda.synchronize()
     eager_out = out.clone()
     eager_len = dst.lengths.clone()
-    graphs = []
-    for fn in (phase_append, phase_attn, phase_evict):
+    eager_keep = torch.stack(keep_lists)
+
+    def capture(fn):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             fn()
-        graphs.append(g)
+        return g
+
+    g_whole = capture(whole_block)
+    graphs = [capture(fn) for fn in (phase_append, phase_attn, phase_select, phase_compact)]
     torch.cuda.synchronize()
 
     blocks_w = max(1, (args.warmup + LAYERS - 1) // LAYERS)
     blocks = max(1, (args.steps + LAYERS - 1) // LAYERS)
     steps = blocks * LAYERS
-    with torch.cuda.stream(stream):
-        for _ in range(blocks_w):
-            for g in graphs:
-                g.replay()
-    torch.cuda.synchronize()
-    # The replayed graph must reproduce the eager result.
-    assert torch.equal(out, eager_out), "graph replay differs from the eager attention output"
-    assert torch.equal(dst.lengths, eager_len)
+    # Both replay orders must reproduce the eager result.
+    for order in ([g_whole], graphs):
+        with torch.cuda.stream(stream):
+            for _ in range(blocks_w):
+                for g in order:
+                    g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), "graph replay differs from the eager attention output"
+        assert torch.equal(dst.lengths, eager_len)
+        assert torch.equal(torch.stack(keep_lists), eager_keep), "graph replay differs from the eager keep lists"
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(blocks)]
+    # ---- timed region: K steps in decode order ----
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         t_start.record(stream)
         wall0 = time.perf_counter()
-        for bi in range(blocks):
-            graphs[0].replay()
-            ev[bi][0].record(stream)
-            graphs[1].replay()
-            ev[bi][1].record(stream)
-            graphs[2].replay()
+        for _ in range(blocks):
+            g_whole.replay()
         t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    attn_ms = sum(a.elapsed_time(b) for a, b in ev)
+
+    # ---- the same K steps phase by phase, with events between phases ----
+    # ev[bi][p] ends phase p of block bi; phase p starts where the previous
+    # event (or p_start) ends.
+    n_ph = len(graphs)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ph)] for _ in range(blocks)]
+    p_start, p_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        p_start.record(stream)
+        for bi in range(blocks):
+            for p, g in enumerate(graphs):
+                g.replay()
+                ev[bi][p].record(stream)
+        p_end.record(stream)
+    torch.cuda.synchronize()
+    phase_ms = [0.0] * n_ph
+    prev = p_start
+    for bi in range(blocks):
+        for p in range(n_ph):
+            phase_ms[p] += prev.elapsed_time(ev[bi][p])
+            prev = ev[bi][p]
+    attn_ms = phase_ms[1]
+    by_phase_ms = p_start.elapsed_time(p_end)
 
     parts, attn_alg = step_bytes(B, Hq, H, D, bits, L, budget)
     step_alg = sum(parts.values())
@@ -352,6 +409,8 @@ def main(argv=None):
         "attention_us": round(attn_us, 3),
         "attention_kv_gbps": round(attn_gbps, 1),
         "wall_s": round(wall, 3),
+        "phases": phase_table(phase_ms, steps, parts, attn_alg),
+        "ms_per_step_phase_by_phase": round(by_phase_ms / steps, 5),
         "roofline": {
             "bound": "hbm",
             "kernel": "decode attention (attn_split_kernel + attn_combine_kernel)",
