@@ -6,19 +6,19 @@ H2O keep 0.3 = 4 sinks + 1024 recent + 1429 heavy hitters):
 
   1. quantize-append the new token's K and V          (kvc_quant_append)
   2. attention over all 8192 tokens + H2O accumulation (kvc_decode_attn)
-  3. keep-set selection down to 2457 slots, as a mask and
-     an ascending keep list                            (kvc_h2o_select)
-  4. compaction of the kept slots into the other buffer (kvc_compact_gather)
+  3. eviction: keep-set selection down to 2457 slots (a mask and an
+     ascending keep list) and compaction of the kept slots into the other
+     buffer, in one call                               (kvc_h2o_evict)
 
 Steps rotate over 32 distinct layer caches (2.1 GiB, like the 32 layers of the
 model), so every launch streams its 66 MiB from HBM rather than from the
 256 MB Infinity Cache. Inputs are resident in HBM before timing starts.
 
 The timed region replays one HIP graph per 32-layer block in decode order:
-rewind the lengths, then for each layer append, attention, select, compact.
+rewind the lengths, then for each layer append, attention, eviction.
 `value` and `ms_per_step` come from it. The same steps then run again as
-four graphs per block, one per phase ([rewind + 32 appends] [32 attentions]
-[32 selects] [32 compactions]), with HIP events between the phases: they give
+three graphs per block, one per phase ([rewind + 32 appends] [32 attentions]
+[32 evictions]), with HIP events between the phases: they give
 each phase's time ("phases") and the attention kernels' average duration, from
 which the roofline fraction is computed.
 
@@ -70,20 +70,22 @@ def step_bytes(B, Hq, H, D, bits, L, budget):
         "append": B * H * (2 * D * 2 + 2 * (rb + 4) + 4 + 4),   # fp16 in; codes, scales, position, score out
         "attention": kv + B * Hq * D * 2 + B * Hq * D * 4,      # KV + q (fp16) + out (fp32)
         "h2o": 2 * B * H * L * 4,                                # score read-modify-write
-        "select": B * H * L * 4 + B * H * L + B * H * budget * 4,  # scores in; mask and keep list out
-        "compact": B * H * budget * 4 + 2 * B * H * budget * (2 * (rb + 4) + 8),  # list; kept rows in and out
+        # scores in; mask and keep list out; kept rows (codes, scales, position, score) in and out
+        "evict": B * H * (L * 4 + L + budget * 4) + 2 * B * H * budget * (2 * (rb + 4) + 8),
     }
     return parts, kv + B * Hq * D * 2   # attention kernel's own algorithmic bytes (KV + q)
 
 
 def phase_table(phase_ms, steps, parts, attn_alg):
     """Per-phase time and HBM roofline fraction of one step. Each phase is one
-    replayed graph (one launch per layer buffer, or two for attention) timed
-    with events on the replay stream; bytes are the phase's algorithmic bytes:
+    replayed graph (one launch per layer buffer, two for attention) timed with
+    events on the replay stream; bytes are the phase's algorithmic bytes:
     attention counts the KV stream and q as in the roofline entry, plus the
-    H2O score read-modify-write its merge kernel does."""
-    names = ("append", "attention", "select", "compact")
-    alg = (parts["append"], attn_alg + parts["h2o"], parts["select"], parts["compact"])
+    H2O score read-modify-write its merge kernel does; eviction counts the
+    selection's score reads, mask and keep-list writes and the compaction's
+    kept rows in and out."""
+    names = ("append", "attention", "evict")
+    alg = (parts["append"], attn_alg + parts["h2o"], parts["evict"])
     table = {}
     for name, ms, b in zip(names, phase_ms, alg):
         us = ms * 1e3 / steps
@@ -292,14 +294,13 @@ def main(argv=None):
         for i in range(LAYERS):
             kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L, workspace=ws_attn)
 
-    def phase_select():
-        for i in range(LAYERS):
-            kvc.kvc_h2o_select(caches[i], scores[i], budget, S, R, masks[i], keep_index=keep_lists[i],
-                               max_len_hint=L)
+    def evict(i):
+        kvc.kvc_h2o_evict(caches[i], scores[i], budget, S, R, keep_lists[i], dst, dst_score, keep_mask=masks[i],
+                          max_len_hint=L)
 
-    def phase_compact():
+    def phase_evict():
         for i in range(LAYERS):
-            kvc.kvc_compact_gather(caches[i], scores[i], keep_lists[i], budget, dst, dst_score)
+            evict(i)
 
     def whole_block():
         # Decode order: each layer's append, attention and eviction in turn.
@@ -307,9 +308,7 @@ def main(argv=None):
         for i in range(LAYERS):
             kvc.kvc_quant_append(caches[i], k_new, v_new, h2o_score=scores[i], max_len_hint=L - 1)
             kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L, workspace=ws_attn)
-            kvc.kvc_h2o_select(caches[i], scores[i], budget, S, R, masks[i], keep_index=keep_lists[i],
-                               max_len_hint=L)
-            kvc.kvc_compact_gather(caches[i], scores[i], keep_lists[i], budget, dst, dst_score)
+            evict(i)
 
     # ---- eager pass, then capture the whole block and each phase as graphs ----
     stream = torch.cuda.Stream()
@@ -327,7 +326,7 @@ def main(argv=None):
         return g
 
     g_whole = capture(whole_block)
-    graphs = [capture(fn) for fn in (phase_append, phase_attn, phase_select, phase_compact)]
+    graphs = [capture(fn) for fn in (phase_append, phase_attn, phase_evict)]
     torch.cuda.synchronize()
 
     blocks_w = max(1, (args.warmup + LAYERS - 1) // LAYERS)

@@ -66,6 +66,7 @@ def _load():
         "kvc_compact_workspace_bytes": (SZ, [D, I32]),
         "kvc_compact": (I32, [D, P, P, D, P, I32, P, SZ, P]),
         "kvc_compact_gather": (I32, [D, P, P, I32, D, P, P]),
+        "kvc_h2o_evict": (I32, [D, P, I32, I32, I32, P, P, D, P, I32, P]),
         "kvc_pool_create": (P, [I32, I32, U64]),
         "kvc_pool_destroy": (None, [P]),
         "kvc_pool_reserve": (I32, [P, I32, I32]),
@@ -291,6 +292,25 @@ def kvc_compact_gather(src, src_score, keep_index, n_keep: int, dst, dst_score=N
                                   _ptr(dst_score), _stream(stream)), "kvc_compact_gather")
     if isinstance(dst, KVCache) and isinstance(src, KVCache):
         dst.max_len = min(src.max_len, n_keep)
+
+
+def kvc_h2o_evict(src, h2o_score, budget: int, n_sink: int, n_recent: int, keep_index, dst, dst_score=None,
+                  keep_mask=None, max_len_hint: Optional[int] = None, stream=None):
+    """Selection and compaction in one call: the keep set of ``kvc_h2o_select``
+    copied into ``dst`` as ``kvc_compact_gather`` copies it (see kvc.h)."""
+    import torch
+    ds, dd = _desc(src), _desc(dst)
+    _need(h2o_score, torch.float32, "h2o_score", ds.batch * ds.num_kv_heads * ds.capacity)
+    _need(dst_score, torch.float32, "dst_score", dd.batch * dd.num_kv_heads * dd.capacity)
+    _need(keep_index, torch.int32, "keep_index", ds.batch * ds.num_kv_heads * budget)
+    _need(keep_mask, torch.uint8, "keep_mask", ds.batch * ds.num_kv_heads * ds.capacity)
+    if max_len_hint is None:
+        max_len_hint = src.max_len
+    _check(lib.kvc_h2o_evict(ctypes.byref(ds), _ptr(h2o_score), budget, n_sink, n_recent, _ptr(keep_mask),
+                             _ptr(keep_index), ctypes.byref(dd), _ptr(dst_score), max_len_hint, _stream(stream)),
+           "kvc_h2o_evict")
+    if isinstance(dst, KVCache) and isinstance(src, KVCache):
+        dst.max_len = min(src.max_len, budget)
 
 
 class BlockPool:

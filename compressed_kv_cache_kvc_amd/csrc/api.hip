@@ -294,4 +294,38 @@ int32_t kvc_compact_gather(const kvc_cache_t* src, const float* src_score, const
                        "kvc_compact_gather launch");
 }
 
+int32_t kvc_h2o_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budget, int32_t n_sink,
+                      int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
+                      float* dst_score, int32_t max_len_hint, void* stream) {
+  clear_error();
+  int32_t st = check_compact_pair(src, dst, nullptr, nullptr);
+  if (st) return st;
+  if (!h2o_score || !keep_index) return fail(KVC_ERR_INVALID_ARG, "h2o_score and keep_index must not be NULL");
+  if (budget < 1) return fail(KVC_ERR_INVALID_ARG, "budget must be >= 1");
+  if (n_sink < 0 || n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
+  if ((long long)n_sink + n_recent > budget) return fail(KVC_ERR_INVALID_ARG, "n_sink + n_recent exceeds budget");
+  if (budget > src->capacity) return fail(KVC_ERR_CAPACITY, "budget exceeds capacity");
+  if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
+  if (max_len_hint > src->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
+  const size_t rows = (size_t)src->batch * src->num_kv_heads;
+  if ((st = check_out_of_place(src, h2o_score, keep_index, rows * budget * sizeof(int32_t), dst, dst_score, nullptr,
+                               0)))
+    return st;
+  if (keep_mask && (st = check_out_of_place(src, h2o_score, keep_mask, rows * src->capacity, dst, dst_score,
+                                            nullptr, 0)))
+    return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (evict_fits_one_launch(max_len_hint, n_sink, n_recent))
+    return device_status(launch_evict(*src, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, *dst,
+                                      dst_score, max_len_hint, s),
+                         "kvc_h2o_evict launch");
+  // Longer rows: the selection kernel writes the keep list, the gather copies it.
+  st = device_status(launch_select(*src, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, max_len_hint, s),
+                     "kvc_h2o_evict select launch");
+  if (st) return st;
+  return device_status(launch_compact_gather(*src, dst_score ? h2o_score : nullptr, keep_index, budget, *dst,
+                                             dst_score, s),
+                       "kvc_h2o_evict gather launch");
+}
+
 }  // extern "C"

@@ -47,6 +47,13 @@ hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st);
 hipError_t launch_select(const kvc_cache_t& c, const float* score, int budget, int n_sink,
                          int n_recent, uint8_t* mask, int32_t* keep_index, int max_len, hipStream_t st);
 
+// Selection and compaction in one launch; only for rows of at most 8192
+// candidates (evict_fits_one_launch).
+bool evict_fits_one_launch(int max_len, int n_sink, int n_recent);
+hipError_t launch_evict(const kvc_cache_t& c, const float* score, int budget, int n_sink, int n_recent,
+                        uint8_t* mask, int32_t* keep_index, const kvc_cache_t& dst, float* dst_score, int max_len,
+                        hipStream_t st);
+
 hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const uint8_t* mask,
                           const kvc_cache_t& dst, float* dst_score, int32_t* counts, int chunks,
                           hipStream_t st);

@@ -8,6 +8,8 @@
  *                     plus optional H2O accumulation of attention mass
  *   kvc_h2o_select    sink + recent-window + top-k heavy-hitter keep mask
  *   kvc_compact       stable out-of-place compaction of the kept slots
+ *                     (kvc_compact_gather: from the keep list instead;
+ *                     kvc_h2o_evict: selection and compaction in one call)
  * and a host-side paged block pool (kvc_pool_*) that yields block tables.
  *
  * Conventions shared by every call:
@@ -237,6 +239,35 @@ int32_t kvc_compact(const kvc_cache_t* src, const float* src_score, const uint8_
  */
 int32_t kvc_compact_gather(const kvc_cache_t* src, const float* src_score, const int32_t* keep_index,
                            int32_t n_keep, const kvc_cache_t* dst, float* dst_score, void* stream);
+
+/*
+ * Eviction in one call: the keep set of kvc_h2o_select, moved to dst as
+ * kvc_compact_gather moves it. Sources: those two calls ("KV Cache
+ * Compression Report", sections 3.3 and 3.4; "KV Cache optimization
+ * techniques" tutorial, sections 2.2 and 2.4).
+ *
+ * For each (b, g) row with L = src->lengths[b], the slots kvc_h2o_select would
+ * keep (with the same budget, n_sink, n_recent and h2o_score) are copied in
+ * ascending order to slots 0 .. min(L, budget) - 1 of dst: K and V codes and
+ * scales, positions when both caches have them, and scores into dst_score
+ * when it is not NULL. dst->lengths[b] = min(L, budget), dst->num_seen[b] =
+ * src->num_seen[b]; slots of dst at or beyond the new length are left
+ * untouched. keep_index (required, device int32 [batch][num_kv_heads][budget])
+ * and keep_mask (may be NULL, device uint8 [batch][num_kv_heads][capacity])
+ * receive exactly what kvc_h2o_select writes into them.
+ * When max_len_hint - n_sink - n_recent <= 8192, one launch does both steps
+ * (each row's workgroups select redundantly and each copies a share of the
+ * kept rows); longer rows take the two launches of the separate calls.
+ * h2o_score must hold non-negative, non-NaN values.
+ * Errors: those of kvc_h2o_select and kvc_compact_gather: INVALID_ARG for bad
+ * descriptors, differing src/dst geometries, NULL h2o_score or keep_index,
+ * budget < 1, n_sink or n_recent < 0, n_sink + n_recent > budget, or a dst
+ * buffer overlapping src, h2o_score, keep_mask or keep_index; CAPACITY if
+ * budget or max_len_hint > capacity; UNSUPPORTED for paged caches.
+ */
+int32_t kvc_h2o_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budget, int32_t n_sink,
+                      int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
+                      float* dst_score, int32_t max_len_hint, void* stream);
 
 /*
  * Paged block pool (host only; no device memory is touched).

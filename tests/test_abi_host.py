@@ -158,6 +158,22 @@ def test_compact_validation():
     assert gather(src, dst, n=513) == CAPACITY
     assert gather(src, dst, idx=0x1100000) == INVALID   # list overlaps dst codes
     assert gather(paged, dst) == UNSUPPORTED
+    evict = lambda s_, d_, idx=0x5000000, budget=16, ns=4, nr=4, hint=16, score=0x4000000, mask=None, dsc=None: \
+        lib.kvc_h2o_evict(ctypes.byref(s_), score, budget, ns, nr, mask, idx, ctypes.byref(d_), dsc, hint, None)
+    assert evict(src, bad) == INVALID
+    assert evict(src, other) == INVALID
+    assert evict(src, dst, idx=None) == INVALID
+    assert evict(src, dst, score=None) == INVALID
+    assert evict(src, dst, budget=0) == INVALID
+    assert evict(src, dst, ns=-1) == INVALID
+    assert evict(src, dst, ns=10, nr=10) == INVALID     # sinks + window exceed the budget
+    assert evict(src, dst, budget=513) == CAPACITY
+    assert evict(src, dst, hint=-1) == INVALID
+    assert evict(src, dst, hint=513) == CAPACITY
+    assert evict(src, dst, idx=0x1100000) == INVALID    # list overlaps dst codes
+    assert evict(src, dst, mask=0x1200000) == INVALID   # mask overlaps dst codes
+    assert evict(src, dst, dsc=0x4000000) == INVALID    # dst scores overlap the src scores
+    assert evict(paged, dst) == UNSUPPORTED
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 512) >= 4 * 1 * 4
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 2048) == 0   # beyond capacity
 

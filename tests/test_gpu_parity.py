@@ -216,6 +216,83 @@ def test_compact_bit_exact(bits, D, L, keep_n):
         assert host(out.num_seen).tolist() == [L] * B
 
 
+def _assert_same_cache(a, b, a_score=None, b_score=None):
+    """Every buffer of two caches (and score arrays) equal bit for bit."""
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "positions", "lengths", "num_seen"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    if a_score is not None:
+        assert torch.equal(a_score, b_score), "scores"
+
+
+@pytest.mark.parametrize("bits,D,B,H,L,budget,S,R", [
+    (8, 128, 2, 3, 9000, 2457, 4, 1024),   # one launch, 8 workgroups per row, 7972 candidates
+    (4, 128, 2, 3, 3000, 1000, 4, 100),    # INT4 rows of 64 bytes
+    (8, 64, 2, 3, 3000, 1000, 0, 100),     # no sinks
+    (4, 64, 2, 3, 3000, 1000, 4, 100),     # rows of 32 bytes
+    (8, 128, 2, 3, 99, 100, 4, 10),        # L <= budget: every slot kept
+    (8, 128, 2, 3, 2000, 1028, 4, 1024),   # no heavy hitters
+    (8, 64, 5, 32, 1500, 500, 4, 64),      # 160 rows: one workgroup per row
+    (8, 64, 2, 3, 20000, 5000, 4, 256),    # 19740 candidates: the two-launch path
+])
+@pytest.mark.parametrize("with_mask", [True, False])
+def test_evict_bit_exact(bits, D, B, H, L, budget, S, R, with_mask):
+    """kvc_h2o_evict equals kvc_h2o_select followed by kvc_compact_gather on
+    every buffer, and the oracle's selection and compaction on the kept slots;
+    tie classes, an all-equal row and zero scores included."""
+    print(f"[evict] bits={bits} D={D} B={B} H={H} L={L} budget={budget} S={S} R={R} mask={with_mask}", flush=True)
+    rng = np.random.default_rng(L + budget + bits + D)
+    w = get("tiny_mha").scaled(context=L, batch=B, num_q_heads=H, num_kv_heads=H, head_dim=D, bits=bits)
+    d = draw(w)
+    cap = max(L, budget) + 37
+    gc, ref, score = prefill_both(w, d, capacity=cap)
+    sc = rng.random((B, H, cap)).astype(np.float32) * 3
+    sc[:, :, ::7] = np.float32(0.5)
+    sc[:, min(1, H - 1), :] = np.float32(1.0)
+    sc[:, :, ::3] = 0.0
+    score.copy_(dev(sc))
+    outs = []
+    for fused in (True, False):
+        dst = make_gpu_cache(w, cap)
+        dst.k_codes.fill_(0x5A)
+        dst_score = dst.score_buffer()
+        dst_score.fill_(-1.0)
+        kidx = torch.full((B, H, budget), -7, dtype=torch.int32, device="cuda")
+        mask = torch.full((B, H, cap), 9, dtype=torch.uint8, device="cuda")
+        if fused:
+            kvc.kvc_h2o_evict(gc, score, budget, S, R, kidx, dst, dst_score, keep_mask=mask if with_mask else None,
+                              max_len_hint=L)
+        else:
+            kvc.kvc_h2o_select(gc, score, budget, S, R, mask, keep_index=kidx, max_len_hint=L)
+            kvc.kvc_compact_gather(gc, score, kidx, budget, dst, dst_score)
+        outs.append((dst, dst_score, kidx, mask))
+    torch.cuda.synchronize()
+    (dst, dst_score, kidx, mask), (dst2, dst2_score, kidx2, mask2) = outs
+    _assert_same_cache(dst, dst2, dst_score, dst2_score)
+    assert torch.equal(kidx, kidx2)
+    if with_mask:
+        assert torch.equal(mask, mask2)
+    else:
+        assert torch.all(mask == 9)
+    n_keep = min(L, budget)
+    keep = np.stack([np.stack([oracle.select_keep(sc[b, g, :L].astype(np.float64), L, budget, S, R)
+                               for g in range(H)]) for b in range(B)])
+    ki = host(kidx)
+    assert np.all(ki[:, :, n_keep:] == -7)
+    for b in range(B):
+        for g in range(H):
+            assert np.array_equal(ki[b, g, :n_keep], np.nonzero(keep[b, g])[0]), (b, g)
+    full = np.zeros((B, H, cap), bool)
+    full[:, :, :L] = keep
+    ref.score[:] = sc
+    ref.compact(full)
+    assert_codes_equal(dst, ref)
+    ds = host(dst_score)
+    assert np.array_equal(ds[:, :, :n_keep], sc[full].reshape(B, H, n_keep))
+    assert np.all(ds[:, :, n_keep:] == -1.0)   # slots past the new length untouched
+    assert np.all(host(dst.k_codes)[:, :, n_keep:] == 0x5A)
+    assert host(dst.num_seen).tolist() == [L] * B
+
+
 # ------------------------------------------------------- whole decode step --
 
 def _full_step(w, d, prior=()):
@@ -246,7 +323,16 @@ def _full_step(w, d, prior=()):
     dst = make_gpu_cache(w, gc.capacity)
     dst_score = dst.score_buffer()
     kvc.kvc_compact_gather(gc, score, dev(ref_list), w.budget, dst, dst_score)
+    # The one-call eviction (the benchmark's launch configuration) equals the
+    # GPU's own selection followed by the gather, on every buffer.
+    dst_s, dst_e = make_gpu_cache(w, gc.capacity), make_gpu_cache(w, gc.capacity)
+    dst_s_score, dst_e_score = dst_s.score_buffer(), dst_e.score_buffer()
+    kidx_e, mask_e = torch.zeros_like(kidx), torch.zeros_like(mask)
+    kvc.kvc_compact_gather(gc, score, kidx, w.budget, dst_s, dst_s_score)
+    kvc.kvc_h2o_evict(gc, score, w.budget, w.n_sink, w.n_recent, kidx_e, dst_e, dst_e_score, keep_mask=mask_e)
     torch.cuda.synchronize()
+    _assert_same_cache(dst_e, dst_s, dst_e_score, dst_s_score)
+    assert torch.equal(kidx_e, kidx) and torch.equal(mask_e, mask)
     ref.compact(keep_ref)
     assert_codes_equal(dst, ref)
     print(f"max-abs out err {err:.2e}, worst score rel err {rel:.2e}, ambiguous {amb}", flush=True)
