@@ -4,9 +4,9 @@ A step is one pass of the whole hot path over one layer of the LLaMA-7B-shaped
 workload (B=1, 32 query/KV heads, D=128, 8192 tokens, INT8 per-token cache,
 H2O keep 0.3 = 4 sinks + 1024 recent + 1429 heavy hitters):
 
-  1. quantize-append the new token's K and V          (kvc_quant_append)
-  2. attention over all 8192 tokens + H2O accumulation (kvc_decode_attn)
-  3. eviction: keep-set selection down to 2457 slots (a mask and an
+  1. quantize-append the new token's K and V, then attention over all 8192
+     tokens + H2O accumulation, in one call            (kvc_append_decode_attn)
+  2. eviction: keep-set selection down to 2457 slots (a mask and an
      ascending keep list) and compaction of the kept slots into the other
      buffer, in one call                               (kvc_h2o_evict)
 
@@ -15,9 +15,9 @@ model), so every launch streams its 66 MiB from HBM rather than from the
 256 MB Infinity Cache. Inputs are resident in HBM before timing starts.
 
 The timed region replays one HIP graph per 32-layer block in decode order:
-rewind the lengths, then for each layer append, attention, eviction.
+rewind the lengths, then for each layer append + attention, eviction.
 `value` and `ms_per_step` come from it. The same steps then run again as
-three graphs per block, one per phase ([rewind + 32 appends] [32 attentions]
+two graphs per block, one per phase ([rewind + 32 append-attentions]
 [32 evictions]), with HIP events between the phases: they give
 each phase's time ("phases") and the attention kernels' average duration, from
 which the roofline fraction is computed.
@@ -78,14 +78,14 @@ def step_bytes(B, Hq, H, D, bits, L, budget):
 
 def phase_table(phase_ms, steps, parts, attn_alg):
     """Per-phase time and HBM roofline fraction of one step. Each phase is one
-    replayed graph (one launch per layer buffer, two for attention) timed with
-    events on the replay stream; bytes are the phase's algorithmic bytes:
-    attention counts the KV stream and q as in the roofline entry, plus the
-    H2O score read-modify-write its merge kernel does; eviction counts the
-    selection's score reads, mask and keep-list writes and the compaction's
-    kept rows in and out."""
-    names = ("append", "attention", "evict")
-    alg = (parts["append"], attn_alg + parts["h2o"], parts["evict"])
+    replayed graph (two launches per layer buffer for the append and attention,
+    one for eviction) timed with events on the replay stream; bytes are the
+    phase's algorithmic bytes: the append's inputs and cache writes, the KV
+    stream and q as in the roofline entry, and the H2O score
+    read-modify-write; eviction counts the selection's score reads, mask and
+    keep-list writes and the compaction's kept rows in and out."""
+    names = ("append_attention", "evict")
+    alg = (parts["append"] + attn_alg + parts["h2o"], parts["evict"])
     table = {}
     for name, ms, b in zip(names, phase_ms, alg):
         us = ms * 1e3 / steps
@@ -285,14 +285,14 @@ def main(argv=None):
                           device="cuda")
     torch.cuda.synchronize()
 
-    def phase_append():
-        lengths_all.fill_(L - 1)
-        for i in range(LAYERS):
-            kvc.kvc_quant_append(caches[i], k_new, v_new, h2o_score=scores[i], max_len_hint=L - 1)
+    def append_attn(i):
+        kvc.kvc_append_decode_attn(caches[i], k_new, v_new, q, out, h2o_score=scores[i], max_len_hint=L - 1,
+                                   workspace=ws_attn)
 
     def phase_attn():
+        lengths_all.fill_(L - 1)
         for i in range(LAYERS):
-            kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L, workspace=ws_attn)
+            append_attn(i)
 
     def evict(i):
         kvc.kvc_h2o_evict(caches[i], scores[i], budget, S, R, keep_lists[i], dst, dst_score, keep_mask=masks[i],
@@ -306,8 +306,7 @@ def main(argv=None):
         # Decode order: each layer's append, attention and eviction in turn.
         lengths_all.fill_(L - 1)
         for i in range(LAYERS):
-            kvc.kvc_quant_append(caches[i], k_new, v_new, h2o_score=scores[i], max_len_hint=L - 1)
-            kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L, workspace=ws_attn)
+            append_attn(i)
             evict(i)
 
     # ---- eager pass, then capture the whole block and each phase as graphs ----
@@ -326,7 +325,7 @@ def main(argv=None):
         return g
 
     g_whole = capture(whole_block)
-    graphs = [capture(fn) for fn in (phase_append, phase_attn, phase_evict)]
+    graphs = [capture(fn) for fn in (phase_attn, phase_evict)]
     torch.cuda.synchronize()
 
     blocks_w = max(1, (args.warmup + LAYERS - 1) // LAYERS)
@@ -376,7 +375,7 @@ def main(argv=None):
         for p in range(n_ph):
             phase_ms[p] += prev.elapsed_time(ev[bi][p])
             prev = ev[bi][p]
-    attn_ms = phase_ms[1]
+    attn_ms = phase_ms[0]
     by_phase_ms = p_start.elapsed_time(p_end)
 
     parts, attn_alg = step_bytes(B, Hq, H, D, bits, L, budget)
@@ -412,7 +411,7 @@ def main(argv=None):
         "ms_per_step_phase_by_phase": round(by_phase_ms / steps, 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode attention (attn_split_kernel + attn_combine_kernel)",
+            "kernel": "decode attention with the new token's append (attn_split_kernel + attn_combine_kernel)",
             "achieved": round(attn_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -62,6 +62,7 @@ def _load():
         "kvc_quant_append": (I32, [D, P, P, I32, P, I32, P]),
         "kvc_decode_attn_workspace_bytes": (SZ, [D, I32, I32, I32]),
         "kvc_decode_attn": (I32, [D, P, I32, P, P, I32, P, SZ, P]),
+        "kvc_append_decode_attn": (I32, [D, P, P, P, I32, P, P, I32, P, SZ, P]),
         "kvc_h2o_select": (I32, [D, P, I32, I32, I32, P, P, I32, P]),
         "kvc_compact_workspace_bytes": (SZ, [D, I32]),
         "kvc_compact": (I32, [D, P, P, D, P, I32, P, SZ, P]),
@@ -241,6 +242,31 @@ def kvc_decode_attn(cache, q, out, h2o_score=None, max_len_hint: Optional[int] =
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     _check(lib.kvc_decode_attn(ctypes.byref(d), _ptr(q), Hq, _ptr(out), _ptr(h2o_score), max_len_hint,
                                _ptr(workspace), workspace.numel(), _stream(stream)), "kvc_decode_attn")
+
+
+def kvc_append_decode_attn(cache, k_new, v_new, q, out, h2o_score=None, max_len_hint: Optional[int] = None,
+                           workspace=None, stream=None):
+    """Append one token per sequence (``k_new``/``v_new`` fp16 ``[B][Hkv][1][D]``
+    or ``[B][Hkv][D]``) and attend over the cache that includes it, in one call
+    (see kvc.h). ``max_len_hint`` bounds the lengths before the append."""
+    import torch
+    d = _desc(cache)
+    Hq = q.shape[1]
+    _need(k_new, torch.float16, "k_new", d.batch * d.num_kv_heads * d.head_dim)
+    _need(v_new, torch.float16, "v_new", d.batch * d.num_kv_heads * d.head_dim)
+    _need(q, torch.float16, "q", d.batch * Hq * d.head_dim)
+    _need(out, torch.float32, "out", d.batch * Hq * d.head_dim)
+    _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    if workspace is None:
+        n = kvc_decode_attn_workspace_bytes(d, Hq, max_len_hint + 1, h2o_score is not None)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.kvc_append_decode_attn(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, _ptr(out),
+                                      _ptr(h2o_score), max_len_hint, _ptr(workspace), workspace.numel(),
+                                      _stream(stream)), "kvc_append_decode_attn")
+    if isinstance(cache, KVCache):
+        cache.max_len = max_len_hint + 1
 
 
 def kvc_h2o_select(cache, h2o_score, budget: int, n_sink: int, n_recent: int, keep_mask, keep_index=None,

@@ -80,7 +80,7 @@ int32_t check_cache(const kvc_cache_t* c, const char* name) {
 
 struct AttnGeom {
   int splits, tiles;
-  size_t off_ml, off_logits, total;
+  size_t off_ml, off_logits, off_stash, total;
 };
 
 // Launch geometry of the decode-attention kernels. A split covers `tiles`
@@ -113,7 +113,8 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
   g->tiles = (int)nt;
   g->off_ml = part_o;
   g->off_logits = part_o + part_ml;
-  g->total = part_o + part_ml + logits;
+  g->off_stash = part_o + part_ml + logits;
+  g->total = g->off_stash + align256(2 * (size_t)c->batch * sizeof(int32_t));
   return KVC_OK;
 }
 
@@ -205,11 +206,18 @@ size_t kvc_decode_attn_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_h
   return g.total;
 }
 
-int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_heads, float* out, float* h2o_score,
-                        int32_t max_len_hint, void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace kvc {
+namespace {
+
+// Shared body of kvc_decode_attn and kvc_append_decode_attn; `span_hint` is
+// the largest length the attention sees (after the append, if any).
+int32_t decode_attn_call(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                         int32_t num_q_heads, float* out, float* h2o_score, int32_t span_hint, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   AttnGeom g;
-  int32_t st = attn_geometry(cache, num_q_heads, max_len_hint, h2o_score != nullptr, &g);
+  int32_t st = attn_geometry(cache, num_q_heads, span_hint, h2o_score != nullptr, &g);
   if (st) return st;
   if (!q || !out) return fail(KVC_ERR_INVALID_ARG, "q and out must not be NULL");
   if (!workspace || workspace_bytes < g.total)
@@ -224,11 +232,40 @@ int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_h
   a.part_o = reinterpret_cast<float*>(ws);
   a.part_ml = reinterpret_cast<float*>(ws + g.off_ml);
   a.logits = h2o_score ? reinterpret_cast<float*>(ws + g.off_logits) : nullptr;
+  a.k_new = static_cast<const __half*>(k_new);
+  a.v_new = static_cast<const __half*>(v_new);
+  a.stash = reinterpret_cast<int32_t*>(ws + g.off_stash);
   a.num_q_heads = num_q_heads;
   a.splits = g.splits;
   a.tiles = g.tiles;
   a.qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
-  return device_status(launch_decode_attn(a, static_cast<hipStream_t>(stream)), "kvc_decode_attn launch");
+  return device_status(launch_decode_attn(a, static_cast<hipStream_t>(stream)), "decode attention launch");
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" {
+
+int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_heads, float* out, float* h2o_score,
+                        int32_t max_len_hint, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return decode_attn_call(cache, nullptr, nullptr, q, num_q_heads, out, h2o_score, max_len_hint, workspace,
+                          workspace_bytes, stream);
+}
+
+int32_t kvc_append_decode_attn(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                               int32_t num_q_heads, float* out, float* h2o_score, int32_t max_len_hint,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int32_t st = check_cache(cache, "cache");
+  if (st) return st;
+  if (!k_new || !v_new) return fail(KVC_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+  if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
+  if ((long long)max_len_hint + 1 > cache->capacity)
+    return fail(KVC_ERR_CAPACITY, "max_len_hint %d + 1 exceeds capacity %d", max_len_hint, cache->capacity);
+  return decode_attn_call(cache, k_new, v_new, q, num_q_heads, out, h2o_score, max_len_hint + 1, workspace,
+                          workspace_bytes, stream);
 }
 
 int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t budget, int32_t n_sink,

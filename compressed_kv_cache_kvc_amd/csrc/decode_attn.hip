@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "kvc_internal.h"
+#include "quant_row.h"
 
 namespace kvc {
 namespace {
@@ -187,8 +188,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits, NT = a.tiles;
   const long long span = (long long)S * NT * TS;  // logit slots per query head
   // Uniform by construction; readfirstlane keeps it (and the buffer resources
-  // built from it) in scalar registers.
-  const int L = __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), (int)span));
+  // built from it) in scalar registers. With an append, the new token is slot
+  // L_old and the attention covers it.
+  const bool app = a.k_new != nullptr;
+  const int L_old = __builtin_amdgcn_readfirstlane(c.lengths[b]);
+  const int L = __builtin_amdgcn_readfirstlane(min(min(L_old + (app ? 1 : 0), c.capacity), (int)span));
 
   __shared__ __align__(16) uint8_t v_stage[4][64 * VROW];
   __shared__ __align__(16) int8_t w_limb[4][NRS][16][64];
@@ -225,6 +229,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   // below L only for it < nb.
   auto block_t0 = [&](int it) { return ((s * NT + it) * 4 + wave) * 64; };
   const int nb = max(0, min(NT, (L - ((s * NT) * 4 + wave) * 64 + 255) / 256));
+
+  // Append: the wave whose block `it_new` holds slot L_old quantizes the new
+  // token's K and V rows into the cache before its first loads (the
+  // quantizer of the append kernels, so the codes are identical), sets its
+  // position and zeroes its score. It waits for those stores just before
+  // issuing that block; no other wave reads the slot, so no barrier is needed.
+  // Workgroup (0, 0) of each sequence keeps the old length and count for the
+  // merge kernel, which advances them once no workgroup reads them.
+  int it_new = -1;
+  if (app) {
+    if (s == 0 && g == 0 && tid == 0) {
+      a.stash[b] = L_old;
+      a.stash[c.batch + b] = c.num_seen[b];
+    }
+    const int qb = L_old >> 6;  // 64-token block of the new slot
+    if (L_old >= 0 && L_old < c.capacity && L_old < span && (qb >> 2) / NT == s && (qb & 3) == wave) {
+      it_new = (qb >> 2) % NT;
+      const long long row = cache_row(c, b, g, L_old);
+      if (row >= 0) {
+        const long long src = ((long long)b * H + g) * D;
+        const quant::RowVals<D> kx = quant::load_row<D>(a.k_new + src, lane);
+        const quant::RowVals<D> vx = quant::load_row<D>(a.v_new + src, lane);
+        quant::quant_vals<BITS, D>(kx, static_cast<uint8_t*>(c.k_codes) + row * RB, c.k_scale + row, lane);
+        quant::quant_vals<BITS, D>(vx, static_cast<uint8_t*>(c.v_codes) + row * RB, c.v_scale + row, lane);
+        if (lane == 0) {
+          if (c.positions) c.positions[row] = c.num_seen[b];
+          if (a.score) a.score[((long long)b * H + g) * c.capacity + L_old] = 0.f;
+        }
+      }
+    }
+  }
+  // Before issuing block `it`: the new token's stores have completed (gfx9
+  // counts stores with loads; vmcnt(0)).
+  auto wait_new = [&](int it) {
+    if (it == it_new) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      it_new = -1;
+    }
+  };
 
   // Registers of one block's loads; two sets keep two blocks in flight.
   using KT = typename std::conditional<BITS == 8, i32x4, i32x2>::type;
@@ -298,6 +341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
         xq[hi][e] = h < gh ? __half2float(a.q[((long long)b * Hq + g * G + hp + h) * D + lane * EPL + e]) : 0.f;
       }
     Regs ra;
+    wait_new(0);
     issue(ra, 0);
 #pragma unroll
     for (int hi = 0; hi < HPW; ++hi) {
@@ -495,7 +539,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
       asm volatile("" ::: "memory");
     };
     for (int it = 0; it < nb; ++it) {
-      if (it > 0) issue(ra, it);
+      if (it > 0) {
+        wait_new(it);
+        issue(ra, it);
+      }
       process(ra, it);
     }
 
@@ -563,7 +610,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits;
   const long long span = (long long)S * a.tiles * TS;
-  const int L = __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), (int)span));
+  // With an append, the length before it comes from the split kernel (the
+  // cache's own length is advanced here, by one workgroup).
+  const bool app = a.k_new != nullptr;
+  const int L = __builtin_amdgcn_readfirstlane(
+      min(min(app ? a.stash[b] + 1 : c.lengths[b], c.capacity), (int)span));
   const bool out_block = x < G;
   const int h_lo = out_block ? x : 0, nh = out_block ? 1 : G;
   float* minv = fac + nh * S;  // [nh][2]: m, 1/l
@@ -630,6 +681,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
 #pragma unroll
       for (int p = 1; p < PARTS; ++p) r += part[p][d];
       a.out[((long long)b * Hq + g * G + x) * D + d] = r;
+    }
+    if (app && x == 0 && g == 0 && tid == 0) {
+      c.lengths[b] = a.stash[b] + 1;
+      c.num_seen[b] = a.stash[c.batch + b] + 1;
     }
     return;
   }

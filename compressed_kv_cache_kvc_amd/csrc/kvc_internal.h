@@ -37,6 +37,11 @@ struct AttnLaunch {
   float* part_o;     // [B][Hq][S][D]
   float* part_ml;    // [B][Hq][S][2]  (max in log2 units, sum)
   float* logits;     // [B][Hq][S * tiles * kSplitTokens], log2 units (only with H2O)
+  // With k_new and v_new ([B][Hkv][D] fp16): append one token per sequence
+  // first (slot lengths[b]); NULL: attention only.
+  const __half* k_new;
+  const __half* v_new;
+  int32_t* stash;    // [2][B]: lengths and num_seen before the append
   int num_q_heads;
   int splits;        // S: workgroups per (sequence, KV head)
   int tiles;         // 256-token tiles per split

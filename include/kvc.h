@@ -6,6 +6,8 @@
  *   kvc_quant_append  per-token symmetric INT8/INT4 quantize-on-write of K, V
  *   kvc_decode_attn   softmax(q K^T / sqrt(D)) V with dequantization fused in,
  *                     plus optional H2O accumulation of attention mass
+ *                     (kvc_append_decode_attn: the one-token append and the
+ *                     attention in one call)
  *   kvc_h2o_select    sink + recent-window + top-k heavy-hitter keep mask
  *   kvc_compact       stable out-of-place compaction of the kept slots
  *                     (kvc_compact_gather: from the keep list instead;
@@ -171,6 +173,30 @@ size_t kvc_decode_attn_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_h
 int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_heads,
                         float* out, float* h2o_score, int32_t max_len_hint,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step's append and attention in one call: kvc_quant_append of one
+ * token per sequence (n_new = 1), then kvc_decode_attn over the cache that
+ * includes it. Sources: those of the two calls ("KV Cache optimization
+ * techniques" tutorial, sections 1.1 and 1.2; "KV Cache Compression Report",
+ * sections 1.1, 3.2 and 3.4).
+ *
+ * k_new, v_new: device fp16 [batch][num_kv_heads][head_dim], the new token of
+ * each sequence; it goes to slot lengths[b] (codes, scale, position =
+ * num_seen[b], and score 0 before the H2O update), then lengths[b] and
+ * num_seen[b] advance by one, exactly as kvc_quant_append does. The cache's
+ * codes, scales, positions, lengths, scores and `out` equal those of the two
+ * separate calls bit for bit. max_len_hint bounds the lengths before the
+ * append; the workspace needs kvc_decode_attn_workspace_bytes(cache,
+ * num_q_heads, max_len_hint + 1, with_h2o) bytes. The append happens inside
+ * the attention kernels (the wave that reads the new slot writes it first), so
+ * the step takes two launches instead of three.
+ * Errors: those of both calls; CAPACITY if max_len_hint + 1 > capacity.
+ */
+int32_t kvc_append_decode_attn(const kvc_cache_t* cache, const void* k_new, const void* v_new,
+                               const void* q, int32_t num_q_heads, float* out, float* h2o_score,
+                               int32_t max_len_hint, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * Keep-set selection: attention sinks + recent window + heavy hitters.

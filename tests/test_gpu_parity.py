@@ -149,6 +149,110 @@ def test_empty_sequence_gives_zero_output():
     assert np.all(o[1] == 0) and np.all(np.isfinite(o[0]))
 
 
+# ------------------------------------------------- append + attention, fused --
+
+def _append_attn_pair(gcA, gcB, sA, sB, knew, vnew, q, hint, hq):
+    """The two-call step on cache A, the one-call step on cache B."""
+    B, D = gcA.batch, gcA.head_dim
+    outA = torch.empty((B, hq, D), dtype=torch.float32, device="cuda")
+    outB = torch.empty_like(outA)
+    kvc.kvc_quant_append(gcA, knew, vnew, h2o_score=sA, max_len_hint=hint)
+    kvc.kvc_decode_attn(gcA, q, outA, h2o_score=sA, max_len_hint=hint + 1)
+    kvc.kvc_append_decode_attn(gcB, knew, vnew, q, outB, h2o_score=sB, max_len_hint=hint)
+    torch.cuda.synchronize()
+    return outA, outB
+
+
+@pytest.mark.parametrize("hq,hkv,bits,D,lens,h2o,cap_extra", [
+    (4, 4, 8, 128, [299, 100, 0], True, 5),      # MHA; one sequence starts empty
+    (16, 4, 8, 128, [1000, 513, 64], True, 40),  # GQA 4
+    (16, 2, 4, 128, [700, 255, 256], True, 0),   # INT4, GQA 8; new slot = last slot of sequence 0
+    (8, 4, 8, 64, [300, 301, 302], True, 3),     # D = 64
+    (32, 2, 8, 128, [600, 10, 599], True, 7),    # GQA 16: two passes of 8 heads
+    (8, 4, 8, 128, [2100, 1500, 2048], False, 9),  # no H2O; several tiles per split
+])
+def test_append_decode_attn_bit_exact(hq, hkv, bits, D, lens, h2o, cap_extra):
+    """kvc_append_decode_attn equals kvc_quant_append + kvc_decode_attn on
+    every cache buffer, the scores and the output, bit for bit, and the oracle's
+    append and attention."""
+    print(f"[append+attn] hq={hq} hkv={hkv} bits={bits} D={D} lens={lens} h2o={h2o}", flush=True)
+    B, Lmax = len(lens), max(lens)
+    w = get("tiny_mha").scaled(context=Lmax + 1, batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, bits=bits)
+    d = draw(w)
+    cap = Lmax + 1 + cap_extra
+    rng = np.random.default_rng(Lmax + hq)
+    sc = (rng.random((B, hkv, cap)) * 0.1).astype(np.float32)
+    caches = []
+    for _ in range(2):
+        gc = make_gpu_cache(w, cap, bits)
+        if Lmax:
+            kvc.kvc_quant_append(gc, dev(d["k"][:, :, :Lmax]), dev(d["v"][:, :, :Lmax]))
+        gc.lengths.copy_(dev(np.array(lens, np.int32)))
+        gc.num_seen.copy_(dev(np.array(lens, np.int32) + 3))
+        gc.max_len = Lmax
+        caches.append((gc, dev(sc) if h2o else None))
+    (gcA, sA), (gcB, sB) = caches
+    ref = oracle.RefCache(B, hkv, D, cap, bits)
+    if Lmax:
+        ref.append(d["k"][:, :, :Lmax], d["v"][:, :, :Lmax])
+    ref.lengths[:] = lens
+    ref.num_seen[:] = np.array(lens) + 3
+    ref.score[:] = sc
+    knew, vnew = d["k"][:, :, Lmax:Lmax + 1], d["v"][:, :, Lmax:Lmax + 1]
+    outA, outB = _append_attn_pair(gcA, gcB, sA, sB, dev(knew), dev(vnew), dev(d["q"]), Lmax, hq)
+    _assert_same_cache(gcA, gcB, sA, sB)
+    assert torch.equal(outA, outB)
+    ref.append(knew, vnew)
+    ro, _ = ref.attend(d["q"], h2o=h2o)
+    assert_out_close(host(outB), ro)
+    assert_codes_equal(gcB, ref)
+    if h2o:
+        assert_scores_close(host(sB), ref.score, ref.lengths)
+
+
+def test_append_decode_attn_paged():
+    """Paged cache (16-token blocks, seeded block placement): the one-call
+    step equals the two calls bit for bit."""
+    B, H, hq, D, bs, L = 3, 4, 8, 128, 16, 333
+    w = get("tiny_mha").scaled(context=L + 1, batch=B, num_q_heads=hq, num_kv_heads=H, head_dim=D, bits=8)
+    d = draw(w)
+    per = (L + 1 + bs - 1) // bs + 1
+    perm = np.random.default_rng(5).permutation(B * per).astype(np.int32).reshape(B, per)
+    caches = []
+    for _ in range(2):
+        gc = kvc.KVCache(B, H, D, 0, 8, block_size=bs, num_blocks=B * per, max_blocks_per_seq=per)
+        gc.block_table.copy_(dev(perm))
+        kvc.kvc_quant_append(gc, dev(d["k"][:, :, :L]), dev(d["v"][:, :, :L]), max_len_hint=0)
+        gc.lengths.copy_(dev(np.array([L, L - 17, 5], np.int32)))
+        caches.append((gc, gc.score_buffer()))
+    (gcA, sA), (gcB, sB) = caches
+    knew, vnew = dev(d["k"][:, :, L:L + 1]), dev(d["v"][:, :, L:L + 1])
+    outA, outB = _append_attn_pair(gcA, gcB, sA, sB, knew, vnew, dev(d["q"]), L, hq)
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "lengths", "num_seen"):
+        assert torch.equal(getattr(gcA, name), getattr(gcB, name)), name
+    assert torch.equal(sA, sB) and torch.equal(outA, outB)
+
+
+def test_append_decode_attn_llama7b_full_size():
+    """The benchmarked step at full size (8191 cached tokens + the new one,
+    32 heads): the one-call step equals the two calls bit for bit."""
+    w = get("llama7b_8k")
+    print("[append+attn] llama7b_8k full size", flush=True)
+    d = draw(w)
+    L = w.context - 1
+    caches = []
+    for _ in range(2):
+        gc = make_gpu_cache(w)
+        s = gc.score_buffer()
+        kvc.kvc_quant_append(gc, dev(d["k"][:, :, :L]), dev(d["v"][:, :, :L]), h2o_score=s)
+        caches.append((gc, s))
+    (gcA, sA), (gcB, sB) = caches
+    knew, vnew = dev(d["k"][:, :, L:]), dev(d["v"][:, :, L:])
+    outA, outB = _append_attn_pair(gcA, gcB, sA, sB, knew, vnew, dev(d["q"]), L, w.num_q_heads)
+    _assert_same_cache(gcA, gcB, sA, sB)
+    assert torch.equal(outA, outB)
+
+
 # ---------------------------------------------------------- select/compact --
 
 @pytest.mark.parametrize("L,budget,S,R", [(512, 128, 4, 64), (3000, 1000, 4, 100), (9000, 2457, 4, 1024),
