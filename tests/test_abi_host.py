@@ -116,6 +116,24 @@ def test_decode_attn_validation():
     assert lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), 6, 16, 0) == 0
 
 
+def test_append_decode_attn_validation():
+    d = desc()
+    call = lambda hint=16, k=FAKE, v=FAKE, q=FAKE, hq=4, ws=FAKE * 256, nbytes=1 << 30: lib.kvc_append_decode_attn(
+        ctypes.byref(d), k, v, q, hq, FAKE, None, hint, ws, nbytes, None)
+    assert call(k=None) == INVALID
+    assert call(v=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(hint=-1) == INVALID
+    assert call(hint=512) == CAPACITY                 # no slot left for the new token
+    assert call(hq=6) == INVALID
+    need = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), 4, 17, 0)
+    assert call(nbytes=need - 1) == INVALID           # sized for hint + 1 tokens
+    assert call(ws=FAKE * 256 + 4) == INVALID
+    bad = desc(bits=3)
+    assert lib.kvc_append_decode_attn(ctypes.byref(bad), FAKE, FAKE, FAKE, 4, FAKE, None, 16, FAKE * 256, 1 << 30,
+                                      None) == INVALID
+
+
 def test_select_validation():
     d = desc()
     sel = lambda budget, s, r, hint=16, score=FAKE, mask=FAKE: lib.kvc_h2o_select(
