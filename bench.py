@@ -46,9 +46,10 @@ METRIC = "decode-attn KV GB/s & tokens/s (fraction of HBM peak), INT8, L=8192, 1
 # attention sources it was taken on; any change to them reports null.
 TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/kvc_internal.h",
+                   "compressed_kv_cache_kvc_amd/csrc/quant_row.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "10b759f36d648dd9aaacd995294479b9be9bc93a7408d51ed35f1f85013cd168"
-TRAFFIC_BYTES = 74294381
+TRAFFIC_SHA256 = "8af2f14fb492542caa19f839044b6f8913a22242196e8c5f626c90cc2d490f16"
+TRAFFIC_BYTES = 74343233
 
 
 def attention_traffic():
