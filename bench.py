@@ -4,21 +4,24 @@ A step is one pass of the whole hot path over one layer of the LLaMA-7B-shaped
 workload (B=1, 32 query/KV heads, D=128, 8192 tokens, INT8 per-token cache,
 H2O keep 0.3 = 4 sinks + 1024 recent + 1429 heavy hitters):
 
-  1. quantize-append the new token's K and V, then attention over all 8192
-     tokens + H2O accumulation, in one call            (kvc_append_decode_attn)
-  2. eviction: keep-set selection down to 2457 slots (a mask and an
+  1. quantize-append the new token's K and V,
+  2. attention over all 8192 tokens + H2O accumulation,
+  3. eviction: keep-set selection down to 2457 slots (a mask and an
      ascending keep list) and compaction of the kept slots into the other
-     buffer, in one call                               (kvc_h2o_evict)
+     buffer,
+in one call of two launches (kvc_decode_step: the split attention kernel,
+then the eviction kernel that also merges the splits).
 
 Steps rotate over 32 distinct layer caches (2.1 GiB, like the 32 layers of the
 model), so every launch streams its 66 MiB from HBM rather than from the
 256 MB Infinity Cache. Inputs are resident in HBM before timing starts.
 
 The timed region replays one HIP graph per 32-layer block in decode order:
-rewind the lengths, then for each layer append + attention, eviction.
-`value` and `ms_per_step` come from it. The same steps then run again as
-two graphs per block, one per phase ([rewind + 32 append-attentions]
-[32 evictions]), with HIP events between the phases: they give
+rewind the lengths, then each layer's step. `value` and `ms_per_step` come
+from it. The same steps then run again as the separate calls, two graphs per
+block, one per phase ([rewind + 32 kvc_append_decode_attn] [32
+kvc_h2o_evict]; the attention's own merge kernel runs there), with HIP events
+between the phases: they give
 each phase's time ("phases") and the attention kernels' average duration, from
 which the roofline fraction is computed.
 
@@ -304,11 +307,12 @@ def main(argv=None):
             evict(i)
 
     def whole_block():
-        # Decode order: each layer's append, attention and eviction in turn.
+        # Decode order: each layer's step (append, attention, H2O, eviction;
+        # two launches) in turn.
         lengths_all.fill_(L - 1)
         for i in range(LAYERS):
-            append_attn(i)
-            evict(i)
+            kvc.kvc_decode_step(caches[i], k_new, v_new, q, out, scores[i], budget, S, R, keep_lists[i], dst,
+                                dst_score, keep_mask=masks[i], max_len_hint=L - 1, workspace=ws_attn)
 
     # ---- eager pass, then capture the whole block and each phase as graphs ----
     stream = torch.cuda.Stream()

@@ -68,6 +68,7 @@ def _load():
         "kvc_compact": (I32, [D, P, P, D, P, I32, P, SZ, P]),
         "kvc_compact_gather": (I32, [D, P, P, I32, D, P, P]),
         "kvc_h2o_evict": (I32, [D, P, I32, I32, I32, P, P, D, P, I32, P]),
+        "kvc_decode_step": (I32, [D, P, P, P, I32, P, P, I32, I32, I32, P, P, D, P, I32, P, SZ, P]),
         "kvc_pool_create": (P, [I32, I32, U64]),
         "kvc_pool_destroy": (None, [P]),
         "kvc_pool_reserve": (I32, [P, I32, I32]),
@@ -337,6 +338,37 @@ def kvc_h2o_evict(src, h2o_score, budget: int, n_sink: int, n_recent: int, keep_
            "kvc_h2o_evict")
     if isinstance(dst, KVCache) and isinstance(src, KVCache):
         dst.max_len = min(src.max_len, budget)
+
+
+def kvc_decode_step(cache, k_new, v_new, q, out, h2o_score, budget: int, n_sink: int, n_recent: int, keep_index,
+                    dst, dst_score, keep_mask=None, max_len_hint: Optional[int] = None, workspace=None, stream=None):
+    """A whole decode step in one call (see kvc.h): append the new token,
+    attend with H2O, evict from ``cache`` into ``dst`` (``dst_score`` receives
+    the kept tokens' accumulated scores)."""
+    import torch
+    d, dd = _desc(cache), _desc(dst)
+    Hq = q.shape[1]
+    _need(k_new, torch.float16, "k_new", d.batch * d.num_kv_heads * d.head_dim)
+    _need(v_new, torch.float16, "v_new", d.batch * d.num_kv_heads * d.head_dim)
+    _need(q, torch.float16, "q", d.batch * Hq * d.head_dim)
+    _need(out, torch.float32, "out", d.batch * Hq * d.head_dim)
+    _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
+    _need(dst_score, torch.float32, "dst_score", dd.batch * dd.num_kv_heads * dd.capacity)
+    _need(keep_index, torch.int32, "keep_index", d.batch * d.num_kv_heads * budget)
+    _need(keep_mask, torch.uint8, "keep_mask", d.batch * d.num_kv_heads * d.capacity)
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    if workspace is None:
+        n = kvc_decode_attn_workspace_bytes(d, Hq, max_len_hint + 1, True)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.kvc_decode_step(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, _ptr(out), _ptr(h2o_score),
+                               budget, n_sink, n_recent, _ptr(keep_mask), _ptr(keep_index), ctypes.byref(dd),
+                               _ptr(dst_score), max_len_hint, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "kvc_decode_step")
+    if isinstance(cache, KVCache):
+        cache.max_len = max_len_hint + 1
+    if isinstance(dst, KVCache):
+        dst.max_len = min(max_len_hint + 1, budget)
 
 
 class BlockPool:

@@ -211,11 +211,12 @@ size_t kvc_decode_attn_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_h
 namespace kvc {
 namespace {
 
-// Shared body of kvc_decode_attn and kvc_append_decode_attn; `span_hint` is
-// the largest length the attention sees (after the append, if any).
-int32_t decode_attn_call(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
-                         int32_t num_q_heads, float* out, float* h2o_score, int32_t span_hint, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+// Validation and launch arguments shared by the attention entry points;
+// `span_hint` is the largest length the attention sees (after the append, if
+// any).
+int32_t prepare_attn(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                     int32_t num_q_heads, float* out, float* h2o_score, int32_t span_hint, void* workspace,
+                     size_t workspace_bytes, AttnLaunch* a) {
   AttnGeom g;
   int32_t st = attn_geometry(cache, num_q_heads, span_hint, h2o_score != nullptr, &g);
   if (st) return st;
@@ -223,23 +224,86 @@ int32_t decode_attn_call(const kvc_cache_t* cache, const void* k_new, const void
   if (!workspace || workspace_bytes < g.total)
     return fail(KVC_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", g.total, workspace ? workspace_bytes : 0);
   if ((uintptr_t)workspace % 256) return fail(KVC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  AttnLaunch a;
-  a.c = *cache;
-  a.q = static_cast<const __half*>(q);
-  a.out = out;
-  a.score = h2o_score;
+  a->c = *cache;
+  a->q = static_cast<const __half*>(q);
+  a->out = out;
+  a->score = h2o_score;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.part_o = reinterpret_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float*>(ws + g.off_ml);
-  a.logits = h2o_score ? reinterpret_cast<float*>(ws + g.off_logits) : nullptr;
-  a.k_new = static_cast<const __half*>(k_new);
-  a.v_new = static_cast<const __half*>(v_new);
-  a.stash = reinterpret_cast<int32_t*>(ws + g.off_stash);
-  a.num_q_heads = num_q_heads;
-  a.splits = g.splits;
-  a.tiles = g.tiles;
-  a.qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
+  a->part_o = reinterpret_cast<float*>(ws);
+  a->part_ml = reinterpret_cast<float*>(ws + g.off_ml);
+  a->logits = h2o_score ? reinterpret_cast<float*>(ws + g.off_logits) : nullptr;
+  a->k_new = static_cast<const __half*>(k_new);
+  a->v_new = static_cast<const __half*>(v_new);
+  a->stash = reinterpret_cast<int32_t*>(ws + g.off_stash);
+  a->num_q_heads = num_q_heads;
+  a->splits = g.splits;
+  a->tiles = g.tiles;
+  a->qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
+  return KVC_OK;
+}
+
+int32_t decode_attn_call(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                         int32_t num_q_heads, float* out, float* h2o_score, int32_t span_hint, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  AttnLaunch a;
+  const int32_t st = prepare_attn(cache, k_new, v_new, q, num_q_heads, out, h2o_score, span_hint, workspace,
+                                  workspace_bytes, &a);
+  if (st) return st;
   return device_status(launch_decode_attn(a, static_cast<hipStream_t>(stream)), "decode attention launch");
+}
+
+// Checks of the eviction arguments shared by kvc_h2o_evict and kvc_decode_step
+// (`max_len` is the largest length the eviction sees).
+int32_t check_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budget, int32_t n_sink, int32_t n_recent,
+                    const uint8_t* keep_mask, const int32_t* keep_index, const kvc_cache_t* dst,
+                    const float* dst_score, int32_t max_len, const void* workspace, size_t ws_bytes) {
+  int32_t st = check_compact_pair(src, dst, nullptr, nullptr);
+  if (st) return st;
+  if (!h2o_score || !keep_index) return fail(KVC_ERR_INVALID_ARG, "h2o_score and keep_index must not be NULL");
+  if (budget < 1) return fail(KVC_ERR_INVALID_ARG, "budget must be >= 1");
+  if (n_sink < 0 || n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
+  if ((long long)n_sink + n_recent > budget) return fail(KVC_ERR_INVALID_ARG, "n_sink + n_recent exceeds budget");
+  if (budget > src->capacity) return fail(KVC_ERR_CAPACITY, "budget exceeds capacity");
+  if (max_len < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
+  if (max_len > src->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
+  const size_t rows = (size_t)src->batch * src->num_kv_heads;
+  if ((st = check_out_of_place(src, h2o_score, keep_index, rows * budget * sizeof(int32_t), dst, dst_score, workspace,
+                               ws_bytes)))
+    return st;
+  if (keep_mask && (st = check_out_of_place(src, h2o_score, keep_mask, rows * src->capacity, dst, dst_score,
+                                            workspace, ws_bytes)))
+    return st;
+  return KVC_OK;
+}
+
+// Eviction launches: one kernel for rows of up to 8192 candidates, else the
+// selection kernel writes the keep list and the gather copies it.
+int32_t evict_launch(const EvictArgs& e, hipStream_t s, const char* what) {
+  if (evict_fits_one_launch(e.max_len, e.n_sink, e.n_recent)) return device_status(launch_evict(e, s), what);
+  int32_t st = device_status(launch_select(e.c, e.score, e.budget, e.n_sink, e.n_recent, e.mask, e.keep_index,
+                                           e.max_len, s),
+                             what);
+  if (st) return st;
+  return device_status(launch_compact_gather(e.c, e.dst_score ? e.score : nullptr, e.keep_index, e.budget, e.dst,
+                                             e.dst_score, s),
+                       what);
+}
+
+EvictArgs evict_args(const kvc_cache_t* src, const float* h2o_score, int32_t budget, int32_t n_sink,
+                     int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
+                     float* dst_score, int32_t max_len) {
+  EvictArgs e{};
+  e.c = *src;
+  e.score = h2o_score;
+  e.budget = budget;
+  e.n_sink = n_sink;
+  e.n_recent = n_recent;
+  e.mask = keep_mask;
+  e.keep_index = keep_index;
+  e.dst = *dst;
+  e.dst_score = dst_score;
+  e.max_len = max_len;
+  return e;
 }
 
 }  // namespace
@@ -335,34 +399,54 @@ int32_t kvc_h2o_evict(const kvc_cache_t* src, const float* h2o_score, int32_t bu
                       int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
                       float* dst_score, int32_t max_len_hint, void* stream) {
   clear_error();
-  int32_t st = check_compact_pair(src, dst, nullptr, nullptr);
+  const int32_t st = check_evict(src, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,
+                                 max_len_hint, nullptr, 0);
   if (st) return st;
-  if (!h2o_score || !keep_index) return fail(KVC_ERR_INVALID_ARG, "h2o_score and keep_index must not be NULL");
-  if (budget < 1) return fail(KVC_ERR_INVALID_ARG, "budget must be >= 1");
-  if (n_sink < 0 || n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
-  if ((long long)n_sink + n_recent > budget) return fail(KVC_ERR_INVALID_ARG, "n_sink + n_recent exceeds budget");
-  if (budget > src->capacity) return fail(KVC_ERR_CAPACITY, "budget exceeds capacity");
+  return evict_launch(evict_args(src, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,
+                                 max_len_hint),
+                      static_cast<hipStream_t>(stream), "kvc_h2o_evict launch");
+}
+
+int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                        int32_t num_q_heads, float* out, float* h2o_score, int32_t budget, int32_t n_sink,
+                        int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
+                        float* dst_score, int32_t max_len_hint, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  clear_error();
+  int32_t st = check_cache(cache, "cache");
+  if (st) return st;
+  if (!k_new || !v_new) return fail(KVC_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+  if (!h2o_score || !dst_score) return fail(KVC_ERR_INVALID_ARG, "h2o_score and dst_score must not be NULL");
   if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
-  if (max_len_hint > src->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
-  const size_t rows = (size_t)src->batch * src->num_kv_heads;
-  if ((st = check_out_of_place(src, h2o_score, keep_index, rows * budget * sizeof(int32_t), dst, dst_score, nullptr,
-                               0)))
+  if ((long long)max_len_hint + 1 > cache->capacity)
+    return fail(KVC_ERR_CAPACITY, "max_len_hint %d + 1 exceeds capacity %d", max_len_hint, cache->capacity);
+  AttnLaunch a;
+  if ((st = prepare_attn(cache, k_new, v_new, q, num_q_heads, out, h2o_score, max_len_hint + 1, workspace,
+                         workspace_bytes, &a)))
     return st;
-  if (keep_mask && (st = check_out_of_place(src, h2o_score, keep_mask, rows * src->capacity, dst, dst_score,
-                                            nullptr, 0)))
+  if ((st = check_evict(cache, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,
+                        max_len_hint + 1, workspace, workspace_bytes)))
     return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (evict_fits_one_launch(max_len_hint, n_sink, n_recent))
-    return device_status(launch_evict(*src, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, *dst,
-                                      dst_score, max_len_hint, s),
-                         "kvc_h2o_evict launch");
-  // Longer rows: the selection kernel writes the keep list, the gather copies it.
-  st = device_status(launch_select(*src, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, max_len_hint, s),
-                     "kvc_h2o_evict select launch");
-  if (st) return st;
-  return device_status(launch_compact_gather(*src, dst_score ? h2o_score : nullptr, keep_index, budget, *dst,
-                                             dst_score, s),
-                       "kvc_h2o_evict gather launch");
+  EvictArgs e = evict_args(cache, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,
+                           max_len_hint + 1);
+  if (evict_fits_one_launch(e.max_len, n_sink, n_recent) &&
+      evict_can_merge(num_q_heads, cache->num_kv_heads, a.splits)) {
+    // Two launches: the split kernel (with the append), then the eviction
+    // kernel that also merges the splits.
+    if ((st = device_status(launch_attn_split(a, s), "kvc_decode_step split launch"))) return st;
+    e.part_o = a.part_o;
+    e.part_ml = a.part_ml;
+    e.logits = a.logits;
+    e.stash = a.stash;
+    e.out = out;
+    e.num_q_heads = num_q_heads;
+    e.splits = a.splits;
+    e.span = (long long)a.splits * a.tiles * kSplitTokens;
+    return device_status(launch_evict(e, s), "kvc_decode_step eviction launch");
+  }
+  if ((st = device_status(launch_decode_attn(a, s), "kvc_decode_step attention launch"))) return st;
+  return evict_launch(e, s, "kvc_decode_step eviction launch");
 }
 
 }  // extern "C"

@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "kvc_internal.h"
+#include "merge.h"
 #include "quant_row.h"
 
 namespace kvc {
@@ -138,16 +139,8 @@ __device__ __forceinline__ float head_reduce(float v) {
   return v;
 }
 
-__device__ __forceinline__ float exp2_or_zero(float x) {
-  return x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x);
-}
-
-// Weight of a partial softmax state with max m_part inside a merged state with
-// max m_total >= m_part; an empty part (m_part = -inf) weighs 0, also when the
-// merged state is empty too.
-__device__ __forceinline__ float part_weight(float m_part, float m_total) {
-  return m_part == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_part - m_total);
-}
+using merge::exp2_or_zero;
+using merge::part_weight;
 
 __device__ __forceinline__ unsigned sel4(const unsigned* v, int i) {
   return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
@@ -647,18 +640,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   // Split statistics: one wave per head, lanes over the splits.
   for (int i = wave; i < nh; i += 4) {
     const float* ml = a.part_ml + ((long long)b * Hq + g * G + h_lo + i) * S * 2;
-    float m = -INFINITY;
-    for (int sp = lane; sp < S; sp += 64) m = fmaxf(m, ml[2 * sp]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int sp = lane; sp < S; sp += 64) {
-      const float f = part_weight(ml[2 * sp], m);
-      fac[i * S + sp] = f;
-      l = fmaf(ml[2 * sp + 1], f, l);
-    }
-    l = wave_sum(l);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    for (int sp = lane; sp < S; sp += 64) fac[i * S + sp] *= inv;
+    float m, inv;
+    merge::split_stats(ml, S, fac + i * S, m, inv);
     if (lane == 0) {
       minv[2 * i] = m;
       minv[2 * i + 1] = inv;
@@ -696,9 +679,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
       float add = 0.f;
 #pragma unroll
       for (int i = 0; i < kPrefetchHeads; ++i)
-        if (i < G) add = fmaf(exp2_or_zero(lg[i][k] - minv[2 * i]), minv[2 * i + 1], add);
-      for (int i = kPrefetchHeads; i < G; ++i)
-        add = fmaf(exp2_or_zero(lrow[i * span + t] - minv[2 * i]), minv[2 * i + 1], add);
+        if (i < G) add = merge::h2o_add(add, lg[i][k], minv[2 * i], minv[2 * i + 1]);
+      for (int i = kPrefetchHeads; i < G; ++i) add = merge::h2o_add(add, lrow[i * span + t], minv[2 * i], minv[2 * i + 1]);
       srow[t] = sc[k] + add;
     }
   }
@@ -726,14 +708,21 @@ hipError_t launch_paged(const AttnLaunch& a, int G, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st) {
+hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  hipError_t e;
   if (a.c.bits == 8)
-    e = a.c.head_dim == 64 ? launch_paged<8, 64>(a, G, st) : launch_paged<8, 128>(a, G, st);
-  else
-    e = a.c.head_dim == 64 ? launch_paged<4, 64>(a, G, st) : launch_paged<4, 128>(a, G, st);
+    return a.c.head_dim == 64 ? launch_paged<8, 64>(a, G, st) : launch_paged<8, 128>(a, G, st);
+  return a.c.head_dim == 64 ? launch_paged<4, 64>(a, G, st) : launch_paged<4, 128>(a, G, st);
+}
+
+hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st) {
+  const hipError_t e = launch_attn_split(a, st);
   if (e != hipSuccess) return e;
+  return launch_attn_merge(a, st);
+}
+
+hipError_t launch_attn_merge(const AttnLaunch& a, hipStream_t st) {
+  const int G = a.num_q_heads / a.c.num_kv_heads;
   const long long span = (long long)a.splits * a.tiles * TS;
   const int h2o_blocks = a.score ? (int)((span + kH2oChunk - 1) / kH2oChunk) : 0;
   const int nh = G;  // the H2O blocks need every head's statistics

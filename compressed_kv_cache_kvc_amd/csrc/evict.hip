@@ -20,6 +20,14 @@
 // follow it. One launch instead of two: no drain between selection
 // and compaction, and the kept-slot list never travels through memory on its
 // way to the copy.
+//
+// In a one-call decode step (kvc_decode_step) the same kernel also takes over
+// the attention's merge: it reads the split kernel's per-split statistics and
+// spilled logits, applies the H2O update to the scores it loads (the merge
+// kernel's arithmetic, merge.h), selects on the updated scores, copies the
+// kept tokens with them, and merges the attention output of the row's query
+// heads. The step then takes two launches: the split kernel, this one.
+#include "merge.h"
 #include "radix_select.h"
 
 namespace kvc {
@@ -27,7 +35,7 @@ namespace {
 
 constexpr int kLog2NT = 10;
 constexpr int kNT = 1 << kLog2NT;  // threads per workgroup
-constexpr int kKPT = 8;    // candidate keys per thread (in registers)
+constexpr int kKPT = 8;            // candidate keys per thread (in registers)
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -35,14 +43,16 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // slot dest_of(e): K and V codes (RB/16 lanes per row, 16-byte accesses),
 // scales, position and score. A pass covers up to RPP = kNT * 16 / RB
 // consecutive entries: lane group r0 = tid / (RB/16) holds the codes of entry
-// e0 + r0, thread tid the other fields of entry e0 + tid.
-template <int RB>
+// e0 + r0, thread tid the other fields of entry e0 + tid. GK > 0: the score
+// is updated with the step's H2O mass (GK logits per entry) when stored.
+template <int RB, int GK>
 struct Pass {
   static constexpr int LPR = RB / 16;
   static constexpr int RPP = kNT / LPR;
   u32x4 k, v;
   float ks, vs, sc;
   int pos;
+  float lg[GK > 0 ? GK : 1];
 };
 
 struct RowIO {
@@ -58,27 +68,52 @@ struct RowIO {
   int* dpos;
   const float* ssc;  // NULL unless dst scores are written
   float* dsc;
+  // H2O update of the copied scores (merging kernels): the row's logits
+  // (head h of slot t at lg[h * span + t]), the heads' (m, 1/l) and the
+  // number of slots the update covers.
+  const float* lg;
+  long long span;
+  const float* mstat;
+  int G, L_h2o;
 };
 
-template <int RB, typename SlotOf>
-__device__ __forceinline__ void load_pass(Pass<RB>& P, const RowIO& io, int e0, int e1, SlotOf slot_of) {
-  const int tid = threadIdx.x, part = tid % Pass<RB>::LPR, r0 = tid / Pass<RB>::LPR;
+template <int GK>
+__device__ __forceinline__ float updated_score(const RowIO& io, float sc, const float* lg, int slot) {
+  if (GK == 0 || slot >= io.L_h2o) return sc;
+  float add = 0.f;
+#pragma unroll
+  for (int h = 0; h < (GK > 0 ? GK : 1); ++h)
+    if (h < io.G) add = merge::h2o_add(add, lg[h], io.mstat[2 * h], io.mstat[2 * h + 1]);
+  return sc + add;
+}
+
+template <int RB, int GK, typename SlotOf>
+__device__ __forceinline__ void load_pass(Pass<RB, GK>& P, const RowIO& io, int e0, int e1, SlotOf slot_of) {
+  const int tid = threadIdx.x, part = tid % Pass<RB, GK>::LPR, r0 = tid / Pass<RB, GK>::LPR;
   if (e0 >= e1) return;  // uniform
   const long long s = slot_of(min(e0 + r0, e1 - 1));  // every lane loads; spare lanes repeat the last entry
   P.k = *reinterpret_cast<const u32x4*>(io.sk + s * RB + part * 16);
   P.v = *reinterpret_cast<const u32x4*>(io.sv + s * RB + part * 16);
   if (tid < e1 - e0) {
-    const long long se = slot_of(e0 + tid);
+    const int se = slot_of(e0 + tid);
     P.ks = io.sks[se];
     P.vs = io.svs[se];
     if (io.spos) P.pos = io.spos[se];
-    if (io.ssc) P.sc = io.ssc[se];
+    if (io.ssc) {
+      P.sc = io.ssc[se];
+      if (GK > 0) {
+#pragma unroll
+        for (int h = 0; h < (GK > 0 ? GK : 1); ++h)
+          P.lg[h] = io.lg[min(h, io.G - 1) * io.span + min((long long)se, io.span - 1)];
+      }
+    }
   }
 }
 
-template <int RB, typename DestOf>
-__device__ __forceinline__ void store_pass(const Pass<RB>& P, const RowIO& io, int e0, int e1, DestOf dest_of) {
-  const int tid = threadIdx.x, part = tid % Pass<RB>::LPR, r0 = tid / Pass<RB>::LPR;
+template <int RB, int GK, typename SlotOf, typename DestOf>
+__device__ __forceinline__ void store_pass(const Pass<RB, GK>& P, const RowIO& io, int e0, int e1, SlotOf slot_of,
+                                           DestOf dest_of) {
+  const int tid = threadIdx.x, part = tid % Pass<RB, GK>::LPR, r0 = tid / Pass<RB, GK>::LPR;
   if (e0 >= e1) return;
   if (e0 + r0 < e1) {
     const long long d = dest_of(e0 + r0);
@@ -91,35 +126,38 @@ __device__ __forceinline__ void store_pass(const Pass<RB>& P, const RowIO& io, i
     io.dks[de] = P.ks;
     io.dvs[de] = P.vs;
     if (io.spos) io.dpos[de] = P.pos;
-    if (io.ssc) io.dsc[de] = P.sc;
+    if (io.ssc) io.dsc[de] = updated_score<GK>(io, P.sc, P.lg, slot_of(e0 + tid));
   }
 }
 
 // Entries [e0, e1), BATCH passes in flight at a time.
-template <int RB, int BATCH, typename SlotOf, typename DestOf>
+template <int RB, int GK, int BATCH, typename SlotOf, typename DestOf>
 __device__ __forceinline__ void copy_entries(const RowIO& io, int e0, int e1, SlotOf slot_of, DestOf dest_of) {
-  constexpr int RPP = Pass<RB>::RPP;
+  constexpr int RPP = Pass<RB, GK>::RPP;
   for (int e = e0; e < e1; e += RPP * BATCH) {
-    Pass<RB> ps[BATCH];
+    Pass<RB, GK> ps[BATCH];
 #pragma unroll
-    for (int q = 0; q < BATCH; ++q) load_pass<RB>(ps[q], io, e + q * RPP, min(e1, e + (q + 1) * RPP), slot_of);
+    for (int q = 0; q < BATCH; ++q) load_pass<RB, GK>(ps[q], io, e + q * RPP, min(e1, e + (q + 1) * RPP), slot_of);
 #pragma unroll
-    for (int q = 0; q < BATCH; ++q) store_pass<RB>(ps[q], io, e + q * RPP, min(e1, e + (q + 1) * RPP), dest_of);
+    for (int q = 0; q < BATCH; ++q)
+      store_pass<RB, GK>(ps[q], io, e + q * RPP, min(e1, e + (q + 1) * RPP), slot_of, dest_of);
   }
 }
 
+}  // namespace
+
 // Grid (num_kv_heads << log2_parts, batch); 2^log2_parts workgroups per row,
-// at most kNT.
+// at most kNT. GK > 0: merge the attention splits first (num_q_heads /
+// num_kv_heads <= GK query heads per KV head).
 //
 // gfx9 counts stores in the same counter as loads, so a wait for a load also
 // waits for every store issued before it: stores come after the loads whose
 // data the workgroup waits for.
-template <int RB>
-__global__ __launch_bounds__(kNT) void evict_kernel(kvc_cache_t c, const float* __restrict__ score, int budget,
-                                                    int n_sink, int n_recent, uint8_t* __restrict__ mask,
-                                                    int32_t* __restrict__ keep_index, kvc_cache_t dst,
-                                                    float* __restrict__ dst_score, int max_len, int log2_parts) {
+template <int RB, int GK>
+__global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   constexpr int NT = kNT, KPT = kKPT;
+  constexpr bool MERGE = GK > 0;
+  constexpr int GL = MERGE ? GK : 1;
   __shared__ int hist[radix::kBins];
   __shared__ int scan_tmp[16];
   __shared__ unsigned mm_tmp[32];
@@ -127,34 +165,130 @@ __global__ __launch_bounds__(kNT) void evict_kernel(kvc_cache_t c, const float* 
   __shared__ unsigned small[64];
   // Staged keys; after the threshold search, the kept candidates in order.
   __shared__ __align__(16) unsigned stage_lds[NT * KPT];
+  // Merging: the heads' (m, 1/l), their split weights, the output partials.
+  __shared__ float mstat[2 * GL];
+  __shared__ float facl[MERGE ? GL * kEvictMaxSplits : 1];
+  __shared__ float opart[MERGE ? 256 : 1];
+  const kvc_cache_t& c = e.c;
+  const int budget = e.budget, n_sink = e.n_sink, n_recent = e.n_recent, log2_parts = e.log2_parts;
   const int parts = 1 << log2_parts;
   const int p = blockIdx.x & (parts - 1), g = blockIdx.x >> log2_parts, b = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid >> 6;
   const long long bg = (long long)b * c.num_kv_heads + g;
   const long long rowoff = bg * c.capacity;
-  const float* row = score + rowoff;
+  const float* row = e.score + rowoff;
+  const int Hq = MERGE ? e.num_q_heads : 0, G = MERGE ? Hq / c.num_kv_heads : 0, S = e.splits;
+  const float* lrow = MERGE ? e.logits + ((long long)b * Hq + g * G) * e.span : nullptr;
   // Coalesced loads of slots n_sink .. n_sink + NT*KPT - 1 (clamped to the
-  // row), issued before the sequence length is known.
-  unsigned v[KPT];
+  // row), issued before the sequence length is known: scores, and when
+  // merging the heads' logits of the same slots.
+  float sv[KPT];
+  float lgv[KPT][GL];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) v[j] = radix::order_key(row[min(n_sink + tid + j * NT, c.capacity - 1)]);
-  const int L = __builtin_amdgcn_readfirstlane(min(min(c.lengths[b], c.capacity), max_len));
-  // The new length, written last (after every load this workgroup waits for).
+  for (int j = 0; j < KPT; ++j) {
+    const int slot = min(n_sink + tid + j * NT, c.capacity - 1);
+    sv[j] = row[slot];
+    if (MERGE) {
+#pragma unroll
+      for (int h = 0; h < GL; ++h) lgv[j][h] = lrow[min(h, G - 1) * e.span + min((long long)slot, e.span - 1)];
+    }
+  }
+  // Merging, output of the row's first query head merged here (h = p): the
+  // split partials of thread (pi, d) = (tid / D, tid % D), tid < 256, load
+  // now with the scores; the sum is taken once the statistics are known.
+  constexpr int kPre = 8;
+  const int D = c.head_dim, PARTS = 256 / D;
+  const bool merges = MERGE && p < G;
+  float opre[MERGE ? kPre : 1];
+  const float* po = MERGE ? e.part_o + ((long long)b * Hq + g * G + p) * S * D + tid % D : nullptr;
+  if (merges && tid < 256) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) opre[k] = po[(long long)min(tid / D + k * PARTS, S - 1) * D];
+  }
+  // Merging: the lengths before this step's append come from the split
+  // kernel (this kernel advances the cache's own); the H2O update covers the
+  // slots the merge kernel would update.
+  const int L_src = MERGE ? e.stash[b] + 1 : c.lengths[b];
+  const int L = __builtin_amdgcn_readfirstlane(min(min(L_src, c.capacity), e.max_len));
+  const int L_h2o = MERGE ? __builtin_amdgcn_readfirstlane(min(min(L_src, c.capacity), (int)min(e.span, (long long)c.capacity))) : 0;
+  if (MERGE) {
+    // Statistics: wave h takes head h (G <= GK <= 16 waves).
+    if (wave < G) {
+      float m, inv;
+      merge::split_stats(e.part_ml + ((long long)b * Hq + g * G + wave) * S * 2, S, facl + wave * S, m, inv);
+      if ((tid & 63) == 0) {
+        mstat[2 * wave] = m;
+        mstat[2 * wave + 1] = inv;
+      }
+    }
+    __syncthreads();
+  }
+  // The new lengths, written last (after every load this workgroup waits for).
   auto set_length = [&]() {
     if (p == 0 && g == 0 && tid == 0) {
-      dst.lengths[b] = min(L, budget);
-      dst.num_seen[b] = c.num_seen[b];
+      const int seen = MERGE ? e.stash[c.batch + b] + 1 : c.num_seen[b];
+      if (MERGE) {
+        c.lengths[b] = L_src;
+        c.num_seen[b] = seen;
+      }
+      e.dst.lengths[b] = min(L, budget);
+      e.dst.num_seen[b] = seen;
     }
   };
-  uint8_t* m = mask ? mask + rowoff : nullptr;
-  int32_t* kidx = keep_index ? keep_index + bg * budget : nullptr;
+  // Merging: the attention output of the row's query heads h = p, p + parts,
+  // ... in the merge kernel's order (PARTS threads per channel over every
+  // PARTS-th split, then the PARTS sums). Head p: the partial sums right after
+  // the statistics (merge_first), the total after a later barrier
+  // (merge_first_out); further heads at the end (merge_rest).
+  auto merge_first = [&]() {
+    if (merges && tid < 256) {
+      const int pi = tid / D;
+      float o = 0.f;
+#pragma unroll
+      for (int k = 0; k < kPre; ++k)
+        if (pi + k * PARTS < S) o = fmaf(opre[k], facl[p * S + pi + k * PARTS], o);
+      for (int sp = pi + kPre * PARTS; sp < S; sp += PARTS) o = fmaf(po[(long long)sp * D], facl[p * S + sp], o);
+      opart[tid] = o;  // = opart[pi * D + d]
+    }
+  };
+  auto merge_first_out = [&]() {
+    if (merges && tid < D) {
+      float r = opart[tid];
+      for (int q = 1; q < PARTS; ++q) r += opart[q * D + tid];
+      e.out[((long long)b * Hq + g * G + p) * D + tid] = r;
+    }
+  };
+  auto merge_rest = [&]() {
+    if (!MERGE) return;
+    for (int h = p + parts; h < G; h += parts) {
+      if (tid < 256) {
+        const int d = tid % D, pi = tid / D;
+        const float* po = e.part_o + ((long long)b * Hq + g * G + h) * S * D + d;
+        float o = 0.f;
+        for (int sp = pi; sp < S; sp += PARTS) o = fmaf(po[(long long)sp * D], facl[h * S + sp], o);
+        opart[pi * D + d] = o;
+      }
+      __syncthreads();
+      if (tid < D) {
+        float r = opart[tid];
+        for (int q = 1; q < PARTS; ++q) r += opart[q * D + tid];
+        e.out[((long long)b * Hq + g * G + h) * D + tid] = r;
+      }
+      __syncthreads();
+    }
+  };
+  merge_first();
+  uint8_t* m = e.mask ? e.mask + rowoff : nullptr;
+  int32_t* kidx = e.keep_index ? e.keep_index + bg * budget : nullptr;
   const RowIO io{static_cast<const uint8_t*>(c.k_codes) + rowoff * RB,
                  static_cast<const uint8_t*>(c.v_codes) + rowoff * RB,
-                 static_cast<uint8_t*>(dst.k_codes) + rowoff * RB,
-                 static_cast<uint8_t*>(dst.v_codes) + rowoff * RB,
-                 c.k_scale + rowoff, c.v_scale + rowoff, dst.k_scale + rowoff, dst.v_scale + rowoff,
-                 (c.positions && dst.positions) ? c.positions + rowoff : nullptr,
-                 (c.positions && dst.positions) ? dst.positions + rowoff : nullptr,
-                 dst_score ? row : nullptr, dst_score ? dst_score + rowoff : nullptr};
+                 static_cast<uint8_t*>(e.dst.k_codes) + rowoff * RB,
+                 static_cast<uint8_t*>(e.dst.v_codes) + rowoff * RB,
+                 c.k_scale + rowoff, c.v_scale + rowoff, e.dst.k_scale + rowoff, e.dst.v_scale + rowoff,
+                 (c.positions && e.dst.positions) ? c.positions + rowoff : nullptr,
+                 (c.positions && e.dst.positions) ? e.dst.positions + rowoff : nullptr,
+                 e.dst_score ? row : nullptr, e.dst_score ? e.dst_score + rowoff : nullptr,
+                 lrow, e.span, mstat, G, L_h2o};
   // Kept entries: "fixed" ones (sinks and the recent window; every slot when
   // L <= budget), known from L alone, and heavy hitters, known after the
   // threshold search. Each kind is split evenly over the row's workgroups:
@@ -167,7 +301,7 @@ __global__ __launch_bounds__(kNT) void evict_kernel(kvc_cache_t c, const float* 
   const int n_fixed = all ? L : n_sink + n_recent;
   auto fixed_slot = [&](int f) { return f < n_self ? f : hi + (f - n_self); };
   auto fixed_dest = [&](int f) { return f < n_self ? f : lo + n_heavy + (f - n_self); };
-  constexpr int RPP = Pass<RB>::RPP;
+  constexpr int RPP = Pass<RB, GK>::RPP;
   const int f0 = (int)(((long long)n_fixed * p) >> log2_parts);
   const int f1 = (int)(((long long)n_fixed * (p + 1)) >> log2_parts);
   const int fa = min(f1, f0 + RPP);  // the first pass of fixed entries
@@ -179,14 +313,32 @@ __global__ __launch_bounds__(kNT) void evict_kernel(kvc_cache_t c, const float* 
       if (kidx) kidx[fixed_dest(f)] = fixed_slot(f);
     }
   };
-  Pass<RB> pre;
+  Pass<RB, GK> pre;
   if (all) {
-    load_pass<RB>(pre, io, f0, fa, fixed_slot);
+    load_pass<RB, GK>(pre, io, f0, fa, fixed_slot);
     fixed_entries();
-    store_pass<RB>(pre, io, f0, fa, fixed_dest);
-    copy_entries<RB, 2>(io, fa, f1, fixed_slot, fixed_dest);
+    store_pass<RB, GK>(pre, io, f0, fa, fixed_slot, fixed_dest);
+    copy_entries<RB, GK, 2>(io, fa, f1, fixed_slot, fixed_dest);
+    __syncthreads();
+    merge_first_out();
+    merge_rest();
     set_length();
     return;
+  }
+  // Keys of the coalesced slots: the scores, with this step's H2O mass when
+  // merging (slots below L_h2o, as the merge kernel updates them).
+  unsigned v[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    float s = sv[j];
+    if (MERGE && n_sink + tid + j * NT < L_h2o) {
+      float add = 0.f;
+#pragma unroll
+      for (int h = 0; h < GL; ++h)
+        if (h < G) add = merge::h2o_add(add, lgv[j][h], mstat[2 * h], mstat[2 * h + 1]);
+      s = s + add;
+    }
+    v[j] = radix::order_key(s);
   }
   const int n = hi - lo;
   int k = n_heavy;
@@ -215,8 +367,9 @@ __global__ __launch_bounds__(kNT) void evict_kernel(kvc_cache_t c, const float* 
   for (int j = 0; j < KPT; ++j) stage_lds[tid + j * NT] = v[j];
   // The first pass of fixed rows loads during the search (barriers here wait
   // for LDS only), and is stored after it.
-  load_pass<RB>(pre, io, f0, fa, fixed_slot);
+  load_pass<RB, GK>(pre, io, f0, fa, fixed_slot);
   __syncthreads();
+  merge_first_out();
   fixed_entries();  // stores: after the wait for the scores
 #pragma unroll
   for (int q = 0; q < KPT; q += 4) {
@@ -282,28 +435,42 @@ __global__ __launch_bounds__(kNT) void evict_kernel(kvc_cache_t c, const float* 
   auto rest_slot = [&](int e) { return e < nfr ? fixed_slot(fa + e) : heavy[h0 + e - nfr]; };
   auto rest_dest = [&](int e) { return e < nfr ? fixed_dest(fa + e) : lo + h0 + (e - nfr); };
   constexpr int HB = 2;
-  Pass<RB> hp[HB];
+  Pass<RB, GK> hp[HB];
 #pragma unroll
-  for (int q = 0; q < HB; ++q) load_pass<RB>(hp[q], io, q * RPP, min(total, (q + 1) * RPP), rest_slot);
-  store_pass<RB>(pre, io, f0, fa, fixed_dest);
+  for (int q = 0; q < HB; ++q) load_pass<RB, GK>(hp[q], io, q * RPP, min(total, (q + 1) * RPP), rest_slot);
+  store_pass<RB, GK>(pre, io, f0, fa, fixed_slot, fixed_dest);
   if (kidx)
     for (int h = h0 + tid; h < h1; h += NT) kidx[lo + h] = heavy[h];
 #pragma unroll
-  for (int q = 0; q < HB; ++q) store_pass<RB>(hp[q], io, q * RPP, min(total, (q + 1) * RPP), rest_dest);
-  copy_entries<RB, 2>(io, HB * RPP, total, rest_slot, rest_dest);
+  for (int q = 0; q < HB; ++q)
+    store_pass<RB, GK>(hp[q], io, q * RPP, min(total, (q + 1) * RPP), rest_slot, rest_dest);
+  copy_entries<RB, GK, 2>(io, HB * RPP, total, rest_slot, rest_dest);
+  merge_rest();
   set_length();
 }
 
-template <int RB>
-hipError_t launch_rb(const kvc_cache_t& c, const float* score, int budget, int n_sink, int n_recent, uint8_t* mask,
-                     int32_t* keep_index, const kvc_cache_t& dst, float* dst_score, int max_len, hipStream_t st) {
+namespace {
+
+template <int RB, int GK>
+hipError_t launch_rb(const EvictArgs& a, hipStream_t st) {
   // About 256 workgroups over the rows, at most 8 per row.
-  const long long rows = (long long)c.batch * c.num_kv_heads;
+  const long long rows = (long long)a.c.batch * a.c.num_kv_heads;
   int lp = 0;
   while (lp < 3 && rows << (lp + 1) <= 256) ++lp;
-  hipLaunchKernelGGL((evict_kernel<RB>), dim3(c.num_kv_heads << lp, c.batch), dim3(kNT), 0, st, c, score, budget,
-                     n_sink, n_recent, mask, keep_index, dst, dst_score, max_len, lp);
+  EvictArgs e = a;
+  e.log2_parts = lp;
+  hipLaunchKernelGGL((evict_kernel<RB, GK>), dim3(a.c.num_kv_heads << lp, a.c.batch), dim3(kNT), 0, st, e);
   return hipGetLastError();
+}
+
+template <int GK>
+hipError_t launch_gk(const EvictArgs& a, hipStream_t st) {
+  switch (a.c.head_dim * a.c.bits / 8) {
+    case 32: return launch_rb<32, GK>(a, st);
+    case 64: return launch_rb<64, GK>(a, st);
+    case 128: return launch_rb<128, GK>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -312,16 +479,17 @@ bool evict_fits_one_launch(int max_len, int n_sink, int n_recent) {
   return (long long)max_len - n_sink - n_recent <= (long long)kNT * kKPT;
 }
 
-hipError_t launch_evict(const kvc_cache_t& c, const float* score, int budget, int n_sink, int n_recent,
-                        uint8_t* mask, int32_t* keep_index, const kvc_cache_t& dst, float* dst_score, int max_len,
-                        hipStream_t st) {
-  switch (c.head_dim * c.bits / 8) {
-    case 32: return launch_rb<32>(c, score, budget, n_sink, n_recent, mask, keep_index, dst, dst_score, max_len, st);
-    case 64: return launch_rb<64>(c, score, budget, n_sink, n_recent, mask, keep_index, dst, dst_score, max_len, st);
-    case 128:
-      return launch_rb<128>(c, score, budget, n_sink, n_recent, mask, keep_index, dst, dst_score, max_len, st);
-    default: return hipErrorInvalidValue;
-  }
+bool evict_can_merge(int num_q_heads, int num_kv_heads, int splits) {
+  const int G = num_q_heads / num_kv_heads;
+  return G <= kEvictMaxMergeHeads && (long long)splits <= kEvictMaxSplits;
+}
+
+hipError_t launch_evict(const EvictArgs& a, hipStream_t st) {
+  if (!a.part_ml) return launch_gk<0>(a, st);
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  if (G <= 1) return launch_gk<1>(a, st);
+  if (G <= 2) return launch_gk<2>(a, st);
+  return launch_gk<4>(a, st);
 }
 
 }  // namespace kvc

@@ -47,17 +47,40 @@ struct AttnLaunch {
   int tiles;         // 256-token tiles per split
   float qk_log2;     // log2(e) / sqrt(head_dim)
 };
-hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st);
+hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st);  // split, then merge
+hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st);
+hipError_t launch_attn_merge(const AttnLaunch& a, hipStream_t st);
 
 hipError_t launch_select(const kvc_cache_t& c, const float* score, int budget, int n_sink,
                          int n_recent, uint8_t* mask, int32_t* keep_index, int max_len, hipStream_t st);
 
 // Selection and compaction in one launch; only for rows of at most 8192
-// candidates (evict_fits_one_launch).
+// candidates (evict_fits_one_launch). With part_ml set, the launch also merges
+// the attention splits of the same step (evict_can_merge).
+struct EvictArgs {
+  kvc_cache_t c;
+  const float* score;
+  int budget, n_sink, n_recent;
+  uint8_t* mask;        // may be NULL
+  int32_t* keep_index;  // may be NULL
+  kvc_cache_t dst;
+  float* dst_score;     // may be NULL
+  int max_len;
+  int log2_parts;       // set by the launcher
+  // Merging (part_ml NULL: none): the split kernel's outputs of the step.
+  const float* part_o;
+  const float* part_ml;
+  const float* logits;
+  const int32_t* stash;
+  float* out;
+  int num_q_heads, splits;
+  long long span;
+};
+constexpr int kEvictMaxMergeHeads = 4;  // query heads per KV head
+constexpr int kEvictMaxSplits = 1024;
 bool evict_fits_one_launch(int max_len, int n_sink, int n_recent);
-hipError_t launch_evict(const kvc_cache_t& c, const float* score, int budget, int n_sink, int n_recent,
-                        uint8_t* mask, int32_t* keep_index, const kvc_cache_t& dst, float* dst_score, int max_len,
-                        hipStream_t st);
+bool evict_can_merge(int num_q_heads, int num_kv_heads, int splits);
+hipError_t launch_evict(const EvictArgs& a, hipStream_t st);
 
 hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const uint8_t* mask,
                           const kvc_cache_t& dst, float* dst_score, int32_t* counts, int chunks,

@@ -12,6 +12,8 @@
  *   kvc_compact       stable out-of-place compaction of the kept slots
  *                     (kvc_compact_gather: from the keep list instead;
  *                     kvc_h2o_evict: selection and compaction in one call)
+ *   kvc_decode_step   the whole step (append, attention, H2O, eviction) in
+ *                     one call of two launches
  * and a host-side paged block pool (kvc_pool_*) that yields block tables.
  *
  * Conventions shared by every call:
@@ -294,6 +296,39 @@ int32_t kvc_compact_gather(const kvc_cache_t* src, const float* src_score, const
 int32_t kvc_h2o_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budget, int32_t n_sink,
                       int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
                       float* dst_score, int32_t max_len_hint, void* stream);
+
+/*
+ * A whole decode step in one call: kvc_append_decode_attn (with H2O) followed
+ * by kvc_h2o_evict from `cache` into `dst`. Sources: those of the two calls
+ * (tutorial sections 1.1, 1.2, 2.2, 2.4; report sections 1.1, 3.2 to 3.4;
+ * eviction-and-reuse survey, section 3.3).
+ *
+ * Results: `out`, the cache's codes, scales, positions, lengths and num_seen,
+ * keep_index, keep_mask (may be NULL) and every buffer of dst including
+ * dst_score (required: the kept tokens' accumulated scores) equal those of the
+ * two calls bit for bit. The source scores h2o_score are input to the step;
+ * afterwards they hold, for slots below the new length, either the old or the
+ * updated values (the new token's slot holds 0 or its mass), since the
+ * one-launch path below does not write them back: dst_score is the state a
+ * decode loop continues from.
+ *
+ * When num_q_heads / num_kv_heads <= 4 and max_len_hint + 1 - n_sink -
+ * n_recent <= 8192, the step is two launches: the split attention kernel
+ * (appending the new token) and the eviction kernel, which also merges the
+ * splits (the output and the H2O update of the scores it selects on and
+ * copies). Otherwise it runs the separate calls' launches. max_len_hint
+ * bounds the lengths before the append; the workspace is that of
+ * kvc_append_decode_attn (kvc_decode_attn_workspace_bytes(cache, num_q_heads,
+ * max_len_hint + 1, 1)) and must not overlap any cache buffer.
+ * Errors: those of kvc_append_decode_attn and kvc_h2o_evict (with
+ * max_len_hint + 1 as the eviction's hint), and INVALID_ARG for a NULL
+ * h2o_score or dst_score.
+ */
+int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                        int32_t num_q_heads, float* out, float* h2o_score, int32_t budget,
+                        int32_t n_sink, int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index,
+                        const kvc_cache_t* dst, float* dst_score, int32_t max_len_hint,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Paged block pool (host only; no device memory is touched).

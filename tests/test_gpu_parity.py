@@ -253,6 +253,92 @@ def test_append_decode_attn_llama7b_full_size():
     assert torch.equal(outA, outB)
 
 
+def _step_caches(w, lens, cap, seed):
+    """Two identical GPU caches with Lmax = max(lens) prefilled tokens, then
+    per-sequence lengths `lens`, and the same random scores."""
+    d = draw(w)
+    B, Lmax = len(lens), max(lens)
+    sc = (np.random.default_rng(seed).random((B, w.num_kv_heads, cap)) * 0.1).astype(np.float32)
+    out = []
+    for _ in range(2):
+        gc = make_gpu_cache(w, cap)
+        kvc.kvc_quant_append(gc, dev(d["k"][:, :, :Lmax]), dev(d["v"][:, :, :Lmax]))
+        gc.lengths.copy_(dev(np.array(lens, np.int32)))
+        gc.num_seen.copy_(dev(np.array(lens, np.int32) + 2))
+        gc.max_len = Lmax
+        out.append((gc, dev(sc)))
+    return d, out
+
+
+def _step_pair(w, d, caches, lens, budget, S, R, with_mask):
+    """kvc_append_decode_attn + kvc_h2o_evict on the first cache, kvc_decode_step
+    on the second; returns both sides' outputs."""
+    B, H, Hq, D, Lmax = len(lens), w.num_kv_heads, w.num_q_heads, w.head_dim, max(lens)
+    knew, vnew = dev(d["k"][:, :, Lmax:Lmax + 1]), dev(d["v"][:, :, Lmax:Lmax + 1])
+    q = dev(d["q"])
+    res = []
+    for i, (gc, sc) in enumerate(caches):
+        dst = make_gpu_cache(w, gc.capacity)
+        dst.k_codes.fill_(0x33)
+        dsc = dst.score_buffer()
+        dsc.fill_(-2.0)
+        kidx = torch.full((B, H, budget), -5, dtype=torch.int32, device="cuda")
+        mask = torch.full((B, H, gc.capacity), 7, dtype=torch.uint8, device="cuda") if with_mask else None
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        if i == 0:
+            kvc.kvc_append_decode_attn(gc, knew, vnew, q, out, h2o_score=sc, max_len_hint=Lmax)
+            kvc.kvc_h2o_evict(gc, sc, budget, S, R, kidx, dst, dsc, keep_mask=mask, max_len_hint=Lmax + 1)
+        else:
+            kvc.kvc_decode_step(gc, knew, vnew, q, out, sc, budget, S, R, kidx, dst, dsc, keep_mask=mask,
+                                max_len_hint=Lmax)
+        res.append((gc, out, dst, dsc, kidx, mask))
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("hq,hkv,bits,D,lens,budget,S,R,with_mask", [
+    (4, 4, 8, 128, [2999, 1000, 500], 1000, 4, 100, True),     # MHA, two launches; one row within budget
+    (8, 2, 8, 128, [3000, 2500, 2900], 1000, 4, 100, False),   # GQA 4, two launches, no mask
+    (4, 2, 4, 128, [2000, 1999, 100], 700, 4, 64, True),       # INT4, GQA 2
+    (8, 4, 8, 64, [1500, 1400, 1300], 500, 0, 64, True),       # D = 64, no sinks
+    (4, 4, 8, 128, [1200, 1100, 1000], 1028, 4, 1024, True),   # no heavy hitters
+    (16, 2, 8, 128, [2000, 1500, 1000], 600, 4, 64, True),     # GQA 8: the separate launches
+    (4, 4, 8, 64, [20000, 19000, 100], 5000, 4, 256, True),    # long rows: selection + gather
+])
+def test_decode_step_bit_exact(hq, hkv, bits, D, lens, budget, S, R, with_mask):
+    """kvc_decode_step equals kvc_append_decode_attn + kvc_h2o_evict: output,
+    keep list, mask, the source cache and every buffer of dst (with the kept
+    tokens' accumulated scores), bit for bit."""
+    print(f"[step] hq={hq} hkv={hkv} bits={bits} D={D} lens={lens} budget={budget}", flush=True)
+    w = get("tiny_mha").scaled(context=max(lens) + 1, batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                               head_dim=D, bits=bits)
+    d, caches = _step_caches(w, lens, max(lens) + 1 + 11, seed=budget + hq)
+    (gA, oA, dA, sA, kA, mA), (gB, oB, dB, sB, kB, mB) = _step_pair(w, d, caches, lens, budget, S, R, with_mask)
+    assert torch.equal(oA, oB)
+    assert torch.equal(kA, kB)
+    if with_mask:
+        assert torch.equal(mA, mB)
+    _assert_same_cache(dA, dB, sA, sB)
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "positions", "lengths", "num_seen"):
+        assert torch.equal(getattr(gA, name), getattr(gB, name)), name
+    assert host(dB.lengths).tolist() == [min(n + 1, budget) for n in lens]
+
+
+def test_decode_step_llama7b_full_size():
+    """The benchmarked step at full size (8191 cached tokens + the new one,
+    32 heads, keep 2457): kvc_decode_step equals the two calls bit for bit."""
+    w = get("llama7b_8k")
+    print("[step] llama7b_8k full size", flush=True)
+    L = w.context - 1
+    d, caches = _step_caches(w, [L], w.context, seed=3)
+    (gA, oA, dA, sA, kA, mA), (gB, oB, dB, sB, kB, mB) = _step_pair(w, d, caches, [L], w.budget, w.n_sink,
+                                                                     w.n_recent, True)
+    assert torch.equal(oA, oB) and torch.equal(kA, kB) and torch.equal(mA, mB)
+    _assert_same_cache(dA, dB, sA, sB)
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "positions", "lengths", "num_seen"):
+        assert torch.equal(getattr(gA, name), getattr(gB, name)), name
+
+
 # ---------------------------------------------------------- select/compact --
 
 @pytest.mark.parametrize("L,budget,S,R", [(512, 128, 4, 64), (3000, 1000, 4, 100), (9000, 2457, 4, 1024),
