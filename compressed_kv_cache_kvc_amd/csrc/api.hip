@@ -252,6 +252,26 @@ int32_t decode_attn_call(const kvc_cache_t* cache, const void* k_new, const void
   return device_status(launch_decode_attn(a, static_cast<hipStream_t>(stream)), "decode attention launch");
 }
 
+// The step's workspace (written by the split kernel, read by the eviction
+// kernel) may overlap no buffer of either cache, their scores, nor the keep
+// list or mask.
+int32_t check_workspace_disjoint(const void* ws, size_t ws_bytes, const kvc_cache_t* c, const float* c_score,
+                                 const kvc_cache_t* d, const float* d_score, const void* keep_index,
+                                 size_t keep_bytes, const void* keep_mask, size_t mask_bytes) {
+  const size_t rows = (size_t)c->batch * c->num_kv_heads * c->capacity;
+  const size_t RB = (size_t)c->head_dim * c->bits / 8;
+  const void* bufs[] = {c->k_codes, c->v_codes, c->k_scale, c->v_scale, c->positions, c_score, c->lengths,
+                        c->num_seen, d->k_codes, d->v_codes, d->k_scale, d->v_scale, d->positions, d_score,
+                        d->lengths, d->num_seen, keep_index, keep_mask};
+  const size_t lens[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, (size_t)c->batch * 4,
+                         (size_t)c->batch * 4, rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4,
+                         (size_t)c->batch * 4, (size_t)c->batch * 4, keep_bytes, mask_bytes};
+  for (int i = 0; i < 18; ++i)
+    if (overlap(ws, ws_bytes, bufs[i], lens[i]))
+      return fail(KVC_ERR_INVALID_ARG, "the workspace overlaps buffer %d of the caches, scores or keep outputs", i);
+  return KVC_OK;
+}
+
 // Checks of the eviction arguments shared by kvc_h2o_evict and kvc_decode_step
 // (`max_len` is the largest length the eviction sees).
 int32_t check_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budget, int32_t n_sink, int32_t n_recent,
@@ -426,6 +446,10 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
     return st;
   if ((st = check_evict(cache, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,
                         max_len_hint + 1, workspace, workspace_bytes)))
+    return st;
+  const size_t rows = (size_t)cache->batch * cache->num_kv_heads;
+  if ((st = check_workspace_disjoint(workspace, workspace_bytes, cache, h2o_score, dst, dst_score, keep_index,
+                                     rows * budget * sizeof(int32_t), keep_mask, rows * cache->capacity)))
     return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   EvictArgs e = evict_args(cache, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,

@@ -192,6 +192,23 @@ def test_compact_validation():
     assert evict(src, dst, mask=0x1200000) == INVALID   # mask overlaps dst codes
     assert evict(src, dst, dsc=0x4000000) == INVALID    # dst scores overlap the src scores
     assert evict(paged, dst) == UNSUPPORTED
+    # The whole step: the append and attention checks, then the eviction's.
+    ws = 0x7000000
+    need = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(src), 4, 17, 1)
+    step = lambda s_=src, d_=dst, k=FAKE, q=FAKE, sc=0x4000000, dsc=0x4100000, idx=0x5000000, budget=16, hint=16, \
+        w=ws, n=need, mask=None: lib.kvc_decode_step(ctypes.byref(s_), k, k, q, 4, 0x8000000, sc, budget, 4, 4, mask,
+                                                     idx, ctypes.byref(d_), dsc, hint, w, n, None)
+    assert step(k=None) == INVALID
+    assert step(sc=None) == INVALID
+    assert step(dsc=None) == INVALID                  # the kept scores are the step's H2O state
+    assert step(idx=None) == INVALID
+    assert step(hint=512) == CAPACITY
+    assert step(hint=-1) == INVALID
+    assert step(n=need - 1) == INVALID
+    assert step(budget=0) == INVALID
+    assert step(d_=bad) == INVALID
+    assert step(w=0x1100000) == INVALID               # workspace overlaps dst codes
+    assert step(s_=paged) == UNSUPPORTED
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 512) >= 4 * 1 * 4
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 2048) == 0   # beyond capacity
 
