@@ -641,7 +641,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   for (int i = wave; i < nh; i += 4) {
     const float* ml = a.part_ml + ((long long)b * Hq + g * G + h_lo + i) * S * 2;
     float m, inv;
-    merge::split_stats(ml, S, fac + i * S, m, inv);
+    merge::split_stats(merge::load_split_ml(ml, S), ml, S, fac + i * S, m, inv);
     if (lane == 0) {
       minv[2 * i] = m;
       minv[2 * i + 1] = inv;

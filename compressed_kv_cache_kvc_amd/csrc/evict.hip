@@ -146,8 +146,12 @@ __device__ __forceinline__ void copy_entries(const RowIO& io, int e0, int e1, Sl
 
 }  // namespace
 
-// Grid (num_kv_heads << log2_parts, batch); 2^log2_parts workgroups per row,
-// at most kNT. GK > 0: merge the attention splits first (num_q_heads /
+// One-dimensional grid of rows << log2_parts workgroups (2^log2_parts per
+// (sequence, KV head) row, at most kNT). Workgroups go to the 8 XCDs round
+// robin by index; when the row count is a multiple of 8 (xcd_rows), the
+// workgroups of a row get indices that are equal mod 8, so they share one
+// XCD and its L2 serves the row's scores (and logits) to all of them after
+// the first. GK > 0: merge the attention splits first (num_q_heads /
 // num_kv_heads <= GK query heads per KV head).
 //
 // gfx9 counts stores in the same counter as loads, so a wait for a load also
@@ -172,13 +176,34 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   const kvc_cache_t& c = e.c;
   const int budget = e.budget, n_sink = e.n_sink, n_recent = e.n_recent, log2_parts = e.log2_parts;
   const int parts = 1 << log2_parts;
-  const int p = blockIdx.x & (parts - 1), g = blockIdx.x >> log2_parts, b = blockIdx.y, tid = threadIdx.x;
+  const unsigned wg = blockIdx.x;
+  const unsigned rowi = e.xcd_rows ? (wg & 7u) + 8u * (wg >> (3 + log2_parts)) : wg >> log2_parts;
+  const int p = e.xcd_rows ? (int)((wg >> 3) & (unsigned)(parts - 1)) : (int)(wg & (unsigned)(parts - 1));
+  const int g = (int)(rowi % (unsigned)c.num_kv_heads), b = (int)(rowi / (unsigned)c.num_kv_heads);
+  const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const long long bg = (long long)b * c.num_kv_heads + g;
   const long long rowoff = bg * c.capacity;
   const float* row = e.score + rowoff;
   const int Hq = MERGE ? e.num_q_heads : 0, G = MERGE ? Hq / c.num_kv_heads : 0, S = e.splits;
   const float* lrow = MERGE ? e.logits + ((long long)b * Hq + g * G) * e.span : nullptr;
+  // Merging: wave h < G holds head h's split states (loaded first, so the
+  // statistics wait for nothing else).
+  const float* mlh = MERGE ? e.part_ml + ((long long)b * Hq + g * G + min(wave, G - 1)) * S * 2 : nullptr;
+  merge::SplitML mlr;
+  if (MERGE && wave < G) mlr = merge::load_split_ml(mlh, S);
+  // Merging, output of the row's first query head merged here (h = p): the
+  // split partials of thread (pi, d) = (tid / D, tid % D), tid < 256, load
+  // before the scores; the sum is taken once the statistics are known.
+  constexpr int kPre = 8;
+  const int D = c.head_dim, PARTS = 256 / D;
+  const bool merges = MERGE && p < G;
+  float opre[MERGE ? kPre : 1];
+  const float* po = MERGE ? e.part_o + ((long long)b * Hq + g * G + p) * S * D + tid % D : nullptr;
+  if (merges && tid < 256) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) opre[k] = po[(long long)min(tid / D + k * PARTS, S - 1) * D];
+  }
   // Coalesced loads of slots n_sink .. n_sink + NT*KPT - 1 (clamped to the
   // row), issued before the sequence length is known: scores, and when
   // merging the heads' logits of the same slots.
@@ -193,18 +218,6 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
       for (int h = 0; h < GL; ++h) lgv[j][h] = lrow[min(h, G - 1) * e.span + min((long long)slot, e.span - 1)];
     }
   }
-  // Merging, output of the row's first query head merged here (h = p): the
-  // split partials of thread (pi, d) = (tid / D, tid % D), tid < 256, load
-  // now with the scores; the sum is taken once the statistics are known.
-  constexpr int kPre = 8;
-  const int D = c.head_dim, PARTS = 256 / D;
-  const bool merges = MERGE && p < G;
-  float opre[MERGE ? kPre : 1];
-  const float* po = MERGE ? e.part_o + ((long long)b * Hq + g * G + p) * S * D + tid % D : nullptr;
-  if (merges && tid < 256) {
-#pragma unroll
-    for (int k = 0; k < kPre; ++k) opre[k] = po[(long long)min(tid / D + k * PARTS, S - 1) * D];
-  }
   // Merging: the lengths before this step's append come from the split
   // kernel (this kernel advances the cache's own); the H2O update covers the
   // slots the merge kernel would update.
@@ -215,7 +228,7 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
     // Statistics: wave h takes head h (G <= GK <= 16 waves).
     if (wave < G) {
       float m, inv;
-      merge::split_stats(e.part_ml + ((long long)b * Hq + g * G + wave) * S * 2, S, facl + wave * S, m, inv);
+      merge::split_stats(mlr, mlh, S, facl + wave * S, m, inv);
       if ((tid & 63) == 0) {
         mstat[2 * wave] = m;
         mstat[2 * wave + 1] = inv;
@@ -459,7 +472,10 @@ hipError_t launch_rb(const EvictArgs& a, hipStream_t st) {
   while (lp < 3 && rows << (lp + 1) <= 256) ++lp;
   EvictArgs e = a;
   e.log2_parts = lp;
-  hipLaunchKernelGGL((evict_kernel<RB, GK>), dim3(a.c.num_kv_heads << lp, a.c.batch), dim3(kNT), 0, st, e);
+  e.xcd_rows = rows % 8 == 0;
+  const long long wgs = rows << lp;
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((evict_kernel<RB, GK>), dim3((unsigned)wgs), dim3(kNT), 0, st, e);
   return hipGetLastError();
 }
 

@@ -67,6 +67,7 @@ struct EvictArgs {
   float* dst_score;     // may be NULL
   int max_len;
   int log2_parts;       // set by the launcher
+  int xcd_rows;         // set by the launcher: the workgroups of a row share an XCD
   // Merging (part_ml NULL: none): the split kernel's outputs of the step.
   const float* part_o;
   const float* part_ml;

@@ -25,25 +25,55 @@ __device__ __forceinline__ float part_weight(float m_part, float m_total) {
   return m_part == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_part - m_total);
 }
 
+// Split states of one head as a wave holds them: lane l has splits
+// l + 64 r, r < kStatRegs (m = -inf and l = 0 past S); splits past 64 *
+// kStatRegs are read again by split_stats.
+constexpr int kStatRegs = 4;
+struct SplitML {
+  float m[kStatRegs], l[kStatRegs];
+};
+
+__device__ __forceinline__ SplitML load_split_ml(const float* ml, int S) {
+  const int lane = threadIdx.x & 63;
+  SplitML r;
+#pragma unroll
+  for (int q = 0; q < kStatRegs; ++q) {
+    const int sp = lane + 64 * q;
+    const float m = ml[2 * min(sp, S - 1)], l = ml[2 * min(sp, S - 1) + 1];  // unconditional loads
+    r.m[q] = sp < S ? m : -INFINITY;
+    r.l[q] = sp < S ? l : 0.f;
+  }
+  return r;
+}
+
 // Statistics of one head from its S split states ml[2 s] = m_s, ml[2 s + 1] =
-// l_s, computed by one wave (lanes over the splits): the global max m and
-// 1/l (0 for an empty head); fac[s] (may be NULL) receives each split's
-// output weight exp2(m_s - m) / l.
-__device__ __forceinline__ void split_stats(const float* ml, int S, float* fac, float& m_out, float& inv_out) {
+// l_s (the first 64 * kStatRegs already in `r`), computed by one wave, lanes
+// over the splits: the global max m and 1/l (0 for an empty head); fac[s] (may
+// be NULL) receives each split's output weight exp2(m_s - m) / l. Each lane
+// accumulates its splits in increasing order; padded entries add exactly 0.
+__device__ __forceinline__ void split_stats(const SplitML& r, const float* ml, int S, float* fac, float& m_out,
+                                            float& inv_out) {
   const int lane = threadIdx.x & 63;
   float m = -INFINITY;
-  for (int sp = lane; sp < S; sp += 64) m = fmaxf(m, ml[2 * sp]);
+#pragma unroll
+  for (int q = 0; q < kStatRegs; ++q) m = fmaxf(m, r.m[q]);
+  for (int sp = lane + 64 * kStatRegs; sp < S; sp += 64) m = fmaxf(m, ml[2 * sp]);
   m = wave_max(m);
-  float l = 0.f;
-  for (int sp = lane; sp < S; sp += 64) {
-    const float f = part_weight(ml[2 * sp], m);
-    if (fac) fac[sp] = f;
-    l = fmaf(ml[2 * sp + 1], f, l);
+  float l = 0.f, f[kStatRegs];
+#pragma unroll
+  for (int q = 0; q < kStatRegs; ++q) {
+    f[q] = part_weight(r.m[q], m);
+    l = fmaf(r.l[q], f[q], l);
   }
+  for (int sp = lane + 64 * kStatRegs; sp < S; sp += 64) l = fmaf(ml[2 * sp + 1], part_weight(ml[2 * sp], m), l);
   l = wave_sum(l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (fac)
-    for (int sp = lane; sp < S; sp += 64) fac[sp] *= inv;
+  if (fac) {
+#pragma unroll
+    for (int q = 0; q < kStatRegs; ++q)
+      if (lane + 64 * q < S) fac[lane + 64 * q] = f[q] * inv;
+    for (int sp = lane + 64 * kStatRegs; sp < S; sp += 64) fac[sp] = part_weight(ml[2 * sp], m) * inv;
+  }
   m_out = m;
   inv_out = inv;
 }
