@@ -50,9 +50,10 @@ METRIC = "decode-attn KV GB/s & tokens/s (fraction of HBM peak), INT8, L=8192, 1
 TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/kvc_internal.h",
                    "compressed_kv_cache_kvc_amd/csrc/quant_row.h",
+                   "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "8af2f14fb492542caa19f839044b6f8913a22242196e8c5f626c90cc2d490f16"
-TRAFFIC_BYTES = 74343233
+TRAFFIC_SHA256 = "12ac5a5362188d4f0fa70dffa356be2734dc4c5d1e5419cab2c852503500400c"
+TRAFFIC_BYTES = 74350398
 
 
 def attention_traffic():
