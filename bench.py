@@ -150,6 +150,38 @@ def copy_calibration(torch, mib):
     return 0
 
 
+def read_probe(kvc, torch, nbytes, blocks=4):
+    """HBM read ceiling of one launch: kvc_bw_probe over 32 buffers of the
+    attention's KV size in turn (so every launch reads from HBM, as the
+    attention does), replayed as one graph per 32 launches."""
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(LAYERS)]
+    sink = torch.empty(kvc.kvc_bw_probe_sink_bytes(), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for buf in bufs:
+            kvc.kvc_bw_probe(buf, sink)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for buf in bufs:
+            kvc.kvc_bw_probe(buf, sink)
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(blocks):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (blocks * LAYERS)
+    del bufs, g
+    torch.cuda.empty_cache()
+    return {"kernel": "bw_probe_kernel (kvc_bw_probe)", "bytes_per_launch": nbytes, "us": round(us, 3),
+            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def secondary_attention(kvc, torch, reps=16):
     """Decode-attention throughput of the other workloads at full size, as KV
     GB/s of algorithmic bytes (codes + scales + q) and the fraction of the
@@ -425,6 +457,9 @@ def main(argv=None):
             "traffic": attention_traffic(),
         },
     }
+    probe = read_probe(kvc, torch, attn_alg)
+    probe["attention_frac_of_probe"] = round(attn_gbps / probe["gbps"], 4)
+    rec["hbm_read_probe"] = probe
     if not args.no_secondary:
         rec["secondary_attention"] = secondary_attention(kvc, torch)
     if not args.no_cpu_baseline:

@@ -69,6 +69,8 @@ def _load():
         "kvc_compact_gather": (I32, [D, P, P, I32, D, P, P]),
         "kvc_h2o_evict": (I32, [D, P, I32, I32, I32, P, P, D, P, I32, P]),
         "kvc_decode_step": (I32, [D, P, P, P, I32, P, P, I32, I32, I32, P, P, D, P, I32, P, SZ, P]),
+        "kvc_bw_probe_sink_bytes": (SZ, []),
+        "kvc_bw_probe": (I32, [P, SZ, P, SZ, P]),
         "kvc_pool_create": (P, [I32, I32, U64]),
         "kvc_pool_destroy": (None, [P]),
         "kvc_pool_reserve": (I32, [P, I32, I32]),
@@ -369,6 +371,17 @@ def kvc_decode_step(cache, k_new, v_new, q, out, h2o_score, budget: int, n_sink:
         cache.max_len = max_len_hint + 1
     if isinstance(dst, KVCache):
         dst.max_len = min(max_len_hint + 1, budget)
+
+
+def kvc_bw_probe_sink_bytes() -> int:
+    return lib.kvc_bw_probe_sink_bytes()
+
+
+def kvc_bw_probe(src, sink, stream=None):
+    """One streaming read of the device tensor ``src`` (see kvc.h); ``sink`` is
+    a device uint8 tensor of ``kvc_bw_probe_sink_bytes()`` bytes."""
+    _check(lib.kvc_bw_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                            sink.numel() * sink.element_size(), _stream(stream)), "kvc_bw_probe")
 
 
 class BlockPool:

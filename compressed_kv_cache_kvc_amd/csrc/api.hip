@@ -415,6 +415,20 @@ int32_t kvc_compact_gather(const kvc_cache_t* src, const float* src_score, const
                        "kvc_compact_gather launch");
 }
 
+size_t kvc_bw_probe_sink_bytes(void) { return (size_t)bw_probe_workgroups() * sizeof(uint32_t); }
+
+int32_t kvc_bw_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+  clear_error();
+  if (!src || !sink) return fail(KVC_ERR_INVALID_ARG, "src and sink must not be NULL");
+  if (bytes == 0 || bytes % 16) return fail(KVC_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if ((uintptr_t)src % 16) return fail(KVC_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  if (sink_bytes < kvc_bw_probe_sink_bytes())
+    return fail(KVC_ERR_INVALID_ARG, "sink needs %zu bytes", kvc_bw_probe_sink_bytes());
+  if (overlap(src, bytes, sink, sink_bytes)) return fail(KVC_ERR_INVALID_ARG, "sink overlaps src");
+  return device_status(launch_bw_probe(src, bytes, static_cast<unsigned*>(sink), static_cast<hipStream_t>(stream)),
+                       "kvc_bw_probe launch");
+}
+
 int32_t kvc_h2o_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budget, int32_t n_sink,
                       int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
                       float* dst_score, int32_t max_len_hint, void* stream) {

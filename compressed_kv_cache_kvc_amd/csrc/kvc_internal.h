@@ -89,6 +89,11 @@ hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const 
 hipError_t launch_compact_gather(const kvc_cache_t& src, const float* src_score, const int32_t* keep_index,
                                  int n_keep, const kvc_cache_t& dst, float* dst_score, hipStream_t st);
 
+// Read-bandwidth probe: reads bytes (a multiple of 16) from src once; writes
+// bw_probe_workgroups() words to sink.
+int bw_probe_workgroups();
+hipError_t launch_bw_probe(const void* src, size_t bytes, unsigned* sink, hipStream_t st);
+
 // ---- device helpers ----
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp_f(float old, float v) {

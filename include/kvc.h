@@ -331,6 +331,19 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Measurement helper (not a step of the method): one streaming read of
+ * `bytes` bytes of device memory at `src` (16-byte aligned, bytes a positive
+ * multiple of 16) with the decode-attention kernel's 16-byte load width, 4096
+ * workgroups. It gives the HBM read ceiling one launch reaches, the
+ * practical reference next to the nominal 8 TB/s for the attention's roofline.
+ * `sink` (device, kvc_bw_probe_sink_bytes() bytes, disjoint from src) receives
+ * one word per workgroup. Errors: INVALID_ARG for NULL pointers, a bad size or
+ * alignment, a small or overlapping sink.
+ */
+size_t kvc_bw_probe_sink_bytes(void);
+int32_t kvc_bw_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
+
+/*
  * Paged block pool (host only; no device memory is touched).
  * Source: "KV Cache optimization techniques" tutorial, section 3.2
  * (PagedAttention): fixed-size blocks, a per-sequence block list, a reference

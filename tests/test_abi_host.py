@@ -134,6 +134,19 @@ def test_append_decode_attn_validation():
                                       None) == INVALID
 
 
+def test_bw_probe_validation():
+    n = lib.kvc_bw_probe_sink_bytes()
+    assert n >= 4
+    probe = lambda src=FAKE * 16, nbytes=1 << 20, sink=0x9000000, sb=n: lib.kvc_bw_probe(src, nbytes, sink, sb, None)
+    assert probe(src=None) == INVALID
+    assert probe(sink=None) == INVALID
+    assert probe(nbytes=0) == INVALID
+    assert probe(nbytes=100) == INVALID                # not a multiple of 16
+    assert probe(src=FAKE * 16 + 4) == INVALID         # misaligned
+    assert probe(sb=n - 1) == INVALID
+    assert probe(sink=FAKE * 16 + 64) == INVALID       # inside src
+
+
 def test_select_validation():
     d = desc()
     sel = lambda budget, s, r, hint=16, score=FAKE, mask=FAKE: lib.kvc_h2o_select(

@@ -149,6 +149,21 @@ def test_empty_sequence_gives_zero_output():
     assert np.all(o[1] == 0) and np.all(np.isfinite(o[0]))
 
 
+# --------------------------------------------------- read-bandwidth probe --
+
+def test_bw_probe_reads_every_word():
+    """The probe's per-workgroup XOR words fold to the XOR of the whole buffer
+    (so every 16-byte word was read), on a size with a ragged tail."""
+    rng = np.random.default_rng(11)
+    words = rng.integers(0, 2**32, size=(4 << 20) // 4 + 20, dtype=np.uint32)
+    src = dev(words.view(np.uint8))
+    sink = torch.zeros(kvc.kvc_bw_probe_sink_bytes(), dtype=torch.uint8, device="cuda")
+    kvc.kvc_bw_probe(src, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
+
+
 # ------------------------------------------------- append + attention, fused --
 
 def _append_attn_pair(gcA, gcB, sA, sB, knew, vnew, q, hint, hq):
