@@ -150,6 +150,48 @@ def copy_calibration(torch, mib):
     return 0
 
 
+def layer_schedules(kvc, torch, caches, scores, lengths_all, k_new, v_new, q, out, dst, dst_score, ws, L, S, R,
+                    stream, blocks):
+    """The decode-order step with per-layer budgets from the pyramid schedules
+    (kvc_layer_budgets, base = the context, floor = sinks + window): layer i
+    of the 32 keeps budgets[i] tokens. Time per layer-step over the same
+    number of 32-layer blocks as the headline."""
+    B, H = caches[0].batch, caches[0].num_kv_heads
+    lists = [torch.zeros((B, H, L), dtype=torch.int32, device="cuda") for _ in range(LAYERS)]
+    res = {}
+    for name, sched, ratio in (("linear", kvc.KVC_SCHEDULE_LINEAR, 0.0), ("quadratic", kvc.KVC_SCHEDULE_QUADRATIC, 0.2)):
+        budgets = kvc.kvc_layer_budgets(sched, LAYERS, L, ratio, S + R)
+
+        def block():
+            lengths_all.fill_(L - 1)
+            for i in range(LAYERS):
+                kvc.kvc_decode_step(caches[i], k_new, v_new, q, out, scores[i], budgets[i], S, R, lists[i], dst,
+                                    dst_score, max_len_hint=L - 1, workspace=ws)
+
+        with torch.cuda.stream(stream):
+            block()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            block()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(blocks):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = {"ratio": ratio if sched == kvc.KVC_SCHEDULE_QUADRATIC else None,
+                     "budget_first_layer": budgets[0], "budget_last_layer": budgets[-1],
+                     "mean_budget": round(sum(budgets) / LAYERS, 1),
+                     "us_per_step": round(e0.elapsed_time(e1) * 1e3 / (blocks * LAYERS), 3)}
+        del g
+    return res
+
+
 def read_probe(kvc, torch, nbytes, blocks=4):
     """HBM read ceiling of one launch: kvc_bw_probe over 32 buffers of the
     attention's KV size in turn (so every launch reads from HBM, as the
@@ -457,10 +499,14 @@ def main(argv=None):
             "traffic": attention_traffic(),
         },
     }
+    if not args.no_secondary:
+        rec_sched = layer_schedules(kvc, torch, caches, scores, lengths_all, k_new, v_new, q, out, dst, dst_score,
+                                    ws_attn, L, S, R, stream, blocks)
     probe = read_probe(kvc, torch, attn_alg)
     probe["attention_frac_of_probe"] = round(attn_gbps / probe["gbps"], 4)
     rec["hbm_read_probe"] = probe
     if not args.no_secondary:
+        rec["layer_schedules"] = rec_sched
         rec["secondary_attention"] = secondary_attention(kvc, torch)
     if not args.no_cpu_baseline:
         t_cpu, n_cpu, cores = cpu_baseline(w, d, args.cpu_seconds)

@@ -71,6 +71,7 @@ def _load():
         "kvc_decode_step": (I32, [D, P, P, P, I32, P, P, I32, I32, I32, P, P, D, P, I32, P, SZ, P]),
         "kvc_bw_probe_sink_bytes": (SZ, []),
         "kvc_bw_probe": (I32, [P, SZ, P, SZ, P]),
+        "kvc_layer_budgets": (I32, [I32, I32, I32, ctypes.c_double, I32, P]),
         "kvc_pool_create": (P, [I32, I32, U64]),
         "kvc_pool_destroy": (None, [P]),
         "kvc_pool_reserve": (I32, [P, I32, I32]),
@@ -371,6 +372,18 @@ def kvc_decode_step(cache, k_new, v_new, q, out, h2o_score, budget: int, n_sink:
         cache.max_len = max_len_hint + 1
     if isinstance(dst, KVCache):
         dst.max_len = min(max_len_hint + 1, budget)
+
+
+KVC_SCHEDULE_LINEAR, KVC_SCHEDULE_QUADRATIC = 0, 1
+
+
+def kvc_layer_budgets(schedule: int, num_layers: int, base: int, base_ratio: float = 0.0,
+                      min_budget: int = 0) -> list:
+    """Per-layer keep budgets of a pyramid schedule (see kvc.h), as a list."""
+    out = (ctypes.c_int32 * max(num_layers, 1))()
+    _check(lib.kvc_layer_budgets(schedule, num_layers, base, float(base_ratio), min_budget, out),
+           "kvc_layer_budgets")
+    return list(out)[:num_layers]
 
 
 def kvc_bw_probe_sink_bytes() -> int:

@@ -331,6 +331,27 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Per-layer keep budgets (host only): the pyramid schedules of the pages.
+ * Sources: "KV Cache optimization techniques" tutorial, section 2.3
+ * (PyramidKV, linear: layer l of n keeps the fraction 1 - 0.8 l / n, shallow
+ * layers keep more) and the eviction-and-reuse survey, section 4 (quadratic:
+ * r + (1 - r)(l / n)^2 from a base ratio r, deep layers keep more; the page
+ * assumes n = 80, here n = num_layers).
+ *
+ * budgets_host[l] = max(min_budget, (int32)(base * ratio_l)) for l <
+ * num_layers, the product truncated toward zero, in double arithmetic. Layer
+ * l's budget is then the `budget` argument of kvc_h2o_select,
+ * kvc_h2o_evict or kvc_decode_step for that layer (min_budget =
+ * n_sink + n_recent keeps their precondition). base_ratio is used by the
+ * quadratic schedule only.
+ * Errors: INVALID_ARG for a NULL output, num_layers < 1, base < 1,
+ * min_budget < 0, an unknown schedule or a base_ratio outside [0, 1].
+ */
+enum { KVC_SCHEDULE_LINEAR = 0, KVC_SCHEDULE_QUADRATIC = 1 };
+int32_t kvc_layer_budgets(int32_t schedule, int32_t num_layers, int32_t base, double base_ratio,
+                          int32_t min_budget, int32_t* budgets_host);
+
+/*
  * Measurement helper (not a step of the method): one streaming read of
  * `bytes` bytes of device memory at `src` (16-byte aligned, bytes a positive
  * multiple of 16) with the decode-attention kernel's 16-byte load width, 4096

@@ -498,6 +498,42 @@ def test_evict_bit_exact(bits, D, B, H, L, budget, S, R, with_mask):
     assert host(dst.num_seen).tolist() == [L] * B
 
 
+@pytest.mark.parametrize("sched,r", [(0, 0.0), (1, 0.2)])
+def test_layer_budget_schedule(sched, r):
+    """A 4-layer eviction loop with the pyramid schedule's budgets
+    (kvc_layer_budgets): each layer's keep list and compacted cache equal the
+    oracle's selection and compaction at that layer's budget."""
+    B, H, D, L, S, R = 2, 4, 64, 3000, 4, 64
+    budgets = kvc.kvc_layer_budgets(sched, 4, L, r, S + R)
+    assert budgets == oracle.layer_budgets(sched, 4, L, r, S + R)
+    print(f"[schedule] {sched} budgets {budgets}", flush=True)
+    w = get("tiny_mha").scaled(context=L, batch=B, num_q_heads=H, num_kv_heads=H, head_dim=D, bits=8)
+    d = draw(w)
+    gc, ref, score = prefill_both(w, d, capacity=L)
+    rng = np.random.default_rng(17 + sched)
+    for layer, budget in enumerate(budgets):
+        sc = rng.random((B, H, L)).astype(np.float32)
+        score.copy_(dev(sc))
+        dst = make_gpu_cache(w, L)
+        dsc = dst.score_buffer()
+        kidx = torch.full((B, H, budget), -1, dtype=torch.int32, device="cuda")
+        kvc.kvc_h2o_evict(gc, score, budget, S, R, kidx, dst, dsc, max_len_hint=L)
+        torch.cuda.synchronize()
+        keep = np.stack([np.stack([oracle.select_keep(sc[b, g].astype(np.float64), L, budget, S, R)
+                                   for g in range(H)]) for b in range(B)])
+        ki = host(kidx)
+        for b in range(B):
+            for g in range(H):
+                assert np.array_equal(ki[b, g, :min(L, budget)], np.nonzero(keep[b, g])[0]), (layer, b, g)
+        r2 = oracle.RefCache(B, H, D, L, 8)
+        r2.k_codes[:], r2.v_codes[:], r2.k_scale[:], r2.v_scale[:] = ref.k_codes, ref.v_codes, ref.k_scale, ref.v_scale
+        r2.positions[:], r2.lengths[:], r2.num_seen[:] = ref.positions, ref.lengths, ref.num_seen
+        r2.score[:] = sc
+        r2.compact(keep)
+        assert_codes_equal(dst, r2)
+        assert host(dst.lengths).tolist() == [min(L, budget)] * B
+
+
 # ------------------------------------------------------- whole decode step --
 
 def _full_step(w, d, prior=()):
