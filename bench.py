@@ -280,6 +280,17 @@ def secondary_attention(kvc, torch, reps=16):
     us = timed(lambda i: kvc.kvc_decode_attn(gc, q, out, max_len_hint=hint, workspace=ws), 1)
     report("paged_b32", w, int(lengths.sum()) * H * 2 * (D + 4) + q.numel() * 2, us,
            {"tokens": int(lengths.sum()), "h2o": False})
+    # Block-granular eviction of the same batch (retention 0.5): one launch
+    # over random scores, the table rewritten into a view of the same pools.
+    sc = torch.rand((B, H, gc.capacity), device="cuda")
+    dv, dsc = gc.table_view(), torch.empty((B, H, gc.capacity), device="cuda")
+    freed = torch.empty((B, gc.max_blocks_per_seq), dtype=torch.int32, device="cuda")
+    fcount = torch.empty((B,), dtype=torch.int32, device="cuda")
+    us_be = timed(lambda i: kvc.kvc_paged_block_evict(gc, sc, 0.5, dv, dsc, freed, fcount, max_len_hint=hint), 1)
+    res["paged_b32_block_evict"] = {"workload": "paged_b32", "us_per_launch": round(us_be, 2), "retention": 0.5,
+                                    "blocks": int(sum(nblk)), "blocks_freed": int(fcount.sum().item()),
+                                    "score_bytes_moved": int(2 * 4 * H * (int(lengths.sum()) // 2))}
+    del sc, dv, dsc, freed, fcount
     del gc, ws
     torch.cuda.empty_cache()
 

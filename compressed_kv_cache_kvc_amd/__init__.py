@@ -72,10 +72,12 @@ def _load():
         "kvc_bw_probe_sink_bytes": (SZ, []),
         "kvc_bw_probe": (I32, [P, SZ, P, SZ, P]),
         "kvc_layer_budgets": (I32, [I32, I32, I32, ctypes.c_double, I32, P]),
+        "kvc_paged_block_evict": (I32, [D, P, ctypes.c_double, D, P, P, P, I32, P]),
         "kvc_pool_create": (P, [I32, I32, U64]),
         "kvc_pool_destroy": (None, [P]),
         "kvc_pool_reserve": (I32, [P, I32, I32]),
         "kvc_pool_free": (I32, [P, I32]),
+        "kvc_pool_release": (I32, [P, I32, P, I32]),
         "kvc_pool_num_free": (I32, [P]),
         "kvc_pool_num_blocks": (I32, [P, I32]),
         "kvc_pool_block_table": (I32, [P, P, I32, I32, P]),
@@ -197,6 +199,20 @@ class KVCache:
         d.positions = _ptr(self.positions)
         d.block_table = _ptr(self.block_table)
         return d
+
+    def table_view(self):
+        """A paged cache over the same pools with its own block table, lengths
+        and num_seen: the destination of ``kvc_paged_block_evict``."""
+        import copy
+        import torch
+        if not self.block_size:
+            raise ValueError("table_view needs a paged cache")
+        v = copy.copy(self)
+        v.block_table = torch.full_like(self.block_table, -1)
+        v.lengths = torch.zeros_like(self.lengths)
+        v.num_seen = torch.zeros_like(self.num_seen)
+        v.desc = v._make_desc()
+        return v
 
     def score_buffer(self):
         """A zeroed fp32 H2O score array ``[B][Hkv][capacity]``."""
@@ -374,6 +390,26 @@ def kvc_decode_step(cache, k_new, v_new, q, out, h2o_score, budget: int, n_sink:
         dst.max_len = min(max_len_hint + 1, budget)
 
 
+def kvc_paged_block_evict(src, h2o_score, retention: float, dst, dst_score, freed, freed_count,
+                          max_len_hint: Optional[int] = None, stream=None):
+    """Block-granular H2O eviction on a paged cache (see kvc.h): ``dst`` shares
+    ``src``'s pools (``src.table_view()``); ``freed`` int32 ``[B][max_blocks]``
+    and ``freed_count`` int32 ``[B]`` receive the released physical blocks."""
+    import torch
+    ds, dd = _desc(src), _desc(dst)
+    _need(h2o_score, torch.float32, "h2o_score", ds.batch * ds.num_kv_heads * ds.capacity)
+    _need(dst_score, torch.float32, "dst_score", dd.batch * dd.num_kv_heads * dd.capacity)
+    _need(freed, torch.int32, "freed", ds.batch * ds.max_blocks_per_seq)
+    _need(freed_count, torch.int32, "freed_count", ds.batch)
+    if max_len_hint is None:
+        max_len_hint = src.max_len
+    _check(lib.kvc_paged_block_evict(ctypes.byref(ds), _ptr(h2o_score), float(retention), ctypes.byref(dd),
+                                     _ptr(dst_score), _ptr(freed), _ptr(freed_count), max_len_hint,
+                                     _stream(stream)), "kvc_paged_block_evict")
+    if isinstance(dst, KVCache) and isinstance(src, KVCache):
+        dst.max_len = src.max_len
+
+
 KVC_SCHEDULE_LINEAR, KVC_SCHEDULE_QUADRATIC = 0, 1
 
 
@@ -418,6 +454,11 @@ class BlockPool:
 
     def free(self, seq_id: int) -> None:
         _check(lib.kvc_pool_free(self._p, seq_id), "kvc_pool_free")
+
+    def release(self, seq_id: int, blocks) -> None:
+        """Give back the listed blocks of a sequence (refcounted, all or nothing)."""
+        arr = (ctypes.c_int32 * max(len(blocks), 1))(*[int(x) for x in blocks])
+        _check(lib.kvc_pool_release(self._p, seq_id, arr, len(blocks)), "kvc_pool_release")
 
     @property
     def num_free(self) -> int:

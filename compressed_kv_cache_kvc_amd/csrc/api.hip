@@ -415,6 +415,50 @@ int32_t kvc_compact_gather(const kvc_cache_t* src, const float* src_score, const
                        "kvc_compact_gather launch");
 }
 
+int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, double retention,
+                              const kvc_cache_t* dst, float* dst_score, int32_t* freed, int32_t* freed_count,
+                              int32_t max_len_hint, void* stream) {
+  clear_error();
+  int32_t st = check_cache(src, "src");
+  if (st) return st;
+  if ((st = check_cache(dst, "dst"))) return st;
+  if (src->block_size == 0 || dst->block_size == 0)
+    return fail(KVC_ERR_INVALID_ARG, "block eviction needs paged caches");
+  if (src->bits != dst->bits || src->batch != dst->batch || src->num_kv_heads != dst->num_kv_heads ||
+      src->head_dim != dst->head_dim || src->capacity != dst->capacity ||
+      src->max_blocks_per_seq != dst->max_blocks_per_seq || src->num_blocks != dst->num_blocks)
+    return fail(KVC_ERR_INVALID_ARG, "src and dst geometries differ");
+  if (src->k_codes != dst->k_codes || src->v_codes != dst->v_codes || src->k_scale != dst->k_scale ||
+      src->v_scale != dst->v_scale)
+    return fail(KVC_ERR_INVALID_ARG, "dst must share src's code and scale pools");
+  if (!h2o_score || !dst_score || !freed || !freed_count)
+    return fail(KVC_ERR_INVALID_ARG, "h2o_score, dst_score, freed and freed_count must not be NULL");
+  if (!(retention >= 0.0 && retention <= 1.0)) return fail(KVC_ERR_INVALID_ARG, "retention must lie in [0, 1]");
+  if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
+  if (max_len_hint > src->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
+  if (src->max_blocks_per_seq > kBlockEvictMaxBlocks)
+    return fail(KVC_ERR_UNSUPPORTED, "block eviction supports up to %d blocks per sequence", kBlockEvictMaxBlocks);
+  const size_t B = (size_t)src->batch, MB = (size_t)src->max_blocks_per_seq;
+  const size_t score_bytes = B * src->num_kv_heads * (size_t)src->capacity * sizeof(float);
+  // Outputs (dst table, lengths, num_seen, scores, freed lists) overlap no input
+  // (src table, lengths, num_seen, scores) and no other output.
+  const void* in[] = {src->block_table, src->lengths, src->num_seen, h2o_score};
+  const size_t in_len[] = {B * MB * 4, B * 4, B * 4, score_bytes};
+  const void* out[] = {dst->block_table, dst->lengths, dst->num_seen, dst_score, freed, freed_count};
+  const size_t out_len[] = {B * MB * 4, B * 4, B * 4, score_bytes, B * MB * 4, B * 4};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlap(out[i], out_len[i], in[j], in_len[j]))
+        return fail(KVC_ERR_INVALID_ARG, "output %d overlaps input %d (eviction is out of place)", i, j);
+    for (int j = 0; j < i; ++j)
+      if (overlap(out[i], out_len[i], out[j], out_len[j]))
+        return fail(KVC_ERR_INVALID_ARG, "outputs %d and %d overlap", j, i);
+  }
+  return device_status(launch_block_evict(*src, h2o_score, retention, *dst, dst_score, freed, freed_count,
+                                          max_len_hint, static_cast<hipStream_t>(stream)),
+                       "kvc_paged_block_evict launch");
+}
+
 size_t kvc_bw_probe_sink_bytes(void) { return (size_t)bw_probe_workgroups() * sizeof(uint32_t); }
 
 int32_t kvc_bw_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream) {

@@ -1,0 +1,168 @@
+// Block-granular H2O eviction on a paged cache: whole 16-token blocks leave,
+// and compaction is a rewrite of the block table.
+//
+// The eviction-and-reuse survey (section 4) evicts KV blocks by attention
+// score: the blocks are sorted by their mean score (a stable sort, lowest
+// first) and the first int(n * (1 - retention)) of them are evicted, their
+// references released so the pool can reuse them ("KV Cache optimization
+// techniques" tutorial, section 3.2: a block returns to the free set when its
+// reference count drops to zero). Here a block's score is the mean H2O score
+// over its filled slots and every KV head of the sequence (a physical block
+// holds all heads), and n is the number of blocks the sequence's length
+// covers. The kept blocks keep their order, so the tokens keep theirs: the
+// destination's table lists them first, its length counts their tokens (only
+// the last block can be partial), and the scores move with their blocks. The
+// codes and scales stay where they are: source and destination share the
+// pools.
+//
+// One 256-thread workgroup per sequence: block means into LDS (16-byte
+// loads, four heads in flight), then each block's rank in the stable order
+// by counting (n^2 comparisons from LDS, made for the decode-sized tables of a
+// paged batch), a block scan for the kept and freed positions, and the score
+// rows moved in 16-byte pieces, eight loads in flight per thread. One CU per
+// sequence bounds it: on the 32-sequence paged batch (5114 blocks) a launch
+// takes about 43 us, whatever the loads in flight per thread.
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kBT = 256;
+
+__global__ __launch_bounds__(kBT) void block_evict_kernel(kvc_cache_t src, const float* __restrict__ score,
+                                                          double retention, kvc_cache_t dst,
+                                                          float* __restrict__ dst_score, int32_t* __restrict__ freed,
+                                                          int32_t* __restrict__ freed_count, int max_len) {
+  extern __shared__ float lds[];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int H = src.num_kv_heads, BS = src.block_size, MB = src.max_blocks_per_seq;
+  const long long cap = src.capacity;
+  float* mean = lds;                                    // [MB]
+  int* keep = reinterpret_cast<int*>(lds + MB);         // [MB]: 1 kept, 0 evicted
+  int* src_of = keep + MB;                              // [MB]: kept block at each new position
+  __shared__ int scan_tmp[kBT / 64];
+  const int L = __builtin_amdgcn_readfirstlane(min(min(src.lengths[b], src.capacity), max_len));
+  const int nb = (L + BS - 1) / BS;
+  const int32_t* srow = src.block_table + (long long)b * MB;
+  // Mean score of each block: heads in order, slots in order, fp32. A block
+  // row is 16 floats (four 16-byte loads, in bounds: the capacity is a whole
+  // number of blocks); kHB heads' loads are in flight at a time, and slots past
+  // the length are masked out of the sum.
+  constexpr int kHB = 4;
+  for (int j = tid; j < nb; j += kBT) {
+    const int fill = min(BS, L - BS * j);
+    float acc = 0.f;
+    for (int h0 = 0; h0 < H; h0 += kHB) {
+      float4 w[kHB][4];
+#pragma unroll
+      for (int hh = 0; hh < kHB; ++hh) {
+        const float4* sc = reinterpret_cast<const float4*>(score + ((long long)b * H + min(h0 + hh, H - 1)) * cap +
+                                                           (long long)BS * j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[hh][q] = sc[q];
+      }
+#pragma unroll
+      for (int hh = 0; hh < kHB; ++hh) {
+        if (h0 + hh < H) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x[4] = {w[hh][q].x, w[hh][q].y, w[hh][q].z, w[hh][q].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (4 * q + c < fill) acc += x[c];
+          }
+        }
+      }
+    }
+    mean[j] = acc / (float)(fill * H);
+  }
+  __syncthreads();
+  // Stable ascending order by mean: block j's rank counts the blocks with a
+  // lower mean, or an equal mean and a lower index; ranks below n_evict go.
+  const int n_evict = (int)((double)nb * (1.0 - retention));
+  for (int j = tid; j < nb; j += kBT) {
+    const float mj = mean[j];
+    int rank = 0;
+    for (int i = 0; i < nb; ++i) {
+      const float mi = mean[i];
+      rank += (mi < mj) | ((mi == mj) & (i < j));
+    }
+    keep[j] = rank >= n_evict;
+  }
+  __syncthreads();
+  // Kept and freed positions: thread t owns blocks [t*per, t*per + per).
+  const int per = (nb + kBT - 1) / kBT;
+  const int j0 = min(tid * per, nb), j1 = min(j0 + per, nb);
+  int kc = 0;
+  for (int j = j0; j < j1; ++j) kc += keep[j];
+  int kpos = block_inclusive_scan<kBT>(kc, scan_tmp) - kc;  // kept blocks before j0
+  int fpos = j0 - kpos;                                       // evicted blocks before j0
+  const int n_kept = nb - n_evict;
+  int32_t* drow = const_cast<int32_t*>(dst.block_table) + (long long)b * MB;
+  int32_t* frow = freed + (long long)b * MB;
+  for (int j = j0; j < j1; ++j) {
+    if (keep[j]) {
+      src_of[kpos] = j;
+      drow[kpos++] = srow[j];
+    } else {
+      frow[fpos++] = srow[j];
+    }
+  }
+  for (int i = n_kept + tid; i < MB; i += kBT) drow[i] = -1;
+  __syncthreads();
+  // Scores move with their blocks: new block i takes old block src_of[i], in
+  // 16-byte pieces (4 per block row), kMB pieces per thread loaded before
+  // any is stored; slots past a partial block's fill are not written.
+  constexpr int kMB = 8;
+  const long long pieces = (long long)n_kept * H * 4;
+  for (long long w0 = tid; w0 < pieces; w0 += (long long)kBT * kMB) {
+    float4 v[kMB];
+#pragma unroll
+    for (int u = 0; u < kMB; ++u) {
+      const long long w = min(w0 + (long long)u * kBT, pieces - 1);
+      const int q = (int)(w & 3);
+      const long long r = w >> 2;
+      const int h = (int)(r % H), i = (int)(r / H);
+      v[u] = reinterpret_cast<const float4*>(score + ((long long)b * H + h) * cap + (long long)BS * src_of[i])[q];
+    }
+#pragma unroll
+    for (int u = 0; u < kMB; ++u) {
+      const long long w = w0 + (long long)u * kBT;
+      if (w < pieces) {
+        const int q = (int)(w & 3);
+        const long long r = w >> 2;
+        const int h = (int)(r % H), i = (int)(r / H);
+        const int fill = min(BS, L - BS * src_of[i]);
+        float* d = dst_score + ((long long)b * H + h) * cap + (long long)BS * i + 4 * q;
+        if (4 * q + 4 <= fill) {
+          *reinterpret_cast<float4*>(d) = v[u];
+        } else {
+          const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          for (int c = 0; c < 4; ++c)
+            if (4 * q + c < fill) d[c] = x[c];
+        }
+      }
+    }
+  }
+  if (tid == 0) {
+    // Only the last block can be partial; it stays last when kept.
+    const int last_fill = nb > 0 ? L - BS * (nb - 1) : 0;
+    const int new_len = n_kept == 0 ? 0 : (nb > 0 && keep[nb - 1] ? BS * (n_kept - 1) + last_fill : BS * n_kept);
+    dst.lengths[b] = new_len;
+    dst.num_seen[b] = src.num_seen[b];
+    freed_count[b] = n_evict;
+  }
+}
+
+}  // namespace
+
+size_t block_evict_lds_bytes(int max_blocks_per_seq) { return (size_t)max_blocks_per_seq * 3 * sizeof(float); }
+
+hipError_t launch_block_evict(const kvc_cache_t& src, const float* score, double retention, const kvc_cache_t& dst,
+                              float* dst_score, int32_t* freed, int32_t* freed_count, int max_len, hipStream_t st) {
+  hipLaunchKernelGGL(block_evict_kernel, dim3(src.batch), dim3(kBT), block_evict_lds_bytes(src.max_blocks_per_seq), st,
+                     src, score, retention, dst, dst_score, freed, freed_count, max_len);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

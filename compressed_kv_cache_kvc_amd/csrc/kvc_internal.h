@@ -89,6 +89,13 @@ hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const 
 hipError_t launch_compact_gather(const kvc_cache_t& src, const float* src_score, const int32_t* keep_index,
                                  int n_keep, const kvc_cache_t& dst, float* dst_score, hipStream_t st);
 
+// Block-granular eviction on a paged cache (one workgroup per sequence;
+// block_evict_lds_bytes of dynamic LDS).
+size_t block_evict_lds_bytes(int max_blocks_per_seq);
+constexpr int kBlockEvictMaxBlocks = 8192;
+hipError_t launch_block_evict(const kvc_cache_t& src, const float* score, double retention, const kvc_cache_t& dst,
+                              float* dst_score, int32_t* freed, int32_t* freed_count, int max_len, hipStream_t st);
+
 // Read-bandwidth probe: reads bytes (a multiple of 16) from src once; writes
 // bw_probe_workgroups() words to sink.
 int bw_probe_workgroups();

@@ -108,6 +108,35 @@ int32_t kvc_pool_free(kvc_pool_t* pool, int32_t seq_id) {
   return KVC_OK;
 }
 
+int32_t kvc_pool_release(kvc_pool_t* pool, int32_t seq_id, const int32_t* blocks_host, int32_t n) {
+  kvc::clear_error();
+  if (!pool) return kvc::fail(KVC_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0 || (n > 0 && !blocks_host)) return kvc::fail(KVC_ERR_INVALID_ARG, "bad block list");
+  auto it = pool->seqs.find(seq_id);
+  if (it == pool->seqs.end()) return kvc::fail(KVC_ERR_INVALID_ARG, "unknown sequence %d", seq_id);
+  std::vector<int32_t>& blocks = it->second;
+  // All or nothing: every listed block must be one of the sequence's, once.
+  std::vector<char> drop(blocks.size(), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    size_t k = 0;
+    while (k < blocks.size() && (blocks[k] != blocks_host[i] || drop[k])) ++k;
+    if (k == blocks.size())
+      return kvc::fail(KVC_ERR_INVALID_ARG, "block %d is not held by sequence %d", blocks_host[i], seq_id);
+    drop[k] = 1;
+  }
+  std::vector<int32_t> kept;
+  kept.reserve(blocks.size() - (size_t)n);
+  for (size_t k = 0; k < blocks.size(); ++k) {
+    if (!drop[k]) {
+      kept.push_back(blocks[k]);
+    } else if (--pool->refcount[blocks[k]] == 0) {
+      pool->free_list.push_back(blocks[k]);
+    }
+  }
+  blocks.swap(kept);
+  return KVC_OK;
+}
+
 int32_t kvc_pool_num_free(const kvc_pool_t* pool) { return pool ? (int32_t)pool->free_list.size() : -1; }
 
 int32_t kvc_pool_num_blocks(const kvc_pool_t* pool, int32_t seq_id) {

@@ -331,6 +331,41 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block-granular H2O eviction on a paged cache: whole 16-token blocks are
+ * evicted and compaction is a rewrite of the block table (no codes move).
+ * Sources: eviction-and-reuse survey, section 4 (evict blocks by attention
+ * score: sort by mean score, lowest first, stable, and evict the first
+ * int(n * (1 - retention)); evicted blocks release their reference) and
+ * "KV Cache optimization techniques" tutorial, section 3.2 (block table,
+ * reference counts).
+ *
+ * For each sequence b with L = min(src->lengths[b], max_len_hint) and
+ * n = ceil(L / 16) blocks: a block's score is the mean of h2o_score over its
+ * filled slots and all KV heads (fp32, heads then slots in order); with
+ * n_evict = (int)(n * (1 - retention)) in double arithmetic, the n_evict
+ * blocks first in ascending order of score (equal scores: lower block index
+ * first) are evicted. dst's table row b lists the kept physical blocks in
+ * their order, then -1; dst->lengths[b] counts their tokens (the last block
+ * may be partial and stays last); dst->num_seen[b] = src->num_seen[b];
+ * dst_score[b][h] holds the kept blocks' scores at their new slots (slots at
+ * or past the new length untouched); freed[b][0..n_evict) lists the evicted
+ * physical blocks in block order and freed_count[b] = n_evict (give them back
+ * with kvc_pool_release).
+ *
+ * src and dst are paged caches with the same geometry that share the code and
+ * scale pools; dst's block table, lengths and num_seen are its own (device
+ * buffers the call writes). Cost: n^2 comparisons per sequence in one
+ * workgroup, sized for decode-length tables.
+ * Errors: INVALID_ARG for bad or contiguous descriptors, different
+ * geometries or pools, NULL arrays, retention outside [0, 1], overlapping
+ * inputs and outputs; CAPACITY if max_len_hint > capacity; UNSUPPORTED above
+ * 8192 blocks per sequence.
+ */
+int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, double retention,
+                              const kvc_cache_t* dst, float* dst_score, int32_t* freed,
+                              int32_t* freed_count, int32_t max_len_hint, void* stream);
+
+/*
  * Per-layer keep budgets (host only): the pyramid schedules of the pages.
  * Sources: "KV Cache optimization techniques" tutorial, section 2.3
  * (PyramidKV, linear: layer l of n keeps the fraction 1 - 0.8 l / n, shallow
@@ -391,6 +426,15 @@ int32_t kvc_pool_reserve(kvc_pool_t* pool, int32_t seq_id, int32_t num_tokens);
 int32_t kvc_pool_free(kvc_pool_t* pool, int32_t seq_id);
 
 /* Blocks on the free list (-1 for a NULL pool). */
+/* Give back blocks of sequence seq_id (the blocks kvc_paged_block_evict frees):
+ * each is removed from the sequence's list, whose other blocks keep their
+ * order, and its reference count drops; at zero it returns to the free set
+ * (tutorial section 3.2; eviction-and-reuse survey, section 4: evicted blocks
+ * release their reference). All or nothing: INVALID_ARG and no change for an
+ * unknown sequence, a NULL list with n > 0, n < 0, or a block the sequence
+ * does not hold (each listed once). */
+int32_t kvc_pool_release(kvc_pool_t* pool, int32_t seq_id, const int32_t* blocks_host, int32_t n);
+
 int32_t kvc_pool_num_free(const kvc_pool_t* pool);
 
 /* Blocks held by seq_id, or -1 if it is unknown. */

@@ -20,6 +20,8 @@ What it computes, and the page passage each part follows:
 * ``cache``     a reference cache and the decode-step schedule
 * ``schedule``  per-layer keep budgets, the pyramid schedules (tutorial
                 §2.3; eviction-and-reuse survey §4)
+* ``blocks``    block-granular H2O eviction on a paged cache (survey §4;
+                tutorial §3.2)
 
 Floating point is fp64 throughout, except where the method fixes fp32: the
 quantization scale and the quotient that is rounded to a code, both taken as
@@ -31,6 +33,7 @@ invariants, brute force on tiny inputs and the values the pages print.
 from .attention import attend_head_group, decode_attention, paged_decode_attention, paged_gather
 from .cache import RefCache, paged_append
 from .eviction import compact_row, h2o_accumulate, kth_threshold, select_keep
+from .blocks import block_evict, move_block_scores
 from .schedule import layer_budgets
 from .quant import (QMAX, QMIN, compressed_bytes_per_token_head, dequantize, kv_bytes_per_token,
                     pack_int4, quantize_rows, unpack_int4)
@@ -40,5 +43,5 @@ __all__ = [
     "kv_bytes_per_token", "compressed_bytes_per_token_head",
     "attend_head_group", "decode_attention", "paged_decode_attention", "paged_gather",
     "h2o_accumulate", "select_keep", "kth_threshold", "compact_row",
-    "RefCache", "paged_append", "layer_budgets",
+    "RefCache", "paged_append", "layer_budgets", "block_evict", "move_block_scores",
 ]

@@ -134,6 +134,30 @@ def test_append_decode_attn_validation():
                                       None) == INVALID
 
 
+def test_paged_block_evict_validation():
+    src = desc(block_size=16, max_blocks_per_seq=32, num_blocks=64, positions=None, block_table=0xA000000,
+               lengths=0xA100000, num_seen=0xA100100)
+    dst = desc(block_size=16, max_blocks_per_seq=32, num_blocks=64, positions=None, block_table=0xB000000,
+               lengths=0xB100000, num_seen=0xB100100)
+    call = lambda s_=src, d_=dst, sc=0xC000000, dsc=0xD000000, fr=0xE000000, fc=0xE100000, r=0.5, hint=100: \
+        lib.kvc_paged_block_evict(ctypes.byref(s_), sc, r, ctypes.byref(d_), dsc, fr, fc, hint, None)
+    assert call(r=1.5) == INVALID
+    assert call(r=float("nan")) == INVALID
+    assert call(sc=None) == INVALID
+    assert call(fr=None) == INVALID
+    assert call(hint=-1) == INVALID
+    assert call(hint=513) == CAPACITY
+    other_pool = desc(block_size=16, max_blocks_per_seq=32, num_blocks=64, positions=None, block_table=0xB000000,
+                      lengths=0xB100000, num_seen=0xB100100, k_codes=0xF000000)
+    assert call(d_=other_pool) == INVALID            # dst must share the pools
+    same_table = desc(block_size=16, max_blocks_per_seq=32, num_blocks=64, positions=None, block_table=0xA000000,
+                      lengths=0xB100000, num_seen=0xB100100)
+    assert call(d_=same_table) == INVALID            # out of place
+    assert call(dsc=0xC000000) == INVALID            # dst scores on the src scores
+    assert call(fr=0xB000000) == INVALID             # freed list on dst's table
+    assert call(s_=desc(), d_=desc()) == INVALID     # contiguous caches
+
+
 def test_bw_probe_validation():
     n = lib.kvc_bw_probe_sink_bytes()
     assert n >= 4

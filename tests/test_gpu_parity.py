@@ -650,6 +650,69 @@ def test_paged_decode_reduced(bits):
     assert rb == kc.shape[-1]
 
 
+def test_paged_block_evict():
+    """Block-granular eviction: the rewritten table, lengths, freed blocks and
+    moved scores equal the oracle's (exact ties included), attention through
+    the new table equals the oracle's over the kept tokens, and the freed
+    blocks go back to the pool."""
+    B, H, Hq, D, bs = 3, 4, 8, 128, 16
+    lens = np.array([333, 160, 17])
+    mb = 24
+    pool = kvc.BlockPool(80, bs, shuffle_seed=99)
+    for b in range(B):
+        pool.reserve(b, int(lens[b]))
+    table = pool.block_table(list(range(B)), mb)
+    gc = kvc.KVCache(B, H, D, 0, 8, block_size=bs, num_blocks=80, max_blocks_per_seq=mb)
+    gc.block_table.copy_(dev(table))
+    rng = np.random.default_rng(23)
+    kp, vp = np.zeros((80, H, bs, D), np.int8), np.zeros((80, H, bs, D), np.int8)
+    ksp, vsp = np.zeros((80, H, bs), np.float32), np.zeros((80, H, bs), np.float32)
+    for b in range(B):
+        k16 = rng.standard_normal((1, H, int(lens[b]), D)).astype(np.float16)
+        v16 = rng.standard_normal((1, H, int(lens[b]), D)).astype(np.float16)
+        one = kvc.KvcCacheDesc.from_buffer_copy(gc.desc)
+        one.batch = 1
+        one.block_table = gc.block_table[b].data_ptr()
+        one.lengths = gc.lengths[b:b + 1].data_ptr()
+        one.num_seen = gc.num_seen[b:b + 1].data_ptr()
+        kvc.kvc_quant_append(one, dev(k16), dev(v16), max_len_hint=0)
+        oracle.paged_append(kp, ksp, vp, vsp, table[b:b + 1], np.zeros(1, np.int64), k16, v16, 8, bs)
+    cap = gc.capacity
+    sc = rng.random((B, H, cap)).astype(np.float32)
+    sc[0, :, 5 * bs:6 * bs] = sc[0, :, 2 * bs:3 * bs]      # exact tie between blocks 2 and 5
+    sc[1, :, 0:bs] = sc[1, :, 7 * bs:8 * bs]               # and between blocks 0 and 7
+    score = dev(sc)
+    dst = gc.table_view()
+    dst_score = torch.full((B, H, cap), -3.0, dtype=torch.float32, device="cuda")
+    freed = torch.full((B, mb), -9, dtype=torch.int32, device="cuda")
+    fcount = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    retention = 0.6
+    kvc.kvc_paged_block_evict(gc, score, retention, dst, dst_score, freed, fcount, max_len_hint=int(lens.max()))
+    torch.cuda.synchronize()
+    new_table, new_lens = host(dst.block_table), host(dst.lengths)
+    fr, fc, ds = host(freed), host(fcount), host(dst_score)
+    want_table = np.zeros_like(table)
+    for b in range(B):
+        row, nl, fb, kept = oracle.block_evict(list(table[b]), int(lens[b]), sc[b].astype(np.float64), retention)
+        want_table[b] = row
+        assert new_table[b].tolist() == row, b
+        assert int(new_lens[b]) == nl and int(fc[b]) == len(fb), b
+        assert fr[b, :len(fb)].tolist() == fb and np.all(fr[b, len(fb):] == -9), b
+        moved = oracle.move_block_scores(sc[b], kept, int(lens[b]))
+        assert np.array_equal(ds[b, :, :nl], moved[:, :nl]), b
+        assert np.all(ds[b, :, nl:] == -3.0), b
+        pool.release(b, fb)
+    assert host(dst.num_seen).tolist() == lens.tolist()
+    assert pool.num_free == 80 - sum(int(x) for x in ((new_lens + bs - 1) // bs))
+    assert pool.block_table(list(range(B)), mb).tolist() == want_table.tolist()
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    kvc.kvc_decode_attn(dst, dev(q), out, max_len_hint=int(new_lens.max()))
+    ro = oracle.paged_decode_attention(q, kp, ksp, vp, vsp, want_table, new_lens.astype(np.int64), bs)
+    torch.cuda.synchronize()
+    assert_out_close(host(out), ro)
+
+
 # ------------------------------------------------ full-size configurations --
 # The larger workloads run at full size on the GPU, in the launch configuration
 # the library picks for them; the oracle checks sampled sequences or rows
