@@ -18,12 +18,13 @@ model), so every launch streams its 66 MiB from HBM rather than from the
 
 The timed region replays one HIP graph per 32-layer block in decode order:
 rewind the lengths, then each layer's step. `value` and `ms_per_step` come
-from it. The same steps then run again as the separate calls, two graphs per
-block, one per phase ([rewind + 32 kvc_append_decode_attn] [32
-kvc_h2o_evict]; the attention's own merge kernel runs there), with HIP events
-between the phases: they give
-each phase's time ("phases") and the attention kernels' average duration, from
-which the roofline fraction is computed.
+from it. The same steps then run again as separate calls, three graphs per
+block, one per phase ([rewind + 32 kvc_decode_attn_split with the append]
+[32 kvc_decode_attn_merge] [32 kvc_h2o_evict]), with HIP events between the
+phases: they give
+each phase's time ("phases") and the split kernel's average duration, from
+which the roofline fraction is computed (the split kernel streams the KV
+cache; it is the same kernel the step launches).
 
 Prints one JSON line. Run ``python bench.py --help`` for options.
 """
@@ -43,17 +44,17 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn KV GB/s & tokens/s (fraction of HBM peak), INT8, L=8192, 1 GPU"
 
-# HBM bytes one decode-attention launch (split + combine) moves on this
-# workload, from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by the same
-# counters on a plain 64 MiB device copy. The figure holds only for the
-# attention sources it was taken on; any change to them reports null.
+# HBM bytes one launch of the split attention kernel moves on this workload,
+# from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by the same counters
+# on a plain 64 MiB device copy. The figure holds only for the attention
+# sources it was taken on; any change to them reports null.
 TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/kvc_internal.h",
                    "compressed_kv_cache_kvc_amd/csrc/quant_row.h",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "12ac5a5362188d4f0fa70dffa356be2734dc4c5d1e5419cab2c852503500400c"
-TRAFFIC_BYTES = 74350398
+TRAFFIC_SHA256 = "5fdb6809371b457a3e30bf75537301492b553aea333a6f961803596f947c7311"
+TRAFFIC_BYTES = 70765042
 
 
 def attention_traffic():
@@ -73,7 +74,8 @@ def step_bytes(B, Hq, H, D, bits, L, budget):
     kv = B * H * L * 2 * (rb + 4)                        # codes + fp32 scales, K and V
     parts = {
         "append": B * H * (2 * D * 2 + 2 * (rb + 4) + 4 + 4),   # fp16 in; codes, scales, position, score out
-        "attention": kv + B * Hq * D * 2 + B * Hq * D * 4,      # KV + q (fp16) + out (fp32)
+        "attention": kv + B * Hq * D * 2,                       # KV + q (fp16)
+        "out": B * Hq * D * 4,                                  # out (fp32)
         "h2o": 2 * B * H * L * 4,                                # score read-modify-write
         # scores in; mask and keep list out; kept rows (codes, scales, position, score) in and out
         "evict": B * H * (L * 4 + L + budget * 4) + 2 * B * H * budget * (2 * (rb + 4) + 8),
@@ -83,14 +85,14 @@ def step_bytes(B, Hq, H, D, bits, L, budget):
 
 def phase_table(phase_ms, steps, parts, attn_alg):
     """Per-phase time and HBM roofline fraction of one step. Each phase is one
-    replayed graph (two launches per layer buffer for the append and attention,
-    one for eviction) timed with events on the replay stream; bytes are the
-    phase's algorithmic bytes: the append's inputs and cache writes, the KV
-    stream and q as in the roofline entry, and the H2O score
-    read-modify-write; eviction counts the selection's score reads, mask and
-    keep-list writes and the compaction's kept rows in and out."""
-    names = ("append_attention", "evict")
-    alg = (parts["append"] + attn_alg + parts["h2o"], parts["evict"])
+    replayed graph (one launch per layer buffer) timed with events on the
+    replay stream; bytes are the phase's algorithmic bytes: the split kernel
+    moves the append's inputs and cache writes, the KV stream and q (the
+    roofline entry's bytes); the merge the H2O score read-modify-write and the
+    output; eviction the selection's score reads, mask and keep-list writes
+    and the compaction's kept rows in and out."""
+    names = ("attention_split", "attention_merge", "evict")
+    alg = (parts["append"] + attn_alg, parts["h2o"] + parts["out"], parts["evict"])
     table = {}
     for name, ms, b in zip(names, phase_ms, alg):
         us = ms * 1e3 / steps
@@ -375,14 +377,21 @@ def main(argv=None):
                           device="cuda")
     torch.cuda.synchronize()
 
-    def append_attn(i):
-        kvc.kvc_append_decode_attn(caches[i], k_new, v_new, q, out, h2o_score=scores[i], max_len_hint=L - 1,
-                                   workspace=ws_attn)
+    # Phase by phase, the attention runs as its two calls, split (with the
+    # append) then merge; each layer buffer has its own workspace, since all
+    # 32 splits run before the first merge.
+    ws_layers = [torch.zeros_like(ws_attn) for _ in range(LAYERS)]
 
-    def phase_attn():
+    def phase_split():
         lengths_all.fill_(L - 1)
         for i in range(LAYERS):
-            append_attn(i)
+            kvc.kvc_decode_attn_split(caches[i], q, ws_layers[i], k_new=k_new, v_new=v_new, h2o_score=scores[i],
+                                      max_len_hint=L - 1)
+
+    def phase_merge():
+        for i in range(LAYERS):
+            kvc.kvc_decode_attn_merge(caches[i], Hq, out, ws_layers[i], appended=True, h2o_score=scores[i],
+                                      max_len_hint=L - 1)
 
     def evict(i):
         kvc.kvc_h2o_evict(caches[i], scores[i], budget, S, R, keep_lists[i], dst, dst_score, keep_mask=masks[i],
@@ -416,7 +425,7 @@ def main(argv=None):
         return g
 
     g_whole = capture(whole_block)
-    graphs = [capture(fn) for fn in (phase_attn, phase_evict)]
+    graphs = [capture(fn) for fn in (phase_split, phase_merge, phase_evict)]
     torch.cuda.synchronize()
 
     blocks_w = max(1, (args.warmup + LAYERS - 1) // LAYERS)
@@ -502,7 +511,8 @@ def main(argv=None):
         "ms_per_step_phase_by_phase": round(by_phase_ms / steps, 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode attention with the new token's append (attn_split_kernel + attn_combine_kernel)",
+            "kernel": "attn_split_kernel: the KV stream of the step (with the new token's append), timed through "
+                  "kvc_decode_attn_split",
             "achieved": round(attn_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

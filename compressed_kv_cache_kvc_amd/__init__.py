@@ -63,6 +63,8 @@ def _load():
         "kvc_decode_attn_workspace_bytes": (SZ, [D, I32, I32, I32]),
         "kvc_decode_attn": (I32, [D, P, I32, P, P, I32, P, SZ, P]),
         "kvc_append_decode_attn": (I32, [D, P, P, P, I32, P, P, I32, P, SZ, P]),
+        "kvc_decode_attn_split": (I32, [D, P, P, P, I32, P, I32, P, SZ, P]),
+        "kvc_decode_attn_merge": (I32, [D, I32, I32, P, P, I32, P, SZ, P]),
         "kvc_h2o_select": (I32, [D, P, I32, I32, I32, P, P, I32, P]),
         "kvc_compact_workspace_bytes": (SZ, [D, I32]),
         "kvc_compact": (I32, [D, P, P, D, P, I32, P, SZ, P]),
@@ -286,6 +288,40 @@ def kvc_append_decode_attn(cache, k_new, v_new, q, out, h2o_score=None, max_len_
                                       _ptr(h2o_score), max_len_hint, _ptr(workspace), workspace.numel(),
                                       _stream(stream)), "kvc_append_decode_attn")
     if isinstance(cache, KVCache):
+        cache.max_len = max_len_hint + 1
+
+
+def kvc_decode_attn_split(cache, q, workspace, k_new=None, v_new=None, h2o_score=None,
+                          max_len_hint: Optional[int] = None, stream=None):
+    """The split phase of the attention (with the new token's append when
+    ``k_new``/``v_new`` are given); finish with ``kvc_decode_attn_merge``."""
+    import torch
+    d = _desc(cache)
+    Hq = q.shape[1]
+    _need(q, torch.float16, "q", d.batch * Hq * d.head_dim)
+    _need(k_new, torch.float16, "k_new", d.batch * d.num_kv_heads * d.head_dim)
+    _need(v_new, torch.float16, "v_new", d.batch * d.num_kv_heads * d.head_dim)
+    _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    _check(lib.kvc_decode_attn_split(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, _ptr(h2o_score),
+                                     max_len_hint, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "kvc_decode_attn_split")
+
+
+def kvc_decode_attn_merge(cache, num_q_heads: int, out, workspace, appended: bool = False, h2o_score=None,
+                          max_len_hint: Optional[int] = None, stream=None):
+    """The merge phase after ``kvc_decode_attn_split`` (see kvc.h)."""
+    import torch
+    d = _desc(cache)
+    _need(out, torch.float32, "out", d.batch * num_q_heads * d.head_dim)
+    _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    _check(lib.kvc_decode_attn_merge(ctypes.byref(d), int(bool(appended)), num_q_heads, _ptr(out), _ptr(h2o_score),
+                                     max_len_hint, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "kvc_decode_attn_merge")
+    if appended and isinstance(cache, KVCache):
         cache.max_len = max_len_hint + 1
 
 

@@ -235,6 +235,7 @@ int32_t prepare_attn(const kvc_cache_t* cache, const void* k_new, const void* v_
   a->k_new = static_cast<const __half*>(k_new);
   a->v_new = static_cast<const __half*>(v_new);
   a->stash = reinterpret_cast<int32_t*>(ws + g.off_stash);
+  a->append = k_new != nullptr;
   a->num_q_heads = num_q_heads;
   a->splits = g.splits;
   a->tiles = g.tiles;
@@ -336,6 +337,45 @@ int32_t kvc_decode_attn(const kvc_cache_t* cache, const void* q, int32_t num_q_h
   clear_error();
   return decode_attn_call(cache, nullptr, nullptr, q, num_q_heads, out, h2o_score, max_len_hint, workspace,
                           workspace_bytes, stream);
+}
+
+int32_t kvc_decode_attn_split(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                              int32_t num_q_heads, float* h2o_score, int32_t max_len_hint, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  clear_error();
+  int32_t st = check_cache(cache, "cache");
+  if (st) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(KVC_ERR_INVALID_ARG, "pass both k_new and v_new, or neither");
+  const int app = k_new != nullptr;
+  if (max_len_hint < 0 || (!app && max_len_hint < 1)) return fail(KVC_ERR_INVALID_ARG, "bad max_len_hint");
+  if ((long long)max_len_hint + app > cache->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
+  float dummy_out;
+  AttnLaunch a;
+  if ((st = prepare_attn(cache, k_new, v_new, q, num_q_heads, &dummy_out, h2o_score, max_len_hint + app, workspace,
+                         workspace_bytes, &a)))
+    return st;
+  a.out = nullptr;
+  return device_status(launch_attn_split(a, static_cast<hipStream_t>(stream)), "kvc_decode_attn_split launch");
+}
+
+int32_t kvc_decode_attn_merge(const kvc_cache_t* cache, int32_t appended, int32_t num_q_heads, float* out,
+                              float* h2o_score, int32_t max_len_hint, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  clear_error();
+  int32_t st = check_cache(cache, "cache");
+  if (st) return st;
+  const int app = appended != 0;
+  if (max_len_hint < 0 || (!app && max_len_hint < 1)) return fail(KVC_ERR_INVALID_ARG, "bad max_len_hint");
+  if ((long long)max_len_hint + app > cache->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
+  // The merge reads no q (the shared checks want one: the workspace stands
+  // in) and no new token; `appended` says where the lengths come from.
+  AttnLaunch a;
+  if ((st = prepare_attn(cache, nullptr, nullptr, workspace, num_q_heads, out, h2o_score, max_len_hint + app,
+                         workspace, workspace_bytes, &a)))
+    return st;
+  a.q = nullptr;
+  a.append = app;
+  return device_status(launch_attn_merge(a, static_cast<hipStream_t>(stream)), "kvc_decode_attn_merge launch");
 }
 
 int32_t kvc_append_decode_attn(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,

@@ -605,7 +605,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const long long span = (long long)S * a.tiles * TS;
   // With an append, the length before it comes from the split kernel (the
   // cache's own length is advanced here, by one workgroup).
-  const bool app = a.k_new != nullptr;
+  const bool app = a.append != 0;
   const int L = __builtin_amdgcn_readfirstlane(
       min(min(app ? a.stash[b] + 1 : c.lengths[b], c.capacity), (int)span));
   const bool out_block = x < G;

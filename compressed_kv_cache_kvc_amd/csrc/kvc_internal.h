@@ -42,6 +42,7 @@ struct AttnLaunch {
   const __half* k_new;
   const __half* v_new;
   int32_t* stash;    // [2][B]: lengths and num_seen before the append
+  int append;        // the split appended (the merge takes the lengths from stash)
   int num_q_heads;
   int splits;        // S: workgroups per (sequence, KV head)
   int tiles;         // 256-token tiles per split

@@ -201,6 +201,29 @@ int32_t kvc_append_decode_attn(const kvc_cache_t* cache, const void* k_new, cons
                                void* stream);
 
 /*
+ * The two phases of the attention calls, for callers that schedule them
+ * apart (flash-decoding split and merge; same sources as kvc_decode_attn):
+ * kvc_decode_attn_split runs the split kernel (with k_new and v_new, both
+ * non-NULL, it first appends the new token, as kvc_append_decode_attn does)
+ * and leaves its partial results in the workspace; kvc_decode_attn_merge
+ * (appended = whether the split appended) merges them into `out`, applies the
+ * H2O update and, after an append, advances lengths and num_seen. The pair,
+ * with the same cache, heads, h2o_score (NULL or not), max_len_hint and
+ * workspace, and nothing between them that touches those, equals
+ * kvc_decode_attn (or kvc_append_decode_attn) bit for bit. max_len_hint is as
+ * in those calls (the length before the append, if any).
+ * Errors: as kvc_decode_attn / kvc_append_decode_attn; INVALID_ARG if only
+ * one of k_new, v_new is given.
+ */
+int32_t kvc_decode_attn_split(const kvc_cache_t* cache, const void* k_new, const void* v_new,
+                              const void* q, int32_t num_q_heads, float* h2o_score,
+                              int32_t max_len_hint, void* workspace, size_t workspace_bytes,
+                              void* stream);
+int32_t kvc_decode_attn_merge(const kvc_cache_t* cache, int32_t appended, int32_t num_q_heads,
+                              float* out, float* h2o_score, int32_t max_len_hint, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Keep-set selection: attention sinks + recent window + heavy hitters.
  * Sources: "KV Cache Compression Report", section 3.3 (the first 4 tokens
  * are permanent attention sinks, a window keeps the most recent tokens) and

@@ -225,6 +225,40 @@ def test_append_decode_attn_bit_exact(hq, hkv, bits, D, lens, h2o, cap_extra):
         assert_scores_close(host(sB), ref.score, ref.lengths)
 
 
+@pytest.mark.parametrize("append", [False, True])
+def test_split_then_merge_equals_one_call(append):
+    """kvc_decode_attn_split + kvc_decode_attn_merge equal kvc_decode_attn
+    (or, with the new token, kvc_append_decode_attn) bit for bit: output,
+    scores and every cache buffer."""
+    B, H, Hq, D, L = 2, 4, 8, 128, 1500
+    w = get("tiny_mha").scaled(context=L + 1, batch=B, num_q_heads=Hq, num_kv_heads=H, head_dim=D, bits=8)
+    d = draw(w)
+    runs = []
+    for two_phase in (False, True):
+        gc = make_gpu_cache(w, L + 1)
+        sc = gc.score_buffer()
+        kvc.kvc_quant_append(gc, dev(d["k"][:, :, :L]), dev(d["v"][:, :, :L]), h2o_score=sc)
+        sc.copy_(torch.rand_like(sc, generator=torch.Generator(device="cuda").manual_seed(5)))
+        q = dev(d["q"])
+        kn, vn = (dev(d["k"][:, :, L:]), dev(d["v"][:, :, L:])) if append else (None, None)
+        ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(gc, Hq, L + 1, True), dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        if not two_phase:
+            if append:
+                kvc.kvc_append_decode_attn(gc, kn, vn, q, out, h2o_score=sc, max_len_hint=L, workspace=ws)
+            else:
+                kvc.kvc_decode_attn(gc, q, out, h2o_score=sc, max_len_hint=L, workspace=ws)
+        else:
+            kvc.kvc_decode_attn_split(gc, q, ws, k_new=kn, v_new=vn, h2o_score=sc, max_len_hint=L)
+            kvc.kvc_decode_attn_merge(gc, Hq, out, ws, appended=append, h2o_score=sc, max_len_hint=L)
+        torch.cuda.synchronize()
+        runs.append((gc, sc, out))
+    (ga, sa, oa), (gb, sb, ob) = runs
+    assert torch.equal(oa, ob)
+    _assert_same_cache(ga, gb, sa, sb)
+    assert host(gb.lengths).tolist() == [L + int(append)] * B
+
+
 def test_append_decode_attn_paged():
     """Paged cache (16-token blocks, seeded block placement): the one-call
     step equals the two calls bit for bit."""
