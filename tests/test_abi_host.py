@@ -171,6 +171,24 @@ def test_bw_probe_validation():
     assert probe(sink=FAKE * 16 + 64) == INVALID       # inside src
 
 
+def test_split_and_merge_validation():
+    d = desc()
+    need = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), 4, 17, 1)
+    split = lambda k=None, v=None, q=FAKE, hint=16, ws=FAKE * 256, n=need: lib.kvc_decode_attn_split(
+        ctypes.byref(d), k, v, q, 4, 0x9000000, hint, ws, n, None)
+    merge = lambda app=0, out=FAKE, hint=16, ws=FAKE * 256, n=need: lib.kvc_decode_attn_merge(
+        ctypes.byref(d), app, 4, out, 0x9000000, hint, ws, n, None)
+    assert split(k=FAKE) == INVALID                   # k_new without v_new
+    assert split(q=None) == INVALID
+    assert split(hint=0) == INVALID                   # no token to attend without an append
+    assert split(k=FAKE, v=FAKE, hint=512) == CAPACITY
+    assert split(n=need - 1, k=FAKE, v=FAKE) == INVALID
+    assert merge(out=None) == INVALID
+    assert merge(hint=0) == INVALID
+    assert merge(app=1, hint=512) == CAPACITY
+    assert merge(ws=None) == INVALID
+
+
 def test_select_validation():
     d = desc()
     sel = lambda budget, s, r, hint=16, score=FAKE, mask=FAKE: lib.kvc_h2o_select(
