@@ -40,6 +40,7 @@ class KvcCacheDesc(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("lengths", ctypes.c_void_p), ("num_seen", ctypes.c_void_p),
         ("positions", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("v_bits", ctypes.c_int32),
     ]
 
 
@@ -156,7 +157,8 @@ def _need(t, dtype, name, numel=None):
 class KVCache:
     """Device buffers of one compressed cache (one layer) and its descriptor.
 
-    Contiguous layout (``block_size=0``): codes ``[B][Hkv][capacity][RB]`` uint8,
+    Contiguous layout (``block_size=0``): codes ``[B][Hkv][capacity][RB]`` uint8
+    (RB = head_dim * bits / 8 for K, with ``v_bits`` (if set) for V),
     scales ``[B][Hkv][capacity]`` fp32, positions int32 of the same shape.
     Paged layout (``block_size=16``): codes ``[num_blocks][Hkv][16][RB]``,
     scales ``[num_blocks][Hkv][16]``, a ``[B][max_blocks]`` int32 block table,
@@ -165,11 +167,13 @@ class KVCache:
 
     def __init__(self, batch: int, num_kv_heads: int, head_dim: int, capacity: int, bits: int = 8,
                  device="cuda", block_size: int = 0, num_blocks: int = 0, max_blocks_per_seq: int = 0,
-                 positions: bool = True):
+                 positions: bool = True, v_bits: int = 0):
         import torch
         self.batch, self.num_kv_heads, self.head_dim, self.bits = batch, num_kv_heads, head_dim, bits
+        self.v_bits = v_bits            # 0: V at the K width
         self.block_size = block_size
         rb = row_bytes(head_dim, bits)
+        rbv = row_bytes(head_dim, v_bits or bits)
         if block_size:
             self.capacity = max_blocks_per_seq * block_size
             rows = (num_blocks, num_kv_heads, block_size)
@@ -182,7 +186,7 @@ class KVCache:
             self.positions = torch.zeros(rows, dtype=torch.int32, device=device) if positions else None
         self.num_blocks, self.max_blocks_per_seq = num_blocks, max_blocks_per_seq
         self.k_codes = torch.zeros(rows + (rb,), dtype=torch.uint8, device=device)
-        self.v_codes = torch.zeros(rows + (rb,), dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros(rows + (rbv,), dtype=torch.uint8, device=device)
         self.k_scale = torch.zeros(rows, dtype=torch.float32, device=device)
         self.v_scale = torch.zeros(rows, dtype=torch.float32, device=device)
         self.lengths = torch.zeros(batch, dtype=torch.int32, device=device)
@@ -193,6 +197,7 @@ class KVCache:
     def _make_desc(self) -> KvcCacheDesc:
         d = KvcCacheDesc()
         d.bits, d.batch, d.num_kv_heads, d.head_dim = self.bits, self.batch, self.num_kv_heads, self.head_dim
+        d.v_bits = self.v_bits
         d.capacity, d.block_size = self.capacity, self.block_size
         d.max_blocks_per_seq, d.num_blocks = self.max_blocks_per_seq, self.num_blocks
         d.k_codes, d.v_codes = _ptr(self.k_codes), _ptr(self.v_codes)

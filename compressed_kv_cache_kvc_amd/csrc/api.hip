@@ -52,6 +52,8 @@ int32_t device_status(hipError_t e, const char* what) {
 int32_t check_cache(const kvc_cache_t* c, const char* name) {
   if (!c) return fail(KVC_ERR_INVALID_ARG, "%s is NULL", name);
   if (c->bits != 8 && c->bits != 4) return fail(KVC_ERR_INVALID_ARG, "%s: bits must be 8 or 4 (got %d)", name, c->bits);
+  if (c->v_bits != 0 && c->v_bits != 8 && c->v_bits != 4)
+    return fail(KVC_ERR_INVALID_ARG, "%s: v_bits must be 0, 8 or 4 (got %d)", name, c->v_bits);
   if (c->batch < 1 || c->num_kv_heads < 1)
     return fail(KVC_ERR_INVALID_ARG, "%s: batch and num_kv_heads must be >= 1", name);
   if (c->head_dim != 64 && c->head_dim != 128) {
@@ -95,7 +97,7 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
   if (G > 16) return fail(KVC_ERR_INVALID_ARG, "more than 16 query heads per KV head");
   if (hint < 1) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 1");
   if (hint > c->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint %d exceeds capacity %d", hint, c->capacity);
-  const long long rb = (long long)c->head_dim * c->bits / 8;
+  const long long rb = std::max(k_row_bytes(*c), v_row_bytes(*c));
   if ((long long)c->capacity * rb >= (1LL << 32) - 4096)
     return fail(KVC_ERR_UNSUPPORTED, "one (sequence, KV head) row must stay below 4 GiB");
   if (c->block_size && (long long)c->num_blocks * c->num_kv_heads * c->block_size * rb >= (1LL << 32))
@@ -129,14 +131,14 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 int32_t check_out_of_place(const kvc_cache_t* src, const float* src_score, const void* keep, size_t keep_bytes,
                            const kvc_cache_t* dst, const float* dst_score, const void* workspace, size_t ws_bytes) {
   const size_t rows = (size_t)src->batch * src->num_kv_heads * src->capacity;
-  const size_t RB = (size_t)src->head_dim * src->bits / 8;
+  const size_t RBK = k_row_bytes(*src), RBV = v_row_bytes(*src);
   const void* s_bufs[] = {src->k_codes, src->v_codes, src->k_scale, src->v_scale, src->positions, src_score,
                           keep, src->lengths, src->num_seen};
-  const size_t s_len[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, keep_bytes,
+  const size_t s_len[] = {rows * RBK, rows * RBV, rows * 4, rows * 4, rows * 4, rows * 4, keep_bytes,
                           (size_t)src->batch * 4, (size_t)src->batch * 4};
   const void* d_bufs[] = {dst->k_codes, dst->v_codes, dst->k_scale, dst->v_scale, dst->positions, dst_score,
                           dst->lengths, dst->num_seen, workspace};
-  const size_t d_len[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, (size_t)src->batch * 4,
+  const size_t d_len[] = {rows * RBK, rows * RBV, rows * 4, rows * 4, rows * 4, rows * 4, (size_t)src->batch * 4,
                           (size_t)src->batch * 4, ws_bytes};
   for (int i = 0; i < 9; ++i)
     for (int j = 0; j < 9; ++j)
@@ -152,8 +154,8 @@ int32_t check_compact_pair(const kvc_cache_t* src, const kvc_cache_t* dst, const
   if (st) return st;
   if ((st = check_cache(dst, "dst"))) return st;
   if (src->block_size || dst->block_size) return fail(KVC_ERR_UNSUPPORTED, "compaction of paged caches is not built");
-  if (src->bits != dst->bits || src->batch != dst->batch || src->num_kv_heads != dst->num_kv_heads ||
-      src->head_dim != dst->head_dim || src->capacity != dst->capacity)
+  if (src->bits != dst->bits || vbits_of(*src) != vbits_of(*dst) || src->batch != dst->batch ||
+      src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim || src->capacity != dst->capacity)
     return fail(KVC_ERR_INVALID_ARG, "src and dst geometries differ");
   if ((src_score == nullptr) != (dst_score == nullptr))
     return fail(KVC_ERR_INVALID_ARG, "pass both src_score and dst_score, or neither");
@@ -260,12 +262,12 @@ int32_t check_workspace_disjoint(const void* ws, size_t ws_bytes, const kvc_cach
                                  const kvc_cache_t* d, const float* d_score, const void* keep_index,
                                  size_t keep_bytes, const void* keep_mask, size_t mask_bytes) {
   const size_t rows = (size_t)c->batch * c->num_kv_heads * c->capacity;
-  const size_t RB = (size_t)c->head_dim * c->bits / 8;
+  const size_t RBK = k_row_bytes(*c), RBV = v_row_bytes(*c);
   const void* bufs[] = {c->k_codes, c->v_codes, c->k_scale, c->v_scale, c->positions, c_score, c->lengths,
                         c->num_seen, d->k_codes, d->v_codes, d->k_scale, d->v_scale, d->positions, d_score,
                         d->lengths, d->num_seen, keep_index, keep_mask};
-  const size_t lens[] = {rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4, (size_t)c->batch * 4,
-                         (size_t)c->batch * 4, rows * RB, rows * RB, rows * 4, rows * 4, rows * 4, rows * 4,
+  const size_t lens[] = {rows * RBK, rows * RBV, rows * 4, rows * 4, rows * 4, rows * 4, (size_t)c->batch * 4,
+                         (size_t)c->batch * 4, rows * RBK, rows * RBV, rows * 4, rows * 4, rows * 4, rows * 4,
                          (size_t)c->batch * 4, (size_t)c->batch * 4, keep_bytes, mask_bytes};
   for (int i = 0; i < 18; ++i)
     if (overlap(ws, ws_bytes, bufs[i], lens[i]))
@@ -464,8 +466,8 @@ int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, do
   if ((st = check_cache(dst, "dst"))) return st;
   if (src->block_size == 0 || dst->block_size == 0)
     return fail(KVC_ERR_INVALID_ARG, "block eviction needs paged caches");
-  if (src->bits != dst->bits || src->batch != dst->batch || src->num_kv_heads != dst->num_kv_heads ||
-      src->head_dim != dst->head_dim || src->capacity != dst->capacity ||
+  if (src->bits != dst->bits || vbits_of(*src) != vbits_of(*dst) || src->batch != dst->batch ||
+      src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim || src->capacity != dst->capacity ||
       src->max_blocks_per_seq != dst->max_blocks_per_seq || src->num_blocks != dst->num_blocks)
     return fail(KVC_ERR_INVALID_ARG, "src and dst geometries differ");
   if (src->k_codes != dst->k_codes || src->v_codes != dst->v_codes || src->k_scale != dst->k_scale ||

@@ -11,9 +11,10 @@
 // from the mask (one launch); longer rows get a first launch that writes
 // per-chunk counts. A block scan of the chunk's flags gives each kept slot its
 // destination and lists the kept slots in LDS; the rows are then copied
-// cooperatively, RB/16 lanes per row with 16-byte accesses, and every load of
-// the chunk is issued before the first store so that the copy is bound by
-// bandwidth rather than latency. Reading src and writing dst, which may not
+// cooperatively, RB/16 lanes per row with 16-byte accesses (RB the wider of
+// the K and V rows; lanes past the narrower row's end idle for it), and every
+// load of the chunk is issued before the first store so that the copy is
+// bound by bandwidth rather than latency. Reading src and writing dst, which may not
 // overlap, removes every race.
 #include "kvc_internal.h"
 
@@ -62,19 +63,21 @@ __global__ __launch_bounds__(NT) void compact_count_kernel(kvc_cache_t src, cons
 // batch is issued before its stores. Lanes past the last kept row reload that
 // row (a cache hit) rather than branch, and only their stores are skipped.
 // Thread t also moves the scales, position and score of kept row t.
-template <int RB, int NT>
+template <int RBK, int RBV, int NT>
 __device__ __forceinline__ void copy_rows(const kvc_cache_t& src, const float* __restrict__ src_score,
                                           const kvc_cache_t& dst, float* __restrict__ dst_score, long long rowoff,
                                           const int* list, int total, int off) {
+  constexpr int RB = RBK > RBV ? RBK : RBV;
   constexpr int LPR = RB / 16;        // lanes per row
   constexpr int RPP = NT / LPR;       // rows per pass
   constexpr int BATCH = 8;  // every pass of a 256-row chunk in flight at once (RB <= 128)
   const int tid = threadIdx.x;
-  const uint8_t* sk = static_cast<const uint8_t*>(src.k_codes) + rowoff * RB;
-  const uint8_t* sv = static_cast<const uint8_t*>(src.v_codes) + rowoff * RB;
-  uint8_t* dk = static_cast<uint8_t*>(dst.k_codes) + rowoff * RB;
-  uint8_t* dv = static_cast<uint8_t*>(dst.v_codes) + rowoff * RB;
+  const uint8_t* sk = static_cast<const uint8_t*>(src.k_codes) + rowoff * RBK;
+  const uint8_t* sv = static_cast<const uint8_t*>(src.v_codes) + rowoff * RBV;
+  uint8_t* dk = static_cast<uint8_t*>(dst.k_codes) + rowoff * RBK;
+  uint8_t* dv = static_cast<uint8_t*>(dst.v_codes) + rowoff * RBV;
   const int part = tid % LPR, r0 = tid / LPR;
+  const bool kpart = RBK == RB || part * 16 < RBK, vpart = RBV == RB || part * 16 < RBV;
   const bool mine = tid < total;
   const long long si = rowoff + list[mine ? tid : 0], di = rowoff + off + tid;
   float ksv = 0.f, vsv = 0.f, scv = 0.f;
@@ -91,8 +94,8 @@ __device__ __forceinline__ void copy_rows(const kvc_cache_t& src, const float* _
 #pragma unroll
     for (int p = 0; p < BATCH; ++p) {
       const long long s_row = list[min(r0 + (p0 + p) * RPP, total - 1)];
-      kx[p] = *reinterpret_cast<const u32x4*>(sk + s_row * RB + part * 16);
-      vx[p] = *reinterpret_cast<const u32x4*>(sv + s_row * RB + part * 16);
+      if (kpart) kx[p] = *reinterpret_cast<const u32x4*>(sk + s_row * RBK + part * 16);
+      if (vpart) vx[p] = *reinterpret_cast<const u32x4*>(sv + s_row * RBV + part * 16);
     }
 #pragma unroll
     for (int p = 0; p < BATCH; ++p) {
@@ -101,8 +104,8 @@ __device__ __forceinline__ void copy_rows(const kvc_cache_t& src, const float* _
         const long long d = off + q;
         // Streaming stores: the compacted rows are not read again by this
         // launch, so they should not sit dirty in L2 until the kernel ends.
-        __builtin_nontemporal_store(kx[p], reinterpret_cast<u32x4*>(dk + d * RB + part * 16));
-        __builtin_nontemporal_store(vx[p], reinterpret_cast<u32x4*>(dv + d * RB + part * 16));
+        if (kpart) __builtin_nontemporal_store(kx[p], reinterpret_cast<u32x4*>(dk + d * RBK + part * 16));
+        if (vpart) __builtin_nontemporal_store(vx[p], reinterpret_cast<u32x4*>(dv + d * RBV + part * 16));
       }
     }
   }
@@ -114,7 +117,7 @@ __device__ __forceinline__ void copy_rows(const kvc_cache_t& src, const float* _
   }
 }
 
-template <int RB, bool RECOUNT>
+template <int RBK, int RBV, bool RECOUNT>
 __global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const float* __restrict__ src_score,
                                                           const uint8_t* __restrict__ mask, kvc_cache_t dst,
                                                           float* __restrict__ dst_score,
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const
   if (f) list[incl - 1] = i;
   __syncthreads();
 
-  copy_rows<RB, NT>(src, src_score, dst, dst_score, rowoff, list, total, off);
+  copy_rows<RBK, RBV, NT>(src, src_score, dst, dst_score, rowoff, list, total, off);
   // The chunk holding the row's last slot knows the row's total.
   if (g == 0 && ch == (L - 1) / CH && tid == 0) {
     dst.lengths[b] = off + total;
@@ -204,11 +207,12 @@ __global__ __launch_bounds__(NT) void compact_move_kernel(kvc_cache_t src, const
 // NT) consecutive entries, one entry per thread for the index, scales,
 // position and score, and LPR lanes per entry for the codes, with every load
 // in flight before the first store.
-template <int RB>
+template <int RBK, int RBV>
 __global__ __launch_bounds__(NT) void compact_gather_kernel(kvc_cache_t src, const float* __restrict__ src_score,
                                                             const int32_t* __restrict__ keep_index, int n_keep,
                                                             kvc_cache_t dst, float* __restrict__ dst_score,
                                                             long long entries, int per_wg) {
+  constexpr int RB = RBK > RBV ? RBK : RBV;
   constexpr int LPR = RB / 16;        // lanes per row
   constexpr int RPP = NT / LPR;       // rows per pass
   constexpr int NPASS = NT / RPP;     // passes for NT rows
@@ -250,21 +254,22 @@ __global__ __launch_bounds__(NT) void compact_gather_kernel(kvc_cache_t src, con
   uint8_t* dk = static_cast<uint8_t*>(dst.k_codes);
   uint8_t* dv = static_cast<uint8_t*>(dst.v_codes);
   const int part = tid % LPR, r0 = tid / LPR;
+  const bool kpart = RBK == RB || part * 16 < RBK, vpart = RBV == RB || part * 16 < RBV;
   u32x4 kx[NPASS], vx[NPASS];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
     const long long r = s_row[r0 + p * RPP];
     const long long row = r < 0 ? 0 : r;  // every load valid; unused rows are not stored
-    kx[p] = *reinterpret_cast<const u32x4*>(sk + row * RB + part * 16);
-    vx[p] = *reinterpret_cast<const u32x4*>(sv + row * RB + part * 16);
+    if (kpart) kx[p] = *reinterpret_cast<const u32x4*>(sk + row * RBK + part * 16);
+    if (vpart) vx[p] = *reinterpret_cast<const u32x4*>(sv + row * RBV + part * 16);
   }
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
     const int q = r0 + p * RPP;
     if (s_row[q] >= 0) {
       // Streaming stores: the compacted rows are not read again by this launch.
-      __builtin_nontemporal_store(kx[p], reinterpret_cast<u32x4*>(dk + d_row[q] * RB + part * 16));
-      __builtin_nontemporal_store(vx[p], reinterpret_cast<u32x4*>(dv + d_row[q] * RB + part * 16));
+      if (kpart) __builtin_nontemporal_store(kx[p], reinterpret_cast<u32x4*>(dk + d_row[q] * RBK + part * 16));
+      if (vpart) __builtin_nontemporal_store(vx[p], reinterpret_cast<u32x4*>(dv + d_row[q] * RBV + part * 16));
     }
   }
   if (si >= 0) {
@@ -275,24 +280,24 @@ __global__ __launch_bounds__(NT) void compact_gather_kernel(kvc_cache_t src, con
   }
 }
 
-template <int RB>
+template <int RBK, int RBV>
 hipError_t launch_rb(const kvc_cache_t& src, const float* ss, const uint8_t* mask, const kvc_cache_t& dst,
                      float* ds, int32_t* counts, int chunks, hipStream_t st) {
   const dim3 grid(chunks, src.num_kv_heads, src.batch);
   if (chunks <= kCompactRecountChunks) {
-    hipLaunchKernelGGL((compact_move_kernel<RB, true>), grid, dim3(NT), 0, st, src, ss, mask, dst, ds, counts,
+    hipLaunchKernelGGL((compact_move_kernel<RBK, RBV, true>), grid, dim3(NT), 0, st, src, ss, mask, dst, ds, counts,
                        chunks);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(compact_count_kernel, grid, dim3(NT), 0, st, src, mask, counts, chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((compact_move_kernel<RB, false>), grid, dim3(NT), 0, st, src, ss, mask, dst, ds, counts,
+  hipLaunchKernelGGL((compact_move_kernel<RBK, RBV, false>), grid, dim3(NT), 0, st, src, ss, mask, dst, ds, counts,
                      chunks);
   return hipGetLastError();
 }
 
-template <int RB>
+template <int RBK, int RBV>
 hipError_t launch_gather_rb(const kvc_cache_t& src, const float* ss, const int32_t* keep_index, int n_keep,
                             const kvc_cache_t& dst, float* ds, hipStream_t st) {
   // About 512 workgroups (2 per CU) for the flat list, at most NT entries each.
@@ -300,7 +305,7 @@ hipError_t launch_gather_rb(const kvc_cache_t& src, const float* ss, const int32
   const int per_wg = (int)std::min<long long>(NT, std::max<long long>(1, (entries + 511) / 512));
   const long long wgs = (entries + per_wg - 1) / per_wg;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((compact_gather_kernel<RB>), dim3((unsigned)wgs), dim3(NT), 0, st, src, ss, keep_index, n_keep,
+  hipLaunchKernelGGL((compact_gather_kernel<RBK, RBV>), dim3((unsigned)wgs), dim3(NT), 0, st, src, ss, keep_index, n_keep,
                      dst, ds, entries, per_wg);
   return hipGetLastError();
 }
@@ -309,22 +314,16 @@ hipError_t launch_gather_rb(const kvc_cache_t& src, const float* ss, const int32
 
 hipError_t launch_compact_gather(const kvc_cache_t& src, const float* src_score, const int32_t* keep_index,
                                  int n_keep, const kvc_cache_t& dst, float* dst_score, hipStream_t st) {
-  switch (src.head_dim * src.bits / 8) {
-    case 32: return launch_gather_rb<32>(src, src_score, keep_index, n_keep, dst, dst_score, st);
-    case 64: return launch_gather_rb<64>(src, src_score, keep_index, n_keep, dst, dst_score, st);
-    case 128: return launch_gather_rb<128>(src, src_score, keep_index, n_keep, dst, dst_score, st);
-    default: return hipErrorInvalidValue;
-  }
+  return with_row_bytes(src, [&](auto rbk, auto rbv) {
+    return launch_gather_rb<decltype(rbk)::value, decltype(rbv)::value>(src, src_score, keep_index, n_keep, dst, dst_score, st);
+  });
 }
 
 hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const uint8_t* mask,
                           const kvc_cache_t& dst, float* dst_score, int32_t* counts, int chunks, hipStream_t st) {
-  switch (src.head_dim * src.bits / 8) {
-    case 32: return launch_rb<32>(src, src_score, mask, dst, dst_score, counts, chunks, st);
-    case 64: return launch_rb<64>(src, src_score, mask, dst, dst_score, counts, chunks, st);
-    case 128: return launch_rb<128>(src, src_score, mask, dst, dst_score, counts, chunks, st);
-    default: return hipErrorInvalidValue;
-  }
+  return with_row_bytes(src, [&](auto rbk, auto rbv) {
+    return launch_rb<decltype(rbk)::value, decltype(rbv)::value>(src, src_score, mask, dst, dst_score, counts, chunks, st);
+  });
 }
 
 }  // namespace kvc

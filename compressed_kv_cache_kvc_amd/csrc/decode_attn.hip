@@ -153,11 +153,16 @@ __device__ __forceinline__ unsigned sel4(const unsigned* v, int i) {
 // j = 4c + l / 16, i.e. one token per lane for GP = 1 and one head per 16-lane
 // row for GP >= 4. The PV output of row set rs holds head 4 rs + l / 16 (the
 // same head as the lane's logits) and channel 16 m + l % 16 of block m.
-template <int BITS, int D, int GP, bool PAGED>
+//
+// KBITS and VBITS: the K and V code widths (8 or 4), set apart so a cache can
+// hold K and V at different precisions.
+template <int KBITS, int VBITS, int D, int GP, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3 : 2))) void attn_split_kernel(
     AttnLaunch a) {
-  constexpr int RB = D * BITS / 8;          // bytes per token row in HBM
-  constexpr int KB = BITS == 8 ? 16 : 8;    // HBM bytes per lane per load (16 elements)
+  constexpr int RBK = D * KBITS / 8;        // bytes per K token row in HBM
+  constexpr int RBV = D * VBITS / 8;        // bytes per V token row in HBM
+  constexpr int KB = KBITS == 8 ? 16 : 8;   // HBM bytes per lane per K load (16 elements)
+  constexpr int VKB = VBITS == 8 ? 16 : 8;  // the same for V
   constexpr int NDH = D / 64;               // 64-element halves of a row (QK k = 64)
   constexpr int NCB = D / 16;               // 16-channel blocks (PV n = 16) = lanes per V row
   constexpr int TPV = 64 / NCB;             // tokens per V load instruction
@@ -205,15 +210,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   unsigned pool_rows = 0;
   if (PAGED) {
     pool_rows = (unsigned)c.num_blocks * H * c.block_size;
-    rk = __builtin_amdgcn_make_buffer_rsrc(c.k_codes, 0, pool_rows * RB, kBufferFlags);
-    rv = __builtin_amdgcn_make_buffer_rsrc(c.v_codes, 0, pool_rows * RB, kBufferFlags);
+    rk = __builtin_amdgcn_make_buffer_rsrc(c.k_codes, 0, pool_rows * RBK, kBufferFlags);
+    rv = __builtin_amdgcn_make_buffer_rsrc(c.v_codes, 0, pool_rows * RBV, kBufferFlags);
     rks = __builtin_amdgcn_make_buffer_rsrc(c.k_scale, 0, pool_rows * 4, kBufferFlags);
     rvs = __builtin_amdgcn_make_buffer_rsrc(c.v_scale, 0, pool_rows * 4, kBufferFlags);
   } else {
     const long long base = ((long long)b * H + g) * c.capacity;
     const unsigned valid = (unsigned)c.capacity;
-    rk = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(c.k_codes) + base * RB, 0, valid * RB, kBufferFlags);
-    rv = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(c.v_codes) + base * RB, 0, valid * RB, kBufferFlags);
+    rk = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(c.k_codes) + base * RBK, 0, valid * RBK,
+                                           kBufferFlags);
+    rv = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(c.v_codes) + base * RBV, 0, valid * RBV,
+                                           kBufferFlags);
     rks = __builtin_amdgcn_make_buffer_rsrc(c.k_scale + base, 0, valid * 4, kBufferFlags);
     rvs = __builtin_amdgcn_make_buffer_rsrc(c.v_scale + base, 0, valid * 4, kBufferFlags);
   }
@@ -244,8 +251,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
         const long long src = ((long long)b * H + g) * D;
         const quant::RowVals<D> kx = quant::load_row<D>(a.k_new + src, lane);
         const quant::RowVals<D> vx = quant::load_row<D>(a.v_new + src, lane);
-        quant::quant_vals<BITS, D>(kx, static_cast<uint8_t*>(c.k_codes) + row * RB, c.k_scale + row, lane);
-        quant::quant_vals<BITS, D>(vx, static_cast<uint8_t*>(c.v_codes) + row * RB, c.v_scale + row, lane);
+        quant::quant_vals<KBITS, D>(kx, static_cast<uint8_t*>(c.k_codes) + row * RBK, c.k_scale + row, lane);
+        quant::quant_vals<VBITS, D>(vx, static_cast<uint8_t*>(c.v_codes) + row * RBV, c.v_scale + row, lane);
         if (lane == 0) {
           if (c.positions) c.positions[row] = c.num_seen[b];
           if (a.score) a.score[((long long)b * H + g) * c.capacity + L_old] = 0.f;
@@ -263,9 +270,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   };
 
   // Registers of one block's loads; two sets keep two blocks in flight.
-  using KT = typename std::conditional<BITS == 8, i32x4, i32x2>::type;
+  using KT = typename std::conditional<KBITS == 8, i32x4, i32x2>::type;
   struct Regs {
-    KT kq[4][NDH], vq[BITS == 8 ? 1 : NCB];
+    KT kq[4][NDH];
+    i32x2 vq[VBITS == 8 ? 1 : NCB];
     float ksv[NSC], vsv[NSC];
   };
   // Issue every load of block `it`: K and V scales, then K codes into `r`,
@@ -299,20 +307,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
     for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
       for (int dh = 0; dh < NDH; ++dh) {
-        const unsigned off = row_static(tg, 16 * tg + col) * RB + dh * (RB / NDH) + quad * KB;
-        if constexpr (BITS == 8) r.kq[tg][dh] = load16(rk, off); else r.kq[tg][dh] = load8(rk, off);
+        const unsigned off = row_static(tg, 16 * tg + col) * RBK + dh * (RBK / NDH) + quad * KB;
+        if constexpr (KBITS == 8) r.kq[tg][dh] = load16(rk, off); else r.kq[tg][dh] = load8(rk, off);
       }
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
       // Lane l fills LDS chunk l % NCB of token row TPV j + l / NCB (DMA
       // writes lane l at 16 l), so it fetches the V chunk that belongs there.
       const int t = TPV * j + lane / NCB;
-      if constexpr (BITS == 8) {
-        const unsigned off = row_static((TPV * j) >> 4, t) * RB + vchunk(t, lane % NCB) * 16;
+      if constexpr (VBITS == 8) {
+        const unsigned off = row_static((TPV * j) >> 4, t) * RBV + vchunk(t, lane % NCB) * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, (__attribute__((address_space(3))) void*)&v_stage[wave][j * 1024], 16, off, 0, 0, 0);
       } else {
-        const unsigned off = row_static((TPV * j) >> 4, t) * RB + (lane % NCB) * KB;
+        const unsigned off = row_static((TPV * j) >> 4, t) * RBV + (lane % NCB) * VKB;
         r.vq[j] = load8(rv, off);
       }
     }
@@ -352,21 +360,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
         const int d = lane * EPL + e;
         int lm[4];
         to_limbs(ldexpf(x[e], E), lm);
-        const int pos = BITS == 8 ? d : ((d & ~15) | int4_byte(d & 15));
+        const int pos = KBITS == 8 ? d : ((d & ~15) | int4_byte(d & 15));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           q_limb[h][k][pos] = (int8_t)lm[k];
           lsum[k] += lm[k];
         }
       }
-      if (BITS == 4) {
+      if (KBITS == 4) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) lsum[k] = wave_sum_i(lsum[k]);
       }
       if (lane == 0) {
         q_fac[h] = mx > 0.f ? ldexpf(a.qk_log2, -E) : 0.f;
         // INT4: the codes enter as code + 8, so each limb sum carries 8 * sum(limb).
-        q_off[h] = BITS == 4 ? 8.f * ((float)lsum[0] + (float)lsum[1] * 0x1p-7f + (float)lsum[2] * 0x1p-14f +
+        q_off[h] = KBITS == 4 ? 8.f * ((float)lsum[0] + (float)lsum[1] * 0x1p-7f + (float)lsum[2] * 0x1p-14f +
                                       (float)lsum[3] * 0x1p-21f)
                              : 0.f;
       }
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
 #pragma unroll
         for (int dh = 0; dh < NDH; ++dh) {
           i32x4 kb;
-          if constexpr (BITS == 8) kb = r.kq[tg][dh]; else kb = widen_int4(r.kq[tg][dh]);
+          if constexpr (KBITS == 8) kb = r.kq[tg][dh]; else kb = widen_int4(r.kq[tg][dh]);
           if (GP <= 4) {
             const int cc = tg * GP / 4;
             acc[cc] = mfma(a_operand(tg, 0, dh), kb, acc[cc]);
@@ -497,7 +505,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
         }
       }
       // ---- V rows in LDS: INT8 came by DMA; INT4 is widened here ----
-      if constexpr (BITS == 4) {
+      if constexpr (VBITS == 4) {
 #pragma unroll
         for (int j = 0; j < NCB; ++j) {
           const int t = TPV * j + lane / NCB;
@@ -544,7 +552,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
       l_tot[rs] = head_reduce<GP, false>(l_part[rs]);
-      w_tot[rs] = BITS == 4 ? head_reduce<GP, false>(w_part[rs]) : 0.f;
+      w_tot[rs] = VBITS == 4 ? head_reduce<GP, false>(w_part[rs]) : 0.f;
     }
     __syncthreads();  // every wave is done with v_stage, which red_o reuses
 #pragma unroll
@@ -557,7 +565,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
         }
 #pragma unroll
         for (int m = 0; m < NCB; ++m) {
-          const int ch = m * 16 + (BITS == 8 ? col : int4_elem(col));
+          const int ch = m * 16 + (VBITS == 8 ? col : int4_elem(col));
           red_o[(wave * GP + hh) * D + ch] = o_acc[rs][m] - 8.f * w_tot[rs];
         }
       }
@@ -686,33 +694,38 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   }
 }
 
-template <int BITS, int D, int GP, bool PAGED>
+template <int KBITS, int VBITS, int D, int GP, bool PAGED>
 hipError_t launch_split(const AttnLaunch& a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_split_kernel<BITS, D, GP, PAGED>), dim3(a.splits, a.c.num_kv_heads, a.c.batch),
+  hipLaunchKernelGGL((attn_split_kernel<KBITS, VBITS, D, GP, PAGED>), dim3(a.splits, a.c.num_kv_heads, a.c.batch),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int BITS, int D, bool PAGED>
+template <int KBITS, int VBITS, int D, bool PAGED>
 hipError_t launch_gp(const AttnLaunch& a, int G, hipStream_t st) {
-  if (G == 1) return launch_split<BITS, D, 1, PAGED>(a, st);
-  if (G == 2) return launch_split<BITS, D, 2, PAGED>(a, st);
-  if (G <= 4) return launch_split<BITS, D, 4, PAGED>(a, st);
-  return launch_split<BITS, D, 8, PAGED>(a, st);  // more than 8: passes of 8
+  if (G == 1) return launch_split<KBITS, VBITS, D, 1, PAGED>(a, st);
+  if (G == 2) return launch_split<KBITS, VBITS, D, 2, PAGED>(a, st);
+  if (G <= 4) return launch_split<KBITS, VBITS, D, 4, PAGED>(a, st);
+  return launch_split<KBITS, VBITS, D, 8, PAGED>(a, st);  // more than 8: passes of 8
 }
 
-template <int BITS, int D>
+template <int KBITS, int VBITS, int D>
 hipError_t launch_paged(const AttnLaunch& a, int G, hipStream_t st) {
-  return a.c.block_size ? launch_gp<BITS, D, true>(a, G, st) : launch_gp<BITS, D, false>(a, G, st);
+  return a.c.block_size ? launch_gp<KBITS, VBITS, D, true>(a, G, st) : launch_gp<KBITS, VBITS, D, false>(a, G, st);
+}
+
+template <int KBITS, int VBITS>
+hipError_t launch_dim(const AttnLaunch& a, int G, hipStream_t st) {
+  return a.c.head_dim == 64 ? launch_paged<KBITS, VBITS, 64>(a, G, st) : launch_paged<KBITS, VBITS, 128>(a, G, st);
 }
 
 }  // namespace
 
 hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  if (a.c.bits == 8)
-    return a.c.head_dim == 64 ? launch_paged<8, 64>(a, G, st) : launch_paged<8, 128>(a, G, st);
-  return a.c.head_dim == 64 ? launch_paged<4, 64>(a, G, st) : launch_paged<4, 128>(a, G, st);
+  const int vb = vbits_of(a.c);
+  if (a.c.bits == 8) return vb == 8 ? launch_dim<8, 8>(a, G, st) : launch_dim<8, 4>(a, G, st);
+  return vb == 8 ? launch_dim<4, 8>(a, G, st) : launch_dim<4, 4>(a, G, st);
 }
 
 hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st) {

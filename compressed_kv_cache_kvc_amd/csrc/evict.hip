@@ -40,13 +40,16 @@ constexpr int kKPT = 8;            // candidate keys per thread (in registers)
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Row copies. An entry e of a row moves source slot slot_of(e) to destination
-// slot dest_of(e): K and V codes (RB/16 lanes per row, 16-byte accesses),
-// scales, position and score. A pass covers up to RPP = kNT * 16 / RB
-// consecutive entries: lane group r0 = tid / (RB/16) holds the codes of entry
-// e0 + r0, thread tid the other fields of entry e0 + tid. GK > 0: the score
-// is updated with the step's H2O mass (GK logits per entry) when stored.
-template <int RB, int GK>
+// slot dest_of(e): K and V codes (RBK and RBV bytes per row; RB/16 lanes per
+// row, RB the wider of the two, 16-byte accesses, lanes past the narrower
+// row's end idle for it), scales, position and score. A pass covers up to
+// RPP = kNT * 16 / RB consecutive entries: lane group r0 = tid / (RB/16) holds
+// the codes of entry e0 + r0, thread tid the other fields of entry e0 + tid.
+// GK > 0: the score is updated with the step's H2O mass (GK logits per entry)
+// when stored.
+template <int RBK, int RBV, int GK>
 struct Pass {
+  static constexpr int RB = RBK > RBV ? RBK : RBV;
   static constexpr int LPR = RB / 16;
   static constexpr int RPP = kNT / LPR;
   u32x4 k, v;
@@ -87,13 +90,14 @@ __device__ __forceinline__ float updated_score(const RowIO& io, float sc, const 
   return sc + add;
 }
 
-template <int RB, int GK, typename SlotOf>
-__device__ __forceinline__ void load_pass(Pass<RB, GK>& P, const RowIO& io, int e0, int e1, SlotOf slot_of) {
-  const int tid = threadIdx.x, part = tid % Pass<RB, GK>::LPR, r0 = tid / Pass<RB, GK>::LPR;
+template <int RBK, int RBV, int GK, typename SlotOf>
+__device__ __forceinline__ void load_pass(Pass<RBK, RBV, GK>& P, const RowIO& io, int e0, int e1, SlotOf slot_of) {
+  using PS = Pass<RBK, RBV, GK>;
+  const int tid = threadIdx.x, part = tid % PS::LPR, r0 = tid / PS::LPR;
   if (e0 >= e1) return;  // uniform
   const long long s = slot_of(min(e0 + r0, e1 - 1));  // every lane loads; spare lanes repeat the last entry
-  P.k = *reinterpret_cast<const u32x4*>(io.sk + s * RB + part * 16);
-  P.v = *reinterpret_cast<const u32x4*>(io.sv + s * RB + part * 16);
+  if (RBK == PS::RB || part * 16 < RBK) P.k = *reinterpret_cast<const u32x4*>(io.sk + s * RBK + part * 16);
+  if (RBV == PS::RB || part * 16 < RBV) P.v = *reinterpret_cast<const u32x4*>(io.sv + s * RBV + part * 16);
   if (tid < e1 - e0) {
     const int se = slot_of(e0 + tid);
     P.ks = io.sks[se];
@@ -110,16 +114,19 @@ __device__ __forceinline__ void load_pass(Pass<RB, GK>& P, const RowIO& io, int 
   }
 }
 
-template <int RB, int GK, typename SlotOf, typename DestOf>
-__device__ __forceinline__ void store_pass(const Pass<RB, GK>& P, const RowIO& io, int e0, int e1, SlotOf slot_of,
-                                           DestOf dest_of) {
-  const int tid = threadIdx.x, part = tid % Pass<RB, GK>::LPR, r0 = tid / Pass<RB, GK>::LPR;
+template <int RBK, int RBV, int GK, typename SlotOf, typename DestOf>
+__device__ __forceinline__ void store_pass(const Pass<RBK, RBV, GK>& P, const RowIO& io, int e0, int e1,
+                                           SlotOf slot_of, DestOf dest_of) {
+  using PS = Pass<RBK, RBV, GK>;
+  const int tid = threadIdx.x, part = tid % PS::LPR, r0 = tid / PS::LPR;
   if (e0 >= e1) return;
   if (e0 + r0 < e1) {
     const long long d = dest_of(e0 + r0);
     // Streaming stores: the compacted rows are not read again here.
-    __builtin_nontemporal_store(P.k, reinterpret_cast<u32x4*>(io.dk + d * RB + part * 16));
-    __builtin_nontemporal_store(P.v, reinterpret_cast<u32x4*>(io.dv + d * RB + part * 16));
+    if (RBK == PS::RB || part * 16 < RBK)
+      __builtin_nontemporal_store(P.k, reinterpret_cast<u32x4*>(io.dk + d * RBK + part * 16));
+    if (RBV == PS::RB || part * 16 < RBV)
+      __builtin_nontemporal_store(P.v, reinterpret_cast<u32x4*>(io.dv + d * RBV + part * 16));
   }
   if (tid < e1 - e0) {
     const long long de = dest_of(e0 + tid);
@@ -131,16 +138,17 @@ __device__ __forceinline__ void store_pass(const Pass<RB, GK>& P, const RowIO& i
 }
 
 // Entries [e0, e1), BATCH passes in flight at a time.
-template <int RB, int GK, int BATCH, typename SlotOf, typename DestOf>
+template <int RBK, int RBV, int GK, int BATCH, typename SlotOf, typename DestOf>
 __device__ __forceinline__ void copy_entries(const RowIO& io, int e0, int e1, SlotOf slot_of, DestOf dest_of) {
-  constexpr int RPP = Pass<RB, GK>::RPP;
+  constexpr int RPP = Pass<RBK, RBV, GK>::RPP;
   for (int e = e0; e < e1; e += RPP * BATCH) {
-    Pass<RB, GK> ps[BATCH];
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) load_pass<RB, GK>(ps[q], io, e + q * RPP, min(e1, e + (q + 1) * RPP), slot_of);
+    Pass<RBK, RBV, GK> ps[BATCH];
 #pragma unroll
     for (int q = 0; q < BATCH; ++q)
-      store_pass<RB, GK>(ps[q], io, e + q * RPP, min(e1, e + (q + 1) * RPP), slot_of, dest_of);
+      load_pass<RBK, RBV, GK>(ps[q], io, e + q * RPP, min(e1, e + (q + 1) * RPP), slot_of);
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q)
+      store_pass<RBK, RBV, GK>(ps[q], io, e + q * RPP, min(e1, e + (q + 1) * RPP), slot_of, dest_of);
   }
 }
 
@@ -157,7 +165,7 @@ __device__ __forceinline__ void copy_entries(const RowIO& io, int e0, int e1, Sl
 // gfx9 counts stores in the same counter as loads, so a wait for a load also
 // waits for every store issued before it: stores come after the loads whose
 // data the workgroup waits for.
-template <int RB, int GK>
+template <int RBK, int RBV, int GK>
 __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   constexpr int NT = kNT, KPT = kKPT;
   constexpr bool MERGE = GK > 0;
@@ -293,10 +301,10 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   merge_first();
   uint8_t* m = e.mask ? e.mask + rowoff : nullptr;
   int32_t* kidx = e.keep_index ? e.keep_index + bg * budget : nullptr;
-  const RowIO io{static_cast<const uint8_t*>(c.k_codes) + rowoff * RB,
-                 static_cast<const uint8_t*>(c.v_codes) + rowoff * RB,
-                 static_cast<uint8_t*>(e.dst.k_codes) + rowoff * RB,
-                 static_cast<uint8_t*>(e.dst.v_codes) + rowoff * RB,
+  const RowIO io{static_cast<const uint8_t*>(c.k_codes) + rowoff * RBK,
+                 static_cast<const uint8_t*>(c.v_codes) + rowoff * RBV,
+                 static_cast<uint8_t*>(e.dst.k_codes) + rowoff * RBK,
+                 static_cast<uint8_t*>(e.dst.v_codes) + rowoff * RBV,
                  c.k_scale + rowoff, c.v_scale + rowoff, e.dst.k_scale + rowoff, e.dst.v_scale + rowoff,
                  (c.positions && e.dst.positions) ? c.positions + rowoff : nullptr,
                  (c.positions && e.dst.positions) ? e.dst.positions + rowoff : nullptr,
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   const int n_fixed = all ? L : n_sink + n_recent;
   auto fixed_slot = [&](int f) { return f < n_self ? f : hi + (f - n_self); };
   auto fixed_dest = [&](int f) { return f < n_self ? f : lo + n_heavy + (f - n_self); };
-  constexpr int RPP = Pass<RB, GK>::RPP;
+  constexpr int RPP = Pass<RBK, RBV, GK>::RPP;
   const int f0 = (int)(((long long)n_fixed * p) >> log2_parts);
   const int f1 = (int)(((long long)n_fixed * (p + 1)) >> log2_parts);
   const int fa = min(f1, f0 + RPP);  // the first pass of fixed entries
@@ -326,12 +334,12 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
       if (kidx) kidx[fixed_dest(f)] = fixed_slot(f);
     }
   };
-  Pass<RB, GK> pre;
+  Pass<RBK, RBV, GK> pre;
   if (all) {
-    load_pass<RB, GK>(pre, io, f0, fa, fixed_slot);
+    load_pass<RBK, RBV, GK>(pre, io, f0, fa, fixed_slot);
     fixed_entries();
-    store_pass<RB, GK>(pre, io, f0, fa, fixed_slot, fixed_dest);
-    copy_entries<RB, GK, 2>(io, fa, f1, fixed_slot, fixed_dest);
+    store_pass<RBK, RBV, GK>(pre, io, f0, fa, fixed_slot, fixed_dest);
+    copy_entries<RBK, RBV, GK, 2>(io, fa, f1, fixed_slot, fixed_dest);
     __syncthreads();
     merge_first_out();
     merge_rest();
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   for (int j = 0; j < KPT; ++j) stage_lds[tid + j * NT] = v[j];
   // The first pass of fixed rows loads during the search (barriers here wait
   // for LDS only), and is stored after it.
-  load_pass<RB, GK>(pre, io, f0, fa, fixed_slot);
+  load_pass<RBK, RBV, GK>(pre, io, f0, fa, fixed_slot);
   __syncthreads();
   merge_first_out();
   fixed_entries();  // stores: after the wait for the scores
@@ -448,23 +456,23 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   auto rest_slot = [&](int e) { return e < nfr ? fixed_slot(fa + e) : heavy[h0 + e - nfr]; };
   auto rest_dest = [&](int e) { return e < nfr ? fixed_dest(fa + e) : lo + h0 + (e - nfr); };
   constexpr int HB = 2;
-  Pass<RB, GK> hp[HB];
+  Pass<RBK, RBV, GK> hp[HB];
 #pragma unroll
-  for (int q = 0; q < HB; ++q) load_pass<RB, GK>(hp[q], io, q * RPP, min(total, (q + 1) * RPP), rest_slot);
-  store_pass<RB, GK>(pre, io, f0, fa, fixed_slot, fixed_dest);
+  for (int q = 0; q < HB; ++q) load_pass<RBK, RBV, GK>(hp[q], io, q * RPP, min(total, (q + 1) * RPP), rest_slot);
+  store_pass<RBK, RBV, GK>(pre, io, f0, fa, fixed_slot, fixed_dest);
   if (kidx)
     for (int h = h0 + tid; h < h1; h += NT) kidx[lo + h] = heavy[h];
 #pragma unroll
   for (int q = 0; q < HB; ++q)
-    store_pass<RB, GK>(hp[q], io, q * RPP, min(total, (q + 1) * RPP), rest_slot, rest_dest);
-  copy_entries<RB, GK, 2>(io, HB * RPP, total, rest_slot, rest_dest);
+    store_pass<RBK, RBV, GK>(hp[q], io, q * RPP, min(total, (q + 1) * RPP), rest_slot, rest_dest);
+  copy_entries<RBK, RBV, GK, 2>(io, HB * RPP, total, rest_slot, rest_dest);
   merge_rest();
   set_length();
 }
 
 namespace {
 
-template <int RB, int GK>
+template <int RBK, int RBV, int GK>
 hipError_t launch_rb(const EvictArgs& a, hipStream_t st) {
   // About 256 workgroups over the rows, at most 8 per row.
   const long long rows = (long long)a.c.batch * a.c.num_kv_heads;
@@ -475,18 +483,13 @@ hipError_t launch_rb(const EvictArgs& a, hipStream_t st) {
   e.xcd_rows = rows % 8 == 0;
   const long long wgs = rows << lp;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((evict_kernel<RB, GK>), dim3((unsigned)wgs), dim3(kNT), 0, st, e);
+  hipLaunchKernelGGL((evict_kernel<RBK, RBV, GK>), dim3((unsigned)wgs), dim3(kNT), 0, st, e);
   return hipGetLastError();
 }
 
 template <int GK>
 hipError_t launch_gk(const EvictArgs& a, hipStream_t st) {
-  switch (a.c.head_dim * a.c.bits / 8) {
-    case 32: return launch_rb<32, GK>(a, st);
-    case 64: return launch_rb<64, GK>(a, st);
-    case 128: return launch_rb<128, GK>(a, st);
-    default: return hipErrorInvalidValue;
-  }
+  return with_row_bytes(a.c, [&](auto rbk, auto rbv) { return launch_rb<decltype(rbk)::value, decltype(rbv)::value, GK>(a, st); });
 }
 
 }  // namespace

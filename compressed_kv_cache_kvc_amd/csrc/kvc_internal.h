@@ -7,10 +7,36 @@
 
 #include <algorithm>
 #include <string>
+#include <type_traits>
 
 #include "kvc.h"
 
 namespace kvc {
+
+// Code widths of K and V, and their bytes per token row.
+__host__ __device__ inline int kbits_of(const kvc_cache_t& c) { return c.bits; }
+__host__ __device__ inline int vbits_of(const kvc_cache_t& c) { return c.v_bits ? c.v_bits : c.bits; }
+__host__ __device__ inline int k_row_bytes(const kvc_cache_t& c) { return c.head_dim * kbits_of(c) / 8; }
+__host__ __device__ inline int v_row_bytes(const kvc_cache_t& c) { return c.head_dim * vbits_of(c) / 8; }
+
+// Calls f(RBK, RBV) with the cache's K and V row bytes as compile-time
+// constants (std::integral_constant): 32, 64 or 128 each (head_dim 64 or 128
+// at 4 or 8 bits), equal or one twice the other. Other sizes: invalid value.
+template <typename F>
+hipError_t with_row_bytes(const kvc_cache_t& c, F&& f) {
+  using I32 = std::integral_constant<int, 32>;
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  const int rbk = k_row_bytes(c), rbv = v_row_bytes(c);
+  if (rbk == 32 && rbv == 32) return f(I32{}, I32{});
+  if (rbk == 64 && rbv == 64) return f(I64{}, I64{});
+  if (rbk == 128 && rbv == 128) return f(I128{}, I128{});
+  if (rbk == 64 && rbv == 32) return f(I64{}, I32{});
+  if (rbk == 32 && rbv == 64) return f(I32{}, I64{});
+  if (rbk == 128 && rbv == 64) return f(I128{}, I64{});
+  if (rbk == 64 && rbv == 128) return f(I64{}, I128{});
+  return hipErrorInvalidValue;
+}
 
 // ---- host-side error reporting (thread-local message of the last failure) ----
 void set_error(const char* fmt, ...);

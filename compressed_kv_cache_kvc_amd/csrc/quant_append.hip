@@ -17,12 +17,12 @@ using quant::RowVals;
 // wave loads R rows (row indices clamped, so the loads are unconditional)
 // before reducing any of them; the first batch is issued before the lengths
 // are read, so one memory latency covers both.
-template <int BITS, int D>
+template <int KBITS, int VBITS, int D>
 __global__ __launch_bounds__(1024) void quant_append_seq_kernel(kvc_cache_t c, const __half* __restrict__ kn,
                                                                 const __half* __restrict__ vn, int n_new,
                                                                 float* __restrict__ score) {
   constexpr int R = 4;
-  constexpr int RB = D * BITS / 8;
+  constexpr int RBK = D * KBITS / 8, RBV = D * VBITS / 8;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = c.num_kv_heads;
@@ -48,8 +48,10 @@ __global__ __launch_bounds__(1024) void quant_append_seq_kernel(kvc_cache_t c, c
       const int kv = r & 1, ht = r >> 1, h = ht / n_new, t = ht - h * n_new;
       const long long row = cache_row(c, b, h, L0 + t);
       if (row < 0) continue;
-      uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * RB;
-      quant_vals<BITS, D>(vals[q], dst, (kv ? c.v_scale : c.k_scale) + row, lane);
+      if (kv)  // uniform per wave: rows alternate K, V and a wave's rows differ by 16
+        quant_vals<VBITS, D>(vals[q], static_cast<uint8_t*>(c.v_codes) + row * RBV, c.v_scale + row, lane);
+      else
+        quant_vals<KBITS, D>(vals[q], static_cast<uint8_t*>(c.k_codes) + row * RBK, c.k_scale + row, lane);
       if (kv == 0 && lane == 0) {
         if (c.positions) c.positions[row] = seen + t;
         if (score) score[((long long)b * H + h) * c.capacity + L0 + t] = 0.f;
@@ -65,11 +67,11 @@ __global__ __launch_bounds__(1024) void quant_append_seq_kernel(kvc_cache_t c, c
 
 // Prefill-sized appends: four rows per workgroup over the whole grid; the
 // lengths advance in a second launch once every row has read them.
-template <int BITS, int D>
+template <int KBITS, int VBITS, int D>
 __global__ __launch_bounds__(256) void quant_append_rows_kernel(kvc_cache_t c, const __half* __restrict__ kn,
                                                                 const __half* __restrict__ vn, int n_new,
                                                                 float* __restrict__ score, long long total) {
-  constexpr int RB = D * BITS / 8;
+  constexpr int RBK = D * KBITS / 8, RBV = D * VBITS / 8;
   const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= total) return;
@@ -83,8 +85,10 @@ __global__ __launch_bounds__(256) void quant_append_rows_kernel(kvc_cache_t c, c
   const int L0 = c.lengths[b];
   const long long row = cache_row(c, b, h, L0 + t);
   if (row < 0) return;
-  uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * RB;
-  quant_vals<BITS, D>(vals, dst, (kv ? c.v_scale : c.k_scale) + row, lane);
+  if (kv)
+    quant_vals<VBITS, D>(vals, static_cast<uint8_t*>(c.v_codes) + row * RBV, c.v_scale + row, lane);
+  else
+    quant_vals<KBITS, D>(vals, static_cast<uint8_t*>(c.k_codes) + row * RBK, c.k_scale + row, lane);
   if (kv == 0 && lane == 0) {
     if (c.positions) c.positions[row] = c.num_seen[b] + t;
     if (score) score[bh * c.capacity + L0 + t] = 0.f;
@@ -99,18 +103,18 @@ __global__ void advance_lengths_kernel(int32_t* lengths, int32_t* num_seen, int 
   }
 }
 
-template <int BITS, int D>
+template <int KBITS, int VBITS, int D>
 hipError_t launch_bits(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new, float* score,
                        hipStream_t st) {
   const long long rows_per_seq = (long long)c.num_kv_heads * n_new * 2;
   if (rows_per_seq <= 256) {
-    hipLaunchKernelGGL((quant_append_seq_kernel<BITS, D>), dim3(c.batch), dim3(1024), 0, st, c, kn, vn, n_new,
+    hipLaunchKernelGGL((quant_append_seq_kernel<KBITS, VBITS, D>), dim3(c.batch), dim3(1024), 0, st, c, kn, vn, n_new,
                        score);
     return hipGetLastError();
   }
   const long long total = rows_per_seq * c.batch;
   const long long blocks = (total + 3) / 4;
-  hipLaunchKernelGGL((quant_append_rows_kernel<BITS, D>), dim3((unsigned)blocks), dim3(256), 0, st, c, kn, vn,
+  hipLaunchKernelGGL((quant_append_rows_kernel<KBITS, VBITS, D>), dim3((unsigned)blocks), dim3(256), 0, st, c, kn, vn,
                      n_new, score, total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -119,18 +123,21 @@ hipError_t launch_bits(const kvc_cache_t& c, const __half* kn, const __half* vn,
   return hipGetLastError();
 }
 
-template <int BITS>
+template <int KBITS, int VBITS>
 hipError_t launch_dim(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new, float* score,
                       hipStream_t st) {
-  return c.head_dim == 64 ? launch_bits<BITS, 64>(c, kn, vn, n_new, score, st)
-                          : launch_bits<BITS, 128>(c, kn, vn, n_new, score, st);
+  return c.head_dim == 64 ? launch_bits<KBITS, VBITS, 64>(c, kn, vn, n_new, score, st)
+                          : launch_bits<KBITS, VBITS, 128>(c, kn, vn, n_new, score, st);
 }
 
 }  // namespace
 
 hipError_t launch_quant_append(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new,
                                float* score, hipStream_t st) {
-  return c.bits == 8 ? launch_dim<8>(c, kn, vn, n_new, score, st) : launch_dim<4>(c, kn, vn, n_new, score, st);
+  const int vb = vbits_of(c);
+  if (c.bits == 8)
+    return vb == 8 ? launch_dim<8, 8>(c, kn, vn, n_new, score, st) : launch_dim<8, 4>(c, kn, vn, n_new, score, st);
+  return vb == 8 ? launch_dim<4, 8>(c, kn, vn, n_new, score, st) : launch_dim<4, 4>(c, kn, vn, n_new, score, st);
 }
 
 }  // namespace kvc

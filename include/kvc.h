@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum {
   KVC_OK = 0,
@@ -82,7 +82,7 @@ typedef enum {
  * and element 2j+1 in the high nibble. A token's value is code * scale.
  */
 typedef struct kvc_cache {
-  int32_t bits;                /* 8 or 4 */
+  int32_t bits;                /* 8 or 4: K code width (and V's unless v_bits is set) */
   int32_t batch;               /* sequences, >= 1 */
   int32_t num_kv_heads;        /* >= 1 */
   int32_t head_dim;            /* 64, 128 or 256 */
@@ -98,6 +98,10 @@ typedef struct kvc_cache {
   int32_t* num_seen;
   int32_t* positions;
   const int32_t* block_table;
+  int32_t v_bits;              /* 0 (V as K), 8 or 4: V code width; K and V at different
+                                  widths ("KV Cache optimization techniques" tutorial,
+                                  section 1.1: the quantizer's K-V mode, keys and values at
+                                  different precision) */
 } kvc_cache_t;
 
 /* ABI version compiled into the library (KVC_ABI_VERSION). */

@@ -25,9 +25,13 @@ from .quant import quantize_rows
 class RefCache:
     """Contiguous per-(sequence, KV head) cache with unpacked integer codes."""
 
-    def __init__(self, batch: int, num_kv_heads: int, head_dim: int, capacity: int, bits: int):
+    def __init__(self, batch: int, num_kv_heads: int, head_dim: int, capacity: int, bits: int,
+                 v_bits: int | None = None):
         B, H, D, C = batch, num_kv_heads, head_dim, capacity
         self.bits = bits
+        # Keys and values may use different widths ("KV Cache optimization
+        # techniques" tutorial, section 1.1: the quantizer's K-V mode).
+        self.v_bits = v_bits or bits
         self.capacity = C
         self.k_codes = np.zeros((B, H, C, D), dtype=np.int8)
         self.v_codes = np.zeros((B, H, C, D), dtype=np.int8)
@@ -43,7 +47,7 @@ class RefCache:
         """Append n tokens per sequence: k16, v16 [B][Hkv][n][D] fp16."""
         n = k16.shape[2]
         ck, sk = quantize_rows(k16, self.bits)
-        cv, sv = quantize_rows(v16, self.bits)
+        cv, sv = quantize_rows(v16, self.v_bits)
         for b in range(k16.shape[0]):
             L = int(self.lengths[b])
             if L + n > self.capacity:

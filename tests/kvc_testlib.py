@@ -50,7 +50,7 @@ def assert_codes_equal(gpu_cache, ref: "oracle.RefCache", rows=None):
             if rows is not None and (b, g) not in rows:
                 continue
             assert np.array_equal(k[b, g, :L], oracle_code_bytes(ref.k_codes[b, g, :L], ref.bits)), (b, g)
-            assert np.array_equal(v[b, g, :L], oracle_code_bytes(ref.v_codes[b, g, :L], ref.bits)), (b, g)
+            assert np.array_equal(v[b, g, :L], oracle_code_bytes(ref.v_codes[b, g, :L], ref.v_bits)), (b, g)
             assert np.array_equal(ks[b, g, :L].view(np.uint32), ref.k_scale[b, g, :L].view(np.uint32)), (b, g)
             assert np.array_equal(vs[b, g, :L].view(np.uint32), ref.v_scale[b, g, :L].view(np.uint32)), (b, g)
             if pos is not None:
@@ -99,21 +99,22 @@ def assert_keep_equivalent(mask_gpu: np.ndarray, score_ref: np.ndarray, lengths,
     return ambiguous_total
 
 
-def make_gpu_cache(w, capacity=None, bits=None, positions=True):
+def make_gpu_cache(w, capacity=None, bits=None, positions=True, v_bits=0):
     import compressed_kv_cache_kvc_amd as kvc
     return kvc.KVCache(w.batch, w.num_kv_heads, w.head_dim, capacity or w.context, bits or w.bits,
-                       positions=positions)
+                       positions=positions, v_bits=v_bits)
 
 
-def prefill_both(w, d, capacity=None, bits=None, with_score=True):
-    """Prefill L-1 tokens and append the L-th with both the GPU and the oracle."""
+def prefill_both(w, d, capacity=None, bits=None, with_score=True, v_bits=0):
+    """Prefill L-1 tokens and append the L-th with both the GPU and the oracle
+    (V at ``v_bits`` when set, else at the K width)."""
     import compressed_kv_cache_kvc_amd as kvc
     bits = bits or w.bits
     cap = capacity or w.context
     L = d["k"].shape[2]
-    gc = make_gpu_cache(w, cap, bits)
+    gc = make_gpu_cache(w, cap, bits, v_bits=v_bits)
     score = gc.score_buffer() if with_score else None
-    ref = oracle.RefCache(w.batch, w.num_kv_heads, w.head_dim, cap, bits)
+    ref = oracle.RefCache(w.batch, w.num_kv_heads, w.head_dim, cap, bits, v_bits=v_bits or None)
     if L > 1:
         kvc.kvc_quant_append(gc, dev(d["k"][:, :, :L - 1]), dev(d["v"][:, :, :L - 1]), h2o_score=score)
         ref.append(d["k"][:, :, :L - 1], d["v"][:, :, :L - 1])

@@ -42,7 +42,7 @@ def test_exports_match_binding_names():
 
 
 def test_version_and_status_strings():
-    assert kvc.kvc_abi_version() == 1
+    assert kvc.kvc_abi_version() == 2
     assert kvc.kvc_status_str(0) == "KVC_OK"
     assert kvc.kvc_status_str(2) == "KVC_ERR_CAPACITY"
     assert kvc.kvc_status_str(99) == "KVC_UNKNOWN"
@@ -72,6 +72,7 @@ def attn(d, hq=4, hint=16, ws=FAKE * 256, nbytes=1 << 30, q=FAKE, out=FAKE, scor
     ("bits", 3, INVALID), ("bits", 16, INVALID), ("batch", 0, INVALID), ("num_kv_heads", 0, INVALID),
     ("head_dim", 96, UNSUPPORTED), ("head_dim", 100, INVALID), ("capacity", 0, INVALID),
     ("k_codes", None, INVALID), ("lengths", None, INVALID), ("block_size", 8, UNSUPPORTED),
+    ("v_bits", 2, INVALID), ("v_bits", 16, INVALID),
 ])
 def test_descriptor_validation(field, value, status):
     d = desc(**{field: value})
@@ -218,6 +219,9 @@ def test_compact_validation():
     other = desc(k_codes=0x1100000, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
                  positions=0x1500000, lengths=0x1600000, num_seen=0x1600100, capacity=256)
     assert call(src, other) == INVALID
+    vmix = desc(k_codes=0x1100000, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
+                positions=0x1500000, lengths=0x1600000, num_seen=0x1600100, v_bits=4)
+    assert call(src, vmix) == INVALID                 # V widths differ
     assert call(src, dst, ss=0x4000000) == INVALID    # one score array without the other
     assert call(src, dst, w=None) == INVALID
     assert call(src, dst, hint=513) == CAPACITY

@@ -12,7 +12,7 @@ import oracle
 from workloads import draw, get
 
 from kvc_testlib import (assert_codes_equal, assert_keep_equivalent, assert_out_close, assert_scores_close, dev,
-                         host, make_gpu_cache, prefill_both)
+                         host, make_gpu_cache, oracle_code_bytes, prefill_both)
 
 pytestmark = pytest.mark.gpu
 
@@ -302,7 +302,7 @@ def test_append_decode_attn_llama7b_full_size():
     assert torch.equal(outA, outB)
 
 
-def _step_caches(w, lens, cap, seed):
+def _step_caches(w, lens, cap, seed, v_bits=0):
     """Two identical GPU caches with Lmax = max(lens) prefilled tokens, then
     per-sequence lengths `lens`, and the same random scores."""
     d = draw(w)
@@ -310,7 +310,7 @@ def _step_caches(w, lens, cap, seed):
     sc = (np.random.default_rng(seed).random((B, w.num_kv_heads, cap)) * 0.1).astype(np.float32)
     out = []
     for _ in range(2):
-        gc = make_gpu_cache(w, cap)
+        gc = make_gpu_cache(w, cap, v_bits=v_bits)
         kvc.kvc_quant_append(gc, dev(d["k"][:, :, :Lmax]), dev(d["v"][:, :, :Lmax]))
         gc.lengths.copy_(dev(np.array(lens, np.int32)))
         gc.num_seen.copy_(dev(np.array(lens, np.int32) + 2))
@@ -327,7 +327,7 @@ def _step_pair(w, d, caches, lens, budget, S, R, with_mask):
     q = dev(d["q"])
     res = []
     for i, (gc, sc) in enumerate(caches):
-        dst = make_gpu_cache(w, gc.capacity)
+        dst = make_gpu_cache(w, gc.capacity, v_bits=gc.v_bits)
         dst.k_codes.fill_(0x33)
         dsc = dst.score_buffer()
         dsc.fill_(-2.0)
@@ -884,3 +884,173 @@ def test_llama70b_int4_full_size():
         assert np.array_equal(host(dst.positions[b, g, :w.budget]), pos)
         gpu_sc = host(dst_score[b, g, :w.budget]).astype(np.float64)
         assert np.all(np.abs(gpu_sc - sc) <= 1e-5 * np.abs(sc) + 1e-30)
+
+
+# ------------------------------------------- K and V at different widths --
+
+MIXED = [(8, 4), (4, 8)]
+
+
+@pytest.mark.parametrize("bits,v_bits", MIXED)
+@pytest.mark.parametrize("D,L", [(128, 300), (64, 700)])
+def test_mixed_quant_append_bit_exact(bits, v_bits, D, L):
+    """K codes at `bits`, V codes at `v_bits`: both append kernels (the
+    prefill-sized rows kernel, then the one-token sequence kernel)."""
+    print(f"[mixed quant] bits={bits} v_bits={v_bits} D={D} L={L}", flush=True)
+    w = get("tiny_mha").scaled(context=L, head_dim=D, batch=2)
+    d = draw(w)
+    gc, ref, _ = prefill_both(w, d, bits=bits, v_bits=v_bits)
+    torch.cuda.synchronize()
+    assert gc.v_codes.shape[-1] == D * v_bits // 8
+    assert_codes_equal(gc, ref)
+
+
+@pytest.mark.parametrize("bits,v_bits", MIXED)
+@pytest.mark.parametrize("hq,hkv,D", [(4, 4, 128), (8, 4, 128), (16, 4, 128), (16, 2, 128), (8, 8, 64)])
+def test_mixed_decode_attn(bits, v_bits, hq, hkv, D):
+    """Attention over mixed-width codes (every query-head grouping the kernel
+    has: 1, 2, 4 and 8 per pass) against the oracle, with the H2O scores."""
+    print(f"[mixed attn] bits={bits} v_bits={v_bits} hq={hq} hkv={hkv} D={D}", flush=True)
+    w = get("tiny_mha").scaled(num_q_heads=hq, num_kv_heads=hkv, head_dim=D, batch=2, context=1333)
+    d = draw(w)
+    gc, ref, score = prefill_both(w, d, bits=bits, v_bits=v_bits)
+    out, ro = _attend_both(gc, ref, d["q"], score)
+    assert_out_close(out, ro)
+    assert_scores_close(host(score), ref.score, ref.lengths)
+
+
+@pytest.mark.parametrize("bits,v_bits", MIXED)
+def test_mixed_append_decode_attn(bits, v_bits):
+    """The one-call append + attention equals the two calls bit for bit, and
+    the oracle's append and attention, on ragged lengths."""
+    lens, hq, hkv, D = [700, 255, 64], 8, 2, 128
+    print(f"[mixed append+attn] bits={bits} v_bits={v_bits}", flush=True)
+    B, Lmax = len(lens), max(lens)
+    w = get("tiny_mha").scaled(context=Lmax + 1, batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=D)
+    d = draw(w)
+    cap = Lmax + 6
+    sc = (np.random.default_rng(9).random((B, hkv, cap)) * 0.1).astype(np.float32)
+    caches = []
+    for _ in range(2):
+        gc = make_gpu_cache(w, cap, bits, v_bits=v_bits)
+        kvc.kvc_quant_append(gc, dev(d["k"][:, :, :Lmax]), dev(d["v"][:, :, :Lmax]))
+        gc.lengths.copy_(dev(np.array(lens, np.int32)))
+        gc.num_seen.copy_(dev(np.array(lens, np.int32)))
+        gc.max_len = Lmax
+        caches.append((gc, dev(sc)))
+    (gcA, sA), (gcB, sB) = caches
+    ref = oracle.RefCache(B, hkv, D, cap, bits, v_bits=v_bits)
+    ref.append(d["k"][:, :, :Lmax], d["v"][:, :, :Lmax])
+    ref.lengths[:] = lens
+    ref.num_seen[:] = lens
+    ref.score[:] = sc
+    knew, vnew = d["k"][:, :, Lmax:Lmax + 1], d["v"][:, :, Lmax:Lmax + 1]
+    outA, outB = _append_attn_pair(gcA, gcB, sA, sB, dev(knew), dev(vnew), dev(d["q"]), Lmax, hq)
+    _assert_same_cache(gcA, gcB, sA, sB)
+    assert torch.equal(outA, outB)
+    ref.append(knew, vnew)
+    ro, _ = ref.attend(d["q"], h2o=True)
+    assert_out_close(host(outB), ro)
+    assert_codes_equal(gcB, ref)
+    assert_scores_close(host(sB), ref.score, ref.lengths)
+
+
+@pytest.mark.parametrize("bits,v_bits", MIXED)
+def test_mixed_paged_decode_attn(bits, v_bits):
+    """Paged mixed-width cache (16-token blocks in seeded places): the codes
+    gathered through the table equal the oracle's, and the attention equals
+    the oracle's over the same tokens."""
+    B, H, hq, D, bs, L = 3, 4, 8, 128, 16, 333
+    lens = [L, L - 17, 5]
+    print(f"[mixed paged] bits={bits} v_bits={v_bits}", flush=True)
+    w = get("tiny_mha").scaled(context=L, batch=B, num_q_heads=hq, num_kv_heads=H, head_dim=D)
+    d = draw(w)
+    per = (L + bs - 1) // bs + 1
+    perm = np.random.default_rng(6).permutation(B * per).astype(np.int32).reshape(B, per)
+    gc = kvc.KVCache(B, H, D, 0, bits, block_size=bs, num_blocks=B * per, max_blocks_per_seq=per, v_bits=v_bits)
+    gc.block_table.copy_(dev(perm))
+    kvc.kvc_quant_append(gc, dev(d["k"]), dev(d["v"]), max_len_hint=0)
+    gc.lengths.copy_(dev(np.array(lens, np.int32)))
+    ref = oracle.RefCache(B, H, D, L, bits, v_bits=v_bits)
+    ref.append(d["k"], d["v"])
+    ref.lengths[:] = lens
+    out = torch.empty((B, hq, D), dtype=torch.float32, device="cuda")
+    kvc.kvc_decode_attn(gc, dev(d["q"]), out, max_len_hint=L)
+    ro, _ = ref.attend(d["q"], h2o=False)
+    torch.cuda.synchronize()
+    assert_out_close(host(out), ro)
+    kc, vc = host(gc.k_codes), host(gc.v_codes)
+    for b in range(B):
+        n = lens[b]
+        blocks = perm[b, :(n + bs - 1) // bs]
+        # pool [block, head, slot, bytes] -> [head, token, bytes]
+        kg = kc[blocks].transpose(1, 0, 2, 3).reshape(H, -1, kc.shape[-1])[:, :n]
+        vg = vc[blocks].transpose(1, 0, 2, 3).reshape(H, -1, vc.shape[-1])[:, :n]
+        for g in range(H):
+            assert np.array_equal(kg[g], oracle_code_bytes(ref.k_codes[b, g, :n], bits)), (b, g)
+            assert np.array_equal(vg[g], oracle_code_bytes(ref.v_codes[b, g, :n], v_bits)), (b, g)
+
+
+@pytest.mark.parametrize("bits,v_bits", MIXED)
+@pytest.mark.parametrize("D,L,budget", [(128, 3000, 1000), (64, 20000, 5000)])
+def test_mixed_evict_and_compact(bits, v_bits, D, L, budget):
+    """Eviction (one launch, and selection + gather for the long rows) and the
+    mask compaction on mixed-width rows: equal to each other and to the
+    oracle's selection and compaction."""
+    print(f"[mixed evict] bits={bits} v_bits={v_bits} D={D} L={L}", flush=True)
+    B, H, S, R = 2, 3, 4, 100
+    rng = np.random.default_rng(L + bits)
+    w = get("tiny_mha").scaled(context=L, batch=B, num_q_heads=H, num_kv_heads=H, head_dim=D)
+    d = draw(w)
+    cap = L + 37
+    gc, ref, score = prefill_both(w, d, capacity=cap, bits=bits, v_bits=v_bits)
+    sc = rng.random((B, H, cap)).astype(np.float32) * 3
+    sc[:, :, ::7] = np.float32(0.5)
+    score.copy_(dev(sc))
+    dsts = []
+    for _ in range(3):
+        dst = make_gpu_cache(w, cap, bits, v_bits=v_bits)
+        dst_score = dst.score_buffer()
+        dsts.append((dst, dst_score))
+    kidx = torch.full((B, H, budget), -7, dtype=torch.int32, device="cuda")
+    mask = torch.zeros((B, H, cap), dtype=torch.uint8, device="cuda")
+    kvc.kvc_h2o_evict(gc, score, budget, S, R, kidx, dsts[0][0], dsts[0][1], keep_mask=mask, max_len_hint=L)
+    kvc.kvc_compact_gather(gc, score, kidx, budget, dsts[1][0], dsts[1][1])
+    kvc.kvc_compact(gc, score, mask, dsts[2][0], dsts[2][1])
+    torch.cuda.synchronize()
+    keep = np.stack([np.stack([oracle.select_keep(sc[b, g, :L].astype(np.float64), L, budget, S, R)
+                               for g in range(H)]) for b in range(B)])
+    assert np.array_equal(host(mask)[:, :, :L].astype(bool), keep)
+    full = np.zeros((B, H, cap), bool)
+    full[:, :, :L] = keep
+    ref.score[:] = sc
+    ref.compact(full)
+    for dst, dst_score in dsts:
+        assert_codes_equal(dst, ref)
+        assert np.array_equal(host(dst_score)[:, :, :budget], sc[full].reshape(B, H, budget))
+    _assert_same_cache(dsts[0][0], dsts[1][0], dsts[0][1], dsts[1][1])
+
+
+@pytest.mark.parametrize("bits,v_bits", MIXED)
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2)])
+def test_mixed_decode_step(bits, v_bits, hq, hkv):
+    """The one-call decode step (merged attention statistics, H2O update and
+    eviction) on a mixed-width cache equals the separate calls bit for bit,
+    and its output equals the oracle's attention."""
+    lens, budget, S, R = [2999, 1000, 500], 1000, 4, 100
+    print(f"[mixed step] bits={bits} v_bits={v_bits} hq={hq} hkv={hkv}", flush=True)
+    w = get("tiny_mha").scaled(context=max(lens) + 1, batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                               head_dim=128, bits=bits)
+    d, caches = _step_caches(w, lens, max(lens) + 12, seed=hq, v_bits=v_bits)
+    ref = oracle.RefCache(len(lens), hkv, 128, max(lens) + 12, bits, v_bits=v_bits)
+    ref.append(d["k"][:, :, :max(lens)], d["v"][:, :, :max(lens)])
+    ref.lengths[:] = lens
+    ref.append(d["k"][:, :, max(lens):max(lens) + 1], d["v"][:, :, max(lens):max(lens) + 1])
+    ro, _ = ref.attend(d["q"], h2o=False)
+    (gA, oA, dA, sA, kA, mA), (gB, oB, dB, sB, kB, mB) = _step_pair(w, d, caches, lens, budget, S, R, True)
+    assert torch.equal(oA, oB) and torch.equal(kA, kB) and torch.equal(mA, mB)
+    _assert_same_cache(dA, dB, sA, sB)
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "positions", "lengths", "num_seen"):
+        assert torch.equal(getattr(gA, name), getattr(gB, name)), name
+    assert_out_close(host(oB), ro)
+    assert host(dB.lengths).tolist() == [min(n + 1, budget) for n in lens]

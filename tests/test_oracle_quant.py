@@ -176,3 +176,24 @@ def test_llama7b_int8_layer_bytes():
     assert 32 * 8192 * per_tok == 69_206_016
     # 70B-shaped INT4 layer: B=4 sequences x 8 KV heads x 131072 tokens.
     assert 4 * 8 * 131072 * oracle.compressed_bytes_per_token_head(128, 4) == 570_425_344
+
+
+def test_mixed_widths_are_the_two_uniform_halves():
+    """A cache with INT8 keys and INT4 values (the tutorial's K-V mode, section
+    1.1) holds the K half of an all-INT8 cache and the V half of an all-INT4
+    cache, and its attention is that over those dequantized halves."""
+    rng = np.random.default_rng(41)
+    B, H, D, L = 2, 2, 64, 40
+    k = rng.standard_normal((B, H, L, D)).astype(np.float16)
+    v = rng.standard_normal((B, H, L, D)).astype(np.float16)
+    mixed = oracle.RefCache(B, H, D, L, 8, v_bits=4)
+    k8, v4 = oracle.RefCache(B, H, D, L, 8), oracle.RefCache(B, H, D, L, 4)
+    for c in (mixed, k8, v4):
+        c.append(k, v)
+    assert np.array_equal(mixed.k_codes, k8.k_codes) and np.array_equal(mixed.k_scale, k8.k_scale)
+    assert np.array_equal(mixed.v_codes, v4.v_codes) and np.array_equal(mixed.v_scale, v4.v_scale)
+    assert mixed.v_codes.min() >= -8 and mixed.v_codes.max() <= 7
+    q = rng.standard_normal((B, 4, D)).astype(np.float16)
+    out, _ = mixed.attend(q, h2o=False)
+    want, _ = oracle.decode_attention(q, k8.k_codes, k8.k_scale, v4.v_codes, v4.v_scale, mixed.lengths)
+    assert np.array_equal(out, want)
