@@ -53,8 +53,8 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/quant_row.h",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "5fdb6809371b457a3e30bf75537301492b553aea333a6f961803596f947c7311"
-TRAFFIC_BYTES = 70765042
+TRAFFIC_SHA256 = "59d88fe8787bcdd91164f2feb55c5f4b1ddd0b0af713e3201b984d57c13e149f"
+TRAFFIC_BYTES = 70766067
 
 
 def attention_traffic():
