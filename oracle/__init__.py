@@ -22,6 +22,8 @@ What it computes, and the page passage each part follows:
                 §2.3; eviction-and-reuse survey §4)
 * ``blocks``    block-granular H2O eviction on a paged cache (survey §4;
                 tutorial §3.2)
+* ``tiers``     fp16 sink and recent tiers of a quantized cache (report §3.2;
+                tutorial §1.3)
 
 Floating point is fp64 throughout, except where the method fixes fp32: the
 quantization scale and the quotient that is rounded to a code, both taken as
@@ -30,18 +32,20 @@ correctly rounded fp32 results.
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 invariants, brute force on tiny inputs and the values the pages print.
 """
-from .attention import attend_head_group, decode_attention, paged_decode_attention, paged_gather
+from .attention import attend_head_group, attend_values, decode_attention, paged_decode_attention, paged_gather
 from .cache import RefCache, paged_append
 from .eviction import compact_row, h2o_accumulate, kth_threshold, select_keep
 from .blocks import block_evict, move_block_scores
 from .schedule import layer_budgets
+from .tiers import tier_bounds, tier_values
 from .quant import (QMAX, QMIN, compressed_bytes_per_token_head, dequantize, kv_bytes_per_token,
                     pack_int4, quantize_rows, unpack_int4)
 
 __all__ = [
     "QMAX", "QMIN", "quantize_rows", "dequantize", "pack_int4", "unpack_int4",
     "kv_bytes_per_token", "compressed_bytes_per_token_head",
-    "attend_head_group", "decode_attention", "paged_decode_attention", "paged_gather",
+    "attend_head_group", "attend_values", "decode_attention", "paged_decode_attention", "paged_gather",
     "h2o_accumulate", "select_keep", "kth_threshold", "compact_row",
     "RefCache", "paged_append", "layer_budgets", "block_evict", "move_block_scores",
+    "tier_bounds", "tier_values",
 ]

@@ -40,9 +40,17 @@ def attend_head_group(q16: np.ndarray, kc: np.ndarray, ks: np.ndarray,
     q16 [G][D] fp16; kc, vc [L][D] integer codes (unpacked); ks, vs [L] fp32.
     Returns (out [G][D] fp64, p [G][L] fp64).
     """
+    return attend_values(q16, dequantize(kc, ks), dequantize(vc, vs))
+
+
+def attend_values(q16: np.ndarray, K: np.ndarray, V: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """softmax(q K^T / sqrt(D)) V for the G query heads of one KV head, given
+    the key and value rows as numbers: K, V [L][D] (any real dtype, taken in
+    fp64). Returns (out [G][D] fp64, p [G][L] fp64).
+    """
     D = q16.shape[-1]
-    K = dequantize(kc, ks)                   # [L][D]
-    V = dequantize(vc, vs)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
     q = q16.astype(np.float64)               # [G][D]
     s = (q @ K.T) / math.sqrt(D)             # [G][L]
     m = s.max(axis=1, keepdims=True)

@@ -17,16 +17,17 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode_attention
+from .attention import attend_values, decode_attention
 from .eviction import compact_row, h2o_accumulate, select_keep
 from .quant import quantize_rows
+from .tiers import tier_values
 
 
 class RefCache:
     """Contiguous per-(sequence, KV head) cache with unpacked integer codes."""
 
     def __init__(self, batch: int, num_kv_heads: int, head_dim: int, capacity: int, bits: int,
-                 v_bits: int | None = None):
+                 v_bits: int | None = None, fp16_sinks: int = 0, fp16_recent: int = 0):
         B, H, D, C = batch, num_kv_heads, head_dim, capacity
         self.bits = bits
         # Keys and values may use different widths ("KV Cache optimization
@@ -41,6 +42,14 @@ class RefCache:
         self.score = np.zeros((B, H, C), dtype=np.float64)
         self.lengths = np.zeros(B, dtype=np.int64)
         self.num_seen = np.zeros(B, dtype=np.int64)
+        # fp16 tiers ("KV Cache Compression Report", section 3.2: sinks in fp16;
+        # tutorial section 1.3: recent tokens in fp16). Every slot keeps the
+        # fp16 row it was written with; attention reads it on the tiers.
+        self.fp16_sinks, self.fp16_recent = fp16_sinks, fp16_recent
+        self.tiered = fp16_sinks > 0 or fp16_recent > 0
+        if self.tiered:
+            self.k_raw = np.zeros((B, H, C, D), dtype=np.float16)
+            self.v_raw = np.zeros((B, H, C, D), dtype=np.float16)
 
     # -- quantize-on-write ------------------------------------------------
     def append(self, k16: np.ndarray, v16: np.ndarray) -> None:
@@ -58,14 +67,20 @@ class RefCache:
             self.k_scale[b, :, sl] = sk[b]
             self.v_scale[b, :, sl] = sv[b]
             self.positions[b, :, sl] = self.num_seen[b] + np.arange(n)
+            if self.tiered:
+                self.k_raw[b, :, sl] = k16[b]
+                self.v_raw[b, :, sl] = v16[b]
             self.score[b, :, sl] = 0.0
             self.lengths[b] += n
             self.num_seen[b] += n
 
     # -- attention + H2O --------------------------------------------------
     def attend(self, q16: np.ndarray, h2o: bool = True):
-        out, probs = decode_attention(q16, self.k_codes, self.k_scale, self.v_codes,
-                                      self.v_scale, self.lengths)
+        if self.tiered:
+            out, probs = self._attend_tiered(q16)
+        else:
+            out, probs = decode_attention(q16, self.k_codes, self.k_scale, self.v_codes,
+                                          self.v_scale, self.lengths)
         if h2o:
             Hkv = self.k_codes.shape[1]
             G = q16.shape[1] // Hkv
@@ -76,8 +91,33 @@ class RefCache:
                                                           p[g * G:(g + 1) * G])
         return out, probs
 
+    def _attend_tiered(self, q16: np.ndarray):
+        B, Hq, D = q16.shape
+        Hkv = self.k_codes.shape[1]
+        G = Hq // Hkv
+        out = np.zeros((B, Hq, D))
+        probs = []
+        for b in range(B):
+            L = int(self.lengths[b])
+            pb = np.zeros((Hq, L))
+            for g in range(Hkv):
+                K = tier_values(self.k_codes[b, g], self.k_scale[b, g], self.k_raw[b, g], L,
+                                self.fp16_sinks, self.fp16_recent)
+                V = tier_values(self.v_codes[b, g], self.v_scale[b, g], self.v_raw[b, g], L,
+                                self.fp16_sinks, self.fp16_recent)
+                o, p = attend_values(q16[b, g * G:(g + 1) * G], K, V)
+                out[b, g * G:(g + 1) * G] = o
+                pb[g * G:(g + 1) * G] = p
+            probs.append(pb)
+        return out, probs
+
     # -- eviction ---------------------------------------------------------
     def select(self, budget: int, n_sink: int, n_recent: int) -> np.ndarray:
+        if self.tiered and (n_sink < self.fp16_sinks or n_recent < self.fp16_recent):
+            # Eviction must keep both tiers whole: the sink tier is slots
+            # [0, fp16_sinks) and the recent tier the newest fp16_recent slots.
+            raise ValueError("eviction must keep the fp16 tiers: n_sink >= fp16_sinks, "
+                             "n_recent >= fp16_recent")
         B, H, C = self.score.shape
         keep = np.zeros((B, H, C), dtype=bool)
         for b in range(B):
@@ -102,6 +142,10 @@ class RefCache:
                 for dst, a in zip((self.k_codes, self.v_codes, self.k_scale, self.v_scale,
                                    self.positions, self.score), arrs):
                     dst[b, g, :cnt] = a
+                if self.tiered:  # the fp16 rows travel with their slots
+                    kr, vr = compact_row(keep[b, g, :L], self.k_raw[b, g, :L], self.v_raw[b, g, :L])
+                    self.k_raw[b, g, :cnt] = kr
+                    self.v_raw[b, g, :cnt] = vr
             self.lengths[b] = cnt
             new_len = cnt
         return new_len
