@@ -41,6 +41,9 @@ class KvcCacheDesc(ctypes.Structure):
         ("lengths", ctypes.c_void_p), ("num_seen", ctypes.c_void_p),
         ("positions", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
         ("v_bits", ctypes.c_int32),
+        ("fp16_sinks", ctypes.c_int32), ("fp16_recent", ctypes.c_int32),
+        ("k_sink16", ctypes.c_void_p), ("v_sink16", ctypes.c_void_p),
+        ("k_recent16", ctypes.c_void_p), ("v_recent16", ctypes.c_void_p),
     ]
 
 
@@ -163,11 +166,18 @@ class KVCache:
     Paged layout (``block_size=16``): codes ``[num_blocks][Hkv][16][RB]``,
     scales ``[num_blocks][Hkv][16]``, a ``[B][max_blocks]`` int32 block table,
     and no positions. ``lengths`` and ``num_seen`` are ``[B]`` int32.
+
+    fp16 tiers (``fp16_sinks``, ``fp16_recent`` > 0): fp16 rows
+    ``[B][Hkv][fp16_sinks][head_dim]`` of the first slots and a ring
+    ``[B][Hkv][fp16_recent][head_dim]`` of the newest positions, attended at
+    fp16. A compaction destination passes ``share_tiers_with=src`` so that both
+    descriptors name the same tier buffers.
     """
 
     def __init__(self, batch: int, num_kv_heads: int, head_dim: int, capacity: int, bits: int = 8,
                  device="cuda", block_size: int = 0, num_blocks: int = 0, max_blocks_per_seq: int = 0,
-                 positions: bool = True, v_bits: int = 0):
+                 positions: bool = True, v_bits: int = 0, fp16_sinks: int = 0, fp16_recent: int = 0,
+                 share_tiers_with: "Optional[KVCache]" = None):
         import torch
         self.batch, self.num_kv_heads, self.head_dim, self.bits = batch, num_kv_heads, head_dim, bits
         self.v_bits = v_bits            # 0: V at the K width
@@ -191,6 +201,18 @@ class KVCache:
         self.v_scale = torch.zeros(rows, dtype=torch.float32, device=device)
         self.lengths = torch.zeros(batch, dtype=torch.int32, device=device)
         self.num_seen = torch.zeros(batch, dtype=torch.int32, device=device)
+        if share_tiers_with is not None:
+            o = share_tiers_with
+            fp16_sinks, fp16_recent = o.fp16_sinks, o.fp16_recent
+            self.k_sink16, self.v_sink16 = o.k_sink16, o.v_sink16
+            self.k_recent16, self.v_recent16 = o.k_recent16, o.v_recent16
+        else:
+            def tier(n):
+                return torch.zeros((batch, num_kv_heads, n, head_dim), dtype=torch.float16,
+                                   device=device) if n else None
+            self.k_sink16, self.v_sink16 = tier(fp16_sinks), tier(fp16_sinks)
+            self.k_recent16, self.v_recent16 = tier(fp16_recent), tier(fp16_recent)
+        self.fp16_sinks, self.fp16_recent = fp16_sinks, fp16_recent
         self.max_len = 0   # host-side upper bound of the device lengths
         self.desc = self._make_desc()
 
@@ -205,6 +227,9 @@ class KVCache:
         d.lengths, d.num_seen = _ptr(self.lengths), _ptr(self.num_seen)
         d.positions = _ptr(self.positions)
         d.block_table = _ptr(self.block_table)
+        d.fp16_sinks, d.fp16_recent = self.fp16_sinks, self.fp16_recent
+        d.k_sink16, d.v_sink16 = _ptr(self.k_sink16), _ptr(self.v_sink16)
+        d.k_recent16, d.v_recent16 = _ptr(self.k_recent16), _ptr(self.v_recent16)
         return d
 
     def table_view(self):

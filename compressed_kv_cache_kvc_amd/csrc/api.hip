@@ -77,11 +77,44 @@ int32_t check_cache(const kvc_cache_t* c, const char* name) {
   } else {
     return fail(KVC_ERR_UNSUPPORTED, "%s: block_size must be 0 (contiguous) or 16 (got %d)", name, c->block_size);
   }
+  if (c->fp16_sinks < 0 || c->fp16_recent < 0)
+    return fail(KVC_ERR_INVALID_ARG, "%s: fp16_sinks and fp16_recent must be >= 0", name);
+  if ((c->fp16_sinks && (!c->k_sink16 || !c->v_sink16)) || (c->fp16_recent && (!c->k_recent16 || !c->v_recent16)))
+    return fail(KVC_ERR_INVALID_ARG, "%s: NULL fp16 tier buffer", name);
+  if (((uintptr_t)c->k_sink16 | (uintptr_t)c->v_sink16 | (uintptr_t)c->k_recent16 | (uintptr_t)c->v_recent16) % 16)
+    return fail(KVC_ERR_INVALID_ARG, "%s: fp16 tier buffers must be 16-byte aligned", name);
+  return KVC_OK;
+}
+
+bool tiered(const kvc_cache_t* c) { return c->fp16_sinks > 0 || c->fp16_recent > 0; }
+
+// The tier kernels copy new rows 16 bytes at a time.
+int32_t check_tier_inputs(const kvc_cache_t* c, const void* k_new, const void* v_new) {
+  if (tiered(c) && (((uintptr_t)k_new | (uintptr_t)v_new) % 16))
+    return fail(KVC_ERR_INVALID_ARG, "with fp16 tiers, k_new and v_new must be 16-byte aligned");
+  return KVC_OK;
+}
+
+// Eviction keeps the fp16 tiers whole only if the sink and recent counts cover
+// them (the tiers are the first and the newest slots of a row).
+int32_t check_tiers_kept(const kvc_cache_t* c, int32_t n_sink, int32_t n_recent) {
+  if (n_sink < c->fp16_sinks || n_recent < c->fp16_recent)
+    return fail(KVC_ERR_INVALID_ARG, "eviction must keep the fp16 tiers (n_sink %d >= fp16_sinks %d, n_recent %d >= "
+                "fp16_recent %d)", n_sink, c->fp16_sinks, n_recent, c->fp16_recent);
+  return KVC_OK;
+}
+
+// A compaction's destination uses the source's fp16 tier buffers.
+int32_t check_same_tiers(const kvc_cache_t* src, const kvc_cache_t* dst) {
+  if (src->fp16_sinks != dst->fp16_sinks || src->fp16_recent != dst->fp16_recent ||
+      (src->fp16_sinks && (src->k_sink16 != dst->k_sink16 || src->v_sink16 != dst->v_sink16)) ||
+      (src->fp16_recent && (src->k_recent16 != dst->k_recent16 || src->v_recent16 != dst->v_recent16)))
+    return fail(KVC_ERR_INVALID_ARG, "src and dst must name the same fp16 tiers");
   return KVC_OK;
 }
 
 struct AttnGeom {
-  int splits, tiles;
+  int splits, tiles, tier_parts;
   size_t off_ml, off_logits, off_stash, total;
 };
 
@@ -106,13 +139,18 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
   const long long rows = (long long)c->batch * c->num_kv_heads;
   const long long nt = std::max(1LL, tiles_total * rows / 512);
   const long long S = (tiles_total + nt - 1) / nt;
-  if (S * (G + 2) > 16384) return fail(KVC_ERR_UNSUPPORTED, "too many splits for one KV head (%lld x %d)", S, G);
+  // fp16 tiers: one extra partial state per 64 tier tokens, after the splits.
+  const long long tier_tok = std::min<long long>((long long)c->fp16_sinks + c->fp16_recent, hint);
+  const long long TP = (tier_tok + kTierTokens - 1) / kTierTokens;
+  const long long P = S + TP;
+  if (P * (G + 2) > 16384) return fail(KVC_ERR_UNSUPPORTED, "too many splits for one KV head (%lld x %d)", P, G);
   const size_t BH = (size_t)c->batch * Hq;
-  const size_t part_o = align256(BH * S * c->head_dim * sizeof(float));
-  const size_t part_ml = align256(BH * S * 2 * sizeof(float));
+  const size_t part_o = align256(BH * P * c->head_dim * sizeof(float));
+  const size_t part_ml = align256(BH * P * 2 * sizeof(float));
   const size_t logits = with_h2o ? align256(BH * S * nt * kSplitTokens * sizeof(float)) : 0;
   g->splits = (int)S;
   g->tiles = (int)nt;
+  g->tier_parts = (int)TP;
   g->off_ml = part_o;
   g->off_logits = part_o + part_ml;
   g->off_stash = part_o + part_ml + logits;
@@ -157,6 +195,7 @@ int32_t check_compact_pair(const kvc_cache_t* src, const kvc_cache_t* dst, const
   if (src->bits != dst->bits || vbits_of(*src) != vbits_of(*dst) || src->batch != dst->batch ||
       src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim || src->capacity != dst->capacity)
     return fail(KVC_ERR_INVALID_ARG, "src and dst geometries differ");
+  if ((st = check_same_tiers(src, dst))) return st;
   if ((src_score == nullptr) != (dst_score == nullptr))
     return fail(KVC_ERR_INVALID_ARG, "pass both src_score and dst_score, or neither");
   return KVC_OK;
@@ -195,6 +234,7 @@ int32_t kvc_quant_append(const kvc_cache_t* cache, const void* k_new, const void
   if ((long long)max_len_hint + n_new > cache->capacity)
     return fail(KVC_ERR_CAPACITY, "max_len_hint %d + n_new %d exceeds capacity %d", max_len_hint, n_new,
                 cache->capacity);
+  if ((st = check_tier_inputs(cache, k_new, v_new))) return st;
   return device_status(launch_quant_append(*cache, static_cast<const __half*>(k_new),
                                            static_cast<const __half*>(v_new), n_new, h2o_score,
                                            static_cast<hipStream_t>(stream)),
@@ -226,6 +266,7 @@ int32_t prepare_attn(const kvc_cache_t* cache, const void* k_new, const void* v_
   if (!workspace || workspace_bytes < g.total)
     return fail(KVC_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", g.total, workspace ? workspace_bytes : 0);
   if ((uintptr_t)workspace % 256) return fail(KVC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if ((st = check_tier_inputs(cache, k_new, v_new))) return st;
   a->c = *cache;
   a->q = static_cast<const __half*>(q);
   a->out = out;
@@ -241,6 +282,8 @@ int32_t prepare_attn(const kvc_cache_t* cache, const void* k_new, const void* v_
   a->num_q_heads = num_q_heads;
   a->splits = g.splits;
   a->tiles = g.tiles;
+  a->tier_parts = g.tier_parts;
+  a->parts = g.splits + g.tier_parts;
   a->qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
   return KVC_OK;
 }
@@ -286,6 +329,7 @@ int32_t check_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budg
   if (budget < 1) return fail(KVC_ERR_INVALID_ARG, "budget must be >= 1");
   if (n_sink < 0 || n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
   if ((long long)n_sink + n_recent > budget) return fail(KVC_ERR_INVALID_ARG, "n_sink + n_recent exceeds budget");
+  if ((st = check_tiers_kept(src, n_sink, n_recent))) return st;
   if (budget > src->capacity) return fail(KVC_ERR_CAPACITY, "budget exceeds capacity");
   if (max_len < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
   if (max_len > src->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
@@ -404,6 +448,7 @@ int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t
   if (budget < 1) return fail(KVC_ERR_INVALID_ARG, "budget must be >= 1");
   if (n_sink < 0 || n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
   if ((long long)n_sink + n_recent > budget) return fail(KVC_ERR_INVALID_ARG, "n_sink + n_recent exceeds budget");
+  if ((st = check_tiers_kept(cache, n_sink, n_recent))) return st;
   if (budget > cache->capacity) return fail(KVC_ERR_CAPACITY, "budget exceeds capacity");
   if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
   if (max_len_hint > cache->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
@@ -466,6 +511,8 @@ int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, do
   if ((st = check_cache(dst, "dst"))) return st;
   if (src->block_size == 0 || dst->block_size == 0)
     return fail(KVC_ERR_INVALID_ARG, "block eviction needs paged caches");
+  if (tiered(src) || tiered(dst))
+    return fail(KVC_ERR_UNSUPPORTED, "block eviction keeps no sinks or window, so it cannot keep fp16 tiers");
   if (src->bits != dst->bits || vbits_of(*src) != vbits_of(*dst) || src->batch != dst->batch ||
       src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim || src->capacity != dst->capacity ||
       src->max_blocks_per_seq != dst->max_blocks_per_seq || src->num_blocks != dst->num_blocks)
@@ -555,7 +602,7 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
   EvictArgs e = evict_args(cache, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,
                            max_len_hint + 1);
   if (evict_fits_one_launch(e.max_len, n_sink, n_recent) &&
-      evict_can_merge(num_q_heads, cache->num_kv_heads, a.splits)) {
+      evict_can_merge(num_q_heads, cache->num_kv_heads, a.parts)) {
     // Two launches: the split kernel (with the append), then the eviction
     // kernel that also merges the splits.
     if ((st = device_status(launch_attn_split(a, s), "kvc_decode_step split launch"))) return st;
@@ -565,7 +612,7 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
     e.stash = a.stash;
     e.out = out;
     e.num_q_heads = num_q_heads;
-    e.splits = a.splits;
+    e.splits = a.parts;  // partial states per head: the splits and the fp16-tier parts
     e.span = (long long)a.splits * a.tiles * kSplitTokens;
     return device_status(launch_evict(e, s), "kvc_decode_step eviction launch");
   }

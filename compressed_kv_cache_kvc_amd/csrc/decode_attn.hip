@@ -191,6 +191,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   const bool app = a.k_new != nullptr;
   const int L_old = __builtin_amdgcn_readfirstlane(c.lengths[b]);
   const int L = __builtin_amdgcn_readfirstlane(min(min(L_old + (app ? 1 : 0), c.capacity), (int)span));
+  // fp16 tiers: slots [t_lo, t_hi) are read from the codes; the sink tier
+  // below and the recent tier above are attended by attn_tier_kernel (their
+  // logits are masked here and not spilled, and blocks past t_hi not read).
+  // Without tiers t_lo = 0 and t_hi = L.
+  const int t_lo = max(0, min(c.fp16_sinks, L));
+  const int t_hi = L - max(0, min(c.fp16_recent, L - t_lo));
 
   __shared__ __align__(16) uint8_t v_stage[4][64 * VROW];
   __shared__ __align__(16) int8_t w_limb[4][NRS][16][64];
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   // This wave's blocks: block `it` starts at token t0(it) and holds tokens
   // below L only for it < nb.
   auto block_t0 = [&](int it) { return ((s * NT + it) * 4 + wave) * 64; };
-  const int nb = max(0, min(NT, (L - ((s * NT) * 4 + wave) * 64 + 255) / 256));
+  const int nb = max(0, min(NT, (t_hi - ((s * NT) * 4 + wave) * 64 + 255) / 256));
 
   // Append: the wave whose block `it_new` holds slot L_old quantizes the new
   // token's K and V rows into the cache before its first loads (the
@@ -453,10 +459,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
       for (int cc = 0; cc < NC; ++cc) {
         const int j = 4 * cc + quad, tok = 16 * (j / GP) + col;
         float x = (limb_sum(acc[cc]) - qo[cc]) * qf[cc] * r.ksv[GP >= 8 ? cc / 2 : cc];
-        if (t0 + tok >= L || !hv[cc]) x = -INFINITY;
+        const int ti = t0 + tok;
+        const bool coded = ti >= t_lo && ti < t_hi;
+        if (!coded || !hv[cc]) x = -INFINITY;
         sv[cc] = x;
-        if (a.logits != nullptr && hv[cc])  // H2O: spill the logit
-          a.logits[((long long)b * Hq + g * G + hp + j % GP) * span + t0 + tok] = x;
+        if (a.logits != nullptr && hv[cc] && (coded || ti >= L))  // H2O: spill the logit (tier slots: their kernel)
+          a.logits[((long long)b * Hq + g * G + hp + j % GP) * span + ti] = x;
       }
 
       // ---- online softmax, one running state per (wave, head) ----
@@ -578,13 +586,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
 #pragma unroll
       for (int w = 0; w < 4; ++w) o = fmaf(red_o[(w * GP + i) * D + d], part_weight(red_m[w][i], M), o);
       const long long hq = (long long)b * Hq + g * G + hp + i;
-      a.part_o[(hq * S + s) * D + d] = o;
+      a.part_o[(hq * a.parts + s) * D + d] = o;
       if (d == 0) {
         float l = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) l = fmaf(red_l[w][i], part_weight(red_m[w][i], M), l);
-        a.part_ml[(hq * S + s) * 2] = M;
-        a.part_ml[(hq * S + s) * 2 + 1] = l;
+        a.part_ml[(hq * a.parts + s) * 2] = M;
+        a.part_ml[(hq * a.parts + s) * 2 + 1] = l;
       }
     }
     __syncthreads();
@@ -609,8 +617,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const kvc_cache_t& c = a.c;
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits;
-  const long long span = (long long)S * a.tiles * TS;
+  // S: the partial states per head (the splits and the fp16-tier parts).
+  const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.parts;
+  const long long span = (long long)a.splits * a.tiles * TS;
   // With an append, the length before it comes from the split kernel (the
   // cache's own length is advanced here, by one workgroup).
   const bool app = a.append != 0;
@@ -724,8 +733,11 @@ hipError_t launch_dim(const AttnLaunch& a, int G, hipStream_t st) {
 hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
   const int vb = vbits_of(a.c);
-  if (a.c.bits == 8) return vb == 8 ? launch_dim<8, 8>(a, G, st) : launch_dim<8, 4>(a, G, st);
-  return vb == 8 ? launch_dim<4, 8>(a, G, st) : launch_dim<4, 4>(a, G, st);
+  hipError_t e;
+  if (a.c.bits == 8) e = vb == 8 ? launch_dim<8, 8>(a, G, st) : launch_dim<8, 4>(a, G, st);
+  else e = vb == 8 ? launch_dim<4, 8>(a, G, st) : launch_dim<4, 4>(a, G, st);
+  if (e != hipSuccess) return e;
+  return launch_attn_tiers(a, st);
 }
 
 hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st) {
@@ -739,7 +751,7 @@ hipError_t launch_attn_merge(const AttnLaunch& a, hipStream_t st) {
   const long long span = (long long)a.splits * a.tiles * TS;
   const int h2o_blocks = a.score ? (int)((span + kH2oChunk - 1) / kH2oChunk) : 0;
   const int nh = G;  // the H2O blocks need every head's statistics
-  const size_t lds = (size_t)nh * (a.splits + 2) * sizeof(float);
+  const size_t lds = (size_t)nh * (a.parts + 2) * sizeof(float);
   const dim3 grid(G + h2o_blocks, a.c.num_kv_heads, a.c.batch);
   const int gmax = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
 #define KVC_COMBINE(DD, GG) \

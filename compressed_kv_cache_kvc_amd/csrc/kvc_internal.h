@@ -45,6 +45,8 @@ int32_t fail(int32_t status, const char* fmt, ...);
 
 // Tokens per split of the decode-attention kernel (one workgroup per split).
 constexpr int kSplitTokens = 256;
+// fp16-tier tokens per workgroup (one wave) of the tier attention kernel.
+constexpr int kTierTokens = 64;
 // Slots per chunk of the compaction kernels.
 constexpr int kCompactChunk = 256;
 // Rows of at most this many chunks are compacted in one launch (each
@@ -60,8 +62,8 @@ struct AttnLaunch {
   const __half* q;
   float* out;
   float* score;      // NULL = no H2O
-  float* part_o;     // [B][Hq][S][D]
-  float* part_ml;    // [B][Hq][S][2]  (max in log2 units, sum)
+  float* part_o;     // [B][Hq][parts][D]
+  float* part_ml;    // [B][Hq][parts][2]  (max in log2 units, sum)
   float* logits;     // [B][Hq][S * tiles * kSplitTokens], log2 units (only with H2O)
   // With k_new and v_new ([B][Hkv][D] fp16): append one token per sequence
   // first (slot lengths[b]); NULL: attention only.
@@ -72,10 +74,19 @@ struct AttnLaunch {
   int num_q_heads;
   int splits;        // S: workgroups per (sequence, KV head)
   int tiles;         // 256-token tiles per split
+  int tier_parts;    // TP: fp16-tier partial states per (sequence, query head), after the S splits
+  int parts;         // S + TP: partial states per query head in part_o / part_ml
   float qk_log2;     // log2(e) / sqrt(head_dim)
 };
 hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st);  // split, then merge
-hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st);
+hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st);  // the code splits and the fp16-tier parts
+// The fp16 tiers' partial states (parts S .. S + TP - 1) and their logits;
+// with an append, also the new token's tier rows.
+hipError_t launch_attn_tiers(const AttnLaunch& a, hipStream_t st);
+// Stores the fp16 rows of n_new appended tokens in the cache's tiers (before
+// the append advances the lengths).
+hipError_t launch_tier_append(const kvc_cache_t& c, const __half* k_new, const __half* v_new, int n_new,
+                              hipStream_t st);
 hipError_t launch_attn_merge(const AttnLaunch& a, hipStream_t st);
 
 hipError_t launch_select(const kvc_cache_t& c, const float* score, int budget, int n_sink,

@@ -134,6 +134,9 @@ hipError_t launch_dim(const kvc_cache_t& c, const __half* kn, const __half* vn, 
 
 hipError_t launch_quant_append(const kvc_cache_t& c, const __half* kn, const __half* vn, int n_new,
                                float* score, hipStream_t st) {
+  // fp16 tiers first: that kernel reads the lengths before this append.
+  const hipError_t e = launch_tier_append(c, kn, vn, n_new, st);
+  if (e != hipSuccess) return e;
   const int vb = vbits_of(c);
   if (c.bits == 8)
     return vb == 8 ? launch_dim<8, 8>(c, kn, vn, n_new, score, st) : launch_dim<8, 4>(c, kn, vn, n_new, score, st);

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum {
   KVC_OK = 0,
@@ -80,6 +80,26 @@ typedef enum {
  * INT8 codes are two's-complement bytes in [-127, 127]. INT4 codes are
  * two's-complement nibbles in [-7, 7], element 2j in the low nibble of byte j
  * and element 2j+1 in the high nibble. A token's value is code * scale.
+ *
+ * fp16 tiers (optional; "KV Cache Compression Report", section 3.2: the
+ * attention-sink tokens keep fp16 K and V; "KV Cache optimization techniques"
+ * tutorial, section 1.3: recent tokens at fp16, older ones quantized). In a row
+ * of L slots, the sink tier is slots [0, ns) with ns = min(fp16_sinks, L) and
+ * the recent tier the last nr = min(fp16_recent, L - ns) slots; attention
+ * reads tier slots at their fp16 values and every other slot from its codes.
+ * Codes are still written for every token.
+ *    k_sink16, v_sink16      fp16 [batch][num_kv_heads][fp16_sinks][head_dim]:
+ *                            the row of slot j < fp16_sinks
+ *    k_recent16, v_recent16  fp16 [batch][num_kv_heads][fp16_recent][head_dim]:
+ *                            a ring, the row of position p at p % fp16_recent,
+ *                            where slot i of the recent tier holds position
+ *                            num_seen - L + i
+ * The appends fill them. The tiers stay valid through eviction only while it
+ * keeps slots [0, fp16_sinks) and the newest fp16_recent slots: the eviction
+ * calls require n_sink >= fp16_sinks and n_recent >= fp16_recent, and a
+ * caller-made keep mask or list must keep those slots. A compaction's
+ * destination names the same tier buffers as its source (they are indexed by
+ * slot or position, both unchanged by a stable compaction).
  */
 typedef struct kvc_cache {
   int32_t bits;                /* 8 or 4: K code width (and V's unless v_bits is set) */
@@ -102,6 +122,12 @@ typedef struct kvc_cache {
                                   widths ("KV Cache optimization techniques" tutorial,
                                   section 1.1: the quantizer's K-V mode, keys and values at
                                   different precision) */
+  int32_t fp16_sinks;          /* >= 0: slots of the fp16 sink tier (0 = none) */
+  int32_t fp16_recent;         /* >= 0: slots of the fp16 recent tier (0 = none) */
+  void* k_sink16;              /* fp16 tier buffers, layouts above; NULL when the tier is 0 */
+  void* v_sink16;
+  void* k_recent16;
+  void* v_recent16;
 } kvc_cache_t;
 
 /* ABI version compiled into the library (KVC_ABI_VERSION). */
@@ -130,11 +156,15 @@ const char* kvc_last_error(void);
  * The row is written at slot lengths[b] + t; positions (if not NULL) get
  * num_seen[b] + t; h2o_score (if not NULL, [batch][num_kv_heads][capacity]
  * fp32) is set to 0 at the new slots. lengths[b] and num_seen[b] then advance
- * by n_new, on the device, in stream order.
+ * by n_new, on the device, in stream order. With fp16 tiers the new fp16 rows
+ * are also stored for them: slot lengths[b] + t < fp16_sinks goes to the sink
+ * buffer, and the newest fp16_recent new tokens go to the recent ring.
  *
  * k_new, v_new: device fp16 [batch][num_kv_heads][n_new][head_dim].
- * Errors: INVALID_ARG for a bad descriptor, NULL inputs or n_new < 1 or
- * max_len_hint < 0; CAPACITY if max_len_hint + n_new > capacity. Paged: the
+ * Errors: INVALID_ARG for a bad descriptor (including negative fp16 tier
+ * sizes, NULL or non-16-byte-aligned tier buffers), NULL inputs, n_new < 1,
+ * max_len_hint < 0, or k_new / v_new not 16-byte aligned on a tiered cache;
+ * CAPACITY if max_len_hint + n_new > capacity. Paged: the
  * blocks for the new slots must already be in the table; slots whose block is
  * missing are skipped by the kernel.
  */
@@ -166,6 +196,9 @@ size_t kvc_decode_attn_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_h
  *   out[b][h][:] = sum_i p_i * scale^V_i * code^V_i
  * If h2o_score is not NULL ([batch][num_kv_heads][capacity] fp32):
  *   h2o_score[b][g][i] += sum over the G query heads of g of p_i.
+ * With fp16 tiers, the key and value of a tier slot are its fp16 rows instead
+ * of code * scale (the tier slots' logits and values are computed in fp32 from
+ * fp16; the codes of the recent tier are not read).
  *
  * q: device fp16 [batch][num_q_heads][head_dim]; out: device fp32
  * [batch][num_q_heads][head_dim]. workspace: device memory of at least
@@ -246,8 +279,9 @@ int32_t kvc_decode_attn_merge(const kvc_cache_t* cache, int32_t appended, int32_
  * entries are left untouched. h2o_score must hold non-negative, non-NaN values
  * (attention mass always is).
  * Errors: INVALID_ARG for a bad descriptor, NULL score or mask, budget < 1,
- * n_sink < 0, n_recent < 0 or n_sink + n_recent > budget; CAPACITY if budget
- * or max_len_hint > capacity.
+ * n_sink < 0, n_recent < 0, n_sink + n_recent > budget, or a tiered cache with
+ * n_sink < fp16_sinks or n_recent < fp16_recent; CAPACITY if budget or
+ * max_len_hint > capacity.
  */
 int32_t kvc_h2o_select(const kvc_cache_t* cache, const float* h2o_score, int32_t budget,
                        int32_t n_sink, int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index,
@@ -273,7 +307,11 @@ size_t kvc_compact_workspace_bytes(const kvc_cache_t* src, int32_t max_len_hint)
  * src and dst must be contiguous caches with the same bits, batch,
  * num_kv_heads, head_dim and capacity; no dst buffer may overlap a src buffer,
  * the mask or the src scores (INVALID_ARG otherwise); paged caches give
- * UNSUPPORTED. workspace: device memory of kvc_compact_workspace_bytes(...).
+ * UNSUPPORTED. With fp16 tiers, dst must name src's tier sizes and buffers
+ * (INVALID_ARG otherwise), and the mask must keep slots [0, fp16_sinks) and
+ * the newest fp16_recent slots of each row (not checked: the tiers would then
+ * describe other tokens). workspace: device memory of
+ * kvc_compact_workspace_bytes(...).
  */
 int32_t kvc_compact(const kvc_cache_t* src, const float* src_score, const uint8_t* keep_mask,
                     const kvc_cache_t* dst, float* dst_score, int32_t max_len_hint,
@@ -386,7 +424,8 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
  * Errors: INVALID_ARG for bad or contiguous descriptors, different
  * geometries or pools, NULL arrays, retention outside [0, 1], overlapping
  * inputs and outputs; CAPACITY if max_len_hint > capacity; UNSUPPORTED above
- * 8192 blocks per sequence.
+ * 8192 blocks per sequence, or for caches with fp16 tiers (block eviction
+ * keeps no sinks or window, so it cannot keep the tiers).
  */
 int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, double retention,
                               const kvc_cache_t* dst, float* dst_score, int32_t* freed,

@@ -42,7 +42,7 @@ def test_exports_match_binding_names():
 
 
 def test_version_and_status_strings():
-    assert kvc.kvc_abi_version() == 2
+    assert kvc.kvc_abi_version() == 3
     assert kvc.kvc_status_str(0) == "KVC_OK"
     assert kvc.kvc_status_str(2) == "KVC_ERR_CAPACITY"
     assert kvc.kvc_status_str(99) == "KVC_UNKNOWN"
@@ -270,6 +270,51 @@ def test_compact_validation():
     assert step(s_=paged) == UNSUPPORTED
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 512) >= 4 * 1 * 4
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 2048) == 0   # beyond capacity
+
+
+def test_fp16_tier_validation():
+    T = dict(fp16_sinks=4, fp16_recent=8, k_sink16=0x8000000, v_sink16=0x8100000, k_recent16=0x8200000,
+             v_recent16=0x8300000)
+    # descriptor: negative, oversized, NULL or misaligned tier buffers
+    for bad in (dict(fp16_sinks=-1), dict(fp16_recent=-2), dict(k_sink16=None),
+                dict(v_recent16=None), dict(k_recent16=0x8200008)):
+        assert append(desc(**{**T, **bad})) == INVALID, bad
+    assert append(desc(fp16_sinks=4)) == INVALID                       # tier without buffers
+    # the tier copies read the new rows 16 bytes at a time
+    assert append(desc(**T), k=FAKE + 8) == INVALID
+    d = desc(**T)
+    need = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), 4, 17, 1)
+    assert need > lib.kvc_decode_attn_workspace_bytes(ctypes.byref(desc()), 4, 17, 1)  # the tier parts
+    assert lib.kvc_append_decode_attn(ctypes.byref(d), FAKE + 8, FAKE, FAKE, 4, FAKE, None, 16, FAKE * 256,
+                                      need, None) == INVALID
+    # eviction must keep both tiers
+    sel = lambda s, r: lib.kvc_h2o_select(ctypes.byref(d), FAKE, 32, s, r, FAKE, None, 16, None)
+    assert sel(3, 8) == INVALID
+    assert sel(4, 7) == INVALID
+    src = desc(k_codes=0x100000, v_codes=0x200000, k_scale=0x300000, v_scale=0x400000,
+               positions=0x500000, lengths=0x600000, num_seen=0x600100, **T)
+    dst = desc(k_codes=0x1100000, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
+               positions=0x1500000, lengths=0x1600000, num_seen=0x1600100, **T)
+    evict = lambda s_, d_, ns=4, nr=8: lib.kvc_h2o_evict(ctypes.byref(s_), 0x4000000, 32, ns, nr, None, 0x5000000,
+                                                         ctypes.byref(d_), None, 16, None)
+    assert evict(src, dst, ns=3) == INVALID
+    assert evict(src, dst, nr=7) == INVALID
+    # a compaction's destination names the source's tier buffers
+    own = desc(k_codes=0x1100000, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
+               positions=0x1500000, lengths=0x1600000, num_seen=0x1600100, **{**T, "k_sink16": 0x9000000})
+    assert evict(src, own) == INVALID
+    assert lib.kvc_compact_gather(ctypes.byref(src), None, 0x5000000, 16, ctypes.byref(own), None, None) == INVALID
+    untiered = desc(k_codes=0x1100000, v_codes=0x1200000, k_scale=0x1300000, v_scale=0x1400000,
+                    positions=0x1500000, lengths=0x1600000, num_seen=0x1600100)
+    assert lib.kvc_compact(ctypes.byref(src), None, 0x2000000, ctypes.byref(untiered), None, 16, 0x3000000, 1 << 20,
+                           None) == INVALID
+    # block eviction keeps no window, so it cannot keep tiers
+    ps = desc(block_size=16, max_blocks_per_seq=32, num_blocks=64, positions=None, block_table=0xA000000,
+              lengths=0xA100000, num_seen=0xA100100, **T)
+    pd = desc(block_size=16, max_blocks_per_seq=32, num_blocks=64, positions=None, block_table=0xB000000,
+              lengths=0xB100000, num_seen=0xB100100, **T)
+    assert lib.kvc_paged_block_evict(ctypes.byref(ps), 0xC000000, 0.5, ctypes.byref(pd), 0xD000000, 0xE000000,
+                                     0xE100000, 100, None) == UNSUPPORTED
 
 
 # -- block pool -----------------------------------------------------------------
