@@ -318,6 +318,38 @@ def secondary_attention(kvc, torch, reps=16):
                {"tokens": B * L, "h2o": True, "bits": w.bits, "q_heads": Hq, "kv_heads": H})
         del caches, scores, ws
         torch.cuda.empty_cache()
+
+    # The LLaMA-7B layer with fp16 tiers, next to the same layer without: the
+    # report's fp16 sinks on an INT8 cache (4 sinks), and the tutorial's hybrid
+    # (INT4 codes, 4 fp16 sinks and the newest int(0.3 L) tokens at fp16). One
+    # whole attention call (split, tier and merge kernels) with H2O, over 32
+    # rotated layer buffers. Bytes: codes + scales of the coded slots, fp16
+    # rows of the tier slots, and q.
+    w = get("llama7b_8k")
+    B, Hq, H, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.context
+    n_bufs = 32
+    for name, bits, s16, r16 in (("llama7b_8k_no_tiers", 8, 0, 0), ("llama7b_8k_fp16_sinks", 8, 4, 0),
+                                 ("llama7b_8k_int4_hybrid", 4, 4, int(0.3 * L))):
+        caches, scores = [], []
+        for i in range(n_bufs):
+            c = kvc.KVCache(B, H, D, L, bits, fp16_sinks=s16, fp16_recent=r16)
+            kv = torch.randn((2, B, H, L, D), device="cuda").half()
+            kvc.kvc_quant_append(c, kv[0], kv[1], max_len_hint=0)
+            del kv
+            caches.append(c)
+            scores.append(c.score_buffer())
+        q = torch.randn((B, Hq, D), device="cuda").half()
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, L, True), dtype=torch.uint8,
+                         device="cuda")
+        us = timed(lambda i: kvc.kvc_decode_attn(caches[i], q, out, h2o_score=scores[i], max_len_hint=L,
+                                                 workspace=ws), n_bufs)
+        tier = min(s16 + r16, L)
+        kv_bytes = B * H * 2 * ((L - tier) * (D * bits // 8 + 4) + tier * D * 2) + q.numel() * 2
+        report(name, w, kv_bytes, us, {"tokens": B * L, "h2o": True, "bits": bits, "fp16_sinks": s16,
+                                       "fp16_recent": r16, "calls": "kvc_decode_attn (split, tiers, merge)"})
+        del caches, scores, ws
+        torch.cuda.empty_cache()
     return res
 
 

@@ -79,10 +79,10 @@ struct AttnLaunch {
   float qk_log2;     // log2(e) / sqrt(head_dim)
 };
 hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st);  // split, then merge
-hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st);  // the code splits and the fp16-tier parts
-// The fp16 tiers' partial states (parts S .. S + TP - 1) and their logits;
-// with an append, also the new token's tier rows.
-hipError_t launch_attn_tiers(const AttnLaunch& a, hipStream_t st);
+// The code splits, then (on a tiered cache) the fp16-tier parts S .. S + TP - 1
+// in a second kernel (with an append, it also stores the new token's tier
+// rows).
+hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st);
 // Stores the fp16 rows of n_new appended tokens in the cache's tiers (before
 // the append advances the lengths).
 hipError_t launch_tier_append(const kvc_cache_t& c, const __half* k_new, const __half* v_new, int n_new,
