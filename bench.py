@@ -52,9 +52,10 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/kvc_internal.h",
                    "compressed_kv_cache_kvc_amd/csrc/quant_row.h",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
+                   "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "59d88fe8787bcdd91164f2feb55c5f4b1ddd0b0af713e3201b984d57c13e149f"
-TRAFFIC_BYTES = 70766067
+TRAFFIC_SHA256 = "f10a226ea538f45dd782242c7659b627fb6af64c653445d67a4058dfad5db525"
+TRAFFIC_BYTES = 70757366
 
 
 def attention_traffic():
