@@ -114,7 +114,7 @@ int32_t check_same_tiers(const kvc_cache_t* src, const kvc_cache_t* dst) {
 }
 
 struct AttnGeom {
-  int splits, tiles, tier_parts;
+  int splits, tiles, last_tiles, tier_parts;
   size_t off_ml, off_logits, off_stash, total;
 };
 
@@ -138,7 +138,14 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
   const long long tiles_total = (hint + kSplitTokens - 1) / kSplitTokens;
   const long long rows = (long long)c->batch * c->num_kv_heads;
   const long long nt = std::max(1LL, tiles_total * rows / 512);
-  const long long S = (tiles_total + nt - 1) / nt;
+  long long S = (tiles_total + nt - 1) / nt;
+  // When the last splits of the rows would spill into a second round of
+  // workgroups (a row just past a multiple of the split size, e.g. a budget
+  // plus the appended token), the last split takes the remainder instead, up
+  // to half a split more.
+  const long long s_fit = std::max(1LL, 512 / rows);
+  if (S > s_fit && tiles_total - (s_fit - 1) * nt <= nt + (nt + 1) / 2) S = s_fit;
+  const long long last = tiles_total - (S - 1) * nt;
   // fp16 tiers: one extra partial state per 64 tier tokens, after the splits.
   const long long tier_tok = std::min<long long>((long long)c->fp16_sinks + c->fp16_recent, hint);
   const long long TP = (tier_tok + kTierTokens - 1) / kTierTokens;
@@ -147,9 +154,10 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
   const size_t BH = (size_t)c->batch * Hq;
   const size_t part_o = align256(BH * P * c->head_dim * sizeof(float));
   const size_t part_ml = align256(BH * P * 2 * sizeof(float));
-  const size_t logits = with_h2o ? align256(BH * S * nt * kSplitTokens * sizeof(float)) : 0;
+  const size_t logits = with_h2o ? align256(BH * ((S - 1) * nt + last) * kSplitTokens * sizeof(float)) : 0;
   g->splits = (int)S;
   g->tiles = (int)nt;
+  g->last_tiles = (int)last;
   g->tier_parts = (int)TP;
   g->off_ml = part_o;
   g->off_logits = part_o + part_ml;
@@ -282,6 +290,7 @@ int32_t prepare_attn(const kvc_cache_t* cache, const void* k_new, const void* v_
   a->num_q_heads = num_q_heads;
   a->splits = g.splits;
   a->tiles = g.tiles;
+  a->last_tiles = g.last_tiles;
   a->tier_parts = g.tier_parts;
   a->parts = g.splits + g.tier_parts;
   a->qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
@@ -613,7 +622,7 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
     e.out = out;
     e.num_q_heads = num_q_heads;
     e.splits = a.parts;  // partial states per head: the splits and the fp16-tier parts
-    e.span = (long long)a.splits * a.tiles * kSplitTokens;
+    e.span = attn_span(a);
     return device_status(launch_evict(e, s), "kvc_decode_step eviction launch");
   }
   if ((st = device_status(launch_decode_attn(a, s), "kvc_decode_step attention launch"))) return st;

@@ -185,7 +185,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int quad = lane >> 4, col = lane & 15;
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits, NT = a.tiles;
-  const long long span = (long long)S * NT * TS;  // logit slots per query head
+  const long long span = attn_span(a);  // logit slots per query head
+  const int NTs = s == S - 1 ? a.last_tiles : NT;  // tiles of this split
   // Uniform by construction; readfirstlane keeps it (and the buffer resources
   // built from it) in scalar registers. With an append, the new token is slot
   // L_old and the attention covers it.
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   // This wave's blocks: block `it` starts at token t0(it) and holds tokens
   // below L only for it < nb.
   auto block_t0 = [&](int it) { return ((s * NT + it) * 4 + wave) * 64; };
-  const int nb = max(0, min(NT, (t_hi - ((s * NT) * 4 + wave) * 64 + 255) / 256));
+  const int nb = max(0, min(NTs, (t_hi - ((s * NT) * 4 + wave) * 64 + 255) / 256));
 
   // Append: the wave whose block `it_new` holds slot L_old quantizes the new
   // token's K and V rows into the cache before its first loads (the
@@ -251,8 +252,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
       a.stash[c.batch + b] = c.num_seen[b];
     }
     const int qb = L_old >> 6;  // 64-token block of the new slot
-    if (L_old >= 0 && L_old < c.capacity && L_old < span && (qb >> 2) / NT == s && (qb & 3) == wave) {
-      it_new = (qb >> 2) % NT;
+    if (L_old >= 0 && L_old < c.capacity && L_old < span && min((qb >> 2) / NT, S - 1) == s && (qb & 3) == wave) {
+      it_new = (qb >> 2) - s * NT;
       const long long row = cache_row(c, b, g, L_old);
       if (row >= 0) {
         const long long src = ((long long)b * H + g) * D;
@@ -620,7 +621,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int lane = tid & 63, wave = tid >> 6;
   // S: the partial states per head (the splits and the fp16-tier parts).
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.parts;
-  const long long span = (long long)a.splits * a.tiles * TS;
+  const long long span = attn_span(a);
   // With an append, the length before it comes from the split kernel (the
   // cache's own length is advanced here, by one workgroup).
   const bool app = a.append != 0;
@@ -771,7 +772,7 @@ hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st) {
 
 hipError_t launch_attn_merge(const AttnLaunch& a, hipStream_t st) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  const long long span = (long long)a.splits * a.tiles * TS;
+  const long long span = attn_span(a);
   const int h2o_blocks = a.score ? (int)((span + kH2oChunk - 1) / kH2oChunk) : 0;
   const int nh = G;  // the H2O blocks need every head's statistics
   const size_t lds = (size_t)nh * (a.parts + 2) * sizeof(float);

@@ -73,11 +73,16 @@ struct AttnLaunch {
   int append;        // the split appended (the merge takes the lengths from stash)
   int num_q_heads;
   int splits;        // S: workgroups per (sequence, KV head)
-  int tiles;         // 256-token tiles per split
+  int tiles;         // 256-token tiles per split, except the last
+  int last_tiles;    // tiles of the last split (it may take a small remainder past `tiles`)
   int tier_parts;    // TP: fp16-tier partial states per (sequence, query head), after the S splits
   int parts;         // S + TP: partial states per query head in part_o / part_ml
   float qk_log2;     // log2(e) / sqrt(head_dim)
 };
+// Logit slots per query head: the tiles of all splits.
+__host__ __device__ inline long long attn_span(const AttnLaunch& a) {
+  return ((long long)(a.splits - 1) * a.tiles + a.last_tiles) * kSplitTokens;
+}
 hipError_t launch_decode_attn(const AttnLaunch& a, hipStream_t st);  // split, then merge
 // The code splits, then (on a tiered cache) the fp16-tier parts S .. S + TP - 1
 // in a second kernel (with an append, it also stores the new token's tier

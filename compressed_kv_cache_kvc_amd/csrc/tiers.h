@@ -39,7 +39,7 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int xt, float* q
   const kvc_cache_t& c = a.c;
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits, P = a.parts;
-  const long long span = (long long)S * a.tiles * kSplitTokens;
+  const long long span = attn_span(a);
   const bool app = a.k_new != nullptr;
   const int L_old = __builtin_amdgcn_readfirstlane(c.lengths[b]);
   const int L = max(0, __builtin_amdgcn_readfirstlane(min(min(L_old + (app ? 1 : 0), c.capacity), (int)span)));

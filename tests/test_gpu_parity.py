@@ -185,6 +185,10 @@ def _append_attn_pair(gcA, gcB, sA, sB, knew, vnew, q, hint, hq):
     (8, 4, 8, 64, [300, 301, 302], True, 3),     # D = 64
     (32, 2, 8, 128, [600, 10, 599], True, 7),    # GQA 16: two passes of 8 heads
     (8, 4, 8, 128, [2100, 1500, 2048], False, 9),  # no H2O; several tiles per split
+    # 64 rows just past 8 tiles: the last split takes the 9th tile (one
+    # dispatch round of workgroups), and the new slot 2048 lies in it
+    (16, 8, 8, 128, [2048, 2048, 1900, 2047, 1024, 2048, 5, 2000], True, 3),
+    (8, 8, 4, 64, [2048, 1, 2048, 2040, 2048, 1500, 2048, 2047], True, 0),
 ])
 def test_append_decode_attn_bit_exact(hq, hkv, bits, D, lens, h2o, cap_extra):
     """kvc_append_decode_attn equals kvc_quant_append + kvc_decode_attn on
