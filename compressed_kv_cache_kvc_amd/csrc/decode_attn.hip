@@ -172,6 +172,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   constexpr int NQ = GP > 4 ? GP / 4 : 1;   // q limb rows held per lane (one per row set)
   constexpr int NSC = GP >= 4 ? 4 : GP;     // scale loads per block
   constexpr int VROW = D;                   // staged V row stride in LDS (chunks XOR-swizzled, see vchunk)
+  // INT4 at D = 128: 16-byte loads, each lane taking two 16-element slices at
+  // once (K: its slices of both 64-element halves, elements 32 quad + 16 dh +
+  // 0..15; V: two adjacent 16-channel chunks of one token).
+  constexpr bool K16 = KBITS == 4 && D == 128;
+  constexpr bool V16 = VBITS == 4 && D == 128;
   static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "GP");
   // LDS chunk (16 bytes) of staged token row t that holds V chunk m: the XOR
   // makes the 64 lanes of a transposed read (tokens 16 q + 0..7 or 8..15 of
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   using KT = typename std::conditional<KBITS == 8, i32x4, i32x2>::type;
   struct Regs {
     KT kq[4][NDH];
-    i32x2 vq[VBITS == 8 ? 1 : NCB];
+    i32x2 vq[VBITS == 8 ? 1 : NCB];  // V16: pairs (2 j, 2 j + 1) hold one 16-byte load
     float ksv[NSC], vsv[NSC];
   };
   // Issue every load of block `it`: K and V scales, then K codes into `r`,
@@ -312,12 +317,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
       r.vsv[si] = load_f32(rvs, row * 4);
     }
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg)
+    for (int tg = 0; tg < 4; ++tg) {
+      if constexpr (K16) {
+        const i32x4 w = load16(rk, row_static(tg, 16 * tg + col) * RBK + quad * 16);
+        r.kq[tg][0] = i32x2{w[0], w[1]};
+        r.kq[tg][1] = i32x2{w[2], w[3]};
+      } else {
 #pragma unroll
-      for (int dh = 0; dh < NDH; ++dh) {
-        const unsigned off = row_static(tg, 16 * tg + col) * RBK + dh * (RBK / NDH) + quad * KB;
-        if constexpr (KBITS == 8) r.kq[tg][dh] = load16(rk, off); else r.kq[tg][dh] = load8(rk, off);
+        for (int dh = 0; dh < NDH; ++dh) {
+          const unsigned off = row_static(tg, 16 * tg + col) * RBK + dh * (RBK / NDH) + quad * KB;
+          if constexpr (KBITS == 8) r.kq[tg][dh] = load16(rk, off); else r.kq[tg][dh] = load8(rk, off);
+        }
       }
+    }
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
       // Lane l fills LDS chunk l % NCB of token row TPV j + l / NCB (DMA
@@ -327,6 +339,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
         const unsigned off = row_static((TPV * j) >> 4, t) * RBV + vchunk(t, lane % NCB) * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, (__attribute__((address_space(3))) void*)&v_stage[wave][j * 1024], 16, off, 0, 0, 0);
+      } else if constexpr (V16) {
+        // 4 lanes per token, 16 tokens per load: lane l takes chunks
+        // 2 (l % 4) and 2 (l % 4) + 1 of token 16 (j / 2) + l / 4.
+        if (j % 2 == 0) {
+          const int tv = 16 * (j / 2) + lane / 4;
+          const i32x4 w = load16(rv, row_static(j / 2, tv) * RBV + (lane % 4) * 16);
+          r.vq[j] = i32x2{w[0], w[1]};
+          r.vq[j + 1] = i32x2{w[2], w[3]};
+        }
       } else {
         const unsigned off = row_static((TPV * j) >> 4, t) * RBV + (lane % NCB) * VKB;
         r.vq[j] = load8(rv, off);
@@ -368,7 +389,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
         const int d = lane * EPL + e;
         int lm[4];
         to_limbs(ldexpf(x[e], E), lm);
-        const int pos = KBITS == 8 ? d : ((d & ~15) | int4_byte(d & 15));
+        // Position of element d in a limb row: the A operand of MFMA dh reads
+        // bytes 64 dh + 16 quad .. + 15, which must hold the elements lane
+        // group quad's K slice holds (INT4: in widened byte order).
+        const int pos = KBITS == 8 ? d
+                        : K16      ? ((d >> 4) & 1) * 64 + (d >> 5) * 16 + int4_byte(d & 15)
+                                   : ((d & ~15) | int4_byte(d & 15));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           q_limb[h][k][pos] = (int8_t)lm[k];
@@ -518,9 +544,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
       if constexpr (VBITS == 4) {
 #pragma unroll
         for (int j = 0; j < NCB; ++j) {
-          const int t = TPV * j + lane / NCB;
+          const int t = V16 ? 16 * (j / 2) + lane / 4 : TPV * j + lane / NCB;
+          const int m = V16 ? 2 * (lane % 4) + (j % 2) : lane % NCB;
           const i32x4 val = widen_int4(r.vq[j]);
-          i32x2* dst = reinterpret_cast<i32x2*>(&v_stage[wave][t * VROW + vchunk(t, lane % NCB) * 16]);
+          i32x2* dst = reinterpret_cast<i32x2*>(&v_stage[wave][t * VROW + vchunk(t, m) * 16]);
           dst[0] = i32x2{val[0], val[1]};
           dst[1] = i32x2{val[2], val[3]};
         }
@@ -643,10 +670,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   if (!out_block && srow) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) sc[k] = srow[min(t0 + k, tl)];
+    // A logit row is span floats (a multiple of 256) in a 256-byte aligned
+    // workspace, so a thread's 4 slots are one 16-byte load; a chunk past the
+    // row reads the row's last 4 slots instead (slots past L are not used).
+    const long long t4 = min((long long)t0, span - 4);
 #pragma unroll
-    for (int i = 0; i < kPrefetchHeads; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) lg[i][k] = lrow[min(i, G - 1) * span + min(t0 + k, tl)];
+    for (int i = 0; i < kPrefetchHeads; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(lrow + min(i, G - 1) * span + t4);
+      lg[i][0] = v.x;
+      lg[i][1] = v.y;
+      lg[i][2] = v.z;
+      lg[i][3] = v.w;
+    }
   }
   const int d = tid % D, pi = tid / D;
   const float* po = a.part_o + ((long long)b * Hq + g * G + h_lo) * S * D + d;
