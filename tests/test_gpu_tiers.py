@@ -165,3 +165,37 @@ def test_tier_decode_step_equals_separate_calls(hq, hkv, bits):
     ref.append(d["k"][:, :, :P + 1], d["v"][:, :, :P + 1])
     ro, _ = ref.attend(d["step_q"][0])
     assert_out_close(host(oB), ro)
+
+
+@pytest.mark.parametrize("bits,hq,hkv", [(8, 8, 4), (4, 16, 2)])
+def test_tier_paged_equals_contiguous(bits, hq, hkv):
+    """A paged tiered cache (blocks in a seeded random order) attends exactly
+    as a contiguous tiered cache holding the same tokens: output and H2O
+    scores bit for bit, on the separate calls and on the fused append; the
+    contiguous side is the one the oracle checks above."""
+    L, D, S16, R16, bs = 700, 128, 4, 80, 16
+    print(f"[tiers paged] bits={bits} hq={hq} hkv={hkv}", flush=True)
+    w = _workload(bits, hq, hkv, D, L, 2)
+    d = draw(w)
+    B, cap = w.batch, 736
+    mb = cap // bs
+    table = np.random.default_rng(7).permutation(B * mb).astype(np.int32).reshape(B, mb)
+    pg = kvc.KVCache(B, hkv, D, 0, bits, block_size=bs, num_blocks=B * mb, max_blocks_per_seq=mb, fp16_sinks=S16,
+                     fp16_recent=R16)
+    pg.block_table.copy_(dev(table))
+    ct = _tiered(w, cap, 0, S16, R16)
+    res = []
+    for c in (pg, ct):
+        score = c.score_buffer()
+        kvc.kvc_quant_append(c, dev(d["k"][:, :, :L]), dev(d["v"][:, :, :L]), h2o_score=score)
+        out1 = torch.empty((B, hq, D), dtype=torch.float32, device="cuda")
+        kvc.kvc_decode_attn(c, dev(d["q"]), out1, h2o_score=score)
+        out2 = torch.empty_like(out1)
+        kvc.kvc_append_decode_attn(c, dev(d["step_k"][1]), dev(d["step_v"][1]), dev(d["step_q"][1]), out2,
+                                   h2o_score=score)
+        torch.cuda.synchronize()
+        res.append((out1, out2, score))
+    (a1, a2, sa), (b1, b2, sb) = res
+    assert torch.equal(a1, b1) and torch.equal(a2, b2) and torch.equal(sa, sb)
+    for name in ("k_sink16", "v_sink16", "k_recent16", "v_recent16", "lengths", "num_seen"):
+        assert torch.equal(getattr(pg, name), getattr(ct, name)), name
