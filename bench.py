@@ -54,7 +54,7 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "f10a226ea538f45dd782242c7659b627fb6af64c653445d67a4058dfad5db525"
+TRAFFIC_SHA256 = "1eced26f376c15287da9d24744fd5133454f1063f7146272e666adc0f006917b"
 TRAFFIC_BYTES = 70757366
 
 
