@@ -24,6 +24,8 @@ What it computes, and the page passage each part follows:
                 tutorial §3.2)
 * ``tiers``     fp16 sink and recent tiers of a quantized cache (report §3.2;
                 tutorial §1.3)
+* ``kvsep``     K and V stored apart: scoring on the quantized K, the output
+                from the top-k tokens' fp16 V rows (report §3.5)
 
 Floating point is fp64 throughout, except where the method fixes fp32: the
 quantization scale and the quotient that is rounded to a code, both taken as
@@ -38,6 +40,7 @@ from .eviction import compact_row, h2o_accumulate, kth_threshold, select_keep
 from .blocks import block_evict, move_block_scores
 from .schedule import layer_budgets
 from .tiers import tier_bounds, tier_values
+from .kvsep import kv_separated_attention
 from .quant import (QMAX, QMIN, compressed_bytes_per_token_head, dequantize, kv_bytes_per_token,
                     pack_int4, quantize_rows, unpack_int4)
 
@@ -47,5 +50,5 @@ __all__ = [
     "attend_head_group", "attend_values", "decode_attention", "paged_decode_attention", "paged_gather",
     "h2o_accumulate", "select_keep", "kth_threshold", "compact_row",
     "RefCache", "paged_append", "layer_budgets", "block_evict", "move_block_scores",
-    "tier_bounds", "tier_values",
+    "tier_bounds", "tier_values", "kv_separated_attention",
 ]
