@@ -75,6 +75,8 @@ def _load():
         "kvc_compact_gather": (I32, [D, P, P, I32, D, P, P]),
         "kvc_h2o_evict": (I32, [D, P, I32, I32, I32, P, P, D, P, I32, P]),
         "kvc_decode_step": (I32, [D, P, P, P, I32, P, P, I32, I32, I32, P, P, D, P, I32, P, SZ, P]),
+        "kvc_decode_attn_kvsep_workspace_bytes": (SZ, [D, I32, I32, I32]),
+        "kvc_decode_attn_kvsep": (I32, [D, P, I32, I32, P, P, I32, P, SZ, P]),
         "kvc_bw_probe_sink_bytes": (SZ, []),
         "kvc_bw_probe": (I32, [P, SZ, P, SZ, P]),
         "kvc_layer_budgets": (I32, [I32, I32, I32, ctypes.c_double, I32, P]),
@@ -486,6 +488,34 @@ def kvc_layer_budgets(schedule: int, num_layers: int, base: int, base_ratio: flo
     _check(lib.kvc_layer_budgets(schedule, num_layers, base, float(base_ratio), min_budget, out),
            "kvc_layer_budgets")
     return list(out)[:num_layers]
+
+
+def kvc_decode_attn_kvsep_workspace_bytes(cache, num_q_heads: int, top_k: int, max_len_hint: int) -> int:
+    return lib.kvc_decode_attn_kvsep_workspace_bytes(ctypes.byref(_desc(cache)), num_q_heads, top_k, max_len_hint)
+
+
+def kvc_decode_attn_kvsep(cache, q, top_k: int, v_host, out, max_len_hint: Optional[int] = None, workspace=None,
+                          stream=None):
+    """K/V-separated attention (see kvc.h): scores on the cache's quantized K,
+    the output from the top_k tokens' fp16 V rows per KV head, hot rows from
+    the cache's fp16 tiers and cold rows from ``v_host``, a pinned CPU fp16
+    tensor ``[B][Hkv][capacity][D]`` indexed by slot."""
+    import torch
+    d = _desc(cache)
+    Hq = q.shape[1]
+    _need(q, torch.float16, "q", d.batch * Hq * d.head_dim)
+    _need(out, torch.float32, "out", d.batch * Hq * d.head_dim)
+    if v_host.device.type != "cpu" or not v_host.is_pinned() or v_host.dtype != torch.float16 \
+            or not v_host.is_contiguous() or v_host.numel() != d.batch * d.num_kv_heads * d.capacity * d.head_dim:
+        raise ValueError("v_host must be a contiguous pinned CPU fp16 tensor [B][Hkv][capacity][D]")
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    if workspace is None:
+        n = kvc_decode_attn_kvsep_workspace_bytes(d, Hq, top_k, max_len_hint)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.kvc_decode_attn_kvsep(ctypes.byref(d), _ptr(q), Hq, top_k, v_host.data_ptr(), _ptr(out),
+                                     max_len_hint, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "kvc_decode_attn_kvsep")
 
 
 def kvc_bw_probe_sink_bytes() -> int:

@@ -557,6 +557,64 @@ int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, do
                        "kvc_paged_block_evict launch");
 }
 
+size_t kvc_decode_attn_kvsep_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_heads, int32_t top_k,
+                                             int32_t max_len_hint) {
+  AttnGeom g;
+  if (!cache || top_k < 1 || top_k > cache->capacity || attn_geometry(cache, num_q_heads, max_len_hint, 1, &g))
+    return 0;
+  const size_t rows = (size_t)cache->batch * cache->num_kv_heads;
+  return g.total + align256(rows * cache->capacity * sizeof(float)) + align256(rows * top_k * sizeof(int32_t));
+}
+
+int32_t kvc_decode_attn_kvsep(const kvc_cache_t* cache, const void* q, int32_t num_q_heads, int32_t top_k,
+                              const void* v_host, float* out, int32_t max_len_hint, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  clear_error();
+  int32_t st = check_cache(cache, "cache");
+  if (st) return st;
+  if (top_k < 1) return fail(KVC_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (top_k > cache->capacity) return fail(KVC_ERR_CAPACITY, "top_k %d exceeds capacity %d", top_k, cache->capacity);
+  if (!v_host || (uintptr_t)v_host % 16) return fail(KVC_ERR_INVALID_ARG, "v_host must be a 16-byte aligned host array");
+  AttnGeom g;
+  if ((st = attn_geometry(cache, num_q_heads, max_len_hint, 1, &g))) return st;
+  const size_t rows = (size_t)cache->batch * cache->num_kv_heads;
+  const size_t off_score = g.total, off_keep = off_score + align256(rows * cache->capacity * sizeof(float));
+  const size_t need = off_keep + align256(rows * top_k * sizeof(int32_t));
+  if (!workspace || workspace_bytes < need)
+    return fail(KVC_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* tscore = reinterpret_cast<float*>(ws + off_score);
+  int32_t* keep = reinterpret_cast<int32_t*>(ws + off_keep);
+  AttnLaunch a;
+  if ((st = prepare_attn(cache, nullptr, nullptr, q, num_q_heads, out, tscore, max_len_hint, workspace,
+                         workspace_bytes, &a)))
+    return st;
+  // The cold V rows are read by the device straight from pinned host memory.
+  void* v_dev = nullptr;
+  if (hipHostGetDevicePointer(&v_dev, const_cast<void*>(v_host), 0) != hipSuccess || !v_dev) {
+    (void)hipGetLastError();  // do not leave the failed query's error for the next call
+    return fail(KVC_ERR_INVALID_ARG, "v_host must be pinned host memory the device can read (hipHostMalloc)");
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = device_status(launch_fill_zero(tscore, (long long)(rows * cache->capacity), s), "kvsep score clear")))
+    return st;
+  if ((st = device_status(launch_decode_attn(a, s), "kvsep attention launch"))) return st;
+  if ((st = device_status(launch_select(*cache, tscore, top_k, 0, 0, nullptr, keep, max_len_hint, s),
+                          "kvsep selection launch")))
+    return st;
+  KvsepArgs k{};
+  k.c = *cache;
+  k.logits = a.logits;
+  k.span = attn_span(a);
+  k.keep = keep;
+  k.top_k = top_k;
+  k.max_len = max_len_hint;
+  k.v_host = static_cast<const __half*>(v_dev);
+  k.out = out;
+  k.num_q_heads = num_q_heads;
+  return device_status(launch_kvsep_gather(k, s), "kvsep gather launch");
+}
+
 size_t kvc_bw_probe_sink_bytes(void) { return (size_t)bw_probe_workgroups() * sizeof(uint32_t); }
 
 int32_t kvc_bw_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream) {

@@ -139,6 +139,22 @@ constexpr int kBlockEvictMaxBlocks = 8192;
 hipError_t launch_block_evict(const kvc_cache_t& src, const float* score, double retention, const kvc_cache_t& dst,
                               float* dst_score, int32_t* freed, int32_t* freed_count, int max_len, hipStream_t st);
 
+// K/V-separated attention's last step (kvsep.hip): per (sequence, KV head),
+// the output of each query head from the kept tokens' fp16 V rows.
+struct KvsepArgs {
+  kvc_cache_t c;
+  const float* logits;   // [B][Hq][span] from the attention kernels, log2 units
+  long long span;
+  const int32_t* keep;   // [B][Hkv][top_k] kept slots, ascending
+  int top_k;
+  int max_len;           // the length bound the selection used
+  const __half* v_host;  // device-visible pointer to [B][Hkv][capacity][D] fp16
+  float* out;            // [B][Hq][D]
+  int num_q_heads;
+};
+hipError_t launch_fill_zero(float* p, long long n, hipStream_t st);
+hipError_t launch_kvsep_gather(const KvsepArgs& a, hipStream_t st);
+
 // Read-bandwidth probe: reads bytes (a multiple of 16) from src once; writes
 // bw_probe_workgroups() words to sink.
 int bw_probe_workgroups();

@@ -453,6 +453,42 @@ int32_t kvc_layer_budgets(int32_t schedule, int32_t num_layers, int32_t base, do
                           int32_t min_budget, int32_t* budgets_host);
 
 /*
+ * K/V-separated attention (top-k V).
+ * Source: "KV Cache Compression Report", section 3.5 (K/V stored apart: the
+ * quantized K of every token stays on the GPU to score the query; full-
+ * precision V is kept hot on the GPU or cold in host memory and fetched for
+ * the top-scored tokens only).
+ *
+ * For sequence b and KV head g with L = lengths[b]: the logits s_{h,i} and
+ * probabilities p_{h,i} of kvc_decode_attn (every cached token, each key as
+ * that call reads it: from the codes, or the fp16 row on a tier); the kept set = the min(top_k, L) slots with the largest group mass
+ * sum over the G query heads of g of p_{h,i} (equal mass: lower slot); then
+ * for each query head h of g:
+ *   out[b][h][:] = sum over kept i of exp(s_{h,i}) / sum over kept j of
+ *                  exp(s_{h,j}) * V_i
+ * where V_i is slot i's fp16 row: from the cache's fp16 tiers when slot i is
+ * on one (hot), else from v_host (cold).
+ *
+ * q: device fp16 [batch][num_q_heads][head_dim]; out: device fp32
+ * [batch][num_q_heads][head_dim]. v_host: pinned host memory (hipHostMalloc,
+ * or a pinned torch CPU tensor), fp16 [batch][num_kv_heads][capacity][head_dim]
+ * indexed by slot, owned and kept current by the caller (the row of every
+ * cold slot < L must hold that token's V); the device reads it directly, so
+ * each call moves min(top_k, L) rows per (sequence, KV head) over the host
+ * link. workspace: kvc_decode_attn_kvsep_workspace_bytes(...) bytes, 256-byte
+ * aligned. The cache's H2O scores are not touched.
+ * Errors: those of kvc_decode_attn, plus INVALID_ARG for top_k < 1, a NULL or
+ * unaligned v_host, or v_host not pinned device-readable host memory;
+ * CAPACITY if top_k > capacity.
+ */
+size_t kvc_decode_attn_kvsep_workspace_bytes(const kvc_cache_t* cache, int32_t num_q_heads,
+                                             int32_t top_k, int32_t max_len_hint);
+int32_t kvc_decode_attn_kvsep(const kvc_cache_t* cache, const void* q, int32_t num_q_heads,
+                              int32_t top_k, const void* v_host, float* out,
+                              int32_t max_len_hint, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * Measurement helper (not a step of the method): one streaming read of
  * `bytes` bytes of device memory at `src` (16-byte aligned, bytes a positive
  * multiple of 16) with the decode-attention kernel's 16-byte load width, 4096

@@ -8,8 +8,9 @@ V is kept in fp16, hot rows on the GPU and cold rows in host memory, and only
 the V rows of the top-k scored tokens are fetched to form the output.
 
 Readings (listed in DESIGN.md):
-* The scores are the ordinary attention logits over the quantized keys,
-  s_i = q . (code_i * scale_i) / sqrt(D), for every cached token.
+* The scores are the cache's ordinary attention logits, s_i = q . K_i /
+  sqrt(D) for every cached token, with K_i the key as that attention reads it:
+  code_i * scale_i, or the fp16 row on a cache's fp16 tiers.
 * The top-k is taken per KV head, by the attention probability the group's
   query heads give each token in this step (softmax over all tokens, summed
   over the group) -- the H2O mass of one step, the same granularity as the
@@ -27,21 +28,20 @@ import math
 import numpy as np
 
 from .eviction import select_keep
-from .quant import dequantize
 
 
-def kv_separated_attention(q16: np.ndarray, kc: np.ndarray, ks: np.ndarray, v16: np.ndarray, length: int,
-                           top_k: int):
+def kv_separated_attention(q16: np.ndarray, K: np.ndarray, v16: np.ndarray, length: int, top_k: int):
     """One KV head and the G query heads that read it.
 
-    q16 [G][D] fp16; kc [>= L][D] unpacked K codes; ks [>= L] fp32 K scales;
+    q16 [G][D] fp16; K [>= L][D] the keys as the cache's attention reads them
+    (``dequantize`` of the codes, or ``tier_values`` on a tiered cache);
     v16 [>= L][D] the fp16 V rows. Returns (out [G][D] fp64, keep [L] bool).
     """
     if top_k < 1:
         raise ValueError("top_k must be >= 1")
     L = int(length)
     D = q16.shape[-1]
-    K = dequantize(kc[:L], ks[:L])
+    K = np.asarray(K[:L], dtype=np.float64)
     q = q16.astype(np.float64)
     s = (q @ K.T) / math.sqrt(D)                     # [G][L]
     e = np.exp(s - s.max(axis=1, keepdims=True))

@@ -317,6 +317,28 @@ def test_fp16_tier_validation():
                                      0xE100000, 100, None) == UNSUPPORTED
 
 
+def test_kvsep_validation():
+    d = desc()
+    need = lib.kvc_decode_attn_kvsep_workspace_bytes(ctypes.byref(d), 4, 64, 16)
+    assert need > lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), 4, 16, 1)
+    assert lib.kvc_decode_attn_kvsep_workspace_bytes(ctypes.byref(d), 4, 0, 16) == 0
+    assert lib.kvc_decode_attn_kvsep_workspace_bytes(ctypes.byref(d), 4, 513, 16) == 0
+    call = lambda top_k=64, vh=0x7000000, q=FAKE, out=FAKE, hint=16, ws=FAKE * 256, n=need: \
+        lib.kvc_decode_attn_kvsep(ctypes.byref(d), q, 4, top_k, vh, out, hint, ws, n, None)
+    assert call(top_k=0) == INVALID
+    assert call(top_k=513) == CAPACITY
+    assert call(vh=None) == INVALID
+    assert call(vh=0x7000008) == INVALID              # not 16-byte aligned
+    assert call(q=None) == INVALID
+    assert call(hint=513) == CAPACITY
+    assert call(n=need - 1) == INVALID
+    assert call(ws=None) == INVALID
+    # every argument valid but v_host, which is no pinned host memory: refused
+    # before anything is launched
+    assert call() == INVALID
+    assert "pinned" in kvc.kvc_last_error()
+
+
 # -- block pool -----------------------------------------------------------------
 
 def test_pool_all_or_nothing_and_free():

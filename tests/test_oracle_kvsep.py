@@ -40,7 +40,7 @@ def test_top_k_covering_every_token_is_full_attention(top_k):
     rng = np.random.default_rng(31)
     G, L, D = 2, 9, 16
     q, kc, ks, v = _head(rng, G, L, D, bits=4)
-    out, keep = oracle.kv_separated_attention(q, kc, ks, v, L, top_k)
+    out, keep = oracle.kv_separated_attention(q, oracle.dequantize(kc, ks), v, L, top_k)
     assert keep.all()
     K = oracle.dequantize(kc, ks)
     for h in range(G):
@@ -51,7 +51,7 @@ def test_top_one_returns_the_heaviest_tokens_row():
     rng = np.random.default_rng(32)
     G, L, D = 3, 40, 32
     q, kc, ks, v = _head(rng, G, L, D)
-    out, keep = oracle.kv_separated_attention(q, kc, ks, v, L, 1)
+    out, keep = oracle.kv_separated_attention(q, oracle.dequantize(kc, ks), v, L, 1)
     K = oracle.dequantize(kc, ks)
     s = q.astype(np.float64) @ K.T / math.sqrt(D)
     p = np.exp(s - s.max(axis=1, keepdims=True))
@@ -67,7 +67,7 @@ def test_constant_values_come_back_exactly():
     q, kc, ks, _ = _head(rng, G, L, D)
     v = np.full((L, D), 1.5, np.float16)
     for top_k in (1, 7, 30, 60):
-        out, _ = oracle.kv_separated_attention(q, kc, ks, v, L, top_k)
+        out, _ = oracle.kv_separated_attention(q, oracle.dequantize(kc, ks), v, L, top_k)
         assert np.allclose(out, 1.5, rtol=0, atol=1e-14), top_k
 
     # planted: the full-softmax weights of the kept tokens, not renormalized
@@ -75,7 +75,7 @@ def test_constant_values_come_back_exactly():
     s = q.astype(np.float64) @ K.T / math.sqrt(D)
     p = np.exp(s - s.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
-    _, keep = oracle.kv_separated_attention(q, kc, ks, v, L, 7)
+    _, keep = oracle.kv_separated_attention(q, oracle.dequantize(kc, ks), v, L, 7)
     planted = p[:, keep] @ v[keep].astype(np.float64)
     assert not np.allclose(planted, 1.5, rtol=0, atol=1e-6)
 
@@ -90,7 +90,7 @@ def test_dominant_key_returns_its_row():
     k[0, 0, 17, 0] = 64.0
     kc, ks = oracle.quantize_rows(k, 8)
     for top_k in (1, 5, 30):
-        out, keep = oracle.kv_separated_attention(q, kc[0, 0], ks[0, 0], v, L, top_k)
+        out, keep = oracle.kv_separated_attention(q, oracle.dequantize(kc[0, 0], ks[0, 0]), v, L, top_k)
         assert keep[17]
         assert np.allclose(out[0], v[17].astype(np.float64), rtol=0, atol=1e-20)
 
@@ -100,7 +100,7 @@ def test_selection_is_the_top_k_of_group_mass(seed):
     rng = np.random.default_rng(100 + seed)
     G, L, D, top_k = 4, 50, 16, 12
     q, kc, ks, v = _head(rng, G, L, D)
-    _, keep = oracle.kv_separated_attention(q, kc, ks, v, L, top_k)
+    _, keep = oracle.kv_separated_attention(q, oracle.dequantize(kc, ks), v, L, top_k)
     K = oracle.dequantize(kc, ks)
     s = q.astype(np.float64) @ K.T / math.sqrt(D)
     p = np.exp(s - s.max(axis=1, keepdims=True))
