@@ -366,6 +366,42 @@ def secondary_attention(kvc, torch, reps=16):
                                        "fp16_recent": r16, "calls": "kvc_decode_attn (split, tiers, merge)"})
         del caches, scores, ws
         torch.cuda.empty_cache()
+
+    # K/V-separated attention on the same layer: top_k = the 2457-token keep
+    # budget per KV head, cold V rows read by the device from pinned host
+    # memory; with no tiers every kept row is cold, with 4 fp16 sinks and a
+    # 1024-token fp16 window those rows are hot (on the GPU). Timed eagerly:
+    # each call is hundreds of microseconds of host-link reads.
+    top_k = w.budget
+    for name, s16, r16 in (("llama7b_8k_kvsep_all_cold", 0, 0), ("llama7b_8k_kvsep_hot_window", 4, 1024)):
+        c = kvc.KVCache(B, H, D, L, 8, fp16_sinks=s16, fp16_recent=r16)
+        kv = torch.randn((2, B, H, L, D), device="cuda").half()
+        kvc.kvc_quant_append(c, kv[0], kv[1], max_len_hint=0)
+        v_host = kv[1].cpu().pin_memory()
+        del kv
+        q = torch.randn((B, Hq, D), device="cuda").half()
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(kvc.kvc_decode_attn_kvsep_workspace_bytes(c, Hq, top_k, L), dtype=torch.uint8,
+                         device="cuda")
+        for _ in range(2):
+            kvc.kvc_decode_attn_kvsep(c, q, top_k, v_host, out, max_len_hint=L, workspace=ws)
+        torch.cuda.synchronize()
+        n = 8
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            kvc.kvc_decode_attn_kvsep(c, q, top_k, v_host, out, max_len_hint=L, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        # at least top_k - (sinks + window) kept rows per KV head come from the host
+        cold_rows = B * H * max(0, top_k - (s16 + r16))
+        res[name] = {"workload": name, "us_per_launch": round(us, 2), "top_k": top_k, "fp16_sinks": s16,
+                     "fp16_recent": r16, "kv_bytes_scored": int(B * H * L * (D + 4)),
+                     "host_v_bytes_at_least": int(cold_rows * D * 2),
+                     "calls": "kvc_decode_attn_kvsep (clear, split, merge, select, gather)"}
+        del c, v_host, ws
+        torch.cuda.empty_cache()
     return res
 
 

@@ -35,7 +35,7 @@ __device__ __forceinline__ float block_reduce(float v, float* tmp) {
 template <int D, int GM>
 __global__ __launch_bounds__(256) void kvsep_gather_kernel(KvsepArgs a) {
   constexpr int CPL = D / 64;  // channels per lane
-  constexpr int UN = 8;        // kept tokens per wave per round (their V loads go out together)
+  constexpr int UN = 32;       // kept tokens per wave per round (their V loads go out together)
   const kvc_cache_t& c = a.c;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H;
