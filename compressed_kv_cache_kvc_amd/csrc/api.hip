@@ -563,7 +563,8 @@ size_t kvc_decode_attn_kvsep_workspace_bytes(const kvc_cache_t* cache, int32_t n
   if (!cache || top_k < 1 || top_k > cache->capacity || attn_geometry(cache, num_q_heads, max_len_hint, 1, &g))
     return 0;
   const size_t rows = (size_t)cache->batch * cache->num_kv_heads;
-  return g.total + align256(rows * cache->capacity * sizeof(float)) + align256(rows * top_k * sizeof(int32_t));
+  return g.total + align256(rows * cache->capacity * sizeof(float)) + align256(rows * top_k * sizeof(int32_t)) +
+         align256((size_t)cache->batch * num_q_heads * kKvsepMaxParts * cache->head_dim * sizeof(float));
 }
 
 int32_t kvc_decode_attn_kvsep(const kvc_cache_t* cache, const void* q, int32_t num_q_heads, int32_t top_k,
@@ -579,7 +580,9 @@ int32_t kvc_decode_attn_kvsep(const kvc_cache_t* cache, const void* q, int32_t n
   if ((st = attn_geometry(cache, num_q_heads, max_len_hint, 1, &g))) return st;
   const size_t rows = (size_t)cache->batch * cache->num_kv_heads;
   const size_t off_score = g.total, off_keep = off_score + align256(rows * cache->capacity * sizeof(float));
-  const size_t need = off_keep + align256(rows * top_k * sizeof(int32_t));
+  const size_t off_part = off_keep + align256(rows * top_k * sizeof(int32_t));
+  const size_t need =
+      off_part + align256((size_t)cache->batch * num_q_heads * kKvsepMaxParts * cache->head_dim * sizeof(float));
   if (!workspace || workspace_bytes < need)
     return fail(KVC_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace ? workspace_bytes : 0);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -611,6 +614,11 @@ int32_t kvc_decode_attn_kvsep(const kvc_cache_t* cache, const void* q, int32_t n
   k.max_len = max_len_hint;
   k.v_host = static_cast<const __half*>(v_dev);
   k.out = out;
+  k.part_o = reinterpret_cast<float*>(ws + off_part);
+  // Workgroups per row: about 512 in all (the host link needs many reads in
+  // flight), at most one per 64 kept tokens.
+  k.parts = (int)std::max<long long>(1, std::min<long long>({(long long)kKvsepMaxParts,
+                                                             512 / (long long)rows, ((long long)top_k + 63) / 64}));
   k.num_q_heads = num_q_heads;
   return device_status(launch_kvsep_gather(k, s), "kvsep gather launch");
 }

@@ -150,8 +150,11 @@ struct KvsepArgs {
   int max_len;           // the length bound the selection used
   const __half* v_host;  // device-visible pointer to [B][Hkv][capacity][D] fp16
   float* out;            // [B][Hq][D]
+  float* part_o;         // [B][Hq][parts][D] workspace: each part's sums
+  int parts;             // workgroups per (sequence, KV head), 1..kKvsepMaxParts
   int num_q_heads;
 };
+constexpr int kKvsepMaxParts = 16;
 hipError_t launch_fill_zero(float* p, long long n, hipStream_t st);
 hipError_t launch_kvsep_gather(const KvsepArgs& a, hipStream_t st);
 

@@ -6,7 +6,8 @@
 // top-scored tokens. Here the scores, the softmax statistics and the H2O mass
 // come from the ordinary attention kernels, the selection from the keep-set
 // kernel (top_k per KV head by the step's group mass, no sinks or window),
-// and kvsep_gather_kernel forms, per query head,
+// and kvsep_gather_kernel (several workgroups per row, each over a share of
+// the kept tokens, their sums added in order) forms, per query head,
 //   out = sum over kept i of exp2(s_i - m) / l * v_i,
 // with m and l taken over the kept tokens only and v_i the token's fp16 row:
 // from the cache's fp16 tiers when slot i is on one (hot), else from the
@@ -31,19 +32,24 @@ __device__ __forceinline__ float block_reduce(float v, float* tmp) {
   return MAX ? fmaxf(fmaxf(tmp[0], tmp[1]), fmaxf(tmp[2], tmp[3])) : (tmp[0] + tmp[1]) + (tmp[2] + tmp[3]);
 }
 
-// One workgroup per (KV head g, sequence b); GM >= G query heads.
+// Workgroup (g, b, part): KV head g of sequence b, kept tokens
+// [part * chunk, (part + 1) * chunk) of the row's list; GM >= G query heads.
+// Each part writes its sum for every head to a.part_o; kvsep_reduce_kernel
+// adds the parts in order.
 template <int D, int GM>
 __global__ __launch_bounds__(256) void kvsep_gather_kernel(KvsepArgs a) {
   constexpr int CPL = D / 64;  // channels per lane
   constexpr int UN = 32;       // kept tokens per wave per round (their V loads go out together)
   const kvc_cache_t& c = a.c;
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H;
   // The selection saw at most max_len slots; kept slots are below L.
   const int L = __builtin_amdgcn_readfirstlane(
       max(0, min(min(min(c.lengths[b], c.capacity), (int)a.span), a.max_len)));
   const int seen = __builtin_amdgcn_readfirstlane(c.num_seen[b]);
   const int n = min(L, a.top_k);
+  const int chunk = (n + a.parts - 1) / a.parts;
+  const int i_lo = min(n, part * chunk), i_hi = min(n, i_lo + chunk);
   const long long row = (long long)b * H + g;
   const int32_t* keep = a.keep + row * a.top_k;
   const float* lg = a.logits + ((long long)b * Hq + g * G) * a.span;
@@ -83,13 +89,13 @@ __global__ __launch_bounds__(256) void kvsep_gather_kernel(KvsepArgs a) {
   for (int h = 0; h < GM; ++h)
 #pragma unroll
     for (int e = 0; e < CPL; ++e) o[h][e] = 0.f;
-  for (int i0 = wave; i0 < n; i0 += 4 * UN) {
+  for (int i0 = i_lo + wave; i0 < i_hi; i0 += 4 * UN) {
     float v[UN][CPL];
     int sl[UN];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int i = i0 + 4 * u;
-      sl[u] = i < n ? keep[i] : -1;
+      sl[u] = i < i_hi ? keep[i] : -1;
       if ((unsigned)sl[u] >= (unsigned)L) sl[u] = -1;
       const int s = sl[u];
       const __half* src = s < 0 ? nullptr
@@ -118,14 +124,26 @@ __global__ __launch_bounds__(256) void kvsep_gather_kernel(KvsepArgs a) {
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += 256) {
     const float r = (red_o[0][idx] + red_o[1][idx]) + (red_o[2][idx] + red_o[3][idx]);
-    a.out[((long long)b * Hq + g * G) * D + idx] = r;
+    const int h = idx / D, d = idx - h * D;
+    a.part_o[(((long long)b * Hq + g * G + h) * a.parts + part) * D + d] = r;
+  }
+}
+
+// out[b][h][:] = the parts' sums, added in part order (deterministic).
+__global__ __launch_bounds__(128) void kvsep_reduce_kernel(const float* __restrict__ part_o, float* __restrict__ out,
+                                                           int parts, int D) {
+  const long long bh = blockIdx.x;
+  for (int d = threadIdx.x; d < D; d += 128) {
+    float r = 0.f;
+    for (int p = 0; p < parts; ++p) r += part_o[(bh * parts + p) * D + d];
+    out[bh * D + d] = r;
   }
 }
 
 template <int D>
 hipError_t launch_d(const KvsepArgs& a, hipStream_t st) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  const dim3 grid(a.c.num_kv_heads, a.c.batch);
+  const dim3 grid(a.c.num_kv_heads, a.c.batch, a.parts);
   if (G == 1) hipLaunchKernelGGL((kvsep_gather_kernel<D, 1>), grid, dim3(256), 0, st, a);
   else if (G == 2) hipLaunchKernelGGL((kvsep_gather_kernel<D, 2>), grid, dim3(256), 0, st, a);
   else if (G <= 4) hipLaunchKernelGGL((kvsep_gather_kernel<D, 4>), grid, dim3(256), 0, st, a);
@@ -143,7 +161,11 @@ hipError_t launch_fill_zero(float* p, long long n, hipStream_t st) {
 }
 
 hipError_t launch_kvsep_gather(const KvsepArgs& a, hipStream_t st) {
-  return a.c.head_dim == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+  const hipError_t e = a.c.head_dim == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kvsep_reduce_kernel, dim3((unsigned)((long long)a.c.batch * a.num_q_heads)), dim3(128), 0, st,
+                     a.part_o, a.out, a.parts, a.c.head_dim);
+  return hipGetLastError();
 }
 
 }  // namespace kvc
