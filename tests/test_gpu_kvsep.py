@@ -100,3 +100,30 @@ def test_kvsep_with_all_tokens_kept_equals_fp16_value_attention():
             K = oracle.tier_values(kc[b, g], ks[b, g], d["k"][b, g], L, 4, 128)
             ro, _ = oracle.attend_values(d["q"][b, g * G:(g + 1) * G], K, d["v"][b, g])
             assert np.abs(host(out)[b, g * G:(g + 1) * G] - ro).max() <= OUT_ATOL
+
+
+def test_kvsep_paged_equals_contiguous():
+    """On a paged cache (blocks in a seeded random order, fp16 tiers) the call
+    gives the contiguous cache's output bit for bit; the contiguous side is
+    the one checked against the oracle above."""
+    B, hq, hkv, D, L, bs, top_k = 2, 8, 2, 128, 900, 16, 200
+    w = get("qwen_gqa_stream").scaled(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, bits=8, context=L,
+                                      steps=1)
+    d = draw(w)
+    cap = 912
+    mb = cap // bs
+    table = np.random.default_rng(9).permutation(B * mb).astype(np.int32).reshape(B, mb)
+    pg = kvc.KVCache(B, hkv, D, 0, 8, block_size=bs, num_blocks=B * mb, max_blocks_per_seq=mb, fp16_sinks=4,
+                     fp16_recent=64)
+    pg.block_table.copy_(dev(table))
+    ct = kvc.KVCache(B, hkv, D, cap, 8, fp16_sinks=4, fp16_recent=64)
+    v_host = torch.zeros((B, hkv, cap, D), dtype=torch.float16).pin_memory()
+    v_host[:, :, :L] = torch.from_numpy(d["v"])
+    outs = []
+    for c in (pg, ct):
+        kvc.kvc_quant_append(c, dev(d["k"]), dev(d["v"]))
+        out = torch.empty((B, hq, D), dtype=torch.float32, device="cuda")
+        kvc.kvc_decode_attn_kvsep(c, dev(d["q"]), top_k, v_host, out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
