@@ -54,7 +54,7 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "8476187393f9f6885ae611c6a2307a9b129acf1cbc2da97702a85b00f20871c3"
+TRAFFIC_SHA256 = "767e54d69f87ee1f43918ce9e4a796274b25035bfff3f2bc7ba057135150c672"
 TRAFFIC_BYTES = 70757366
 
 

@@ -22,8 +22,9 @@
 //
 // Split-K (flash-decoding) layout for gfx950:
 //  * grid (splits, KV heads, sequences); a 256-thread workgroup owns `tiles`
-//    256-token tiles of one (sequence, KV head) row and serves every query
-//    head of that KV head (GQA), up to 8 per pass;
+//    256-token tiles of one (sequence, KV head) row (the last split may own a
+//    few more, so the grid stays within one round of resident workgroups)
+//    and serves every query head of that KV head (GQA), up to 8 per pass;
 //  * each wave owns one 64-token block of every tile. It issues the block's
 //    loads at once, raw buffer loads bounded by the cache capacity: scales,
 //    then K codes (registers, in the B-operand layout), then V codes, which
@@ -37,6 +38,10 @@
 //  * the four waves merge once at the end and the split writes (max, sum,
 //    o[D]); a second kernel merges the splits in a fixed order (deterministic).
 // Logits are kept in log2 units (scaled by log2(e)) and exponentiated with exp2.
+//
+// fp16 tiers (report section 3.2: fp16 sinks; tutorial section 1.3: recent
+// tokens at fp16): the split kernel masks the tier slots and skips the recent
+// tier's blocks; attn_tier_kernel (tiers.h) adds them as extra partial states.
 //
 // H2O (report section 3.4; eviction-and-reuse survey section 3.3): with a
 // score array, the split kernel also spills each logit; the merge kernel turns
