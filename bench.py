@@ -54,7 +54,7 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "767e54d69f87ee1f43918ce9e4a796274b25035bfff3f2bc7ba057135150c672"
+TRAFFIC_SHA256 = "84ef5110626831b82cfd0dc8ded47a49649b54c7c56078e26cd86f035f70f134"
 TRAFFIC_BYTES = 70757366
 
 
@@ -304,11 +304,13 @@ def secondary_attention(kvc, torch, reps=16):
     dv, dsc = gc.table_view(), torch.empty((B, H, gc.capacity), device="cuda")
     freed = torch.empty((B, gc.max_blocks_per_seq), dtype=torch.int32, device="cuda")
     fcount = torch.empty((B,), dtype=torch.int32, device="cuda")
-    us_be = timed(lambda i: kvc.kvc_paged_block_evict(gc, sc, 0.5, dv, dsc, freed, fcount, max_len_hint=hint), 1)
+    ws_be = torch.empty(kvc.kvc_paged_block_evict_workspace_bytes(gc), dtype=torch.uint8, device="cuda")
+    us_be = timed(lambda i: kvc.kvc_paged_block_evict(gc, sc, 0.5, dv, dsc, freed, fcount, max_len_hint=hint,
+                                                      workspace=ws_be), 1)
     res["paged_b32_block_evict"] = {"workload": "paged_b32", "us_per_launch": round(us_be, 2), "retention": 0.5,
                                     "blocks": int(sum(nblk)), "blocks_freed": int(fcount.sum().item()),
                                     "score_bytes_moved": int(2 * 4 * H * (int(lengths.sum()) // 2))}
-    del sc, dv, dsc, freed, fcount
+    del sc, dv, dsc, freed, fcount, ws_be
     del gc, ws
     torch.cuda.empty_cache()
 

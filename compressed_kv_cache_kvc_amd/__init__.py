@@ -80,7 +80,8 @@ def _load():
         "kvc_bw_probe_sink_bytes": (SZ, []),
         "kvc_bw_probe": (I32, [P, SZ, P, SZ, P]),
         "kvc_layer_budgets": (I32, [I32, I32, I32, ctypes.c_double, I32, P]),
-        "kvc_paged_block_evict": (I32, [D, P, ctypes.c_double, D, P, P, P, I32, P]),
+        "kvc_paged_block_evict_workspace_bytes": (SZ, [D]),
+        "kvc_paged_block_evict": (I32, [D, P, ctypes.c_double, D, P, P, P, I32, P, SZ, P]),
         "kvc_pool_create": (P, [I32, I32, U64]),
         "kvc_pool_destroy": (None, [P]),
         "kvc_pool_reserve": (I32, [P, I32, I32]),
@@ -458,13 +459,20 @@ def kvc_decode_step(cache, k_new, v_new, q, out, h2o_score, budget: int, n_sink:
         dst.max_len = min(max_len_hint + 1, budget)
 
 
+def kvc_paged_block_evict_workspace_bytes(src) -> int:
+    return lib.kvc_paged_block_evict_workspace_bytes(ctypes.byref(_desc(src)))
+
+
 def kvc_paged_block_evict(src, h2o_score, retention: float, dst, dst_score, freed, freed_count,
-                          max_len_hint: Optional[int] = None, stream=None):
+                          max_len_hint: Optional[int] = None, workspace=None, stream=None):
     """Block-granular H2O eviction on a paged cache (see kvc.h): ``dst`` shares
     ``src``'s pools (``src.table_view()``); ``freed`` int32 ``[B][max_blocks]``
     and ``freed_count`` int32 ``[B]`` receive the released physical blocks."""
     import torch
     ds, dd = _desc(src), _desc(dst)
+    if workspace is None:
+        n = kvc_paged_block_evict_workspace_bytes(ds)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=h2o_score.device)
     _need(h2o_score, torch.float32, "h2o_score", ds.batch * ds.num_kv_heads * ds.capacity)
     _need(dst_score, torch.float32, "dst_score", dd.batch * dd.num_kv_heads * dd.capacity)
     _need(freed, torch.int32, "freed", ds.batch * ds.max_blocks_per_seq)
@@ -473,7 +481,7 @@ def kvc_paged_block_evict(src, h2o_score, retention: float, dst, dst_score, free
         max_len_hint = src.max_len
     _check(lib.kvc_paged_block_evict(ctypes.byref(ds), _ptr(h2o_score), float(retention), ctypes.byref(dd),
                                      _ptr(dst_score), _ptr(freed), _ptr(freed_count), max_len_hint,
-                                     _stream(stream)), "kvc_paged_block_evict")
+                                     _ptr(workspace), workspace.numel(), _stream(stream)), "kvc_paged_block_evict")
     if isinstance(dst, KVCache) and isinstance(src, KVCache):
         dst.max_len = src.max_len
 

@@ -511,9 +511,14 @@ int32_t kvc_compact_gather(const kvc_cache_t* src, const float* src_score, const
                        "kvc_compact_gather launch");
 }
 
+size_t kvc_paged_block_evict_workspace_bytes(const kvc_cache_t* src) {
+  if (!src || src->batch < 1 || src->max_blocks_per_seq < 1) return 0;
+  return align256((size_t)src->batch * src->max_blocks_per_seq * sizeof(float));
+}
+
 int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, double retention,
                               const kvc_cache_t* dst, float* dst_score, int32_t* freed, int32_t* freed_count,
-                              int32_t max_len_hint, void* stream) {
+                              int32_t max_len_hint, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
   int32_t st = check_cache(src, "src");
   if (st) return st;
@@ -542,9 +547,13 @@ int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, do
   // (src table, lengths, num_seen, scores) and no other output.
   const void* in[] = {src->block_table, src->lengths, src->num_seen, h2o_score};
   const size_t in_len[] = {B * MB * 4, B * 4, B * 4, score_bytes};
-  const void* out[] = {dst->block_table, dst->lengths, dst->num_seen, dst_score, freed, freed_count};
-  const size_t out_len[] = {B * MB * 4, B * 4, B * 4, score_bytes, B * MB * 4, B * 4};
-  for (int i = 0; i < 6; ++i) {
+  const size_t ws_need = kvc_paged_block_evict_workspace_bytes(src);
+  if (!workspace || workspace_bytes < ws_need)
+    return fail(KVC_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", ws_need, workspace ? workspace_bytes : 0);
+  if ((uintptr_t)workspace % 256) return fail(KVC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const void* out[] = {dst->block_table, dst->lengths, dst->num_seen, dst_score, freed, freed_count, workspace};
+  const size_t out_len[] = {B * MB * 4, B * 4, B * 4, score_bytes, B * MB * 4, B * 4, ws_need};
+  for (int i = 0; i < 7; ++i) {
     for (int j = 0; j < 4; ++j)
       if (overlap(out[i], out_len[i], in[j], in_len[j]))
         return fail(KVC_ERR_INVALID_ARG, "output %d overlaps input %d (eviction is out of place)", i, j);
@@ -553,7 +562,8 @@ int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, do
         return fail(KVC_ERR_INVALID_ARG, "outputs %d and %d overlap", j, i);
   }
   return device_status(launch_block_evict(*src, h2o_score, retention, *dst, dst_score, freed, freed_count,
-                                          max_len_hint, static_cast<hipStream_t>(stream)),
+                                          static_cast<float*>(workspace), max_len_hint,
+                                          static_cast<hipStream_t>(stream)),
                        "kvc_paged_block_evict launch");
 }
 

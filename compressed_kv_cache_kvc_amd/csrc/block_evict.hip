@@ -15,13 +15,19 @@
 // codes and scales stay where they are: source and destination share the
 // pools.
 //
-// One 256-thread workgroup per sequence: block means into LDS (16-byte
-// loads, four heads in flight), then each block's rank in the stable order
-// by counting (n^2 comparisons from LDS, made for the decode-sized tables of a
-// paged batch), a block scan for the kept and freed positions, and the score
-// rows moved in 16-byte pieces, eight loads in flight per thread. One CU per
-// sequence bounds it: on the 32-sequence paged batch (5114 blocks) a launch
-// takes about 43 us, whatever the loads in flight per thread.
+// Two launches. block_mean_kernel: one wave per block, lanes over (head,
+// quarter row) pairs, 16-byte loads, a fixed-order sum of the filled slots
+// (blocks holding equal scores get equal means), the means to a workspace.
+// block_select_kernel: several workgroups per sequence, each with the means
+// in LDS: every block's rank in the stable order by counting (n^2
+// comparisons, made for decode-sized tables), a block scan for the kept and
+// freed positions (workgroup 0 writes the table, the freed list and the
+// lengths), and a share of the score rows moved in 16-byte pieces, eight
+// loads in flight per thread. One workgroup per sequence doing all of it took
+// about 43 us on the 32-sequence paged batch (5114 blocks), bound by one CU's
+// latency per sequence.
+#include <algorithm>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -29,12 +35,42 @@ namespace {
 
 constexpr int kBT = 256;
 
-__global__ __launch_bounds__(kBT) void block_evict_kernel(kvc_cache_t src, const float* __restrict__ score,
-                                                          double retention, kvc_cache_t dst,
-                                                          float* __restrict__ dst_score, int32_t* __restrict__ freed,
-                                                          int32_t* __restrict__ freed_count, int max_len) {
+// Mean H2O score of each block over its filled slots and all heads.
+__global__ __launch_bounds__(kBT) void block_mean_kernel(kvc_cache_t src, const float* __restrict__ score,
+                                                         float* __restrict__ means, int max_len) {
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
+  const int j = blockIdx.x * (kBT / 64) + (threadIdx.x >> 6);  // this wave's block
+  const int H = src.num_kv_heads, BS = src.block_size, MB = src.max_blocks_per_seq;
+  const long long cap = src.capacity;
+  const int L = __builtin_amdgcn_readfirstlane(min(min(src.lengths[b], src.capacity), max_len));
+  const int nb = (L + BS - 1) / BS;
+  if (j >= nb) return;  // uniform per wave
+  const int fill = min(BS, L - BS * j);
+  // Lane r of each pass takes head r / 4, quarter r % 4 of the 16-slot row (in
+  // bounds: the capacity is a whole number of blocks).
+  float acc = 0.f;
+  for (int r = lane; r < 4 * H; r += 64) {
+    const int h = r >> 2, q = r & 3;
+    const float4 w = reinterpret_cast<const float4*>(score + ((long long)b * H + h) * cap + (long long)BS * j)[q];
+    const float x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (4 * q + c < fill) acc += x[c];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) means[(long long)b * MB + j] = acc / (float)(fill * H);
+}
+
+// Workgroup (part, b): ranks, keep flags and kept positions of sequence b
+// (every part the same), the table rewrite (part 0) and a 1/parts share of
+// the score move.
+__global__ __launch_bounds__(kBT) void block_select_kernel(kvc_cache_t src, const float* __restrict__ score,
+                                                           const float* __restrict__ means, double retention,
+                                                           kvc_cache_t dst, float* __restrict__ dst_score,
+                                                           int32_t* __restrict__ freed,
+                                                           int32_t* __restrict__ freed_count, int max_len) {
   extern __shared__ float lds[];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int part = blockIdx.x, parts = gridDim.x, b = blockIdx.y, tid = threadIdx.x;
   const int H = src.num_kv_heads, BS = src.block_size, MB = src.max_blocks_per_seq;
   const long long cap = src.capacity;
   float* mean = lds;                                    // [MB]
@@ -44,38 +80,7 @@ __global__ __launch_bounds__(kBT) void block_evict_kernel(kvc_cache_t src, const
   const int L = __builtin_amdgcn_readfirstlane(min(min(src.lengths[b], src.capacity), max_len));
   const int nb = (L + BS - 1) / BS;
   const int32_t* srow = src.block_table + (long long)b * MB;
-  // Mean score of each block: heads in order, slots in order, fp32. A block
-  // row is 16 floats (four 16-byte loads, in bounds: the capacity is a whole
-  // number of blocks); kHB heads' loads are in flight at a time, and slots past
-  // the length are masked out of the sum.
-  constexpr int kHB = 4;
-  for (int j = tid; j < nb; j += kBT) {
-    const int fill = min(BS, L - BS * j);
-    float acc = 0.f;
-    for (int h0 = 0; h0 < H; h0 += kHB) {
-      float4 w[kHB][4];
-#pragma unroll
-      for (int hh = 0; hh < kHB; ++hh) {
-        const float4* sc = reinterpret_cast<const float4*>(score + ((long long)b * H + min(h0 + hh, H - 1)) * cap +
-                                                           (long long)BS * j);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[hh][q] = sc[q];
-      }
-#pragma unroll
-      for (int hh = 0; hh < kHB; ++hh) {
-        if (h0 + hh < H) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float x[4] = {w[hh][q].x, w[hh][q].y, w[hh][q].z, w[hh][q].w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (4 * q + c < fill) acc += x[c];
-          }
-        }
-      }
-    }
-    mean[j] = acc / (float)(fill * H);
-  }
+  for (int j = tid; j < nb; j += kBT) mean[j] = means[(long long)b * MB + j];
   __syncthreads();
   // Stable ascending order by mean: block j's rank counts the blocks with a
   // lower mean, or an equal mean and a lower index; ranks below n_evict go.
@@ -103,23 +108,28 @@ __global__ __launch_bounds__(kBT) void block_evict_kernel(kvc_cache_t src, const
   for (int j = j0; j < j1; ++j) {
     if (keep[j]) {
       src_of[kpos] = j;
-      drow[kpos++] = srow[j];
+      if (part == 0) drow[kpos] = srow[j];
+      ++kpos;
     } else {
-      frow[fpos++] = srow[j];
+      if (part == 0) frow[fpos] = srow[j];
+      ++fpos;
     }
   }
-  for (int i = n_kept + tid; i < MB; i += kBT) drow[i] = -1;
+  if (part == 0)
+    for (int i = n_kept + tid; i < MB; i += kBT) drow[i] = -1;
   __syncthreads();
   // Scores move with their blocks: new block i takes old block src_of[i], in
-  // 16-byte pieces (4 per block row), kMB pieces per thread loaded before
-  // any is stored; slots past a partial block's fill are not written.
+  // 16-byte pieces (4 per block row); this part moves pieces [w_lo, w_hi),
+  // kMB per thread loaded before any is stored; slots past a partial block's
+  // fill are not written.
   constexpr int kMB = 8;
   const long long pieces = (long long)n_kept * H * 4;
-  for (long long w0 = tid; w0 < pieces; w0 += (long long)kBT * kMB) {
+  const long long w_lo = pieces * part / parts, w_hi = pieces * (part + 1) / parts;
+  for (long long w0 = w_lo + tid; w0 < w_hi; w0 += (long long)kBT * kMB) {
     float4 v[kMB];
 #pragma unroll
     for (int u = 0; u < kMB; ++u) {
-      const long long w = min(w0 + (long long)u * kBT, pieces - 1);
+      const long long w = min(w0 + (long long)u * kBT, w_hi - 1);
       const int q = (int)(w & 3);
       const long long r = w >> 2;
       const int h = (int)(r % H), i = (int)(r / H);
@@ -128,7 +138,7 @@ __global__ __launch_bounds__(kBT) void block_evict_kernel(kvc_cache_t src, const
 #pragma unroll
     for (int u = 0; u < kMB; ++u) {
       const long long w = w0 + (long long)u * kBT;
-      if (w < pieces) {
+      if (w < w_hi) {
         const int q = (int)(w & 3);
         const long long r = w >> 2;
         const int h = (int)(r % H), i = (int)(r / H);
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(kBT) void block_evict_kernel(kvc_cache_t src, const
       }
     }
   }
-  if (tid == 0) {
+  if (part == 0 && tid == 0) {
     // Only the last block can be partial; it stays last when kept.
     const int last_fill = nb > 0 ? L - BS * (nb - 1) : 0;
     const int new_len = n_kept == 0 ? 0 : (nb > 0 && keep[nb - 1] ? BS * (n_kept - 1) + last_fill : BS * n_kept);
@@ -159,9 +169,17 @@ __global__ __launch_bounds__(kBT) void block_evict_kernel(kvc_cache_t src, const
 size_t block_evict_lds_bytes(int max_blocks_per_seq) { return (size_t)max_blocks_per_seq * 3 * sizeof(float); }
 
 hipError_t launch_block_evict(const kvc_cache_t& src, const float* score, double retention, const kvc_cache_t& dst,
-                              float* dst_score, int32_t* freed, int32_t* freed_count, int max_len, hipStream_t st) {
-  hipLaunchKernelGGL(block_evict_kernel, dim3(src.batch), dim3(kBT), block_evict_lds_bytes(src.max_blocks_per_seq), st,
-                     src, score, retention, dst, dst_score, freed, freed_count, max_len);
+                              float* dst_score, int32_t* freed, int32_t* freed_count, float* means, int max_len,
+                              hipStream_t st) {
+  const int MB = src.max_blocks_per_seq;
+  hipLaunchKernelGGL(block_mean_kernel, dim3((MB + kBT / 64 - 1) / (kBT / 64), src.batch), dim3(kBT), 0, st, src,
+                     score, means, max_len);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // Workgroups per sequence: about 256 in all, at most 8.
+  const int parts = std::max(1, std::min(8, 256 / std::max(1, src.batch)));
+  hipLaunchKernelGGL(block_select_kernel, dim3(parts, src.batch), dim3(kBT), block_evict_lds_bytes(MB), st, src,
+                     score, means, retention, dst, dst_score, freed, freed_count, max_len);
   return hipGetLastError();
 }
 

@@ -132,12 +132,14 @@ hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const 
 hipError_t launch_compact_gather(const kvc_cache_t& src, const float* src_score, const int32_t* keep_index,
                                  int n_keep, const kvc_cache_t& dst, float* dst_score, hipStream_t st);
 
-// Block-granular eviction on a paged cache (one workgroup per sequence;
-// block_evict_lds_bytes of dynamic LDS).
+// Block-granular eviction on a paged cache: the block means (to `means`,
+// [batch][max_blocks_per_seq] fp32), then selection, table rewrite and score
+// move with block_evict_lds_bytes of dynamic LDS per workgroup.
 size_t block_evict_lds_bytes(int max_blocks_per_seq);
 constexpr int kBlockEvictMaxBlocks = 8192;
 hipError_t launch_block_evict(const kvc_cache_t& src, const float* score, double retention, const kvc_cache_t& dst,
-                              float* dst_score, int32_t* freed, int32_t* freed_count, int max_len, hipStream_t st);
+                              float* dst_score, int32_t* freed, int32_t* freed_count, float* means, int max_len,
+                              hipStream_t st);
 
 // K/V-separated attention's last step (kvsep.hip): per (sequence, KV head),
 // the output of each query head from the kept tokens' fp16 V rows.

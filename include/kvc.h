@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum {
   KVC_OK = 0,
@@ -406,7 +406,8 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
  *
  * For each sequence b with L = min(src->lengths[b], max_len_hint) and
  * n = ceil(L / 16) blocks: a block's score is the mean of h2o_score over its
- * filled slots and all KV heads (fp32, heads then slots in order); with
+ * filled slots and all KV heads (an fp32 sum in a fixed order, so blocks
+ * holding equal scores get equal means); with
  * n_evict = (int)(n * (1 - retention)) in double arithmetic, the n_evict
  * blocks first in ascending order of score (equal scores: lower block index
  * first) are evicted. dst's table row b lists the kept physical blocks in
@@ -419,17 +420,21 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
  *
  * src and dst are paged caches with the same geometry that share the code and
  * scale pools; dst's block table, lengths and num_seen are its own (device
- * buffers the call writes). Cost: n^2 comparisons per sequence in one
- * workgroup, sized for decode-length tables.
+ * buffers the call writes). workspace: device memory of
+ * kvc_paged_block_evict_workspace_bytes(src) bytes, 256-byte aligned, disjoint
+ * from every other buffer (the block means). Cost: two launches; n^2
+ * comparisons per sequence, sized for decode-length tables.
  * Errors: INVALID_ARG for bad or contiguous descriptors, different
  * geometries or pools, NULL arrays, retention outside [0, 1], overlapping
- * inputs and outputs; CAPACITY if max_len_hint > capacity; UNSUPPORTED above
+ * inputs and outputs, a missing, small or unaligned workspace; CAPACITY if max_len_hint > capacity; UNSUPPORTED above
  * 8192 blocks per sequence, or for caches with fp16 tiers (block eviction
  * keeps no sinks or window, so it cannot keep the tiers).
  */
+size_t kvc_paged_block_evict_workspace_bytes(const kvc_cache_t* src);
 int32_t kvc_paged_block_evict(const kvc_cache_t* src, const float* h2o_score, double retention,
                               const kvc_cache_t* dst, float* dst_score, int32_t* freed,
-                              int32_t* freed_count, int32_t max_len_hint, void* stream);
+                              int32_t* freed_count, int32_t max_len_hint, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * Per-layer keep budgets (host only): the pyramid schedules of the pages.

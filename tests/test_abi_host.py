@@ -42,7 +42,7 @@ def test_exports_match_binding_names():
 
 
 def test_version_and_status_strings():
-    assert kvc.kvc_abi_version() == 3
+    assert kvc.kvc_abi_version() == 4
     assert kvc.kvc_status_str(0) == "KVC_OK"
     assert kvc.kvc_status_str(2) == "KVC_ERR_CAPACITY"
     assert kvc.kvc_status_str(99) == "KVC_UNKNOWN"
@@ -140,8 +140,15 @@ def test_paged_block_evict_validation():
                lengths=0xA100000, num_seen=0xA100100)
     dst = desc(block_size=16, max_blocks_per_seq=32, num_blocks=64, positions=None, block_table=0xB000000,
                lengths=0xB100000, num_seen=0xB100100)
-    call = lambda s_=src, d_=dst, sc=0xC000000, dsc=0xD000000, fr=0xE000000, fc=0xE100000, r=0.5, hint=100: \
-        lib.kvc_paged_block_evict(ctypes.byref(s_), sc, r, ctypes.byref(d_), dsc, fr, fc, hint, None)
+    need = lib.kvc_paged_block_evict_workspace_bytes(ctypes.byref(src))
+    assert need >= 32 * 4
+    call = lambda s_=src, d_=dst, sc=0xC000000, dsc=0xD000000, fr=0xE000000, fc=0xE100000, r=0.5, hint=100, \
+        ws=0xF100000, n=need: lib.kvc_paged_block_evict(ctypes.byref(s_), sc, r, ctypes.byref(d_), dsc, fr, fc, hint,
+                                                        ws, n, None)
+    assert call(ws=None) == INVALID
+    assert call(n=need - 1) == INVALID
+    assert call(ws=0xF100000 + 16) == INVALID         # not 256-byte aligned
+    assert call(ws=0xD000000) == INVALID              # on dst's scores
     assert call(r=1.5) == INVALID
     assert call(r=float("nan")) == INVALID
     assert call(sc=None) == INVALID
@@ -314,7 +321,7 @@ def test_fp16_tier_validation():
     pd = desc(block_size=16, max_blocks_per_seq=32, num_blocks=64, positions=None, block_table=0xB000000,
               lengths=0xB100000, num_seen=0xB100100, **T)
     assert lib.kvc_paged_block_evict(ctypes.byref(ps), 0xC000000, 0.5, ctypes.byref(pd), 0xD000000, 0xE000000,
-                                     0xE100000, 100, None) == UNSUPPORTED
+                                     0xE100000, 100, 0xF100000, 1 << 20, None) == UNSUPPORTED
 
 
 def test_kvsep_validation():
