@@ -404,6 +404,54 @@ def secondary_attention(kvc, torch, reps=16):
                      "calls": "kvc_decode_attn_kvsep (clear, split, merge, select, gather)"}
         del c, v_host, ws
         torch.cuda.empty_cache()
+
+    # The GQA stream's whole decode step in steady state (c4 after its first
+    # step): 8 sequences of 8192 kept tokens, append the new one, attend with
+    # H2O over 8193, evict back to 8192 (4 sinks + 2048 recent + 6140 heavy),
+    # one kvc_decode_step per step (G = 7: split, merge and the one-launch
+    # eviction). 8 rotated caches share one lengths array, so a fill rewinds
+    # all of them once per 8 steps; the fill is inside the timed graph.
+    w = get("qwen_gqa_stream")
+    B, Hq, H, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    Lk, n_bufs = w.budget, 8
+    lengths_q = torch.zeros((n_bufs, B), dtype=torch.int32, device="cuda")
+    seen_q = torch.zeros((n_bufs, B), dtype=torch.int32, device="cuda")
+    caches, scores = [], []
+    for i in range(n_bufs):
+        c = kvc.KVCache(B, H, D, Lk + 1, w.bits)
+        c.lengths, c.num_seen = lengths_q[i], seen_q[i]
+        c.desc = c._make_desc()
+        kv = torch.randn((2, B, H, Lk, D), device="cuda").half()
+        kvc.kvc_quant_append(c, kv[0], kv[1], max_len_hint=0)
+        del kv
+        caches.append(c)
+        scores.append(c.score_buffer())
+    dstq = kvc.KVCache(B, H, D, Lk + 1, w.bits)
+    dsc = dstq.score_buffer()
+    kidx = torch.empty((B, H, Lk), dtype=torch.int32, device="cuda")
+    knew = torch.randn((B, H, 1, D), device="cuda").half()
+    vnew = torch.randn((B, H, 1, D), device="cuda").half()
+    q = torch.randn((B, Hq, D), device="cuda").half()
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, Lk + 1, True), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        if i % n_bufs == 0:
+            lengths_q.fill_(Lk)
+            seen_q.fill_(Lk)
+        kvc.kvc_decode_step(caches[i % n_bufs], knew, vnew, q, out, scores[i % n_bufs], Lk, w.n_sink, w.n_recent,
+                            kidx, dstq, dsc, max_len_hint=Lk, workspace=ws)
+
+    lengths_q.fill_(Lk)
+    seen_q.fill_(Lk)
+    us = timed(step, 1 << 30, 64)  # launch(i) gets the running index
+    res["qwen_gqa_stream_step"] = {"workload": "qwen_gqa_stream", "us_per_step": round(us, 2),
+                                   "tokens_per_s_per_layer": round(B / (us * 1e-6), 1),
+                                   "kv_bytes_attended": int(B * H * (Lk + 1) * 2 * (D + 4)),
+                                   "calls": "kvc_decode_step (append, attention + H2O, evict 8193 -> 8192)"}
+    del caches, scores, dstq, dsc, ws
+    torch.cuda.empty_cache()
     return res
 
 
