@@ -54,7 +54,7 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "84ef5110626831b82cfd0dc8ded47a49649b54c7c56078e26cd86f035f70f134"
+TRAFFIC_SHA256 = "63a5c6c88e648326583df776c7d92593b7ff528acd725c9078fc4c7d6b9f3970"
 TRAFFIC_BYTES = 70757366
 
 

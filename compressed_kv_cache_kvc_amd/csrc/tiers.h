@@ -105,6 +105,7 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int xt, float* q
     }
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
+      if (j0 + TPI * NH * half >= nt) break;  // no tier token left in this wave (uniform)
       u32x4 kx[NH], vx[NH];
 #pragma unroll
       for (int i = 0; i < NH; ++i) {
@@ -122,6 +123,7 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int xt, float* q
       }
 #pragma unroll
       for (int i = 0; i < NH; ++i) {
+        if (j0 + TPI * (half * NH + i) >= nt) break;  // the rest of the groups are past the tier (uniform)
         const int j = j0 + TPI * (half * NH + i) + r;
         const bool ok = j < nt;
 #pragma unroll
