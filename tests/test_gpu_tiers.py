@@ -129,7 +129,7 @@ def test_tier_short_rows(L):
     assert_scores_close(host(score), ref.score, ref.lengths)
 
 
-@pytest.mark.parametrize("hq,hkv,bits", [(4, 4, 8), (8, 2, 4)])
+@pytest.mark.parametrize("hq,hkv,bits", [(4, 4, 8), (8, 2, 4), (16, 2, 8)])  # G = 8: the step's separate launches
 def test_tier_decode_step_equals_separate_calls(hq, hkv, bits):
     """kvc_decode_step on a tiered cache equals kvc_append_decode_attn +
     kvc_h2o_evict bit for bit (output, keep list, compacted cache, kept
