@@ -54,7 +54,7 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "63a5c6c88e648326583df776c7d92593b7ff528acd725c9078fc4c7d6b9f3970"
+TRAFFIC_SHA256 = "8c0679fcf0b985edfbb9e0f7ce169d6d3db20a357aa921c80c250a75a20a3fcd"
 TRAFFIC_BYTES = 70757366
 
 

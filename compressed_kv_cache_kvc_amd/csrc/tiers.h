@@ -7,8 +7,8 @@
 // keeps recent tokens at fp16 and older ones quantized. In a row of L slots
 // the sink tier is slots [0, ns), ns = min(fp16_sinks, L), and the recent tier
 // the newest nr = min(fp16_recent, L - ns) slots. The split workgroups mask
-// those slots out; here each wave turns 64 tier tokens into one more partial
-// softmax state per query head (part S + 4 x + wave), in the split states'
+// those slots out; here one wave (one workgroup) turns 64 tier tokens into one
+// more partial softmax state per query head (part S + x), in the split states'
 // convention (max in log2 units, sum, unnormalized o), so the merge folds the
 // tiers in with the splits. The tier slots' H2O logits are spilled at their
 // slots.
@@ -18,11 +18,16 @@
 // num_seen - L + i. With an append in the same call, the new token's rows come
 // from k_new / v_new, and the wave that holds it stores them in the tiers.
 //
-// Layout in a wave: LPT = D / 8 lanes per token (16 bytes each), TPI = 64 / LPT
-// tokens per load, NI = 64 / TPI loads per lane for K and for V, issued half
-// at a time (each half's loads together, before its arithmetic). Logits are
-// LPT-lane dot products; the softmax runs online over the token groups; the
-// groups' states are summed at the end. GP query heads per pass.
+// Layout in the wave: LPT = D / 8 lanes per token (16 bytes each), TPI = 64 /
+// LPT tokens per load, NI = 64 / TPI = LPT loads per lane for K and for V,
+// issued half at a time (NH = LPT / 2 loads, together, before the half's
+// arithmetic). A lane's NH partial dot products are summed over the token's
+// LPT lanes by a reduce-scatter (halve the list at each exchange, DPP lane
+// moves), after which lane pair (2 i, 2 i + 1) of a token row holds the logit
+// of group i: one exchange per value instead of a log2(LPT) butterfly per
+// group, and one exp2 per lane. Each half is one online-softmax block; the probabilities go
+// back to the lanes holding the V rows by lane-indexed reads. GP query heads
+// per pass, their q rows in registers.
 #pragma once
 
 #include "kvc_internal.h"
@@ -32,12 +37,61 @@ namespace tier {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// qs: GP * D floats of LDS, free for this workgroup's use.
+// The value of the lane that differs from this one in bits 0..log2(S) (a
+// mirror inside each half-row or row for S = 4, 8; xor 2, xor 1 below):
+// DPP, no LDS round trip.
+template <int S>
+__device__ __forceinline__ float partner(float v) {
+  if constexpr (S == 8) return dpp_f<0x140>(v, v);       // row mirror: lane ^ 15
+  else if constexpr (S == 4) return dpp_f<0x141>(v, v);  // half-row mirror: lane ^ 7
+  else if constexpr (S == 2) return dpp_f<0x4E>(v, v);   // lane ^ 2
+  else return dpp_f<0xB1>(v, v);                         // lane ^ 1
+}
+
+// One exchange of the reduce-scatter: keep half of the list (the upper half
+// where bit S of the lane is set), add the partner's copy of that half.
+template <int S, int N>
+__device__ __forceinline__ void scatter_step(float (&x)[N], int lane) {
+  if constexpr (S >= 2) {
+    constexpr int n = S / 2;
+    const bool up = lane & S;
+#pragma unroll
+    for (int k = 0; k < n; ++k) {
+      const float keep = up ? x[n + k] : x[k], give = up ? x[k] : x[n + k];
+      x[k] = keep + partner<S>(give);
+    }
+    scatter_step<S / 2>(x, lane);
+  }
+}
+
+// Sums x[0..N) over the 2 N lanes of an aligned group (N = 4 or 8): after
+// it, lane l holds the total of list entry (l % (2 N)) / 2. Every partner
+// shares the bits already used, so each exchange adds disjoint lane sets.
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&x)[N], int lane) {
+  static_assert(N == 4 || N == 8, "a row or half-row of lanes");
+  scatter_step<N>(x, lane);
+  return x[0] + partner<1>(x[0]);
+}
+
+// Sum over the wave, in every lane: DPP inside rows, row broadcasts, then
+// lane 63 (the rows the broadcasts leave out hold partial values).
+__device__ __forceinline__ float wave_total(float v) {
+  v += dpp_f<0xB1>(v, v);
+  v += dpp_f<0x4E>(v, v);
+  v += dpp_f<0x141>(v, v);
+  v += dpp_f<0x140>(v, v);
+  v += dpp_f<0x142, 0xA>(v, v);
+  v += dpp_f<0x143, 0xC>(v, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 template <int D, int GP>
-__device__ __forceinline__ void tier_parts(const AttnLaunch& a, int xt, float* qs) {
-  constexpr int LPT = D / 8, TPI = 64 / LPT, NI = kTierTokens / TPI;
+__device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part) {
+  constexpr int LPT = D / 8, TPI = 64 / LPT, NI = kTierTokens / TPI, NH = NI / 2;
+  static_assert(NI == LPT && NH * 2 == LPT, "one token group per lane pair after the reduce-scatter");
   const kvc_cache_t& c = a.c;
-  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits, P = a.parts;
   const long long span = attn_span(a);
   const bool app = a.k_new != nullptr;
@@ -46,8 +100,6 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int xt, float* q
   const int seen = __builtin_amdgcn_readfirstlane(c.num_seen[b]) + (app ? 1 : 0);
   const long long rowid = (long long)b * H + g;
   const int ns = min(c.fp16_sinks, L), nr = min(c.fp16_recent, L - ns), nt = ns + nr;
-  const int part = 4 * xt + wave;  // parts past tier_parts idle (but join the barriers)
-  const bool active = part < a.tier_parts;
   const int j0 = part * kTierTokens;
   const bool new_here = app && L_old >= 0 && L_old < L;  // slot L_old was appended in this call
   const __half* k_sink = static_cast<const __half*>(c.k_sink16) + rowid * c.fp16_sinks * D;
@@ -65,7 +117,7 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int xt, float* q
 
   // The appended token's tier rows, stored by the wave that holds its tier
   // index; no other wave of this launch reads those rows (they read k_new).
-  if (active && new_here) {
+  if (new_here) {
     const int jn = L_old < ns ? L_old : (L_old >= L - nr ? ns + (L_old - (L - nr)) : -1);
     if (jn >= j0 && jn < j0 + kTierTokens && lane < LPT) {
       const u32x4 kx = *reinterpret_cast<const u32x4*>(a.k_new + rowid * D + lane * 8);
@@ -83,23 +135,22 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int xt, float* q
     }
   }
 
-  // ---- per head pass: the wave's tokens in two halves, each half's K and V
-  // loads issued together before its arithmetic; online softmax ----
   const int r = lane / LPT, cc = lane % LPT;  // token within a load, 16-byte chunk of the row
-  constexpr int NH = NI / 2;
+  const int gi = cc >> 1;                     // group whose logit the lane holds after the reduce-scatter
   for (int hp = 0; hp < G; hp += GP) {
-    __syncthreads();  // the previous pass is done with qs
-    for (int i = tid; i < GP * D; i += 256) {
-      const int h = i / D;
-      qs[i] = hp + h < G ? __half2float(a.q[((long long)b * Hq + g * G + hp) * D + i]) : 0.f;
+    float qv[GP][8];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      // q is only 2-byte aligned: element loads
+      const __half* qr = a.q + ((long long)b * Hq + g * G + min(hp + h, G - 1)) * D + cc * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[h][e] = hp + h < G ? __half2float(qr[e]) : 0.f;
     }
-    __syncthreads();
-    if (!active) continue;
     float m_run[GP], l_run[GP], o[GP][8];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
       m_run[h] = -INFINITY;
-      l_run[h] = 0.f;
+      l_run[h] = 0.f;  // this lane's share: lanes with even cc count their token
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
     }
@@ -121,60 +172,73 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int xt, float* q
           vx[i] = *reinterpret_cast<const u32x4*>(vr + cc * 8);
         }
       }
+      const int jt = j0 + TPI * (half * NH + gi) + r;  // the token whose logit this lane ends with
+      const bool ok = jt < nt;
 #pragma unroll
-      for (int i = 0; i < NH; ++i) {
-        if (j0 + TPI * (half * NH + i) >= nt) break;  // the rest of the groups are past the tier (uniform)
-        const int j = j0 + TPI * (half * NH + i) + r;
-        const bool ok = j < nt;
+      for (int h = 0; h < GP; ++h) {
+        if (hp + h >= G) break;  // uniform
+        float dv[NH];
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
+        for (int i = 0; i < NH; ++i) {
           float d = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const unsigned uk = kx[i][e];  // a scalar first: a bit_cast of a vector element reads element 0
             const __half2 hk = __builtin_bit_cast(__half2, uk);
-            d = fmaf(qs[h * D + cc * 8 + 2 * e], __low2float(hk), d);
-            d = fmaf(qs[h * D + cc * 8 + 2 * e + 1], __high2float(hk), d);
+            d = fmaf(qv[h][2 * e], __low2float(hk), d);
+            d = fmaf(qv[h][2 * e + 1], __high2float(hk), d);
           }
+          dv[i] = d;
+        }
+        const float dsum = reduce_scatter<NH>(dv, cc);  // every lane takes part in the exchanges
+        const float lg = ok ? dsum * a.qk_log2 : -INFINITY;
+        if (a.logits && ok && !(cc & 1)) a.logits[((long long)b * Hq + g * G + hp + h) * span + slot_of(jt)] = lg;
+        // The half holds at least one tier token (j0 + TPI NH half < nt), so mn is finite.
+        const float mn = fmaxf(m_run[h], wave_max(lg));
+        const float corr = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - mn);
+        const float p = ok ? __builtin_amdgcn_exp2f(lg - mn) : 0.f;
+        m_run[h] = mn;
+        l_run[h] = fmaf(l_run[h], corr, (cc & 1) ? 0.f : p);
 #pragma unroll
-          for (int s = 1; s < LPT; s <<= 1) d += __shfl_xor(d, s);
-          const bool real = ok && hp + h < G;
-          const float lg = real ? d * a.qk_log2 : -INFINITY;
-          if (a.logits && real && cc == 0) a.logits[((long long)b * Hq + g * G + hp + h) * span + slot_of(j)] = lg;
-          float mb = lg;
+        for (int e = 0; e < 8; ++e) o[h][e] *= corr;
 #pragma unroll
-          for (int s = LPT; s < 64; s <<= 1) mb = fmaxf(mb, __shfl_xor(mb, s));
-          const float mn = fmaxf(m_run[h], mb);
-          const float corr = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - mn);
-          const float p = lg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg - mn);
-          m_run[h] = mn;
-          l_run[h] = fmaf(l_run[h], corr, p);
+        for (int i = 0; i < NH; ++i) {
+          const float pi = __shfl(p, r * LPT + 2 * i);  // probability of this lane's token in group i
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const unsigned uv = vx[i][e];
             const __half2 hv = __builtin_bit_cast(__half2, uv);
-            o[h][2 * e] = fmaf(o[h][2 * e], corr, p * __low2float(hv));
-            o[h][2 * e + 1] = fmaf(o[h][2 * e + 1], corr, p * __high2float(hv));
+            o[h][2 * e] = fmaf(pi, __low2float(hv), o[h][2 * e]);
+            o[h][2 * e + 1] = fmaf(pi, __high2float(hv), o[h][2 * e + 1]);
           }
         }
       }
     }
-    // Sum the token groups (lanes equal mod LPT), then lanes 0..LPT-1 write
-    // channels 8 cc .. 8 cc + 7 of each head's state.
+    // Sum the TPI token rows (lanes equal mod LPT) by a reduce-scatter over
+    // the 8 channels: each lane ends with NO consecutive channels of its chunk.
+    constexpr int NO = 8 * LPT / 64;
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
       if (hp + h >= G) break;
-      float l = l_run[h];
-#pragma unroll
-      for (int s = LPT; s < 64; s <<= 1) l += __shfl_xor(l, s);
+      const float l = wave_total(l_run[h]);
       const long long pi = ((long long)b * Hq + g * G + hp + h) * P + S + part;
+      float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = o[h][e];
+      for (int e = 0; e < 8; ++e) v[e] = o[h][e];
+      int off = 0;
 #pragma unroll
-        for (int s = LPT; s < 64; s <<= 1) v += __shfl_xor(v, s);
-        if (r == 0) a.part_o[pi * D + cc * 8 + e] = v;
+      for (int s = LPT; s < 64; s <<= 1) {
+        const int n = 4 * LPT / s;  // entries kept after this exchange
+        const bool up = lane & s;
+        off += up ? n : 0;
+#pragma unroll
+        for (int k = 0; k < n; ++k) {
+          const float keep = up ? v[n + k] : v[k], give = up ? v[k] : v[n + k];
+          v[k] = keep + __shfl_xor(give, s);
+        }
       }
+#pragma unroll
+      for (int k = 0; k < NO; ++k) a.part_o[pi * D + cc * 8 + off + k] = v[k];
       if (lane == 0) {
         a.part_ml[pi * 2] = m_run[h];
         a.part_ml[pi * 2 + 1] = l;
