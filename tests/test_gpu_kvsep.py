@@ -39,6 +39,8 @@ CASES = [
     (8, 8, 8, 128, 2, 257, 1, 4, 0),         # top_k = 1
     (8, 32, 2, 128, 2, 900, 512, 2, 100),    # GQA 16
     (4, 4, 4, 128, 2, 40, 50, 0, 0),         # L < top_k <= capacity: all kept
+    (8, 32, 32, 128, 1, 8192, 2457, 0, 0),   # the benchmarked layer: every kept row cold
+    (8, 32, 32, 128, 1, 8192, 2457, 4, 1024),  # the benchmarked layer with the hot window
 ]
 
 

@@ -199,3 +199,36 @@ def test_tier_paged_equals_contiguous(bits, hq, hkv):
     assert torch.equal(a1, b1) and torch.equal(a2, b2) and torch.equal(sa, sb)
     for name in ("k_sink16", "v_sink16", "k_recent16", "v_recent16", "lengths", "num_seen"):
         assert torch.equal(getattr(pg, name), getattr(ct, name)), name
+
+
+@pytest.mark.parametrize("path", ["separate", "fused"])
+def test_int4_hybrid_llama7b_full_size(path):
+    """The benchmarked hybrid layer at full size: INT4 codes, 32 heads,
+    D = 128, 8192 tokens, 4 fp16 sinks and the newest int(0.3 L) = 2457 tokens
+    at fp16 (39 tier parts per row), one attention call with H2O (the
+    benchmark's call and length hint on the separate path); every head
+    checked. "fused" appends the 8192nd token inside the attention call (its
+    rows go to the ring there)."""
+    w = get("llama7b_8k").scaled(bits=4)
+    d = draw(w)
+    L, S16, R16 = w.context, 4, int(0.3 * w.context)
+    print(f"[tiers] INT4 hybrid full size, path={path}", flush=True)
+    gc = _tiered(w, L, 0, S16, R16)
+    score = gc.score_buffer()
+    ref = oracle.RefCache(w.batch, w.num_kv_heads, w.head_dim, L, 4, fp16_sinks=S16, fp16_recent=R16)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    if path == "separate":
+        kvc.kvc_quant_append(gc, dev(d["k"]), dev(d["v"]), h2o_score=score)
+        kvc.kvc_decode_attn(gc, dev(d["q"]), out, h2o_score=score, max_len_hint=L)
+    else:
+        kvc.kvc_quant_append(gc, dev(d["k"][:, :, :L - 1]), dev(d["v"][:, :, :L - 1]), h2o_score=score)
+        kvc.kvc_append_decode_attn(gc, dev(d["k"][:, :, L - 1:]), dev(d["v"][:, :, L - 1:]), dev(d["q"]), out,
+                                   h2o_score=score)
+    ref.append(d["k"], d["v"])
+    ro, _ = ref.attend(d["q"])
+    torch.cuda.synchronize()
+    assert_codes_equal(gc, ref)
+    _check_tier_rows(gc, ref, S16, R16)
+    err = assert_out_close(host(out), ro)
+    rel = assert_scores_close(host(score), ref.score, ref.lengths)
+    print(f"max-abs out err {err:.2e}, worst score rel err {rel:.2e}", flush=True)
