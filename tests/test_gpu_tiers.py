@@ -59,6 +59,7 @@ LOOPS = [
     (4, 0, 4, 4, 64, 0, 100),      # recent window only, D = 64, two tier parts
     (8, 4, 16, 2, 128, 2, 37),     # K INT8 / V INT4, GQA 8
     (8, 0, 32, 2, 128, 4, 70),     # GQA 16
+    (8, 0, 8, 4, 64, 4, 50),       # D = 64, GQA 2
 ]
 
 
