@@ -7,7 +7,9 @@ C ABI declared in ``include/kvc.h`` through ctypes, and raises
 package fails loudly when the library has not been built.
 
 Function names match the C entry points (``kvc_quant_append``,
-``kvc_decode_attn``, ``kvc_h2o_select``, ``kvc_compact`` and the
+``kvc_decode_attn`` and its fused and split forms, ``kvc_h2o_select``,
+``kvc_compact``, ``kvc_h2o_evict``, ``kvc_decode_step``, the paged block
+eviction, K/V-separated attention, ``kvc_layer_budgets`` and the
 ``kvc_pool_*`` calls). :class:`KVCache` owns the device buffers one cache
 descriptor points to; :class:`BlockPool` wraps the host block pool.
 """
@@ -21,7 +23,12 @@ __all__ = [
     "KvcError", "KVCache", "BlockPool", "lib", "LIB_PATH",
     "kvc_abi_version", "kvc_status_str", "kvc_last_error",
     "kvc_quant_append", "kvc_decode_attn", "kvc_decode_attn_workspace_bytes",
+    "kvc_append_decode_attn", "kvc_decode_attn_split", "kvc_decode_attn_merge",
     "kvc_h2o_select", "kvc_compact", "kvc_compact_workspace_bytes", "kvc_compact_gather",
+    "kvc_h2o_evict", "kvc_decode_step", "kvc_layer_budgets",
+    "kvc_paged_block_evict", "kvc_paged_block_evict_workspace_bytes",
+    "kvc_decode_attn_kvsep", "kvc_decode_attn_kvsep_workspace_bytes",
+    "kvc_bw_probe", "kvc_bw_probe_sink_bytes",
     "row_bytes",
 ]
 

@@ -39,6 +39,8 @@ def test_exports_match_binding_names():
     for n in declared_functions():
         if not n.startswith("kvc_pool_"):
             assert hasattr(kvc, n), f"binding lacks {n}"
+            assert n in kvc.__all__ or n in ("kvc_status_str", "kvc_last_error"), f"__all__ lacks {n}"
+    assert all(hasattr(kvc, n) for n in kvc.__all__)
 
 
 def test_version_and_status_strings():
