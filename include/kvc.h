@@ -105,7 +105,7 @@ typedef struct kvc_cache {
   int32_t bits;                /* 8 or 4: K code width (and V's unless v_bits is set) */
   int32_t batch;               /* sequences, >= 1 */
   int32_t num_kv_heads;        /* >= 1 */
-  int32_t head_dim;            /* 64, 128 or 256 */
+  int32_t head_dim;            /* 64 or 128 (other multiples of 16 up to 256: UNSUPPORTED) */
   int32_t capacity;            /* slots per (sequence, KV head) */
   int32_t block_size;          /* 0 = contiguous, 16 = paged */
   int32_t max_blocks_per_seq;  /* paged only */
