@@ -54,7 +54,7 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "8c0679fcf0b985edfbb9e0f7ce169d6d3db20a357aa921c80c250a75a20a3fcd"
+TRAFFIC_SHA256 = "5d209113ec6acfdd56e2475c86fc16618cba6f3cfb891d29d5ff3b8969fb5ef5"
 TRAFFIC_BYTES = 70757366
 
 

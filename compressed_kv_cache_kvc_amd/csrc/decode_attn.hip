@@ -745,11 +745,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   }
 }
 
-// Attention over the fp16 tiers (tiers.h): the one wave of workgroup x makes
+// Attention over the fp16 tiers (tiers.h): the two waves of workgroup x make
 // part S + x of each query head, GT heads per pass.
 template <int D, int GT>
-__global__ __launch_bounds__(64) void attn_tier_kernel(AttnLaunch a) {
-  tier::tier_parts<D, GT>(a, blockIdx.x);
+__global__ __launch_bounds__(128) void attn_tier_kernel(AttnLaunch a) {
+  __shared__ float xo[GT * D], xml[2 * GT];
+  tier::tier_parts<D, GT>(a, blockIdx.x, xo, xml);
 }
 
 template <int KBITS, int VBITS, int D, int GP, bool PAGED>
@@ -786,10 +787,10 @@ hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st) {
   if (a.c.bits == 8) e = vb == 8 ? launch_dim<8, 8>(a, G, st) : launch_dim<8, 4>(a, G, st);
   else e = vb == 8 ? launch_dim<4, 8>(a, G, st) : launch_dim<4, 4>(a, G, st);
   if (e != hipSuccess || a.tier_parts <= 0) return e;
-  // The fp16 tiers: one one-wave workgroup per part, right after the splits.
+  // The fp16 tiers: one two-wave workgroup per part, right after the splits.
   const dim3 grid(a.tier_parts, a.c.num_kv_heads, a.c.batch);
   const int gt = G == 1 ? 1 : G == 2 ? 2 : 4;
-#define KVC_TIER(DD, GG) hipLaunchKernelGGL((attn_tier_kernel<DD, GG>), grid, dim3(64), 0, st, a)
+#define KVC_TIER(DD, GG) hipLaunchKernelGGL((attn_tier_kernel<DD, GG>), grid, dim3(128), 0, st, a)
   if (a.c.head_dim == 64) {
     if (gt == 1) KVC_TIER(64, 1);
     else if (gt == 2) KVC_TIER(64, 2);

@@ -7,7 +7,7 @@
 // keeps recent tokens at fp16 and older ones quantized. In a row of L slots
 // the sink tier is slots [0, ns), ns = min(fp16_sinks, L), and the recent tier
 // the newest nr = min(fp16_recent, L - ns) slots. The split workgroups mask
-// those slots out; here one wave (one workgroup) turns 64 tier tokens into one
+// those slots out; here a two-wave workgroup turns 64 tier tokens into one
 // more partial softmax state per query head (part S + x), in the split states'
 // convention (max in log2 units, sum, unnormalized o), so the merge folds the
 // tiers in with the splits. The tier slots' H2O logits are spilled at their
@@ -19,15 +19,16 @@
 // from k_new / v_new, and the wave that holds it stores them in the tiers.
 //
 // Layout in the wave: LPT = D / 8 lanes per token (16 bytes each), TPI = 64 /
-// LPT tokens per load, NI = 64 / TPI = LPT loads per lane for K and for V,
-// issued half at a time (NH = LPT / 2 loads, together, before the half's
-// arithmetic). A lane's NH partial dot products are summed over the token's
-// LPT lanes by a reduce-scatter (halve the list at each exchange, DPP lane
-// moves), after which lane pair (2 i, 2 i + 1) of a token row holds the logit
-// of group i: one exchange per value instead of a log2(LPT) butterfly per
-// group, and one exp2 per lane. Each half is one online-softmax block; the probabilities go
-// back to the lanes holding the V rows by lane-indexed reads. GP query heads
-// per pass, their q rows in registers.
+// LPT tokens per load, NI = 64 / TPI = LPT loads per lane for K and for V.
+// Wave w takes half w of the 64 tokens: its NH = LPT / 2 loads go out
+// together, in one round, before its arithmetic; the two waves' states meet
+// in LDS at the end. A lane's NH partial dot products are summed over the
+// token's LPT lanes by a reduce-scatter (halve the list at each exchange, DPP
+// lane moves), after which lane pair (2 i, 2 i + 1) of a token row holds the
+// logit of group i: one exchange per value instead of a log2(LPT) butterfly
+// per group, and one exp2 per lane. The probabilities go back to the lanes
+// holding the V rows by lane-indexed reads. GP query heads per pass, their q
+// rows in registers.
 #pragma once
 
 #include "kvc_internal.h"
@@ -86,12 +87,14 @@ __device__ __forceinline__ float wave_total(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// xo: GP * D floats and xml: 2 * GP floats of LDS, this workgroup's (two
+// waves, 128 threads).
 template <int D, int GP>
-__device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part) {
+__device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part, float* xo, float* xml) {
   constexpr int LPT = D / 8, TPI = 64 / LPT, NI = kTierTokens / TPI, NH = NI / 2;
   static_assert(NI == LPT && NH * 2 == LPT, "one token group per lane pair after the reduce-scatter");
   const kvc_cache_t& c = a.c;
-  const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63, half = threadIdx.x >> 6;
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits, P = a.parts;
   const long long span = attn_span(a);
   const bool app = a.k_new != nullptr;
@@ -119,7 +122,8 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part) {
   // index; no other wave of this launch reads those rows (they read k_new).
   if (new_here) {
     const int jn = L_old < ns ? L_old : (L_old >= L - nr ? ns + (L_old - (L - nr)) : -1);
-    if (jn >= j0 && jn < j0 + kTierTokens && lane < LPT) {
+    const int h0 = j0 + half * (kTierTokens / 2);
+    if (jn >= h0 && jn < h0 + kTierTokens / 2 && lane < LPT) {
       const u32x4 kx = *reinterpret_cast<const u32x4*>(a.k_new + rowid * D + lane * 8);
       const u32x4 vx = *reinterpret_cast<const u32x4*>(a.v_new + rowid * D + lane * 8);
       if (L_old < c.fp16_sinks) {
@@ -137,6 +141,7 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part) {
 
   const int r = lane / LPT, cc = lane % LPT;  // token within a load, 16-byte chunk of the row
   const int gi = cc >> 1;                     // group whose logit the lane holds after the reduce-scatter
+  constexpr int NO = 8 * LPT / 64;  // channels a lane ends with after the row reduce-scatter
   for (int hp = 0; hp < G; hp += GP) {
     float qv[GP][8];
 #pragma unroll
@@ -146,17 +151,17 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[h][e] = hp + h < G ? __half2float(qr[e]) : 0.f;
     }
-    float m_run[GP], l_run[GP], o[GP][8];
+    // This wave's final state per head: max, sum, and NO channels of o.
+    float m_fin[GP], l_fin[GP], o_fin[GP][NO];
+    int off = 0;  // the lane's first channel within its 8-channel chunk (set by the row reduce-scatter)
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
-      m_run[h] = -INFINITY;
-      l_run[h] = 0.f;  // this lane's share: lanes with even cc count their token
+      m_fin[h] = -INFINITY;
+      l_fin[h] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+      for (int k = 0; k < NO; ++k) o_fin[h][k] = 0.f;
     }
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      if (j0 + TPI * NH * half >= nt) break;  // no tier token left in this wave (uniform)
+    if (j0 + TPI * NH * half < nt) {  // uniform per wave: the half holds tier tokens
       u32x4 kx[NH], vx[NH];
 #pragma unroll
       for (int i = 0; i < NH; ++i) {
@@ -164,10 +169,10 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part) {
         kx[i] = u32x4{0u, 0u, 0u, 0u};
         vx[i] = u32x4{0u, 0u, 0u, 0u};
         if (j < nt) {
-          const long long off = row_off(j);
+          const long long off_j = row_off(j);
           const bool sink = j < ns;
-          const __half* kr = off < 0 ? a.k_new + rowid * D : (sink ? k_sink : k_ring) + off;
-          const __half* vr = off < 0 ? a.v_new + rowid * D : (sink ? v_sink : v_ring) + off;
+          const __half* kr = off_j < 0 ? a.k_new + rowid * D : (sink ? k_sink : k_ring) + off_j;
+          const __half* vr = off_j < 0 ? a.v_new + rowid * D : (sink ? v_sink : v_ring) + off_j;
           kx[i] = *reinterpret_cast<const u32x4*>(kr + cc * 8);
           vx[i] = *reinterpret_cast<const u32x4*>(vr + cc * 8);
         }
@@ -193,14 +198,12 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part) {
         const float dsum = reduce_scatter<NH>(dv, cc);  // every lane takes part in the exchanges
         const float lg = ok ? dsum * a.qk_log2 : -INFINITY;
         if (a.logits && ok && !(cc & 1)) a.logits[((long long)b * Hq + g * G + hp + h) * span + slot_of(jt)] = lg;
-        // The half holds at least one tier token (j0 + TPI NH half < nt), so mn is finite.
-        const float mn = fmaxf(m_run[h], wave_max(lg));
-        const float corr = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - mn);
-        const float p = ok ? __builtin_amdgcn_exp2f(lg - mn) : 0.f;
-        m_run[h] = mn;
-        l_run[h] = fmaf(l_run[h], corr, (cc & 1) ? 0.f : p);
+        // The half holds at least one tier token, so m is finite.
+        const float m = wave_max(lg);
+        const float p = ok ? __builtin_amdgcn_exp2f(lg - m) : 0.f;
+        float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] *= corr;
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
           const float pi = __shfl(p, r * LPT + 2 * i);  // probability of this lane's token in group i
@@ -208,42 +211,66 @@ __device__ __forceinline__ void tier_parts(const AttnLaunch& a, int part) {
           for (int e = 0; e < 4; ++e) {
             const unsigned uv = vx[i][e];
             const __half2 hv = __builtin_bit_cast(__half2, uv);
-            o[h][2 * e] = fmaf(pi, __low2float(hv), o[h][2 * e]);
-            o[h][2 * e + 1] = fmaf(pi, __high2float(hv), o[h][2 * e + 1]);
+            o[2 * e] = fmaf(pi, __low2float(hv), o[2 * e]);
+            o[2 * e + 1] = fmaf(pi, __high2float(hv), o[2 * e + 1]);
           }
         }
+        m_fin[h] = m;
+        l_fin[h] = wave_total((cc & 1) ? 0.f : p);  // lane pairs hold each token twice
+        // Sum the TPI token rows (lanes equal mod LPT) by a reduce-scatter
+        // over the 8 channels: the lane keeps NO consecutive ones.
+        off = 0;
+#pragma unroll
+        for (int s = LPT; s < 64; s <<= 1) {
+          const int n = 4 * LPT / s;  // entries kept after this exchange
+          const bool up = lane & s;
+          off += up ? n : 0;
+#pragma unroll
+          for (int k = 0; k < n; ++k) {
+            const float keep = up ? o[n + k] : o[k], give = up ? o[k] : o[n + k];
+            o[k] = keep + __shfl_xor(give, s);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < NO; ++k) o_fin[h][k] = o[k];
       }
+    } else {
+      // The lane's channel offset is the same whichever wave computes it.
+#pragma unroll
+      for (int s = LPT; s < 64; s <<= 1) off += (lane & s) ? 4 * LPT / s : 0;
     }
-    // Sum the TPI token rows (lanes equal mod LPT) by a reduce-scatter over
-    // the 8 channels: each lane ends with NO consecutive channels of its chunk.
-    constexpr int NO = 8 * LPT / 64;
+    // The two halves meet: wave 1 hands its states to wave 0 through LDS.
+    if (half == 1) {
 #pragma unroll
-    for (int h = 0; h < GP; ++h) {
-      if (hp + h >= G) break;
-      const float l = wave_total(l_run[h]);
-      const long long pi = ((long long)b * Hq + g * G + hp + h) * P + S + part;
-      float v[8];
+      for (int h = 0; h < GP; ++h) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = o[h][e];
-      int off = 0;
-#pragma unroll
-      for (int s = LPT; s < 64; s <<= 1) {
-        const int n = 4 * LPT / s;  // entries kept after this exchange
-        const bool up = lane & s;
-        off += up ? n : 0;
-#pragma unroll
-        for (int k = 0; k < n; ++k) {
-          const float keep = up ? v[n + k] : v[k], give = up ? v[k] : v[n + k];
-          v[k] = keep + __shfl_xor(give, s);
+        for (int k = 0; k < NO; ++k) xo[h * D + cc * 8 + off + k] = o_fin[h][k];
+        if (lane == 0) {
+          xml[2 * h] = m_fin[h];
+          xml[2 * h + 1] = l_fin[h];
         }
       }
+    }
+    __syncthreads();
+    if (half == 0) {
 #pragma unroll
-      for (int k = 0; k < NO; ++k) a.part_o[pi * D + cc * 8 + off + k] = v[k];
-      if (lane == 0) {
-        a.part_ml[pi * 2] = m_run[h];
-        a.part_ml[pi * 2 + 1] = l;
+      for (int h = 0; h < GP; ++h) {
+        if (hp + h >= G) break;
+        const float m1 = xml[2 * h], l1 = xml[2 * h + 1];
+        const float M = fmaxf(m_fin[h], m1);
+        const float w0 = m_fin[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_fin[h] - M);
+        const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+        const long long pi = ((long long)b * Hq + g * G + hp + h) * P + S + part;
+#pragma unroll
+        for (int k = 0; k < NO; ++k)
+          a.part_o[pi * D + cc * 8 + off + k] = o_fin[h][k] * w0 + xo[h * D + cc * 8 + off + k] * w1;
+        if (lane == 0) {
+          a.part_ml[pi * 2] = M;
+          a.part_ml[pi * 2 + 1] = l_fin[h] * w0 + l1 * w1;
+        }
       }
     }
+    __syncthreads();  // xo is free for the next pass
   }
 }
 
