@@ -4,8 +4,9 @@
 once, its inputs restored by ordinary (eager) copies before every replay, and
 each of three replays must reproduce the eager call's outputs and cache
 state bit for bit: the one-call decode step (split kernel, then the
-eviction kernel with the merge) and the fused append + attention on a tiered
-INT4 cache (split, tier and merge kernels).
+eviction kernel with the merge), the fused append + attention on a tiered
+INT4 cache (split, tier and merge kernels), and on a paged cache the
+attention with H2O and the block eviction.
 """
 import numpy as np
 import pytest
@@ -126,3 +127,57 @@ def test_tiered_append_attention_graph_replays(hq, hkv):
     outputs = {"out": out, "score": score, **{"cache." + n: t for n, t in _state(gc).items()}}
     _replays_match(call, restore, outputs)
     assert np.isfinite(out.cpu().numpy()).all()
+
+
+def test_paged_attention_and_block_evict_graph_replays():
+    """The paged cache's attention with H2O (split kernel on the page table,
+    then the merge) and its block eviction (block means, then the table
+    rewrite and score move), each captured and replayed."""
+    B, hq, hkv, D, L, bs = 4, 8, 4, 128, 600, 16
+    print("[graph] paged attention and block eviction", flush=True)
+    w = _workload(8, hq, hkv, L).scaled(batch=B)
+    d = draw(w)
+    mb = (L + 8 + bs - 1) // bs
+    table = np.random.default_rng(5).permutation(B * mb).astype(np.int32).reshape(B, mb)
+    pg = kvc.KVCache(B, hkv, D, 0, 8, block_size=bs, num_blocks=B * mb, max_blocks_per_seq=mb)
+    pg.block_table.copy_(dev(table))
+    score = pg.score_buffer()
+    kvc.kvc_quant_append(pg, dev(d["k"][:, :, :L]), dev(d["v"][:, :, :L]), h2o_score=score)
+    torch.cuda.synchronize()
+    saved_score = score.clone()
+    out = torch.empty((B, hq, D), dtype=torch.float32, device="cuda")
+    q = dev(d["step_q"][0])
+    ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(pg, hq, L, True), dtype=torch.uint8, device="cuda")
+
+    def attend():
+        kvc.kvc_decode_attn(pg, q, out, h2o_score=score, max_len_hint=L, workspace=ws)
+
+    def restore_attend():
+        score.copy_(saved_score)
+        out.zero_()
+
+    _replays_match(attend, restore_attend, {"out": out, "score": score})
+
+    # Block eviction on scores with spread (one attention step's mass is
+    # nearly flat): seeded random scores.
+    score.copy_(torch.from_numpy(np.random.default_rng(6).random((B, hkv, pg.capacity)).astype(np.float32)))
+    dst = pg.table_view()
+    dsc = torch.zeros_like(score)
+    freed = torch.zeros((B, mb), dtype=torch.int32, device="cuda")
+    fcount = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    wsb = torch.empty(kvc.kvc_paged_block_evict_workspace_bytes(pg), dtype=torch.uint8, device="cuda")
+
+    def evict():
+        kvc.kvc_paged_block_evict(pg, score, 0.6, dst, dsc, freed, fcount, max_len_hint=L, workspace=wsb)
+
+    def restore_evict():
+        dst.block_table.fill_(-1)
+        dst.lengths.zero_()
+        dst.num_seen.zero_()
+        dsc.fill_(-3.0)
+        freed.fill_(-9)
+        fcount.fill_(-1)
+
+    _replays_match(evict, restore_evict, {"table": dst.block_table, "lengths": dst.lengths, "num_seen": dst.num_seen,
+                                          "dst_score": dsc, "freed": freed, "freed_count": fcount})
+    assert int(fcount.min()) > 0
