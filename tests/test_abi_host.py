@@ -402,3 +402,35 @@ def test_pool_bad_args():
     p = kvc.BlockPool(4, 16)
     with pytest.raises(kvc.KvcError):
         p.reserve(-1, 5)
+
+
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
+def _attn_ws(B, Hq, D, P, span):
+    """Workspace of one attention call: split partials o [B][Hq][P][D], their
+    (m, l), spilled logits [B][Hq][span], the two per-sequence stash words."""
+    return _a256(B * Hq * P * D * 4) + _a256(B * Hq * P * 2 * 4) + _a256(B * Hq * span * 4) + _a256(2 * B * 4)
+
+
+@pytest.mark.parametrize("name,B,H,Hq,D,cap,hint,tiers,P,span", [
+    # the LLaMA-7B layer: 32 rows x 32 tiles, 16 splits of 2 tiles (512 workgroups)
+    ("llama7b_8k", 1, 32, 32, 128, 8192, 8192, (0, 0), 16, 8192),
+    # the GQA stream's steady state, 8193 tokens (33 tiles): the 17th split is
+    # folded into the 16th, which takes 3 tiles (512 workgroups, not 544)
+    ("qwen_gqa_step", 8, 4, 28, 128, 8200, 8193, (0, 0), 16, 33 * 256),
+    # the INT4 hybrid: 16 splits and ceil((4 + 2457) / 64) = 39 tier parts
+    ("llama7b_8k_int4_hybrid", 1, 32, 32, 128, 8192, 8192, (4, 2457), 16 + 39, 8192),
+    # the 70B layer: 512 tiles per row, 16 splits of 32 tiles
+    ("llama70b_int4", 4, 8, 64, 128, 131072, 131072, (0, 0), 16, 131072),
+])
+def test_attention_workspace_follows_the_split_geometry(name, B, H, Hq, D, cap, hint, tiers, P, span):
+    T = dict(fp16_sinks=tiers[0], fp16_recent=tiers[1], k_sink16=0x8000000, v_sink16=0x8100000,
+             k_recent16=0x8200000, v_recent16=0x8300000) if tiers[0] or tiers[1] else {}
+    d = desc(batch=B, num_kv_heads=H, head_dim=D, capacity=cap, **T)
+    got = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), Hq, hint, 1)
+    assert got == _attn_ws(B, Hq, D, P, span), (name, got, _attn_ws(B, Hq, D, P, span))
+    # without H2O there is no logit spill
+    got0 = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), Hq, hint, 0)
+    assert got0 == got - _a256(B * Hq * span * 4), name
