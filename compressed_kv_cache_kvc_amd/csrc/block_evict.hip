@@ -19,8 +19,9 @@
 // quarter row) pairs, 16-byte loads, a fixed-order sum of the filled slots
 // (blocks holding equal scores get equal means), the means to a workspace.
 // block_select_kernel: several workgroups per sequence, each with the means
-// in LDS: every block's rank in the stable order by counting (n^2
-// comparisons, made for decode-sized tables), a block scan for the kept and
+// in LDS as 64-bit keys (the mean's order-preserving bits, then the block
+// index, so that one unsigned compare gives the stable order): every block's
+// rank by counting (n^2 compares, made for decode-sized tables), a block scan for the kept and
 // freed positions (workgroup 0 writes the table, the freed list and the
 // lengths), and a share of the score rows moved in 16-byte pieces, eight
 // loads in flight per thread. One workgroup per sequence doing all of it took
@@ -69,32 +70,35 @@ __global__ __launch_bounds__(kBT) void block_select_kernel(kvc_cache_t src, cons
                                                            kvc_cache_t dst, float* __restrict__ dst_score,
                                                            int32_t* __restrict__ freed,
                                                            int32_t* __restrict__ freed_count, int max_len) {
-  extern __shared__ float lds[];
+  extern __shared__ __align__(16) unsigned long long lds_keys[];
   const int part = blockIdx.x, parts = gridDim.x, b = blockIdx.y, tid = threadIdx.x;
   const int H = src.num_kv_heads, BS = src.block_size, MB = src.max_blocks_per_seq;
   const long long cap = src.capacity;
-  float* mean = lds;                                    // [MB]
-  int* keep = reinterpret_cast<int*>(lds + MB);         // [MB]: 1 kept, 0 evicted
-  int* src_of = keep + MB;                              // [MB]: kept block at each new position
+  unsigned long long* key = lds_keys;                   // [MB]: (order key of the mean) << 32 | block index
+  int* keep = reinterpret_cast<int*>(lds_keys + MB);    // [MB]: 1 kept, 0 evicted
+  int* src_of = reinterpret_cast<int*>(lds_keys);       // [MB]: kept block at each new position (after the ranks)
   __shared__ int scan_tmp[kBT / 64];
   const int L = __builtin_amdgcn_readfirstlane(min(min(src.lengths[b], src.capacity), max_len));
   const int nb = (L + BS - 1) / BS;
   const int32_t* srow = src.block_table + (long long)b * MB;
-  for (int j = tid; j < nb; j += kBT) mean[j] = means[(long long)b * MB + j];
-  __syncthreads();
-  // Stable ascending order by mean: block j's rank counts the blocks with a
-  // lower mean, or an equal mean and a lower index; ranks below n_evict go.
-  const int n_evict = (int)((double)nb * (1.0 - retention));
   for (int j = tid; j < nb; j += kBT) {
-    const float mj = mean[j];
-    int rank = 0;
-    for (int i = 0; i < nb; ++i) {
-      const float mi = mean[i];
-      rank += (mi < mj) | ((mi == mj) & (i < j));
-    }
-    keep[j] = rank >= n_evict;
+    // + 0: -0 becomes +0, which the float order holds equal to it
+    unsigned u = __float_as_uint(means[(long long)b * MB + j] + 0.f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    key[j] = ((unsigned long long)u << 32) | (unsigned)j;
   }
   __syncthreads();
+  // Stable ascending order by mean: block j's rank counts the blocks with a
+  // lower mean, or an equal mean and a lower index (a smaller key); ranks
+  // below n_evict go.
+  const int n_evict = (int)((double)nb * (1.0 - retention));
+  for (int j = tid; j < nb; j += kBT) {
+    const unsigned long long kj = key[j];
+    int rank = 0;
+    for (int i = 0; i < nb; ++i) rank += key[i] < kj;
+    keep[j] = rank >= n_evict;
+  }
+  __syncthreads();  // the keys are read no more: src_of takes their place
   // Kept and freed positions: thread t owns blocks [t*per, t*per + per).
   const int per = (nb + kBT - 1) / kBT;
   const int j0 = min(tid * per, nb), j1 = min(j0 + per, nb);
@@ -166,7 +170,9 @@ __global__ __launch_bounds__(kBT) void block_select_kernel(kvc_cache_t src, cons
 
 }  // namespace
 
-size_t block_evict_lds_bytes(int max_blocks_per_seq) { return (size_t)max_blocks_per_seq * 3 * sizeof(float); }
+size_t block_evict_lds_bytes(int max_blocks_per_seq) {
+  return (size_t)max_blocks_per_seq * (sizeof(unsigned long long) + sizeof(int));
+}
 
 hipError_t launch_block_evict(const kvc_cache_t& src, const float* score, double retention, const kvc_cache_t& dst,
                               float* dst_score, int32_t* freed, int32_t* freed_count, float* means, int max_len,
