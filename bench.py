@@ -8,23 +8,27 @@ H2O keep 0.3 = 4 sinks + 1024 recent + 1429 heavy hitters):
   2. attention over all 8192 tokens + H2O accumulation,
   3. eviction: keep-set selection down to 2457 slots (a mask and an
      ascending keep list) and compaction of the kept slots into the other
-     buffer,
-in one call of two launches (kvc_decode_step: the split attention kernel,
-then the eviction kernel that also merges the splits).
+     buffer.
 
 Steps rotate over 32 distinct layer caches (2.1 GiB, like the 32 layers of the
 model), so every launch streams its 66 MiB from HBM rather than from the
 256 MB Infinity Cache. Inputs are resident in HBM before timing starts.
 
-The timed region replays one HIP graph per 32-layer block in decode order:
-rewind the lengths, then each layer's step. `value` and `ms_per_step` come
-from it. The same steps then run again as separate calls, three graphs per
-block, one per phase ([rewind + 32 kvc_decode_attn_split with the append]
-[32 kvc_decode_attn_merge] [32 kvc_h2o_evict]), with HIP events between the
-phases: they give
-each phase's time ("phases") and the split kernel's average duration, from
-which the roofline fraction is computed (the split kernel streams the KV
-cache; it is the same kernel the step launches).
+Exactly --warmup untimed steps, then exactly --steps timed steps, in decode
+order (layer 0, 1, ..., 31, 0, ...), twice:
+
+  * as the one-call step (kvc_decode_step: the split attention kernel with
+    the append, then the eviction kernel that also merges the splits):
+    `ms_per_step` and `tokens_per_s`;
+  * as the separate calls (kvc_decode_attn_split with the append,
+    kvc_decode_attn_merge with H2O, kvc_h2o_evict), with HIP events between
+    the phases: `value` is decode attention's KV GB/s, the attention's
+    algorithmic bytes (KV codes and scales, q, out) over the split and merge
+    phases' time; `phases` gives each phase; `roofline` is the split kernel,
+    the step's dominant HBM kernel, alone.
+
+Steps are replayed from HIP graphs of up to 32 layer-steps each (a block of
+fewer layers covers a step count that is not a multiple of 32).
 
 Prints one JSON line. Run ``python bench.py --help`` for options.
 """
@@ -54,17 +58,21 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = "5d209113ec6acfdd56e2475c86fc16618cba6f3cfb891d29d5ff3b8969fb5ef5"
-TRAFFIC_BYTES = 70757366
+TRAFFIC_SHA256 = None   # sources the counters were taken on (None: no measurement yet)
+TRAFFIC_BYTES = None
 
 
 def attention_traffic():
+    return TRAFFIC_BYTES if TRAFFIC_SHA256 is not None and traffic_sources_sha256() == TRAFFIC_SHA256 else None
+
+
+def traffic_sources_sha256():
     import hashlib
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    return TRAFFIC_BYTES if h.hexdigest() == TRAFFIC_SHA256 else None
+    return h.hexdigest()
 HBM_PEAK_GBPS = 8000.0
 LAYERS = 32
 
@@ -81,7 +89,9 @@ def step_bytes(B, Hq, H, D, bits, L, budget):
         # scores in; mask and keep list out; kept rows (codes, scales, position, score) in and out
         "evict": B * H * (L * 4 + L + budget * 4) + 2 * B * H * budget * (2 * (rb + 4) + 8),
     }
-    return parts, kv + B * Hq * D * 2   # attention kernel's own algorithmic bytes (KV + q)
+    # The split kernel's own algorithmic bytes (KV + q), and decode
+    # attention's (KV + q + out: what the split and merge kernels must move).
+    return parts, kv + B * Hq * D * 2, kv + B * Hq * D * 2 + B * Hq * D * 4
 
 
 def phase_table(phase_ms, steps, parts, attn_alg):
@@ -104,8 +114,10 @@ def phase_table(phase_ms, steps, parts, attn_alg):
 
 
 def cpu_baseline(w, d, budget_s=12.0):
-    """Time the fp64 oracle (unchanged) on the host for one full step of the
-    same workload, repeated until about ``budget_s`` seconds have passed."""
+    """Time the fp64 oracle (unchanged) on the host on the same workload: one
+    full step (append, attention + H2O, select, compact), repeated until about
+    ``budget_s`` seconds have passed, then the attention alone (with H2O) on
+    the same cache for about a third of that."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -129,7 +141,19 @@ def cpu_baseline(w, d, budget_s=12.0):
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_total > budget_s or len(times) >= 20:
             break
-    return min(times), len(times), cores
+    # Attention alone: the cache with the new token appended, no eviction.
+    (ref.k_codes[:], ref.v_codes[:], ref.k_scale[:], ref.v_scale[:], ref.positions[:],
+     ref.lengths[:], ref.num_seen[:]) = snap
+    ref.append(d["k"][:, :, L - 1:], d["v"][:, :, L - 1:])
+    attn = []
+    t_total = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        ref.attend(d["q"], h2o=True)
+        attn.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_total > budget_s / 3 or len(attn) >= 20:
+            break
+    return min(times), len(times), min(attn), len(attn), cores
 
 
 def copy_calibration(torch, mib):
@@ -458,7 +482,7 @@ def secondary_attention(kvc, torch, reps=16):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1024, help="timed steps (rounded up to a multiple of 32)")
+    ap.add_argument("--steps", type=int, default=1024, help="timed steps")
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -513,111 +537,129 @@ def main(argv=None):
 
     # Phase by phase, the attention runs as its two calls, split (with the
     # append) then merge; each layer buffer has its own workspace, since all
-    # 32 splits run before the first merge.
+    # the splits of a block run before the first merge.
     ws_layers = [torch.zeros_like(ws_attn) for _ in range(LAYERS)]
 
-    def phase_split():
+    def phase_split(n):
         lengths_all.fill_(L - 1)
-        for i in range(LAYERS):
+        for i in range(n):
             kvc.kvc_decode_attn_split(caches[i], q, ws_layers[i], k_new=k_new, v_new=v_new, h2o_score=scores[i],
                                       max_len_hint=L - 1)
 
-    def phase_merge():
-        for i in range(LAYERS):
+    def phase_merge(n):
+        for i in range(n):
             kvc.kvc_decode_attn_merge(caches[i], Hq, out, ws_layers[i], appended=True, h2o_score=scores[i],
                                       max_len_hint=L - 1)
 
-    def evict(i):
-        kvc.kvc_h2o_evict(caches[i], scores[i], budget, S, R, keep_lists[i], dst, dst_score, keep_mask=masks[i],
-                          max_len_hint=L)
+    def phase_evict(n):
+        for i in range(n):
+            kvc.kvc_h2o_evict(caches[i], scores[i], budget, S, R, keep_lists[i], dst, dst_score, keep_mask=masks[i],
+                              max_len_hint=L)
 
-    def phase_evict():
-        for i in range(LAYERS):
-            evict(i)
-
-    def whole_block():
+    def whole_block(n):
         # Decode order: each layer's step (append, attention, H2O, eviction;
         # two launches) in turn.
         lengths_all.fill_(L - 1)
-        for i in range(LAYERS):
+        for i in range(n):
             kvc.kvc_decode_step(caches[i], k_new, v_new, q, out, scores[i], budget, S, R, keep_lists[i], dst,
                                 dst_score, keep_mask=masks[i], max_len_hint=L - 1, workspace=ws_attn)
 
-    # ---- eager pass, then capture the whole block and each phase as graphs ----
+    # ---- eager pass, then capture blocks of layer-steps as graphs ----
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        whole_block()
+        whole_block(LAYERS)
     torch.cuda.synchronize()
     eager_out = out.clone()
     eager_len = dst.lengths.clone()
     eager_keep = torch.stack(keep_lists)
 
-    def capture(fn):
+    def capture(fn, n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            fn()
+            fn(n)
         return g
 
-    g_whole = capture(whole_block)
-    graphs = [capture(fn) for fn in (phase_split, phase_merge, phase_evict)]
-    torch.cuda.synchronize()
+    graphs = {}
 
-    blocks_w = max(1, (args.warmup + LAYERS - 1) // LAYERS)
-    blocks = max(1, (args.steps + LAYERS - 1) // LAYERS)
-    steps = blocks * LAYERS
-    # Both replay orders must reproduce the eager result.
-    for order in ([g_whole], graphs):
+    def block_graphs(n):
+        """Graphs of n layer-steps (layers 0..n-1): the one-call step, and the
+        three phases of the separate calls."""
+        if n not in graphs:
+            graphs[n] = (capture(whole_block, n), [capture(fn, n) for fn in (phase_split, phase_merge, phase_evict)])
+        return graphs[n]
+
+    def blocks_of(k):
+        return [LAYERS] * (k // LAYERS) + ([k % LAYERS] if k % LAYERS else [])
+
+    g_whole, g_phases = block_graphs(LAYERS)
+    torch.cuda.synchronize()
+    # Set-up check (not counted as warm-up): one 32-layer block replayed in
+    # each order reproduces the eager result.
+    for order in ([g_whole], g_phases):
         with torch.cuda.stream(stream):
-            for _ in range(blocks_w):
-                for g in order:
-                    g.replay()
+            for g in order:
+                g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager_out), "graph replay differs from the eager attention output"
         assert torch.equal(dst.lengths, eager_len)
         assert torch.equal(torch.stack(keep_lists), eager_keep), "graph replay differs from the eager keep lists"
 
-    # ---- timed region: K steps in decode order ----
+    warm, timed = blocks_of(args.warmup), blocks_of(args.steps)
+    for n in set(warm + timed):
+        block_graphs(n)
+    torch.cuda.synchronize()
+
+    # ---- warm-up, then the timed steps as the one-call step ----
+    with torch.cuda.stream(stream):
+        for n in warm:
+            block_graphs(n)[0].replay()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         t_start.record(stream)
         wall0 = time.perf_counter()
-        for _ in range(blocks):
-            g_whole.replay()
+        for n in timed:
+            block_graphs(n)[0].replay()
         t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
 
-    # ---- the same K steps phase by phase, with events between phases ----
+    # ---- the same warm-up and timed steps as separate calls, events between phases ----
     # ev[bi][p] ends phase p of block bi; phase p starts where the previous
     # event (or p_start) ends.
-    n_ph = len(graphs)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ph)] for _ in range(blocks)]
+    with torch.cuda.stream(stream):
+        for n in warm:
+            for g in block_graphs(n)[1]:
+                g.replay()
+    n_ph = 3
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ph)] for _ in timed]
     p_start, p_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         p_start.record(stream)
-        for bi in range(blocks):
-            for p, g in enumerate(graphs):
+        for bi, n in enumerate(timed):
+            for p, g in enumerate(block_graphs(n)[1]):
                 g.replay()
                 ev[bi][p].record(stream)
         p_end.record(stream)
     torch.cuda.synchronize()
     phase_ms = [0.0] * n_ph
     prev = p_start
-    for bi in range(blocks):
+    for bi in range(len(timed)):
         for p in range(n_ph):
             phase_ms[p] += prev.elapsed_time(ev[bi][p])
             prev = ev[bi][p]
-    attn_ms = phase_ms[0]
     by_phase_ms = p_start.elapsed_time(p_end)
+    steps = args.steps
 
-    parts, attn_alg = step_bytes(B, Hq, H, D, bits, L, budget)
+    parts, split_alg, attn_alg = step_bytes(B, Hq, H, D, bits, L, budget)
     step_alg = sum(parts.values())
     ms_per_step = total_ms / steps
-    attn_us = attn_ms * 1e3 / steps
-    value = step_alg / (ms_per_step * 1e-3) / 1e9
-    attn_gbps = attn_alg / (attn_us * 1e-6) / 1e9
+    split_us = phase_ms[0] * 1e3 / steps
+    attn_us = (phase_ms[0] + phase_ms[1]) * 1e3 / steps
+    split_gbps = split_alg / (split_us * 1e-6) / 1e9
+    value = attn_alg / (attn_us * 1e-6) / 1e9
 
     rec = {
         "metric": METRIC,
@@ -625,7 +667,7 @@ def main(argv=None):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": blocks_w * LAYERS,
+        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -635,44 +677,58 @@ def main(argv=None):
         "config": {"workload": "llama7b_8k", "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": D,
                    "context": L, "bits": bits, "budget": budget, "n_sink": S, "n_recent": R,
                    "layer_buffers_rotated": LAYERS},
-        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
-        "step_bytes": step_alg,
-        "step_fraction_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "value_definition": "decode attention's algorithmic bytes (KV codes + fp32 scales + q + out = "
+                            f"{attn_alg} B) / the split + merge time per step (kvc_decode_attn_split with the "
+                            "append, then kvc_decode_attn_merge with H2O), over the timed steps run as "
+                            "separate calls",
         "attention_us": round(attn_us, 3),
-        "attention_kv_gbps": round(attn_gbps, 1),
+        "attention_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "attention_tokens_per_s": round(B / (attn_us * 1e-6), 1),
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "tokens_per_s_32_layers": round(B / (ms_per_step * 1e-3 * LAYERS), 1),
+        "step": {"calls": "kvc_decode_step (two launches)", "us": round(ms_per_step * 1e3, 3),
+                 "bytes": step_alg, "gbps": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),
+                 "frac": round(step_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "wall_s": round(wall, 3),
-        "phases": phase_table(phase_ms, steps, parts, attn_alg),
+        "phases": phase_table(phase_ms, steps, parts, split_alg),
         "ms_per_step_phase_by_phase": round(by_phase_ms / steps, 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_split_kernel: the KV stream of the step (with the new token's append), timed through "
-                  "kvc_decode_attn_split",
-            "achieved": round(attn_gbps, 1),
+            "kernel": "attn_split_kernel<8, 8, 128, 1, false>: the KV stream (with the new token's append), timed "
+                      "through kvc_decode_attn_split",
+            "achieved": round(split_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+            "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
             "traffic": attention_traffic(),
+            "bytes_per_launch": split_alg,
+            "us_per_launch": round(split_us, 3),
+            "frac_with_merge": round(value / HBM_PEAK_GBPS, 4),
         },
     }
     if not args.no_secondary:
         rec_sched = layer_schedules(kvc, torch, caches, scores, lengths_all, k_new, v_new, q, out, dst, dst_score,
-                                    ws_attn, L, S, R, stream, blocks)
-    probe = read_probe(kvc, torch, attn_alg)
-    probe["attention_frac_of_probe"] = round(attn_gbps / probe["gbps"], 4)
+                                    ws_attn, L, S, R, stream, max(1, len(timed)))
+    probe = read_probe(kvc, torch, split_alg)
+    probe["split_frac_of_probe"] = round(split_gbps / probe["gbps"], 4)
     rec["hbm_read_probe"] = probe
     if not args.no_secondary:
         rec["layer_schedules"] = rec_sched
         rec["secondary_attention"] = secondary_attention(kvc, torch)
     if not args.no_cpu_baseline:
-        t_cpu, n_cpu, cores = cpu_baseline(w, d, args.cpu_seconds)
+        t_cpu, n_cpu, t_att, n_att, cores = cpu_baseline(w, d, args.cpu_seconds)
         rec["cpu_baseline"] = {
-            "value": round(step_alg / t_cpu / 1e9, 4),
+            "value": round(attn_alg / t_att / 1e9, 4),
             "unit": "GB/s",
             "cores": cores,
             "kind": "oracle",
-            "sample": f"best of {n_cpu} full oracle steps (append, attention+H2O, select, compact) "
-                      f"of the same 8192-token layer; {t_cpu * 1e3:.1f} ms per step, "
+            "sample": f"the fp64 oracle on the same 8192-token layer: attention + H2O alone best of {n_att} "
+                      f"runs, {t_att * 1e3:.1f} ms ({attn_alg} B of decode-attention bytes); full step (append, "
+                      f"attention + H2O, select, compact) best of {n_cpu}, {t_cpu * 1e3:.1f} ms, "
                       f"{B / t_cpu:.2f} tokens/s",
+            "step_ms": round(t_cpu * 1e3, 2),
+            "attention_ms": round(t_att * 1e3, 2),
+            "step_gbps": round(step_alg / t_cpu / 1e9, 4),
         }
     print(json.dumps(rec))
     return 0

@@ -282,6 +282,9 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   auto merge_rest = [&]() {
     if (!MERGE) return;
     for (int h = p + parts; h < G; h += parts) {
+      // Every earlier reader of opart (merge_first_out, the previous head's
+      // sum) is done before it is overwritten.
+      __syncthreads();
       if (tid < 256) {
         const int d = tid % D, pi = tid / D;
         const float* po = e.part_o + ((long long)b * Hq + g * G + h) * S * D + d;
@@ -295,7 +298,6 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
         for (int q = 1; q < PARTS; ++q) r += opart[q * D + tid];
         e.out[((long long)b * Hq + g * G + h) * D + tid] = r;
       }
-      __syncthreads();
     }
   };
   merge_first();

@@ -306,12 +306,16 @@ def test_append_decode_attn_llama7b_full_size():
     assert torch.equal(outA, outB)
 
 
+def _step_scores(w, lens, cap, seed):
+    return (np.random.default_rng(seed).random((len(lens), w.num_kv_heads, cap)) * 0.1).astype(np.float32)
+
+
 def _step_caches(w, lens, cap, seed, v_bits=0):
     """Two identical GPU caches with Lmax = max(lens) prefilled tokens, then
     per-sequence lengths `lens`, and the same random scores."""
     d = draw(w)
-    B, Lmax = len(lens), max(lens)
-    sc = (np.random.default_rng(seed).random((B, w.num_kv_heads, cap)) * 0.1).astype(np.float32)
+    Lmax = max(lens)
+    sc = _step_scores(w, lens, cap, seed)
     out = []
     for _ in range(2):
         gc = make_gpu_cache(w, cap, v_bits=v_bits)
@@ -321,6 +325,48 @@ def _step_caches(w, lens, cap, seed, v_bits=0):
         gc.max_len = Lmax
         out.append((gc, dev(sc)))
     return d, out
+
+
+def _oracle_step_check(w, d, lens, cap, seed, budget, S, R, out, dst, dst_score, kidx, mask, v_bits=0):
+    """The oracle runs the same decode step from the state _step_caches built
+    (the same prefill, lengths, token counts and scores): append, attention
+    with H2O, selection and compaction. The GPU step's output, keep set (from
+    its mask, else its keep list), compacted cache and kept scores are checked
+    against it under the acceptance rules."""
+    B, H, Lmax = len(lens), w.num_kv_heads, max(lens)
+    ref = oracle.RefCache(B, H, w.head_dim, cap, w.bits, v_bits=v_bits or None)
+    ref.append(d["k"][:, :, :Lmax], d["v"][:, :, :Lmax])
+    ref.lengths[:] = lens
+    ref.num_seen[:] = np.array(lens) + 2
+    ref.score[:] = _step_scores(w, lens, cap, seed)
+    ref.append(d["k"][:, :, Lmax:Lmax + 1], d["v"][:, :, Lmax:Lmax + 1])
+    ro, _ = ref.attend(d["q"], h2o=True)
+    assert_out_close(host(out), ro)
+    L_new = ref.lengths.copy()
+    keep = np.zeros((B, H, cap), bool)
+    ki = host(kidx)
+    m = host(mask) if mask is not None else None
+    for b in range(B):
+        L = int(L_new[b])
+        n_keep = min(L, budget)
+        for g in range(H):
+            if m is not None:
+                assert np.all(np.isin(m[b, g, :L], (0, 1))), (b, g)
+                keep[b, g, :L] = m[b, g, :L] == 1
+                assert np.array_equal(np.nonzero(keep[b, g])[0], ki[b, g, :n_keep]), (b, g)
+            else:
+                row = ki[b, g, :n_keep]
+                assert np.all(np.diff(row) > 0) and row[0] >= 0 and row[-1] < L, (b, g)
+                keep[b, g, row] = True
+    ambiguous = assert_keep_equivalent(keep, ref.score, L_new, budget, S, R)
+    if ref.lengths.max() > budget:
+        ref.compact(keep)
+    else:
+        assert keep[:, :, :Lmax + 1].sum() == int(L_new.sum()) * H
+    assert_codes_equal(dst, ref)
+    assert_scores_close(host(dst_score), ref.score, ref.lengths)
+    assert host(dst.num_seen).tolist() == [n + 3 for n in lens]
+    return ambiguous
 
 
 def _step_pair(w, d, caches, lens, budget, S, R, with_mask):
@@ -357,15 +403,22 @@ def _step_pair(w, d, caches, lens, budget, S, R, with_mask):
     (4, 4, 8, 128, [1200, 1100, 1000], 1028, 4, 1024, True),   # no heavy hitters
     (16, 2, 8, 128, [2000, 1500, 1000], 600, 4, 64, True),     # GQA 8: the separate launches
     (4, 4, 8, 64, [20000, 19000, 100], 5000, 4, 256, True),    # long rows: selection + gather
+    # 72 rows at GQA 4 (2 workgroups per row, so each merges two query heads)
+    # and 136 rows at GQA 2 (1 workgroup per row), rows within and past the budget.
+    (32, 8, 8, 128, [1200, 300, 1100, 499, 800, 1000, 200, 1300, 650], 500, 4, 64, True),
+    (32, 8, 8, 128, [1200, 300, 1100, 499, 800, 1000, 200, 1300, 650], 500, 4, 64, False),
+    (16, 8, 8, 128, [700, 150, 600, 299] * 4 + [640], 300, 4, 32, True),
 ])
 def test_decode_step_bit_exact(hq, hkv, bits, D, lens, budget, S, R, with_mask):
     """kvc_decode_step equals kvc_append_decode_attn + kvc_h2o_evict: output,
     keep list, mask, the source cache and every buffer of dst (with the kept
-    tokens' accumulated scores), bit for bit."""
+    tokens' accumulated scores), bit for bit; and both equal the oracle's
+    decode step (output, keep set, compacted cache, kept scores)."""
     print(f"[step] hq={hq} hkv={hkv} bits={bits} D={D} lens={lens} budget={budget}", flush=True)
     w = get("tiny_mha").scaled(context=max(lens) + 1, batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
                                head_dim=D, bits=bits)
-    d, caches = _step_caches(w, lens, max(lens) + 1 + 11, seed=budget + hq)
+    cap, seed = max(lens) + 1 + 11, budget + hq
+    d, caches = _step_caches(w, lens, cap, seed=seed)
     (gA, oA, dA, sA, kA, mA), (gB, oB, dB, sB, kB, mB) = _step_pair(w, d, caches, lens, budget, S, R, with_mask)
     assert torch.equal(oA, oB)
     assert torch.equal(kA, kB)
@@ -375,6 +428,7 @@ def test_decode_step_bit_exact(hq, hkv, bits, D, lens, budget, S, R, with_mask):
     for name in ("k_codes", "v_codes", "k_scale", "v_scale", "positions", "lengths", "num_seen"):
         assert torch.equal(getattr(gA, name), getattr(gB, name)), name
     assert host(dB.lengths).tolist() == [min(n + 1, budget) for n in lens]
+    _oracle_step_check(w, d, lens, cap, seed, budget, S, R, oB, dB, sB, kB, mB if with_mask else None)
 
 
 def test_decode_step_llama7b_full_size():
