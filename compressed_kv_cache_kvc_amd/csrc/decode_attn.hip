@@ -57,7 +57,14 @@
 namespace kvc {
 namespace {
 
-constexpr int TS = kSplitTokens;  // tokens per tile: 4 waves x 64
+constexpr int TS = kSplitTokens;  // tokens per tile: 4 blocks of 64
+
+// Waves per workgroup of the split kernel, by query heads per pass.
+#ifndef KVC_SPLIT_WAVES
+#define KVC_SPLIT_WAVES 4
+#endif
+template <int GP>
+constexpr int kSplitWaves = GP == 1 ? KVC_SPLIT_WAVES : 4;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -162,9 +169,9 @@ __device__ __forceinline__ unsigned sel4(const unsigned* v, int i) {
 //
 // KBITS and VBITS: the K and V code widths (8 or 4), set apart so a cache can
 // hold K and V at different precisions.
-template <int KBITS, int VBITS, int D, int GP, bool PAGED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3 : 2))) void attn_split_kernel(
-    AttnLaunch a) {
+template <int KBITS, int VBITS, int D, int GP, bool PAGED, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : GP <= 2 ? 3 : 2))) void
+attn_split_kernel(AttnLaunch a) {
   constexpr int RBK = D * KBITS / 8;        // bytes per K token row in HBM
   constexpr int RBV = D * VBITS / 8;        // bytes per V token row in HBM
   constexpr int KB = KBITS == 8 ? 16 : 8;   // HBM bytes per lane per K load (16 elements)
@@ -183,6 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   constexpr bool K16 = KBITS == 4 && D == 128;
   constexpr bool V16 = VBITS == 4 && D == 128;
   static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "GP");
+  static_assert(NW == 4 || NW == 8, "NW");
   // LDS chunk (16 bytes) of staged token row t that holds V chunk m: the XOR
   // makes the 64 lanes of a transposed read (tokens 16 q + 0..7 or 8..15 of
   // one chunk, q = 0..3) touch every LDS bank exactly twice.
@@ -210,13 +218,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
   const int t_lo = max(0, min(c.fp16_sinks, L));
   const int t_hi = L - max(0, min(c.fp16_recent, L - t_lo));
 
-  __shared__ __align__(16) uint8_t v_stage[4][64 * VROW];
-  __shared__ __align__(16) int8_t w_limb[4][NRS][16][64];
+  __shared__ __align__(16) uint8_t v_stage[NW][64 * VROW];
+  __shared__ __align__(16) int8_t w_limb[NW][NRS][16][64];
   __shared__ __align__(16) int8_t q_limb[GP][4][D];
   __shared__ float q_fac[GP], q_off[GP];
-  __shared__ float red_m[4][GP], red_l[4][GP];
-  float* red_o = reinterpret_cast<float*>(&v_stage[0][0]);  // [4][GP][D], used after the block loop
-  static_assert(4 * GP * D * 4 <= 4 * 64 * VROW, "merge buffer fits the staging area");
+  __shared__ float red_m[NW][GP], red_l[NW][GP];
+  float* red_o = reinterpret_cast<float*>(&v_stage[0][0]);  // [NW][GP][D], used after the block loop
+  static_assert(NW * GP * D * 4 <= NW * 64 * VROW, "merge buffer fits the staging area");
 
   // Contiguous: one resource per (sequence, KV head) row of `capacity` tokens;
   // rows past the capacity read 0. Paged: one resource over the whole pool
@@ -243,10 +251,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
     rvs = __builtin_amdgcn_make_buffer_rsrc(c.v_scale + base, 0, valid * 4, kBufferFlags);
   }
 
-  // This wave's blocks: block `it` starts at token t0(it) and holds tokens
-  // below L only for it < nb.
-  auto block_t0 = [&](int it) { return ((s * NT + it) * 4 + wave) * 64; };
-  const int nb = max(0, min(NTs, (t_hi - ((s * NT) * 4 + wave) * 64 + 255) / 256));
+  // This wave's blocks: the split's 64-token blocks j = NW it + wave (4 per
+  // tile); block `it` starts at token t0(it) and holds tokens below L only
+  // for it < nb.
+  auto block_t0 = [&](int it) { return (s * NT * 4 + it * NW + wave) * 64; };
+  const int blocks_hi = min(4 * NTs, (t_hi - s * NT * kSplitTokens + 63) / 64) - wave;
+  const int nb = blocks_hi > 0 ? (blocks_hi + NW - 1) / NW : 0;
 
   // Append: the wave whose block `it_new` holds slot L_old quantizes the new
   // token's K and V rows into the cache before its first loads (the
@@ -261,9 +271,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
       a.stash[b] = L_old;
       a.stash[c.batch + b] = c.num_seen[b];
     }
-    const int qb = L_old >> 6;  // 64-token block of the new slot
-    if (L_old >= 0 && L_old < c.capacity && L_old < span && min((qb >> 2) / NT, S - 1) == s && (qb & 3) == wave) {
-      it_new = (qb >> 2) - s * NT;
+    const int qb = L_old >> 6;           // 64-token block of the new slot
+    const int jb = qb - s * NT * 4;      // its block index within this split
+    if (L_old >= 0 && L_old < c.capacity && L_old < span && min((qb >> 2) / NT, S - 1) == s && jb % NW == wave) {
+      it_new = jb / NW;
       const long long row = cache_row(c, b, g, L_old);
       if (row >= 0) {
         const long long src = ((long long)b * H + g) * D;
@@ -362,17 +373,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
 
   for (int hp = 0; hp < G; hp += GP) {
     const int gh = min(GP, G - hp);  // real heads in this pass
-    // ---- q as int8 limbs, per head: wave w takes heads w and w + 4 ----
+    // ---- q as int8 limbs, per head: wave w takes heads w, w + NW, ... ----
     // q is read first and the first block's loads go out right after it, so
     // the q setup overlaps them and waiting for q (loads return in order)
     // does not wait for the cache reads.
-    constexpr int EPL = D / 64, HPW = GP > 4 ? 2 : 1;
+    constexpr int EPL = D / 64, HPW = (GP + NW - 1) / NW;
     float xq[HPW][EPL];
 #pragma unroll
     for (int hi = 0; hi < HPW; ++hi)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const int h = wave + 4 * hi;
+        const int h = wave + NW * hi;
         xq[hi][e] = h < gh ? __half2float(a.q[((long long)b * Hq + g * G + hp + h) * D + lane * EPL + e]) : 0.f;
       }
     Regs ra;
@@ -380,7 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
     issue(ra, 0);
 #pragma unroll
     for (int hi = 0; hi < HPW; ++hi) {
-      const int h = wave + 4 * hi;
+      const int h = wave + NW * hi;
       if (h >= GP) break;
       const float* x = xq[hi];
       float mx = 0.f;
@@ -589,7 +600,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
       process(ra, it);
     }
 
-    // ---- merge the four waves ----
+    // ---- merge the waves ----
     float l_tot[NRS], w_tot[NRS];
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
@@ -613,18 +624,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP <= 2 ? 3
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < gh * D; idx += 256) {
+    for (int idx = tid; idx < gh * D; idx += 64 * NW) {
       const int i = idx / D, d = idx - i * D;
-      const float M = fmaxf(fmaxf(red_m[0][i], red_m[1][i]), fmaxf(red_m[2][i], red_m[3][i]));
+      float M = red_m[0][i];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w][i]);
       float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) o = fmaf(red_o[(w * GP + i) * D + d], part_weight(red_m[w][i], M), o);
+      for (int w = 0; w < NW; ++w) o = fmaf(red_o[(w * GP + i) * D + d], part_weight(red_m[w][i], M), o);
       const long long hq = (long long)b * Hq + g * G + hp + i;
       a.part_o[(hq * a.parts + s) * D + d] = o;
       if (d == 0) {
         float l = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) l = fmaf(red_l[w][i], part_weight(red_m[w][i], M), l);
+        for (int w = 0; w < NW; ++w) l = fmaf(red_l[w][i], part_weight(red_m[w][i], M), l);
         a.part_ml[(hq * a.parts + s) * 2] = M;
         a.part_ml[(hq * a.parts + s) * 2 + 1] = l;
       }
@@ -755,8 +768,9 @@ __global__ __launch_bounds__(128) void attn_tier_kernel(AttnLaunch a) {
 
 template <int KBITS, int VBITS, int D, int GP, bool PAGED>
 hipError_t launch_split(const AttnLaunch& a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_split_kernel<KBITS, VBITS, D, GP, PAGED>), dim3(a.splits, a.c.num_kv_heads, a.c.batch),
-                     dim3(256), 0, st, a);
+  constexpr int NW = kSplitWaves<GP>;
+  hipLaunchKernelGGL((attn_split_kernel<KBITS, VBITS, D, GP, PAGED, NW>), dim3(a.splits, a.c.num_kv_heads, a.c.batch),
+                     dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
