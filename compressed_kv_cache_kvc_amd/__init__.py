@@ -25,7 +25,8 @@ __all__ = [
     "kvc_quant_append", "kvc_decode_attn", "kvc_decode_attn_workspace_bytes",
     "kvc_append_decode_attn", "kvc_decode_attn_split", "kvc_decode_attn_merge",
     "kvc_h2o_select", "kvc_compact", "kvc_compact_workspace_bytes", "kvc_compact_gather",
-    "kvc_h2o_evict", "kvc_decode_step", "kvc_layer_budgets",
+    "kvc_h2o_evict", "kvc_decode_step", "kvc_decode_step_noalloc", "kvc_decode_step_noalloc_max_bytes",
+    "kvc_layer_budgets",
     "kvc_paged_block_evict", "kvc_paged_block_evict_workspace_bytes",
     "kvc_decode_attn_kvsep", "kvc_decode_attn_kvsep_workspace_bytes",
     "kvc_bw_probe", "kvc_bw_probe_sink_bytes",
@@ -82,6 +83,8 @@ def _load():
         "kvc_compact_gather": (I32, [D, P, P, I32, D, P, P]),
         "kvc_h2o_evict": (I32, [D, P, I32, I32, I32, P, P, D, P, I32, P]),
         "kvc_decode_step": (I32, [D, P, P, P, I32, P, P, I32, I32, I32, P, P, D, P, I32, P, SZ, P]),
+        "kvc_decode_step_noalloc_max_bytes": (SZ, []),
+        "kvc_decode_step_noalloc": (I32, [D, P, P, P, I32, P, P, I32, I32, I32, P, P, D, P, I32, P]),
         "kvc_decode_attn_kvsep_workspace_bytes": (SZ, [D, I32, I32, I32]),
         "kvc_decode_attn_kvsep": (I32, [D, P, I32, I32, P, P, I32, P, SZ, P]),
         "kvc_bw_probe_sink_bytes": (SZ, []),
@@ -460,6 +463,38 @@ def kvc_decode_step(cache, k_new, v_new, q, out, h2o_score, budget: int, n_sink:
                                budget, n_sink, n_recent, _ptr(keep_mask), _ptr(keep_index), ctypes.byref(dd),
                                _ptr(dst_score), max_len_hint, _ptr(workspace), workspace.numel(), _stream(stream)),
            "kvc_decode_step")
+    if isinstance(cache, KVCache):
+        cache.max_len = max_len_hint + 1
+    if isinstance(dst, KVCache):
+        dst.max_len = min(max_len_hint + 1, budget)
+
+
+def kvc_decode_step_noalloc_max_bytes() -> int:
+    return lib.kvc_decode_step_noalloc_max_bytes()
+
+
+def kvc_decode_step_noalloc(cache, k_new, v_new, q, out, h2o_score, budget: int, n_sink: int, n_recent: int,
+                            keep_index, dst, dst_score, keep_mask=None, max_len_hint: Optional[int] = None,
+                            stream=None):
+    """``kvc_decode_step`` with the library's static device scratch as its
+    workspace: allocates nothing (see kvc.h)."""
+    import torch
+    d, dd = _desc(cache), _desc(dst)
+    Hq = q.shape[1]
+    _need(k_new, torch.float16, "k_new", d.batch * d.num_kv_heads * d.head_dim)
+    _need(v_new, torch.float16, "v_new", d.batch * d.num_kv_heads * d.head_dim)
+    _need(q, torch.float16, "q", d.batch * Hq * d.head_dim)
+    _need(out, torch.float32, "out", d.batch * Hq * d.head_dim)
+    _need(h2o_score, torch.float32, "h2o_score", d.batch * d.num_kv_heads * d.capacity)
+    _need(dst_score, torch.float32, "dst_score", dd.batch * dd.num_kv_heads * dd.capacity)
+    _need(keep_index, torch.int32, "keep_index", d.batch * d.num_kv_heads * budget)
+    _need(keep_mask, torch.uint8, "keep_mask", d.batch * d.num_kv_heads * d.capacity)
+    if max_len_hint is None:
+        max_len_hint = cache.max_len
+    _check(lib.kvc_decode_step_noalloc(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, _ptr(out),
+                                       _ptr(h2o_score), budget, n_sink, n_recent, _ptr(keep_mask), _ptr(keep_index),
+                                       ctypes.byref(dd), _ptr(dst_score), max_len_hint, _stream(stream)),
+           "kvc_decode_step_noalloc")
     if isinstance(cache, KVCache):
         cache.max_len = max_len_hint + 1
     if isinstance(dst, KVCache):

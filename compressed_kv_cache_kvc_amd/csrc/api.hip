@@ -8,6 +8,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "kvc_internal.h"
@@ -659,12 +660,16 @@ int32_t kvc_h2o_evict(const kvc_cache_t* src, const float* h2o_score, int32_t bu
                       static_cast<hipStream_t>(stream), "kvc_h2o_evict launch");
 }
 
-int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
-                        int32_t num_q_heads, float* out, float* h2o_score, int32_t budget, int32_t n_sink,
-                        int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
-                        float* dst_score, int32_t max_len_hint, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace kvc {
+namespace {
+
+int32_t decode_step_call(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                         int32_t num_q_heads, float* out, float* h2o_score, int32_t budget, int32_t n_sink,
+                         int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
+                         float* dst_score, int32_t max_len_hint, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   int32_t st = check_cache(cache, "cache");
   if (st) return st;
   if (!k_new || !v_new) return fail(KVC_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
@@ -703,6 +708,72 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
   }
   if ((st = device_status(launch_decode_attn(a, s), "kvc_decode_step attention launch"))) return st;
   return evict_launch(e, s, "kvc_decode_step eviction launch");
+}
+
+// The workspace of kvc_decode_step_noalloc: a static device array, one copy
+// per GPU, held until the process ends. Host code uses its device address
+// from hipGetSymbolAddress (taken once per device, with that device current),
+// never the array's name.
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+int32_t scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVC_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVC_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" {
+
+int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                        int32_t num_q_heads, float* out, float* h2o_score, int32_t budget, int32_t n_sink,
+                        int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
+                        float* dst_score, int32_t max_len_hint, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  clear_error();
+  return decode_step_call(cache, k_new, v_new, q, num_q_heads, out, h2o_score, budget, n_sink, n_recent, keep_mask,
+                          keep_index, dst, dst_score, max_len_hint, workspace, workspace_bytes, stream);
+}
+
+size_t kvc_decode_step_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+int32_t kvc_decode_step_noalloc(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                                int32_t num_q_heads, float* out, float* h2o_score, int32_t budget, int32_t n_sink,
+                                int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index, const kvc_cache_t* dst,
+                                float* dst_score, int32_t max_len_hint, void* stream) {
+  clear_error();
+  int32_t st = check_cache(cache, "cache");
+  if (st) return st;
+  if (max_len_hint < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
+  if ((long long)max_len_hint + 1 > cache->capacity)
+    return fail(KVC_ERR_CAPACITY, "max_len_hint %d + 1 exceeds capacity %d", max_len_hint, cache->capacity);
+  AttnGeom g;
+  if ((st = attn_geometry(cache, num_q_heads, max_len_hint + 1, 1, &g))) return st;
+  if (g.total > kNoallocScratchBytes)
+    return fail(KVC_ERR_CAPACITY, "the step needs %zu bytes of workspace; the static scratch holds %zu", g.total,
+                kNoallocScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return decode_step_call(cache, k_new, v_new, q, num_q_heads, out, h2o_score, budget, n_sink, n_recent, keep_mask,
+                          keep_index, dst, dst_score, max_len_hint, ws, kNoallocScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -396,6 +396,32 @@ int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvc_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same step with the same results; its workspace is a static device
+ * array inside the library (one per GPU, kvc_decode_step_noalloc_max_bytes()
+ * bytes = 16 MiB, held until the process ends) instead of a caller buffer.
+ * The call allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine); on its first call on a device it looks up that device's copy of
+ * the array. Nothing in the array needs clearing between calls: every byte a
+ * step reads was written by the same step.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from different threads without stream
+ * order between them) race. Issue them on one stream.
+ *
+ * Errors: those of kvc_decode_step, and KVC_ERR_CAPACITY (nothing enqueued)
+ * when the step's workspace, kvc_decode_attn_workspace_bytes(cache,
+ * num_q_heads, max_len_hint + 1, 1), exceeds the array; KVC_ERR_DEVICE when
+ * the array's device address cannot be obtained.
+ */
+size_t kvc_decode_step_noalloc_max_bytes(void);
+int32_t kvc_decode_step_noalloc(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
+                                int32_t num_q_heads, float* out, float* h2o_score, int32_t budget,
+                                int32_t n_sink, int32_t n_recent, uint8_t* keep_mask, int32_t* keep_index,
+                                const kvc_cache_t* dst, float* dst_score, int32_t max_len_hint, void* stream);
+
+/*
  * Block-granular H2O eviction on a paged cache: whole 16-token blocks are
  * evicted and compaction is a rewrite of the block table (no codes move).
  * Sources: eviction-and-reuse survey, section 4 (evict blocks by attention

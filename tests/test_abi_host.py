@@ -434,3 +434,24 @@ def test_attention_workspace_follows_the_split_geometry(name, B, H, Hq, D, cap, 
     # without H2O there is no logit spill
     got0 = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), Hq, hint, 0)
     assert got0 == got - _a256(B * Hq * span * 4), name
+
+
+def test_decode_step_noalloc_validation():
+    """The allocation-free step checks its arguments and the size of its static
+    workspace on the host, before touching the device."""
+    assert kvc.kvc_decode_step_noalloc_max_bytes() == 16 << 20
+    step = lib.kvc_decode_step_noalloc
+
+    def call(d, hq=4, hint=16, budget=8):
+        return step(ctypes.byref(d), FAKE, FAKE, FAKE, hq, FAKE, FAKE, budget, 0, 4, None, FAKE, ctypes.byref(d),
+                    FAKE, hint, None)
+    assert call(desc(bits=3)) == INVALID
+    assert call(desc(), hint=-1) == INVALID
+    assert call(desc(), hint=512) == CAPACITY            # hint + 1 past the capacity
+    assert call(desc(), hq=6) == INVALID
+    # The 70B-shaped INT4 layer (4 x 131072 tokens, 64 / 8 heads): its logits
+    # alone need 128 MiB, more than the static workspace holds.
+    big = desc(bits=4, batch=4, num_kv_heads=8, head_dim=128, capacity=131072)
+    assert lib.kvc_decode_attn_workspace_bytes(ctypes.byref(big), 64, 131072, 1) > 16 << 20
+    assert call(big, hq=64, hint=131071, budget=26214) == CAPACITY
+    assert "static scratch" in kvc.kvc_last_error()
