@@ -40,6 +40,27 @@ int32_t fail(int32_t status, const char* fmt, ...) {
   return status;
 }
 
+int device_cus() {
+  constexpr int kMaxDev = 64, kDefault = 256;
+  static std::mutex m;
+  static int cus[kMaxDev];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return kDefault;
+  }
+  std::lock_guard<std::mutex> lock(m);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      n = kDefault;
+    }
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 namespace {
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -121,8 +142,8 @@ struct AttnGeom {
 
 // Launch geometry of the decode-attention kernels. A split covers `tiles`
 // 256-token tiles (one 64-token block per wave per tile); tiles are grouped so
-// that the grid has about 512 workgroups (2 per CU on 256 CUs, all resident);
-// longer contexts loop over tiles.
+// that the grid has about two workgroups per CU (512 on MI355X's 256 CUs, all
+// resident); longer contexts loop over tiles.
 int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t with_h2o, AttnGeom* g) {
   int32_t st = check_cache(c, "cache");
   if (st) return st;
@@ -138,13 +159,14 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
     return fail(KVC_ERR_UNSUPPORTED, "paged pools must stay below 4 GiB of codes");
   const long long tiles_total = (hint + kSplitTokens - 1) / kSplitTokens;
   const long long rows = (long long)c->batch * c->num_kv_heads;
-  const long long nt = std::max(1LL, tiles_total * rows / 512);
+  const long long target = 2LL * device_cus();
+  const long long nt = std::max(1LL, tiles_total * rows / target);
   long long S = (tiles_total + nt - 1) / nt;
   // When the last splits of the rows would spill into a second round of
   // workgroups (a row just past a multiple of the split size, e.g. a budget
   // plus the appended token), the last split takes the remainder instead, up
   // to half a split more.
-  const long long s_fit = std::max(1LL, 512 / rows);
+  const long long s_fit = std::max(1LL, target / rows);
   if (S > s_fit && tiles_total - (s_fit - 1) * nt <= nt + (nt + 1) / 2) S = s_fit;
   const long long last = tiles_total - (S - 1) * nt;
   // fp16 tiers: one extra partial state per 64 tier tokens, after the splits.

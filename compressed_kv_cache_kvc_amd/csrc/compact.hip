@@ -300,9 +300,10 @@ hipError_t launch_rb(const kvc_cache_t& src, const float* ss, const uint8_t* mas
 template <int RBK, int RBV>
 hipError_t launch_gather_rb(const kvc_cache_t& src, const float* ss, const int32_t* keep_index, int n_keep,
                             const kvc_cache_t& dst, float* ds, hipStream_t st) {
-  // About 512 workgroups (2 per CU) for the flat list, at most NT entries each.
+  // About 2 workgroups per CU for the flat list, at most NT entries each.
   const long long entries = (long long)src.batch * src.num_kv_heads * n_keep;
-  const int per_wg = (int)std::min<long long>(NT, std::max<long long>(1, (entries + 511) / 512));
+  const long long target = 2LL * device_cus();
+  const int per_wg = (int)std::min<long long>(NT, std::max<long long>(1, (entries + target - 1) / target));
   const long long wgs = (entries + per_wg - 1) / per_wg;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((compact_gather_kernel<RBK, RBV>), dim3((unsigned)wgs), dim3(NT), 0, st, src, ss, keep_index, n_keep,

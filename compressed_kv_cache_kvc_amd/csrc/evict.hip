@@ -476,10 +476,11 @@ namespace {
 
 template <int RBK, int RBV, int GK>
 hipError_t launch_rb(const EvictArgs& a, hipStream_t st) {
-  // About 256 workgroups over the rows, at most 8 per row.
+  // About one workgroup per CU over the rows, at most 8 per row.
   const long long rows = (long long)a.c.batch * a.c.num_kv_heads;
+  const long long target = device_cus();
   int lp = 0;
-  while (lp < 3 && rows << (lp + 1) <= 256) ++lp;
+  while (lp < 3 && rows << (lp + 1) <= target) ++lp;
   EvictArgs e = a;
   e.log2_parts = lp;
   e.xcd_rows = rows % 8 == 0;

@@ -43,6 +43,10 @@ void set_error(const char* fmt, ...);
 void clear_error();
 int32_t fail(int32_t status, const char* fmt, ...);
 
+// Compute units of the current device (host; 256, MI355X's count, when no
+// device answers). Launch geometries aim at a multiple of it.
+int device_cus();
+
 // Tokens per split of the decode-attention kernel (one workgroup per split).
 constexpr int kSplitTokens = 256;
 // fp16-tier tokens per workgroup (one wave) of the tier attention kernel.

@@ -35,6 +35,10 @@
  *    them access memory out of bounds; it can only make results wrong.
  *  - Calls on one stream run in order; calls that write the same buffers must
  *    not overlap on different streams.
+ *  - Head dimension: the kernels are built for head_dim 64 and 128. Every
+ *    other multiple of 16 up to 256 is a well-formed descriptor that every
+ *    device call refuses with KVC_ERR_UNSUPPORTED (nothing enqueued); other
+ *    values are KVC_ERR_INVALID_ARG.
  */
 #ifndef KVC_H_
 #define KVC_H_
@@ -558,7 +562,6 @@ int32_t kvc_pool_reserve(kvc_pool_t* pool, int32_t seq_id, int32_t num_tokens);
  * reaches 0 return to the free list. OK (no-op) for an unknown seq_id. */
 int32_t kvc_pool_free(kvc_pool_t* pool, int32_t seq_id);
 
-/* Blocks on the free list (-1 for a NULL pool). */
 /* Give back blocks of sequence seq_id (the blocks kvc_paged_block_evict frees):
  * each is removed from the sequence's list, whose other blocks keep their
  * order, and its reference count drops; at zero it returns to the free set
@@ -568,6 +571,7 @@ int32_t kvc_pool_free(kvc_pool_t* pool, int32_t seq_id);
  * does not hold (each listed once). */
 int32_t kvc_pool_release(kvc_pool_t* pool, int32_t seq_id, const int32_t* blocks_host, int32_t n);
 
+/* Blocks on the free list (-1 for a NULL pool). */
 int32_t kvc_pool_num_free(const kvc_pool_t* pool);
 
 /* Blocks held by seq_id, or -1 if it is unknown. */
