@@ -65,6 +65,19 @@ constexpr int TS = kSplitTokens;  // tokens per tile: 4 blocks of 64
 #endif
 template <int GP>
 constexpr int kSplitWaves = GP == 1 ? KVC_SPLIT_WAVES : 4;
+// 64-token blocks per chunk: a wave issues a chunk's loads together and takes
+// one softmax rescale and one P.V limb combination per chunk (its blocks'
+// integer P.V sums add up in the MFMA accumulators). Two for one head per pass
+// on a contiguous cache (two waves per SIMD at the grid's size, so the second
+// block's registers and staging area cost no occupancy), one otherwise.
+template <int GP, bool PAGED, int NW>
+constexpr int kChunk = 1;
+// One head per pass on a contiguous cache: the grid holds two waves per SIMD,
+// so the kernel may use 256 registers per lane at no cost in occupancy; it
+// keeps the masked QK operands, issues a block's P.V MFMAs before reading
+// any of their sums, and gives the wave merge its own LDS.
+template <int GP, bool PAGED, int NW>
+constexpr bool kLean = GP == 1 && !PAGED && NW == 4;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -170,8 +183,11 @@ __device__ __forceinline__ unsigned sel4(const unsigned* v, int i) {
 // KBITS and VBITS: the K and V code widths (8 or 4), set apart so a cache can
 // hold K and V at different precisions.
 template <int KBITS, int VBITS, int D, int GP, bool PAGED, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : GP <= 2 ? 3 : 2))) void
-attn_split_kernel(AttnLaunch a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((
+    amdgpu_waves_per_eu(NW == 8 ? 4 : (kChunk<GP, PAGED, NW> == 2 || kLean<GP, PAGED, NW>) ? 2 : GP <= 2 ? 3 : 2)))
+    void attn_split_kernel(AttnLaunch a) {
+  constexpr int CH = kChunk<GP, PAGED, NW>;
+  constexpr bool LEAN = kLean<GP, PAGED, NW>;
   constexpr int RBK = D * KBITS / 8;        // bytes per K token row in HBM
   constexpr int RBV = D * VBITS / 8;        // bytes per V token row in HBM
   constexpr int KB = KBITS == 8 ? 16 : 8;   // HBM bytes per lane per K load (16 elements)
@@ -205,25 +221,25 @@ attn_split_kernel(AttnLaunch a) {
   const int H = c.num_kv_heads, Hq = a.num_q_heads, G = Hq / H, S = a.splits, NT = a.tiles;
   const long long span = attn_span(a);  // logit slots per query head
   const int NTs = s == S - 1 ? a.last_tiles : NT;  // tiles of this split
-  // Uniform by construction; readfirstlane keeps it (and the buffer resources
-  // built from it) in scalar registers. With an append, the new token is slot
-  // L_old and the attention covers it.
   const bool app = a.k_new != nullptr;
-  const int L_old = __builtin_amdgcn_readfirstlane(c.lengths[b]);
-  const int L = __builtin_amdgcn_readfirstlane(min(min(L_old + (app ? 1 : 0), c.capacity), (int)span));
-  // fp16 tiers: slots [t_lo, t_hi) are read from the codes; the sink tier
-  // below and the recent tier above are attended by attn_tier_kernel (their
-  // logits are masked here and not spilled, and blocks past t_hi not read).
-  // Without tiers t_lo = 0 and t_hi = L.
-  const int t_lo = max(0, min(c.fp16_sinks, L));
-  const int t_hi = L - max(0, min(c.fp16_recent, L - t_lo));
+  // The sequence length is loaded first and used only once this wave's first
+  // block of loads has gone out (below): loads return in order, so waiting
+  // for it does not wait for the block, and no wave holds its cache reads
+  // back for a dependent load (which, with the memory system full, takes as
+  // long as the reads queued before it).
+  const int len_raw = c.lengths[b];
 
-  __shared__ __align__(16) uint8_t v_stage[NW][64 * VROW];
-  __shared__ __align__(16) int8_t w_limb[NW][NRS][16][64];
+  __shared__ __align__(16) uint8_t v_stage[CH][NW][64 * VROW];
+  __shared__ __align__(16) int8_t w_limb[NW][CH][NRS][16][64];
   __shared__ __align__(16) int8_t q_limb[GP][4][D];
   __shared__ float q_fac[GP], q_off[GP];
   __shared__ float red_m[NW][GP], red_l[NW][GP];
-  float* red_o = reinterpret_cast<float*>(&v_stage[0][0]);  // [NW][GP][D], used after the block loop
+  // The waves' partial outputs [NW][GP][D]: they reuse the staging area once
+  // every wave is done with it, or have their own (no barrier before they are
+  // written).
+  constexpr bool OWN_RED = CH == 2 || LEAN;
+  __shared__ float red_o_own[OWN_RED ? NW * GP * D : 1];
+  float* red_o = OWN_RED ? red_o_own : reinterpret_cast<float*>(&v_stage[0][0][0]);
   static_assert(NW * GP * D * 4 <= NW * 64 * VROW, "merge buffer fits the staging area");
 
   // Contiguous: one resource per (sequence, KV head) row of `capacity` tokens;
@@ -255,50 +271,7 @@ attn_split_kernel(AttnLaunch a) {
   // tile); block `it` starts at token t0(it) and holds tokens below L only
   // for it < nb.
   auto block_t0 = [&](int it) { return (s * NT * 4 + it * NW + wave) * 64; };
-  const int blocks_hi = min(4 * NTs, (t_hi - s * NT * kSplitTokens + 63) / 64) - wave;
-  const int nb = blocks_hi > 0 ? (blocks_hi + NW - 1) / NW : 0;
-
-  // Append: the wave whose block `it_new` holds slot L_old quantizes the new
-  // token's K and V rows into the cache before its first loads (the
-  // quantizer of the append kernels, so the codes are identical), sets its
-  // position and zeroes its score. It waits for those stores just before
-  // issuing that block; no other wave reads the slot, so no barrier is needed.
-  // Workgroup (0, 0) of each sequence keeps the old length and count for the
-  // merge kernel, which advances them once no workgroup reads them.
-  int it_new = -1;
-  if (app) {
-    if (s == 0 && g == 0 && tid == 0) {
-      a.stash[b] = L_old;
-      a.stash[c.batch + b] = c.num_seen[b];
-    }
-    const int qb = L_old >> 6;           // 64-token block of the new slot
-    const int jb = qb - s * NT * 4;      // its block index within this split
-    if (L_old >= 0 && L_old < c.capacity && L_old < span && min((qb >> 2) / NT, S - 1) == s && jb % NW == wave) {
-      it_new = jb / NW;
-      const long long row = cache_row(c, b, g, L_old);
-      if (row >= 0) {
-        const long long src = ((long long)b * H + g) * D;
-        const quant::RowVals<D> kx = quant::load_row<D>(a.k_new + src, lane);
-        const quant::RowVals<D> vx = quant::load_row<D>(a.v_new + src, lane);
-        quant::quant_vals<KBITS, D>(kx, static_cast<uint8_t*>(c.k_codes) + row * RBK, c.k_scale + row, lane);
-        quant::quant_vals<VBITS, D>(vx, static_cast<uint8_t*>(c.v_codes) + row * RBV, c.v_scale + row, lane);
-        if (lane == 0) {
-          if (c.positions) c.positions[row] = c.num_seen[b];
-          if (a.score) a.score[((long long)b * H + g) * c.capacity + L_old] = 0.f;
-        }
-      }
-    }
-  }
-  // Before issuing block `it`: the new token's stores have completed (gfx9
-  // counts stores with loads; vmcnt(0)).
-  auto wait_new = [&](int it) {
-    if (it == it_new) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      it_new = -1;
-    }
-  };
-
-  // Registers of one block's loads; two sets keep two blocks in flight.
+  // Registers of one block's loads (a chunk holds CH sets).
   using KT = typename std::conditional<KBITS == 8, i32x4, i32x2>::type;
   struct Regs {
     KT kq[4][NDH];
@@ -306,11 +279,11 @@ attn_split_kernel(AttnLaunch a) {
     float ksv[NSC], vsv[NSC];
   };
   // Issue every load of block `it`: K and V scales, then K codes into `r`,
-  // then V codes (INT8: straight into this wave's LDS staging area, swizzled;
-  // INT4: into `r`). Waiting for the scales and K (loads return in order)
-  // does not wait for V. Rows of contiguous caches are tokens; paged rows come
-  // from the block's four 16-token pages.
-  auto issue = [&](Regs& r, int it) {
+  // then V codes (INT8: straight into this wave's LDS staging area `vs`,
+  // swizzled; INT4: into `r`). Waiting for the scales and K (loads return in
+  // order) does not wait for V. Rows of contiguous caches are tokens; paged
+  // rows come from the block's four 16-token pages.
+  auto issue = [&](Regs& r, int it, int vs) {
     unsigned pb[4];
     const int t0 = block_t0(it);
     if (PAGED) {
@@ -354,7 +327,7 @@ attn_split_kernel(AttnLaunch a) {
       if constexpr (VBITS == 8) {
         const unsigned off = row_static((TPV * j) >> 4, t) * RBV + vchunk(t, lane % NCB) * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)&v_stage[wave][j * 1024], 16, off, 0, 0, 0);
+            rv, (__attribute__((address_space(3))) void*)&v_stage[vs][wave][j * 1024], 16, off, 0, 0, 0);
       } else if constexpr (V16) {
         // 4 lanes per token, 16 tokens per load: lane l takes chunks
         // 2 (l % 4) and 2 (l % 4) + 1 of token 16 (j / 2) + l / 4.
@@ -371,29 +344,84 @@ attn_split_kernel(AttnLaunch a) {
     }
   };
 
-  for (int hp = 0; hp < G; hp += GP) {
-    const int gh = min(GP, G - hp);  // real heads in this pass
-    // ---- q as int8 limbs, per head: wave w takes heads w, w + NW, ... ----
-    // q is read first and the first block's loads go out right after it, so
-    // the q setup overlaps them and waiting for q (loads return in order)
-    // does not wait for the cache reads.
-    constexpr int EPL = D / 64, HPW = (GP + NW - 1) / NW;
-    float xq[HPW][EPL];
+  // ---- q of a pass (wave w reads heads w, w + NW, ...), then the pass's
+  // first block: q returns first, so the q setup waits for q alone ----
+  constexpr int EPL = D / 64, HPW = (GP + NW - 1) / NW;
+  // Raw fp16 bits, converted where used, so nothing waits for them here.
+  unsigned short xq[HPW][EPL];
+  const unsigned short* qbits = reinterpret_cast<const unsigned short*>(a.q);
+  auto load_q = [&](int hp, int gh) {
 #pragma unroll
     for (int hi = 0; hi < HPW; ++hi)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int h = wave + NW * hi;
-        xq[hi][e] = h < gh ? __half2float(a.q[((long long)b * Hq + g * G + hp + h) * D + lane * EPL + e]) : 0.f;
+        xq[hi][e] = qbits[((long long)b * Hq + g * G + hp + min(h, gh - 1)) * D + lane * EPL + e];
       }
-    Regs ra;
-    wait_new(0);
-    issue(ra, 0);
+  };
+  Regs rg[CH];
+  load_q(0, min(GP, G));
+  issue(rg[0], 0, 0);  // block 0 of every wave exists; tokens past the length are masked
+
+  // ---- the length (uniform; readfirstlane keeps it in scalar registers) ----
+  // With an append, the new token is slot L_old and the attention covers it.
+  const int L_old = __builtin_amdgcn_readfirstlane(len_raw);
+  const int L = __builtin_amdgcn_readfirstlane(min(min(L_old + (app ? 1 : 0), c.capacity), (int)span));
+  // fp16 tiers: slots [t_lo, t_hi) are read from the codes; the sink tier
+  // below and the recent tier above are attended by attn_tier_kernel (their
+  // logits are masked here and not spilled, and blocks past t_hi not read).
+  // Without tiers t_lo = 0 and t_hi = L.
+  const int t_lo = max(0, min(c.fp16_sinks, L));
+  const int t_hi = L - max(0, min(c.fp16_recent, L - t_lo));
+  const int blocks_hi = min(4 * NTs, (t_hi - s * NT * kSplitTokens + 63) / 64) - wave;
+  const int nb = blocks_hi > 0 ? (blocks_hi + NW - 1) / NW : 0;
+
+  // Append: the wave whose block `it_new` holds slot L_old quantizes the new
+  // token's K and V rows into the cache (the quantizer of the append kernels,
+  // so the codes are identical), sets its position and zeroes its score, then
+  // waits for those stores; no other wave reads the slot, so no barrier is
+  // needed. If the slot is in its block 0, whose loads went out before the
+  // length was known, it loads that block again. Workgroup (0, 0) of each
+  // sequence keeps the old length and count for the merge kernel (at the
+  // end), which advances them once no workgroup reads them.
+  if (app) {
+    const int qb = L_old >> 6;           // 64-token block of the new slot
+    const int jb = qb - s * NT * 4;      // its block index within this split
+    if (L_old >= 0 && L_old < c.capacity && L_old < span && min((qb >> 2) / NT, S - 1) == s && jb % NW == wave) {
+      const long long row = cache_row(c, b, g, L_old);
+      if (row >= 0) {
+        const long long src = ((long long)b * H + g) * D;
+        const quant::RowVals<D> kx = quant::load_row<D>(a.k_new + src, lane);
+        const quant::RowVals<D> vx = quant::load_row<D>(a.v_new + src, lane);
+        quant::quant_vals<KBITS, D>(kx, static_cast<uint8_t*>(c.k_codes) + row * RBK, c.k_scale + row, lane);
+        quant::quant_vals<VBITS, D>(vx, static_cast<uint8_t*>(c.v_codes) + row * RBV, c.v_scale + row, lane);
+        if (lane == 0) {
+          if (c.positions) c.positions[row] = c.num_seen[b];
+          if (a.score) a.score[((long long)b * H + g) * c.capacity + L_old] = 0.f;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have completed (gfx9 counts them with loads)
+      if (jb / NW == 0) issue(rg[0], 0, 0);
+    }
+  }
+
+  for (int hp = 0; hp < G; hp += GP) {
+    const int gh = min(GP, G - hp);  // real heads in this pass
+    if (hp > 0) {
+      load_q(hp, gh);
+      issue(rg[0], 0, 0);
+    }
+#pragma unroll
+    for (int cc = 1; cc < CH; ++cc)
+      if (cc < nb) issue(rg[cc], cc, cc);
+    // ---- q as int8 limbs, per head: wave w takes heads w, w + NW, ... ----
 #pragma unroll
     for (int hi = 0; hi < HPW; ++hi) {
       const int h = wave + NW * hi;
       if (h >= GP) break;
-      const float* x = xq[hi];
+      float x[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = h < gh ? __half2float(__ushort_as_half(xq[hi][e])) : 0.f;
       float mx = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) mx = fmaxf(mx, fabsf(x[e]));
@@ -430,8 +458,11 @@ attn_split_kernel(AttnLaunch a) {
       }
     }
     if (GP < 4) {  // limb rows of heads that do not exist stay zero
-      int* z = reinterpret_cast<int*>(&w_limb[wave][0][4 * GP][0]);
-      for (int i = lane; i < (16 - 4 * GP) * 16; i += 64) z[i] = 0;
+#pragma unroll
+      for (int cc = 0; cc < CH; ++cc) {
+        int* z = reinterpret_cast<int*>(&w_limb[wave][cc][0][4 * GP][0]);
+        for (int i = lane; i < (16 - 4 * GP) * 16; i += 64) z[i] = 0;
+      }
     }
     __syncthreads();
 
@@ -448,12 +479,28 @@ attn_split_kernel(AttnLaunch a) {
       for (int dh = 0; dh < NDH; ++dh)
         qrow[v][dh] = *reinterpret_cast<const i32x4*>(&q_limb[h][col & 3][dh * 64 + quad * 16]);
     }
+    // GP < 4: the masked variants of the operand, built once and kept when
+    // registers allow (LEAN), else rebuilt per use, which keeps 32 registers
+    // free.
+    constexpr int NVAR = GP < 4 ? 4 / GP : 1;
+    constexpr bool KEEP_VAR = CH == 2 || LEAN;
+    i32x4 qvar[KEEP_VAR ? NVAR : 1][NDH];
+    if constexpr (KEEP_VAR) {
+#pragma unroll
+      for (int vi = 0; vi < NVAR; ++vi)
+#pragma unroll
+        for (int dh = 0; dh < NDH; ++dh) {
+          const bool on = slot / GP == vi;
+          const i32x4 q = qrow[0][dh];
+          qvar[vi][dh] = i32x4{on ? q[0] : 0, on ? q[1] : 0, on ? q[2] : 0, on ? q[3] : 0};
+        }
+    }
     auto a_operand = [&](int tg, int v, int dh) -> i32x4 {
       if (GP >= 4) return qrow[v][dh];
-      constexpr int NVAR = GP < 4 ? 4 / GP : 1;  // variants of the masked operand
+      if constexpr (KEEP_VAR) return qvar[tg % NVAR][dh];
       const bool on = slot / GP == tg % NVAR;
       i32x4 q = qrow[0][dh];
-      asm volatile("" : "+v"(q));  // rebuilt per use: hoisting all of them would cost 32 registers
+      asm volatile("" : "+v"(q));  // rebuilt per use
       return i32x4{on ? q[0] : 0, on ? q[1] : 0, on ? q[2] : 0, on ? q[3] : 0};
     };
     float qf[NC], qo[NC];
@@ -476,14 +523,14 @@ attn_split_kernel(AttnLaunch a) {
       for (int m = 0; m < NCB; ++m) o_acc[rs][m] = 0.f;
     }
 
-    // One 64-token block: logits, online softmax, weights, P.V.
-    auto process = [&](Regs& r, int it) {
+    // Logits of one 64-token block: int8 MFMA on raw K codes, scaled by the
+    // token's K scale; tokens off the coded range get -inf. With H2O each
+    // logit is spilled to its slot.
+    auto logits = [&](Regs& r, int it, float* sv) {
       const int t0 = block_t0(it);
-
-      // ---- logits: int8 MFMA on raw K codes ----
-      i32x4 acc[NC];
+      i32x4 acc[NC], acc2[NC];
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) acc[cc] = i32x4{0, 0, 0, 0};
+      for (int cc = 0; cc < NC; ++cc) acc[cc] = acc2[cc] = i32x4{0, 0, 0, 0};
 #pragma unroll
       for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
@@ -492,23 +539,52 @@ attn_split_kernel(AttnLaunch a) {
           if constexpr (KBITS == 8) kb = r.kq[tg][dh]; else kb = widen_int4(r.kq[tg][dh]);
           if (GP <= 4) {
             const int cc = tg * GP / 4;
-            acc[cc] = mfma(a_operand(tg, 0, dh), kb, acc[cc]);
+            // Two accumulator chains (by half row) when one head is served,
+            // so consecutive MFMAs do not wait for each other.
+            if (GP == 1 && dh == 1) acc2[cc] = mfma(a_operand(tg, 0, dh), kb, acc2[cc]);
+            else acc[cc] = mfma(a_operand(tg, 0, dh), kb, acc[cc]);
           } else {
 #pragma unroll
             for (int rs = 0; rs < NRS; ++rs) acc[tg * NRS + rs] = mfma(a_operand(tg, rs, dh), kb, acc[tg * NRS + rs]);
           }
         }
-      float sv[NC];
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
+        if (GP == 1 && NDH > 1) acc[cc] = acc[cc] + acc2[cc];
         const int j = 4 * cc + quad, tok = 16 * (j / GP) + col;
         float x = (limb_sum(acc[cc]) - qo[cc]) * qf[cc] * r.ksv[GP >= 8 ? cc / 2 : cc];
         const int ti = t0 + tok;
         const bool coded = ti >= t_lo && ti < t_hi;
         if (!coded || !hv[cc]) x = -INFINITY;
         sv[cc] = x;
-        if (a.logits != nullptr && hv[cc] && (coded || ti >= L))  // H2O: spill the logit (tier slots: their kernel)
-          a.logits[((long long)b * Hq + g * G + hp + j % GP) * span + ti] = x;
+      }
+    };
+    // H2O: spill a block's logits (tier slots: their kernel). Issued after the
+    // block's P.V, so the wait for the V loads does not also wait for them.
+    auto spill = [&](int it, const float* sv) {
+      if (a.logits == nullptr) return;
+      const int t0 = block_t0(it);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const int j = 4 * cc + quad, ti = t0 + 16 * (j / GP) + col;
+        const bool coded = ti >= t_lo && ti < t_hi;
+        if (hv[cc] && (coded || ti >= L)) a.logits[((long long)b * Hq + g * G + hp + j % GP) * span + ti] = sv[cc];
+      }
+    };
+
+    // One chunk of `ncur` blocks (ncur <= CH): logits, one online-softmax
+    // step over the chunk, the weights as int8 limbs with one exponent per
+    // chunk, then P.V with the blocks' integer sums added in the accumulators.
+    auto process = [&](int it0, int ncur) {
+      float sv[CH][NC];
+#pragma unroll
+      for (int ci = 0; ci < CH; ++ci) {
+        if (ci < ncur) {
+          logits(rg[ci], it0 + ci, sv[ci]);
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) sv[ci][cc] = -INFINITY;
+        }
       }
 
       // ---- online softmax, one running state per (wave, head) ----
@@ -517,8 +593,10 @@ attn_split_kernel(AttnLaunch a) {
       for (int rs = 0; rs < NRS; ++rs) {
         float mb = -INFINITY;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc)
-          if ((GP >= 8 ? cc % NRS : 0) == rs) mb = fmaxf(mb, sv[cc]);
+        for (int ci = 0; ci < CH; ++ci)
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc)
+            if ((GP >= 8 ? cc % NRS : 0) == rs) mb = fmaxf(mb, sv[ci][cc]);
         mb = head_reduce<GP, true>(mb);
         const float mn = fmaxf(m_run[rs], mb);
         corr[rs] = m_run[rs] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rs] - mn);
@@ -526,49 +604,62 @@ attn_split_kernel(AttnLaunch a) {
         l_part[rs] *= corr[rs];
         w_part[rs] *= corr[rs];
       }
-      float wv[NC];
+      float wv[CH][NC];
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        const int rs = GP >= 8 ? cc % NRS : 0;
-        const float p = sv[cc] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[cc] - m_run[rs]);
-        l_part[rs] += p;
-        wv[cc] = sv[cc] == -INFINITY ? 0.f : p * r.vsv[GP >= 8 ? cc / 2 : cc];  // a masked slot's scale may be stale
-        w_part[rs] += wv[cc];
-      }
+      for (int ci = 0; ci < CH; ++ci)
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          const int rs = GP >= 8 ? cc % NRS : 0;
+          const float p = sv[ci][cc] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[ci][cc] - m_run[rs]);
+          l_part[rs] += p;
+          // a masked slot's scale may be stale
+          wv[ci][cc] = sv[ci][cc] == -INFINITY ? 0.f : p * rg[ci].vsv[GP >= 8 ? cc / 2 : cc];
+          w_part[rs] += wv[ci][cc];
+        }
 
       // ---- weights as int8 limbs, rows (head, limb) x 64 tokens, in LDS ----
 #pragma unroll
       for (int rs = 0; rs < NRS; ++rs) {
         float wm = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc)
-          if ((GP >= 8 ? cc % NRS : 0) == rs) wm = fmaxf(wm, wv[cc]);
+        for (int ci = 0; ci < CH; ++ci)
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc)
+            if ((GP >= 8 ? cc % NRS : 0) == rs) wm = fmaxf(wm, wv[ci][cc]);
         wm = head_reduce<GP, true>(wm);
         const int E = limb_exponent(wm);
         wscale[rs] = ldexpf(1.f, -E);
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          if ((GP >= 8 ? cc % NRS : 0) != rs) continue;
-          const int j = 4 * cc + quad, h = j % GP, tok = 16 * (j / GP) + col;
-          int lm[4];
-          to_limbs(ldexpf(wv[cc], E), lm);
+        for (int ci = 0; ci < CH; ++ci) {
+          if (ci >= ncur) continue;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) w_limb[wave][rs][4 * (h & 3) + k][tok] = (int8_t)lm[k];
+          for (int cc = 0; cc < NC; ++cc) {
+            if ((GP >= 8 ? cc % NRS : 0) != rs) continue;
+            const int j = 4 * cc + quad, h = j % GP, tok = 16 * (j / GP) + col;
+            int lm[4];
+            to_limbs(ldexpf(wv[ci][cc], E), lm);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w_limb[wave][ci][rs][4 * (h & 3) + k][tok] = (int8_t)lm[k];
+          }
         }
       }
       // ---- V rows in LDS: INT8 came by DMA; INT4 is widened here ----
       if constexpr (VBITS == 4) {
 #pragma unroll
-        for (int j = 0; j < NCB; ++j) {
-          const int t = V16 ? 16 * (j / 2) + lane / 4 : TPV * j + lane / NCB;
-          const int m = V16 ? 2 * (lane % 4) + (j % 2) : lane % NCB;
-          const i32x4 val = widen_int4(r.vq[j]);
-          i32x2* dst = reinterpret_cast<i32x2*>(&v_stage[wave][t * VROW + vchunk(t, m) * 16]);
-          dst[0] = i32x2{val[0], val[1]};
-          dst[1] = i32x2{val[2], val[3]};
+        for (int ci = 0; ci < CH; ++ci) {
+          if (ci >= ncur) continue;
+#pragma unroll
+          for (int j = 0; j < NCB; ++j) {
+            const int t = V16 ? 16 * (j / 2) + lane / 4 : TPV * j + lane / NCB;
+            const int m = V16 ? 2 * (lane % 4) + (j % 2) : lane % NCB;
+            const i32x4 val = widen_int4(rg[ci].vq[j]);
+            i32x2* dst = reinterpret_cast<i32x2*>(&v_stage[ci][wave][t * VROW + vchunk(t, m) * 16]);
+            dst[0] = i32x2{val[0], val[1]};
+            dst[1] = i32x2{val[2], val[3]};
+          }
         }
       } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the V DMA of this block has landed
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the V DMA of this chunk has landed
       }
       asm volatile("" ::: "memory");
 
@@ -579,35 +670,59 @@ attn_split_kernel(AttnLaunch a) {
       const int tr_row = quad * 16 + (col >> 1), tr_col = (col & 1) * 8;
 #pragma unroll
       for (int rs = 0; rs < NRS; ++rs) {
-        const i32x4 aw = *reinterpret_cast<const i32x4*>(&w_limb[wave][rs][col][quad * 16]);
+        i32x4 aw[CH];
+#pragma unroll
+        for (int ci = 0; ci < CH; ++ci) aw[ci] = *reinterpret_cast<const i32x4*>(&w_limb[wave][ci][rs][col][quad * 16]);
+        // LEAN: every channel block's MFMA is issued before the first sum is
+        // read, so no MFMA result is waited for right after its issue.
+        constexpr int NPV = LEAN ? NCB : 1;
+        i32x4 pvs[NPV];
 #pragma unroll
         for (int m = 0; m < NCB; ++m) {
-          uint8_t* p0 = &v_stage[wave][tr_row * VROW + vchunk(tr_row, m) * 16 + tr_col];
-          uint8_t* p1 = &v_stage[wave][(tr_row + 8) * VROW + vchunk(tr_row + 8, m) * 16 + tr_col];
-          const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p0);
-          const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p1);
-          const i32x4 pv = mfma(aw, i32x4{lo[0], lo[1], hi[0], hi[1]}, i32x4{0, 0, 0, 0});
-          o_acc[rs][m] = fmaf(o_acc[rs][m], corr[rs], wscale[rs] * limb_sum(pv));
+          i32x4 pv = i32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int ci = 0; ci < CH; ++ci) {
+            if (ci >= ncur) continue;
+            uint8_t* p0 = &v_stage[ci][wave][tr_row * VROW + vchunk(tr_row, m) * 16 + tr_col];
+            uint8_t* p1 = &v_stage[ci][wave][(tr_row + 8) * VROW + vchunk(tr_row + 8, m) * 16 + tr_col];
+            const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p0);
+            const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p1);
+            pv = mfma(aw[ci], i32x4{lo[0], lo[1], hi[0], hi[1]}, pv);
+          }
+          if constexpr (LEAN) pvs[m] = pv;
+          else o_acc[rs][m] = fmaf(o_acc[rs][m], corr[rs], wscale[rs] * limb_sum(pv));
+        }
+        if constexpr (LEAN) {
+#pragma unroll
+          for (int m = 0; m < NCB; ++m) o_acc[rs][m] = fmaf(o_acc[rs][m], corr[rs], wscale[rs] * limb_sum(pvs[m]));
         }
       }
       asm volatile("" ::: "memory");
+#pragma unroll
+      for (int ci = 0; ci < CH; ++ci)
+        if (ci < ncur) spill(it0 + ci, sv[ci]);
     };
-    for (int it = 0; it < nb; ++it) {
-      if (it > 0) {
-        wait_new(it);
-        issue(ra, it);
+    for (int it0 = 0; it0 < nb; it0 += CH) {
+      const int ncur = min(CH, nb - it0);
+      if (it0 > 0) {
+#pragma unroll
+        for (int ci = 0; ci < CH; ++ci)
+          if (ci < ncur) issue(rg[ci], it0 + ci, ci);
       }
-      process(ra, it);
+      process(it0, ncur);
     }
 
     // ---- merge the waves ----
+    // A wave with no block of this split still issued block 0's loads (some
+    // into the staging area): they complete before any LDS is reused.
+    if (nb == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
     float l_tot[NRS], w_tot[NRS];
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
       l_tot[rs] = head_reduce<GP, false>(l_part[rs]);
       w_tot[rs] = VBITS == 4 ? head_reduce<GP, false>(w_part[rs]) : 0.f;
     }
-    __syncthreads();  // every wave is done with v_stage, which red_o reuses
+    if (!OWN_RED) __syncthreads();  // every wave is done with v_stage, which red_o reuses
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
       const int hh = (GP >= 8 ? 4 * rs : 0) + quad;  // head of this lane's PV rows
@@ -642,7 +757,11 @@ attn_split_kernel(AttnLaunch a) {
         a.part_ml[(hq * a.parts + s) * 2 + 1] = l;
       }
     }
-    __syncthreads();
+    if (hp + GP < G) __syncthreads();  // the next pass rewrites the LDS this one read
+  }
+  if (app && s == 0 && g == 0 && tid == 0) {
+    a.stash[b] = L_old;
+    a.stash[c.batch + b] = c.num_seen[b];
   }
 }
 
