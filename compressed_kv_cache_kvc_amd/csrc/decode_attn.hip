@@ -789,8 +789,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   // With an append, the length before it comes from the split kernel (the
   // cache's own length is advanced here, by one workgroup).
   const bool app = a.append != 0;
-  const int L = __builtin_amdgcn_readfirstlane(
-      min(min(app ? a.stash[b] + 1 : c.lengths[b], c.capacity), (int)span));
+  // The length is used last (H2O blocks): loaded now, read after the loads
+  // below have gone out.
+  const int len_raw = app ? a.stash[b] + 1 : c.lengths[b];
   const bool out_block = x < G;
   const int h_lo = out_block ? x : 0, nh = out_block ? 1 : G;
   float* minv = fac + nh * S;  // [nh][2]: m, 1/l
@@ -863,6 +864,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
     return;
   }
   if (!srow) return;
+  const int L = __builtin_amdgcn_readfirstlane(min(min(len_raw, c.capacity), (int)span));
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int t = t0 + k;
