@@ -479,6 +479,154 @@ def secondary_attention(kvc, torch, reps=16):
     return res
 
 
+def _graph_time(torch, fn, stream, reps, before=None):
+    """Capture fn() once, then time `reps` replays with events on `stream`
+    (before() runs eagerly, untimed, ahead of each replay); returns the mean
+    and the best replay in microseconds."""
+    with torch.cuda.stream(stream):
+        if before:
+            before()
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    times = []
+    for _ in range(reps):
+        if before:
+            with torch.cuda.stream(stream):
+                before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    del g
+    return sum(times) / len(times), min(times)
+
+
+def config_legs(kvc, torch):
+    """The configured workloads' other legs, each as configured, at full size:
+    the prefill append of the LLaMA-7B layer (8191 tokens); the Qwen GQA
+    stream's whole 64-step loop from 32767 prefilled tokens (step 0 evicts
+    32768 -> 8192, steps 1-63 evict one token per row); the 70B INT4 layer's
+    whole step (append, attention with H2O, the two-launch selection of 24162
+    of 129020 candidates per row, compaction). Cache contents are random
+    device data quantized by the library (timing does not depend on the
+    values); each timed region is a replayed graph, with caches restored
+    before it, untimed."""
+    from workloads import get
+    res = {}
+    stream = torch.cuda.Stream()
+
+    # ---- a1: the prefill append of the LLaMA-7B layer ----
+    w = get("llama7b_8k")
+    B, H, D, L = w.batch, w.num_kv_heads, w.head_dim, w.context
+    c = kvc.KVCache(B, H, D, L, 8)
+    sc = c.score_buffer()
+    kv = torch.randn((2, B, H, L - 1, D), device="cuda").half()
+    mean_us, best_us = _graph_time(torch, lambda: kvc.kvc_quant_append(c, kv[0], kv[1], h2o_score=sc,
+                                                                       max_len_hint=0),
+                                   stream, 8, before=lambda: (c.lengths.zero_(), c.num_seen.zero_()))
+    n = B * H * (L - 1)
+    nbytes = n * 2 * D * 2 + n * 2 * (D + 4) + n * 8  # fp16 in; codes + scales, position + score out
+    res["llama7b_8k_prefill_append"] = {
+        "calls": "kvc_quant_append of 8191 tokens x 32 KV heads", "us": round(mean_us, 2),
+        "bytes": nbytes, "gbps": round(nbytes / (mean_us * 1e-6) / 1e9, 1),
+        "frac": round(nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del c, sc, kv
+    torch.cuda.empty_cache()
+
+    # ---- c4: the Qwen GQA stream, 64 steps from 32767 prefilled tokens ----
+    w = get("qwen_gqa_stream")
+    B, Hq, H, D, L, steps = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.context, w.steps
+    budget, S, R = w.budget, w.n_sink, w.n_recent
+    ca, cb = kvc.KVCache(B, H, D, L, 8), kvc.KVCache(B, H, D, L, 8)
+    sa, sb = ca.score_buffer(), cb.score_buffer()
+    kv = torch.randn((2, B, H, L - 1, D), device="cuda").half()
+    kvc.kvc_quant_append(ca, kv[0], kv[1], max_len_hint=0)
+    del kv
+    pristine = {f: getattr(ca, f).clone() for f in ("k_codes", "v_codes", "k_scale", "v_scale", "positions",
+                                                     "lengths", "num_seen")}
+    qs = torch.randn((steps, B, Hq, D), device="cuda").half()
+    ks = torch.randn((steps, B, H, 1, D), device="cuda").half()
+    vs = torch.randn((steps, B, H, 1, D), device="cuda").half()
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    kidx = torch.empty((B, H, budget), dtype=torch.int32, device="cuda")
+    ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(ca, Hq, L, True), dtype=torch.uint8, device="cuda")
+
+    def restore():
+        for f, t in pristine.items():
+            getattr(ca, f).copy_(t)
+        sa.zero_()
+
+    def step(i):
+        src, ssrc, dst, sdst = (ca, sa, cb, sb) if i % 2 == 0 else (cb, sb, ca, sa)
+        hint = L - 1 if i == 0 else budget
+        kvc.kvc_decode_step(src, ks[i], vs[i], qs[i], out, ssrc, budget, S, R, kidx, dst, sdst, max_len_hint=hint,
+                            workspace=ws)
+
+    def loop():
+        for i in range(steps):
+            step(i)
+
+    loop_us, loop_best = _graph_time(torch, loop, stream, 3, before=restore)
+    step0_us, _ = _graph_time(torch, lambda: step(0), stream, 3, before=restore)
+    res["qwen_gqa_stream_loop"] = {
+        "calls": "64 x kvc_decode_step (append, attention + H2O over 32768 then 8193 tokens, evict to 8192)",
+        "loop_us": round(loop_us, 1), "step0_us": round(step0_us, 1),
+        "steady_step_us": round((loop_us - step0_us) / (steps - 1), 2),
+        "tokens_per_s": round(B * steps / (loop_us * 1e-6), 1)}
+    del ca, cb, sa, sb, pristine, ws
+    torch.cuda.empty_cache()
+
+    # ---- c5: the 70B INT4 layer's whole step ----
+    w = get("llama70b_int4")
+    B, Hq, H, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.context
+    budget, S, R = w.budget, w.n_sink, w.n_recent
+    src, dst = kvc.KVCache(B, H, D, L, 4), kvc.KVCache(B, H, D, L, 4)
+    ssrc, sdst = src.score_buffer(), dst.score_buffer()
+    for b in range(B):  # one sequence at a time keeps the fp16 staging at 1 GB
+        one = kvc.KvcCacheDesc.from_buffer_copy(src.desc)
+        one.batch = 1
+        for f in ("k_codes", "v_codes", "k_scale", "v_scale", "positions", "lengths", "num_seen"):
+            t = getattr(src, f)
+            setattr(one, f, t[b:b + 1].data_ptr())
+        kv = torch.randn((2, 1, H, L - 1, D), device="cuda").half()
+        kvc.kvc_quant_append(one, kv[0], kv[1], max_len_hint=0)
+        del kv
+    q = torch.randn((B, Hq, D), device="cuda").half()
+    kn, vn = torch.randn((B, H, 1, D), device="cuda").half(), torch.randn((B, H, 1, D), device="cuda").half()
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    kidx = torch.empty((B, H, budget), dtype=torch.int32, device="cuda")
+    ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(src, Hq, L, True), dtype=torch.uint8, device="cuda")
+
+    def rewind():
+        src.lengths.fill_(L - 1)
+        src.num_seen.fill_(L - 1)
+
+    def c5_step():
+        rewind()
+        kvc.kvc_decode_step(src, kn, vn, q, out, ssrc, budget, S, R, kidx, dst, sdst, max_len_hint=L - 1,
+                            workspace=ws)
+
+    def c5_evict():
+        kvc.kvc_h2o_evict(src, ssrc, budget, S, R, kidx, dst, sdst, max_len_hint=L)
+
+    step_us, _ = _graph_time(torch, c5_step, stream, 5)
+    evict_us, _ = _graph_time(torch, c5_evict, stream, 5)
+    kv_bytes = B * H * L * 2 * (D // 2 + 4) + q.numel() * 2 + out.numel() * 4
+    res["llama70b_int4_step"] = {
+        "calls": "kvc_decode_step (split, merge, selection, gather: 131072 -> 26214 per row)",
+        "us": round(step_us, 1), "evict_us": round(evict_us, 1),
+        "kv_bytes": int(kv_bytes), "tokens_per_s_per_layer": round(B / (step_us * 1e-6), 1)}
+    del src, dst, ssrc, sdst, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -715,6 +863,7 @@ def main(argv=None):
     if not args.no_secondary:
         rec["layer_schedules"] = rec_sched
         rec["secondary_attention"] = secondary_attention(kvc, torch)
+        rec["config_legs"] = config_legs(kvc, torch)
     if not args.no_cpu_baseline:
         t_cpu, n_cpu, t_att, n_att, cores = cpu_baseline(w, d, args.cpu_seconds)
         rec["cpu_baseline"] = {

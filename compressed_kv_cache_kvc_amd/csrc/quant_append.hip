@@ -65,8 +65,107 @@ __global__ __launch_bounds__(1024) void quant_append_seq_kernel(kvc_cache_t c, c
   }
 }
 
-// Prefill-sized appends: four rows per workgroup over the whole grid; the
-// lengths advance in a second launch once every row has read them.
+// Prefill-sized appends: every K row, then every V row, of the whole append
+// as one flat list over the grid. A row of D fp16 values is D/8 lanes of 16
+// bytes, so one wave instruction loads 64 / (D/8) consecutive rows (1 KB,
+// contiguous); each wave keeps U such loads in flight. The max-abs is a DPP
+// reduction over the row's lanes; each lane then quantizes its 8 values with
+// the same correctly rounded divisions and rounding as quant_row.h (the codes
+// are identical whichever kernel writes them) and stores them with one 8-byte
+// (INT8) or 4-byte (INT4) store. The lengths advance in a second launch once
+// every row has read them.
+template <int D>
+__device__ __forceinline__ float row_lanes_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v, v));   // quad: xor 1
+  v = fmaxf(v, dpp_f<0x4E>(v, v));   // quad: xor 2
+  v = fmaxf(v, dpp_f<0x141>(v, v));  // half-row mirror: 8 lanes
+  if (D == 128) v = fmaxf(v, dpp_f<0x140>(v, v));  // row mirror: 16 lanes
+  return v;
+}
+
+template <int KBITS, int VBITS, int D>
+__global__ __launch_bounds__(256) void quant_append_bulk_kernel(kvc_cache_t c, const __half* __restrict__ kn,
+                                                                const __half* __restrict__ vn, int n_new,
+                                                                float* __restrict__ score, long long tokens) {
+  static_assert(D == 64 || D == 128, "D");
+  constexpr int LPR = D / 8;     // lanes per row, 8 fp16 values each
+  constexpr int RPI = 64 / LPR;  // rows per wave instruction
+  constexpr int U = 4;           // loads in flight per wave
+  const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
+  const long long rows = 2 * tokens;  // K rows [0, tokens), V rows [tokens, 2 tokens)
+  const long long nwaves = (long long)gridDim.x * 4;
+  const int H = c.num_kv_heads;
+  for (long long r0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (RPI * U); r0 < rows;
+       r0 += nwaves * RPI * U) {
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long r = min(r0 + u * RPI + sub, rows - 1);
+      const bool kv = r >= tokens;
+      x[u] = *reinterpret_cast<const uint4*>((kv ? vn : kn) + (kv ? r - tokens : r) * D + part * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long r = r0 + u * RPI + sub;
+      const bool valid = r < rows, kv = r >= tokens;
+      const long long rt = kv ? r - tokens : r;  // (b, h, t) flattened
+      const int t = (int)(rt % n_new);
+      const long long bh = rt / n_new;
+      const int h = (int)(bh % H), b = (int)(bh / H);
+      const __half2* hv = reinterpret_cast<const __half2*>(&x[u]);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 f = __half22float2(hv[i]);
+        v[2 * i] = f.x;
+        v[2 * i + 1] = f.y;
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      amax = row_lanes_max<D>(amax);
+      if (!valid) continue;
+      const int bits = kv ? VBITS : KBITS;
+      const float qmax = bits == 8 ? 127.f : 7.f, qmin = bits == 8 ? -127.f : -8.f;
+      const float sc = __fdiv_rn(amax, qmax);
+      int code[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float q = sc == 0.f ? 0.f : rintf(__fdiv_rn(v[i], sc));
+        code[i] = (int)fminf(fmaxf(q, qmin), qmax);
+      }
+      const int L0 = c.lengths[b];
+      const long long row = cache_row(c, b, h, L0 + t);
+      if (row < 0) continue;
+      if (bits == 8) {
+        unsigned w0 = 0, w1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w0 |= (unsigned)(code[i] & 0xFF) << (8 * i);
+          w1 |= (unsigned)(code[4 + i] & 0xFF) << (8 * i);
+        }
+        uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * D + part * 8;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+      } else {
+        unsigned w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= (unsigned)(code[i] & 0xF) << (4 * i);
+        uint8_t* dst = static_cast<uint8_t*>(kv ? c.v_codes : c.k_codes) + row * (D / 2) + part * 4;
+        *reinterpret_cast<unsigned*>(dst) = w;
+      }
+      if (part == 0) {
+        (kv ? c.v_scale : c.k_scale)[row] = sc;
+        if (!kv) {
+          if (c.positions) c.positions[row] = c.num_seen[b] + t;
+          if (score) score[bh * c.capacity + L0 + t] = 0.f;
+        }
+      }
+    }
+  }
+}
+
+// Prefill-sized appends whose inputs or codes are not aligned for the bulk
+// kernel: four rows per workgroup, one wave per row.
 template <int KBITS, int VBITS, int D>
 __global__ __launch_bounds__(256) void quant_append_rows_kernel(kvc_cache_t c, const __half* __restrict__ kn,
                                                                 const __half* __restrict__ vn, int n_new,
@@ -112,10 +211,21 @@ hipError_t launch_bits(const kvc_cache_t& c, const __half* kn, const __half* vn,
                        score);
     return hipGetLastError();
   }
-  const long long total = rows_per_seq * c.batch;
-  const long long blocks = (total + 3) / 4;
-  hipLaunchKernelGGL((quant_append_rows_kernel<KBITS, VBITS, D>), dim3((unsigned)blocks), dim3(256), 0, st, c, kn, vn,
-                     n_new, score, total);
+  const long long tokens = (long long)c.batch * c.num_kv_heads * n_new;
+  const uintptr_t align = (uintptr_t)kn | (uintptr_t)vn | (uintptr_t)c.k_codes | (uintptr_t)c.v_codes;
+  if (align % 16) {
+    const long long total = rows_per_seq * c.batch;
+    hipLaunchKernelGGL((quant_append_rows_kernel<KBITS, VBITS, D>), dim3((unsigned)((total + 3) / 4)), dim3(256), 0,
+                       st, c, kn, vn, n_new, score, total);
+  } else {
+    // The bulk kernel: about 8 workgroups of 4 waves per CU, grid-stride
+    // over the rows.
+    const long long rows_per_wg = 4LL * (64 / (D / 8)) * 4;
+    const long long blocks = std::max(1LL, std::min((2 * tokens + rows_per_wg - 1) / rows_per_wg,
+                                                     8LL * device_cus()));
+    hipLaunchKernelGGL((quant_append_bulk_kernel<KBITS, VBITS, D>), dim3((unsigned)blocks), dim3(256), 0, st, c, kn,
+                       vn, n_new, score, tokens);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(advance_lengths_kernel, dim3((c.batch + 255) / 256), dim3(256), 0, st, c.lengths,

@@ -46,6 +46,39 @@ def test_quant_append_bit_exact(name, bits, L):
     assert host(gc.num_seen).tolist() == [L] * w.batch
 
 
+@pytest.mark.parametrize("aligned", [True, False])
+@pytest.mark.parametrize("bits,v_bits,D", [(8, 8, 128), (4, 4, 128), (8, 4, 64), (4, 8, 128)])
+def test_quant_append_bulk_edges(aligned, bits, v_bits, D):
+    """Prefill-sized appends: 3 KV heads x 47 tokens per sequence (141 K rows,
+    so a wave instruction straddles the last K and first V rows), appended at
+    different lengths per sequence (one after a short first append); inputs
+    offset by one fp16 element take the per-row kernel. Codes, scales and
+    positions bit-exact against the oracle."""
+    print(f"[quant bulk] aligned={aligned} bits={bits} v_bits={v_bits} D={D}", flush=True)
+    w = get("tiny_mha").scaled(context=60, batch=2, num_q_heads=3, num_kv_heads=3, head_dim=D, bits=bits)
+    d = draw(w)
+    gc = make_gpu_cache(w, 64, bits, v_bits=v_bits)
+    ref = oracle.RefCache(2, 3, D, 64, bits, v_bits=v_bits)
+    k0, v0 = d["k"][:, :, :13], d["v"][:, :, :13]
+    kvc.kvc_quant_append(gc, dev(k0), dev(v0))
+    ref.append(k0, v0)
+    k1, v1 = d["k"][:, :, 13:60], d["v"][:, :, 13:60]
+    if aligned:
+        kd, vd = dev(k1), dev(v1)
+    else:
+        flat_k = torch.zeros(k1.size + 1, dtype=torch.float16, device="cuda")
+        flat_v = torch.zeros(v1.size + 1, dtype=torch.float16, device="cuda")
+        flat_k[1:] = dev(k1).reshape(-1)
+        flat_v[1:] = dev(v1).reshape(-1)
+        kd, vd = flat_k[1:].view(k1.shape), flat_v[1:].view(v1.shape)
+        assert kd.data_ptr() % 16 != 0
+    kvc.kvc_quant_append(gc, kd, vd)
+    ref.append(k1, v1)
+    torch.cuda.synchronize()
+    assert_codes_equal(gc, ref)
+    assert host(gc.num_seen).tolist() == [60, 60]
+
+
 def test_quant_zero_rows_and_halfway_cases():
     """All-zero rows give scale 0 and code 0; amax = 127 rows hit exact halves."""
     w = get("tiny_mha").scaled(context=4)
