@@ -636,6 +636,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the attention-only measurements of the paged, GQA and INT4 workloads")
+    ap.add_argument("--legs-only", action="store_true",
+                    help="instead of the benchmark, run only the configured workloads' other legs (prefill append, "
+                         "GQA stream loop, 70B INT4 step) and print them as one JSON line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the benchmark, run 8 plain device-to-device copies of this many MiB "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -654,6 +657,9 @@ def main(argv=None):
     from workloads import draw, get
 
     torch.cuda.set_device(0)
+    if args.legs_only:
+        print(json.dumps({"config_legs": config_legs(kvc, torch)}))
+        return 0
     w = get("llama7b_8k")
     d = draw(w)
     B, Hq, H, D, L, bits = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.context, w.bits

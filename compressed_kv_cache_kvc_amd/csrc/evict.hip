@@ -36,6 +36,7 @@ namespace {
 constexpr int kLog2NT = 10;
 constexpr int kNT = 1 << kLog2NT;  // threads per workgroup
 constexpr int kKPT = 8;            // candidate keys per thread (in registers)
+constexpr int kHistCopies = 4;     // histogram copies (radix_select.h)
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   constexpr int NT = kNT, KPT = kKPT;
   constexpr bool MERGE = GK > 0;
   constexpr int GL = MERGE ? GK : 1;
-  __shared__ int hist[radix::kBins];
+  __shared__ __align__(16) int hist[radix::kBins * kHistCopies];
   __shared__ int scan_tmp[16];
   __shared__ unsigned mm_tmp[32];
   __shared__ int sel[4];
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
     mm_tmp[tid >> 6] = kmin;
     mm_tmp[16 + (tid >> 6)] = kmax;
   }
-  radix::radix_clear<NT>(hist, sel);
+  radix::radix_clear<NT, kHistCopies>(hist, sel);
   unsigned key[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) stage_lds[tid + j * NT] = v[j];
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   };
   const bool any_heavy = k > 0;
   unsigned T = 0;
-  if (any_heavy) T = radix::radix_threshold_range<NT>(for_keys, k, kmin, kmax, hist, scan_tmp, sel, small);
+  if (any_heavy) T = radix::radix_threshold_range<NT, kHistCopies>(for_keys, k, kmin, kmax, hist, scan_tmp, sel, small);
 
   // Threshold ties ranked in slot order; candidates above T before this
   // thread (both counts fit 16 bits: n <= NT * KPT).

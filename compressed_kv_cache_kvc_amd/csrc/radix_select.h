@@ -12,6 +12,10 @@
 //    histogram increments over many bins (LDS atomics that collide on one
 //    address within a wave instruction serialize; scores are probability mass
 //    and mostly share a few binary exponents);
+//  * the histogram can be replicated (COPIES copies, a lane adding into copy
+//    lane % COPIES, the copies of a bin adjacent): lanes of one wave whose
+//    keys fall in the same bin then collide in groups of at most 64 / COPIES
+//    instead of 64;
 //  * the bin holding the k-th key comes from a block-wide suffix scan; once
 //    that bin holds at most 64 keys, they are gathered into LDS and one wave
 //    ranks them directly (each lane counts the keys above and equal to its
@@ -65,11 +69,11 @@ __device__ __forceinline__ int block_inclusive_scan_1b(int v, int* tmp) {
   return v + add;
 }
 
-// Clears the histogram and the gather counter; a barrier must follow before
-// radix_threshold_range runs.
-template <int NT>
+// Clears the histogram (kBins * COPIES ints) and the gather counter; a
+// barrier must follow before radix_threshold_range runs.
+template <int NT, int COPIES = 1>
 __device__ __forceinline__ void radix_clear(int* hist, int* sel) {
-  for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
+  for (int i = threadIdx.x; i < kBins * COPIES; i += NT) hist[i] = 0;
   if (threadIdx.x == 0) sel[3] = 0;
 }
 
@@ -79,11 +83,13 @@ __device__ __forceinline__ void radix_clear(int* hist, int* sel) {
 // On entry `hist` is zero and sel[3] == 0 (radix_clear, then a barrier). On
 // return, T is the k-th largest key and `k` the number of keys equal to T that
 // are kept.
-template <int NT, typename ForKeys>
+template <int NT, int COPIES = 1, typename ForKeys>
 __device__ __forceinline__ unsigned radix_threshold_range(ForKeys for_keys, int& k, unsigned kmin, unsigned kmax,
                                                           int* hist, int* scan_tmp, int* sel, unsigned* small) {
   constexpr int BPT = kBins / NT;  // bins per thread in the digit search
+  static_assert(COPIES == 1 || COPIES == 4 || COPIES == 8, "COPIES");
   const int tid = threadIdx.x;
+  const int cp = COPIES > 1 ? (tid & (COPIES - 1)) : 0;
   const unsigned diff = kmin ^ kmax;
   if (diff == 0) return kmin;  // every candidate equal: keep the lowest k slots
   int remaining = 32 - __clz(diff);  // low bits still undecided
@@ -97,10 +103,12 @@ __device__ __forceinline__ unsigned radix_threshold_range(ForKeys for_keys, int&
     if (first) {
       // Every real key shares the prefix T of the first pass: add the match
       // flag instead of branching per key.
-      for_keys([&](unsigned u) { atomicAdd(&hist[(u >> shift) & dmask], (int)((u & pmask) == T)); });
+      for_keys([&](unsigned u) {
+        atomicAdd(&hist[((u >> shift) & dmask) * COPIES + cp], (int)((u & pmask) == T));
+      });
     } else {
       for_keys([&](unsigned u) {
-        if ((u & pmask) == T) atomicAdd(&hist[(u >> shift) & dmask], 1);
+        if ((u & pmask) == T) atomicAdd(&hist[((u >> shift) & dmask) * COPIES + cp], 1);
       });
     }
     first = false;
@@ -112,8 +120,19 @@ __device__ __forceinline__ unsigned radix_threshold_range(ForKeys for_keys, int&
     int c[BPT], tot = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-      c[j] = hist[top - j];
-      hist[top - j] = 0;
+      if constexpr (COPIES == 1) {
+        c[j] = hist[top - j];
+        hist[top - j] = 0;
+      } else {
+        int4* h4 = reinterpret_cast<int4*>(hist + (top - j) * COPIES);
+        c[j] = 0;
+#pragma unroll
+        for (int q = 0; q < COPIES / 4; ++q) {
+          const int4 x = h4[q];
+          c[j] += x.x + x.y + x.z + x.w;
+          h4[q] = make_int4(0, 0, 0, 0);
+        }
+      }
       tot += c[j];
     }
     // scan_tmp is next written after the barrier below and the histogram's.
@@ -165,7 +184,7 @@ __device__ __forceinline__ unsigned radix_threshold_range(ForKeys for_keys, int&
 
 // The same with the key range found here: one block reduction, the clear and
 // a barrier come first.
-template <int NT, typename ForKeys>
+template <int NT, int COPIES = 1, typename ForKeys>
 __device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, int* hist, int* scan_tmp,
                                                     unsigned* mm_tmp, int* sel, unsigned* small) {
   unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -174,9 +193,9 @@ __device__ __forceinline__ unsigned radix_threshold(ForKeys for_keys, int& k, in
     kmax = max(kmax, u);
   });
   block_minmax<NT>(kmin, kmax, mm_tmp);
-  radix_clear<NT>(hist, sel);
+  radix_clear<NT, COPIES>(hist, sel);
   __syncthreads();
-  return radix_threshold_range<NT>(for_keys, k, kmin, kmax, hist, scan_tmp, sel, small);
+  return radix_threshold_range<NT, COPIES>(for_keys, k, kmin, kmax, hist, scan_tmp, sel, small);
 }
 
 }  // namespace radix

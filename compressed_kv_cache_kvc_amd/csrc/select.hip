@@ -27,12 +27,16 @@ using radix::kBins;
 using radix::order_key;
 using radix::radix_threshold;
 
-// NT threads; REG: each thread holds KPT consecutive candidates in registers.
+// NT threads; REG: each thread holds KPT consecutive candidates in registers;
+// else the keys are re-read, KMEM loads in flight per thread.
+// The histogram has 8 copies (radix_select.h).
+constexpr int kHistCopies = 8;
+constexpr int KMEM = 32;
 template <int NT, int KPT, bool REG>
 __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* __restrict__ score, int budget,
                                                     int n_sink, int n_recent, uint8_t* __restrict__ mask,
                                                     int32_t* __restrict__ keep_index, int max_len) {
-  __shared__ int hist[kBins];
+  __shared__ __align__(16) int hist[kBins * kHistCopies];
   __shared__ int scan_tmp[16];
   __shared__ unsigned mm_tmp[32];
   __shared__ int sel[4];
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
       mm_tmp[tid >> 6] = kmin;
       mm_tmp[16 + (tid >> 6)] = kmax;
     }
-    radix::radix_clear<NT>(hist, sel);
+    radix::radix_clear<NT, kHistCopies>(hist, sel);
     // The coalesced loads (slot lo + tid + j*NT) go to LDS, then each thread
     // reads its contiguous range back with 16-byte LDS reads (its range starts
     // at a multiple of 4 words); staged slots past the candidates are unused.
@@ -117,12 +121,12 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
 #pragma unroll
       for (int q = 0; q < KPT; ++q) f(key[q]);  // key 0 in unused slots
     } else {
-      for (int base = lo + tid; base < hi; base += KPT * NT) {
-        unsigned kk[KPT];
+      for (int base = lo + tid; base < hi; base += KMEM * NT) {
+        unsigned kk[KMEM];
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) kk[j] = order_key(row[min(base + j * NT, hi - 1)]);
+        for (int j = 0; j < KMEM; ++j) kk[j] = order_key(row[min(base + j * NT, hi - 1)]);
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
+        for (int j = 0; j < KMEM; ++j)
           if (base + j * NT < hi) f(kk[j]);
       }
     }
@@ -134,12 +138,12 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
       for (int q = 0; q < KPT; ++q)
         if (q < cnt) f(i0 + q, key[q]);
     } else {
-      for (int q0 = 0; q0 < cnt; q0 += KPT) {
-        unsigned kk[KPT];
+      for (int q0 = 0; q0 < cnt; q0 += KMEM) {
+        unsigned kk[KMEM];
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) kk[j] = order_key(row[i0 + min(q0 + j, cnt - 1)]);
+        for (int j = 0; j < KMEM; ++j) kk[j] = order_key(row[i0 + min(q0 + j, cnt - 1)]);
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
+        for (int j = 0; j < KMEM; ++j)
           if (q0 + j < cnt) f(i0 + q0 + j, kk[j]);
       }
     }
@@ -147,8 +151,8 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
   const bool any_heavy = k > 0;
   unsigned T = 0;
   if (any_heavy)
-    T = REG ? radix::radix_threshold_range<NT>(for_keys, k, kmin, kmax, hist, scan_tmp, sel, small)
-            : radix_threshold<NT>(for_keys, k, hist, scan_tmp, mm_tmp, sel, small);
+    T = REG ? radix::radix_threshold_range<NT, kHistCopies>(for_keys, k, kmin, kmax, hist, scan_tmp, sel, small)
+            : radix_threshold<NT, kHistCopies>(for_keys, k, hist, scan_tmp, mm_tmp, sel, small);
 
   // Sinks and the recent window are always kept.
   const int n_heavy = budget - n_sink - n_recent;
