@@ -432,9 +432,12 @@ def secondary_attention(kvc, torch, reps=16):
     # The GQA stream's whole decode step in steady state (c4 after its first
     # step): 8 sequences of 8192 kept tokens, append the new one, attend with
     # H2O over 8193, evict back to 8192 (4 sinks + 2048 recent + 6140 heavy),
-    # one kvc_decode_step per step (G = 7: split, merge and the one-launch
-    # eviction). 8 rotated caches share one lengths array, so a fill rewinds
-    # all of them once per 8 steps; the fill is inside the timed graph.
+    # one kvc_decode_step per step. In place (the cache as its destination):
+    # the split kernel, then one launch that merges, selects and moves only
+    # the tokens past the evicted one; out of place (into one other cache):
+    # split, merge and the one-launch eviction copying every kept token.
+    # 8 rotated caches share one lengths array, so a fill rewinds all of them
+    # once per 8 steps; the fill is inside the timed graph.
     w = get("qwen_gqa_stream")
     B, Hq, H, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
     Lk, n_bufs = w.budget, 8
@@ -460,20 +463,28 @@ def secondary_attention(kvc, torch, reps=16):
     ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, Lk + 1, True), dtype=torch.uint8,
                      device="cuda")
 
-    def step(i):
+    def step(i, in_place):
         if i % n_bufs == 0:
             lengths_q.fill_(Lk)
             seen_q.fill_(Lk)
-        kvc.kvc_decode_step(caches[i % n_bufs], knew, vnew, q, out, scores[i % n_bufs], Lk, w.n_sink, w.n_recent,
-                            kidx, dstq, dsc, max_len_hint=Lk, workspace=ws)
+        c, sc = caches[i % n_bufs], scores[i % n_bufs]
+        dst, dst_sc = (c, sc) if in_place else (dstq, dsc)
+        kvc.kvc_decode_step(c, knew, vnew, q, out, sc, Lk, w.n_sink, w.n_recent, kidx, dst, dst_sc, max_len_hint=Lk,
+                            workspace=ws)
 
+    # launch(i) gets the running index
     lengths_q.fill_(Lk)
     seen_q.fill_(Lk)
-    us = timed(step, 1 << 30, 64)  # launch(i) gets the running index
+    us = timed(lambda i: step(i, True), 1 << 30, 64)
+    lengths_q.fill_(Lk)
+    seen_q.fill_(Lk)
+    us_oop = timed(lambda i: step(i, False), 1 << 30, 64)
     res["qwen_gqa_stream_step"] = {"workload": "qwen_gqa_stream", "us_per_step": round(us, 2),
                                    "tokens_per_s_per_layer": round(B / (us * 1e-6), 1),
                                    "kv_bytes_attended": int(B * H * (Lk + 1) * 2 * (D + 4)),
-                                   "calls": "kvc_decode_step (append, attention + H2O, evict 8193 -> 8192)"}
+                                   "calls": "kvc_decode_step in place (append, attention + H2O, evict 8193 -> 8192; "
+                                            "only tokens past the first evicted slot move)",
+                                   "us_per_step_out_of_place": round(us_oop, 2)}
     del caches, scores, dstq, dsc, ws
     torch.cuda.empty_cache()
     return res
@@ -562,23 +573,28 @@ def config_legs(kvc, torch):
             getattr(ca, f).copy_(t)
         sa.zero_()
 
-    def step(i):
-        src, ssrc, dst, sdst = (ca, sa, cb, sb) if i % 2 == 0 else (cb, sb, ca, sa)
+    def step(i, in_place):
+        if in_place:  # the cache is its own destination: only tokens past the first evicted slot move
+            src, ssrc, dst, sdst = ca, sa, ca, sa
+        else:
+            src, ssrc, dst, sdst = (ca, sa, cb, sb) if i % 2 == 0 else (cb, sb, ca, sa)
         hint = L - 1 if i == 0 else budget
         kvc.kvc_decode_step(src, ks[i], vs[i], qs[i], out, ssrc, budget, S, R, kidx, dst, sdst, max_len_hint=hint,
                             workspace=ws)
 
-    def loop():
-        for i in range(steps):
-            step(i)
+    for in_place, key in ((True, "qwen_gqa_stream_loop"), (False, "qwen_gqa_stream_loop_out_of_place")):
+        def loop():
+            for i in range(steps):
+                step(i, in_place)
 
-    loop_us, loop_best = _graph_time(torch, loop, stream, 3, before=restore)
-    step0_us, _ = _graph_time(torch, lambda: step(0), stream, 3, before=restore)
-    res["qwen_gqa_stream_loop"] = {
-        "calls": "64 x kvc_decode_step (append, attention + H2O over 32768 then 8193 tokens, evict to 8192)",
-        "loop_us": round(loop_us, 1), "step0_us": round(step0_us, 1),
-        "steady_step_us": round((loop_us - step0_us) / (steps - 1), 2),
-        "tokens_per_s": round(B * steps / (loop_us * 1e-6), 1)}
+        loop_us, loop_best = _graph_time(torch, loop, stream, 3, before=restore)
+        step0_us, _ = _graph_time(torch, lambda: step(0, in_place), stream, 3, before=restore)
+        res[key] = {
+            "calls": "64 x kvc_decode_step (append, attention + H2O over 32768 then 8193 tokens, evict to 8192), "
+                     + ("in place (dst = the cache)" if in_place else "into the other of two caches"),
+            "loop_us": round(loop_us, 1), "step0_us": round(step0_us, 1),
+            "steady_step_us": round((loop_us - step0_us) / (steps - 1), 2),
+            "tokens_per_s": round(B * steps / (loop_us * 1e-6), 1)}
     del ca, cb, sa, sb, pristine, ws
     torch.cuda.empty_cache()
 

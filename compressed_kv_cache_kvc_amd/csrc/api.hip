@@ -137,7 +137,7 @@ int32_t check_same_tiers(const kvc_cache_t* src, const kvc_cache_t* dst) {
 
 struct AttnGeom {
   int splits, tiles, last_tiles, tier_parts;
-  size_t off_ml, off_logits, off_stash, total;
+  size_t off_ml, off_logits, off_stash, off_ip, total;
 };
 
 // Launch geometry of the decode-attention kernels. A split covers `tiles`
@@ -185,7 +185,11 @@ int32_t attn_geometry(const kvc_cache_t* c, int32_t Hq, int32_t hint, int32_t wi
   g->off_ml = part_o;
   g->off_logits = part_o + part_ml;
   g->off_stash = part_o + part_ml + logits;
-  g->total = g->off_stash + align256(2 * (size_t)c->batch * sizeof(int32_t));
+  g->off_ip = g->off_stash + align256(2 * (size_t)c->batch * sizeof(int32_t));
+  // With H2O (a decode step may follow), room for the control words of an
+  // in-place eviction to any budget up to the capacity.
+  const size_t ip_words = with_h2o && !c->block_size ? evict_inplace_words_bound(*c, c->capacity) : 0;
+  g->total = g->off_ip + align256(ip_words * sizeof(int32_t));
   return KVC_OK;
 }
 
@@ -317,6 +321,8 @@ int32_t prepare_attn(const kvc_cache_t* cache, const void* k_new, const void* v_
   a->tier_parts = g.tier_parts;
   a->parts = g.splits + g.tier_parts;
   a->qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
+  a->zero_words = nullptr;
+  a->zero_count = 0;
   return KVC_OK;
 }
 
@@ -354,7 +360,8 @@ int32_t check_workspace_disjoint(const void* ws, size_t ws_bytes, const kvc_cach
 // (`max_len` is the largest length the eviction sees).
 int32_t check_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budget, int32_t n_sink, int32_t n_recent,
                     const uint8_t* keep_mask, const int32_t* keep_index, const kvc_cache_t* dst,
-                    const float* dst_score, int32_t max_len, const void* workspace, size_t ws_bytes) {
+                    const float* dst_score, int32_t max_len, const void* workspace, size_t ws_bytes,
+                    bool in_place = false) {
   int32_t st = check_compact_pair(src, dst, nullptr, nullptr);
   if (st) return st;
   if (!h2o_score || !keep_index) return fail(KVC_ERR_INVALID_ARG, "h2o_score and keep_index must not be NULL");
@@ -366,6 +373,26 @@ int32_t check_evict(const kvc_cache_t* src, const float* h2o_score, int32_t budg
   if (max_len < 0) return fail(KVC_ERR_INVALID_ARG, "max_len_hint must be >= 0");
   if (max_len > src->capacity) return fail(KVC_ERR_CAPACITY, "max_len_hint exceeds capacity");
   const size_t rows = (size_t)src->batch * src->num_kv_heads;
+  if (in_place) {
+    // The cache is its own destination: every dst buffer is the cache's; the
+    // keep outputs (written during the step) overlap none of them.
+    const bool same = dst->k_codes == src->k_codes && dst->v_codes == src->v_codes && dst->k_scale == src->k_scale &&
+                      dst->v_scale == src->v_scale && dst->positions == src->positions &&
+                      dst->lengths == src->lengths && dst->num_seen == src->num_seen && dst_score == h2o_score;
+    if (!same)
+      return fail(KVC_ERR_INVALID_ARG, "in place, every dst buffer must be the cache's own and dst_score h2o_score");
+    const size_t slots = rows * src->capacity;
+    const void* bufs[] = {src->k_codes, src->v_codes, src->k_scale, src->v_scale, src->positions, h2o_score,
+                          src->lengths, src->num_seen, keep_mask};
+    const size_t lens[] = {slots * k_row_bytes(*src), slots * v_row_bytes(*src), slots * 4, slots * 4, slots * 4,
+                           slots * 4, (size_t)src->batch * 4, (size_t)src->batch * 4, keep_mask ? slots : 0};
+    for (int i = 0; i < 9; ++i) {
+      if (overlap(keep_index, rows * budget * sizeof(int32_t), bufs[i], lens[i]) ||
+          (i < 8 && overlap(keep_mask, keep_mask ? slots : 0, bufs[i], lens[i])))
+        return fail(KVC_ERR_INVALID_ARG, "keep_index or keep_mask overlaps a cache buffer, the scores or each other");
+    }
+    return KVC_OK;
+  }
   if ((st = check_out_of_place(src, h2o_score, keep_index, rows * budget * sizeof(int32_t), dst, dst_score, workspace,
                                ws_bytes)))
     return st;
@@ -703,8 +730,9 @@ int32_t decode_step_call(const kvc_cache_t* cache, const void* k_new, const void
   if ((st = prepare_attn(cache, k_new, v_new, q, num_q_heads, out, h2o_score, max_len_hint + 1, workspace,
                          workspace_bytes, &a)))
     return st;
+  const bool in_place = dst && dst->k_codes == cache->k_codes;
   if ((st = check_evict(cache, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,
-                        max_len_hint + 1, workspace, workspace_bytes)))
+                        max_len_hint + 1, workspace, workspace_bytes, in_place)))
     return st;
   const size_t rows = (size_t)cache->batch * cache->num_kv_heads;
   if ((st = check_workspace_disjoint(workspace, workspace_bytes, cache, h2o_score, dst, dst_score, keep_index,
@@ -713,6 +741,55 @@ int32_t decode_step_call(const kvc_cache_t* cache, const void* k_new, const void
   const hipStream_t s = static_cast<hipStream_t>(stream);
   EvictArgs e = evict_args(cache, h2o_score, budget, n_sink, n_recent, keep_mask, keep_index, dst, dst_score,
                            max_len_hint + 1);
+  if (in_place) {
+    // The split kernel clears the control words; then one eviction launch
+    // selects and moves in place (merging the splits when it can, else after
+    // the merge kernel). Rows past one launch's selection are selected by the
+    // selection kernel first and only moved by the in-place launch.
+    AttnGeom g;
+    if ((st = attn_geometry(cache, num_q_heads, max_len_hint + 1, 1, &g))) return st;
+    // Moving workgroups: about one CU each with the selectors (so that every
+    // workgroup of the launch is resident at once), each moving
+    // kInplaceMinPasses to kInplaceMaxPasses passes of rows.
+    // Movers cover the larger of the budget (destinations) and the longest
+    // row (sources).
+    const long long rows_ip = (long long)cache->batch * cache->num_kv_heads;
+    const long long rpp = evict_inplace_rows_per_pass(*cache);
+    const long long cover = std::max<long long>(budget, e.max_len);
+    const long long movers = std::max(1LL, device_cus() / rows_ip - 1);
+    const int passes = (int)std::min<long long>(kInplaceMaxPasses(std::max(k_row_bytes(*cache), v_row_bytes(*cache))),
+                                                std::max<long long>(kInplaceMinPasses, (cover + movers * rpp - 1) /
+                                                                                           (movers * rpp)));
+    const int chunks = (int)((cover + passes * rpp - 1) / (passes * rpp));
+    int32_t* ip = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + g.off_ip);
+    a.zero_words = ip;
+    a.zero_count = (int)(1 + rows_ip + rows_ip * chunks + rows_ip * kInplaceMaxEvicted);
+    e.ip = ip;
+    e.ip_chunks = chunks;
+    e.ip_passes = passes;
+    e.stash = a.stash;
+    if (evict_fits_one_launch(e.max_len, n_sink, n_recent) &&
+        evict_inplace_can_merge(num_q_heads, cache->num_kv_heads, a.parts)) {
+      if ((st = device_status(launch_attn_split(a, s), "kvc_decode_step split launch"))) return st;
+      e.part_o = a.part_o;
+      e.part_ml = a.part_ml;
+      e.logits = a.logits;
+      e.out = out;
+      e.num_q_heads = num_q_heads;
+      e.splits = a.parts;
+      e.span = attn_span(a);
+      return device_status(launch_evict_inplace(e, s), "kvc_decode_step in-place eviction launch");
+    }
+    if ((st = device_status(launch_decode_attn(a, s), "kvc_decode_step attention launch"))) return st;
+    if (!evict_fits_one_launch(e.max_len, n_sink, n_recent)) {
+      if ((st = device_status(launch_select(e.c, e.score, budget, n_sink, n_recent, e.mask, e.keep_index, e.max_len,
+                                            s),
+                              "kvc_decode_step selection launch")))
+        return st;
+      e.ip_preselected = 1;
+    }
+    return device_status(launch_evict_inplace(e, s), "kvc_decode_step in-place eviction launch");
+  }
   if (evict_fits_one_launch(e.max_len, n_sink, n_recent) &&
       evict_can_merge(num_q_heads, cache->num_kv_heads, a.parts)) {
     // Two launches: the split kernel (with the append), then the eviction

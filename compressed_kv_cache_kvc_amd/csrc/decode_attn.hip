@@ -668,34 +668,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((
       // (+ 8), channels 8h..8h+7 of the block; lane col then holds channel col
       // of those 8 tokens.
       const int tr_row = quad * 16 + (col >> 1), tr_col = (col & 1) * 8;
+      i32x4 aw[NRS][CH];
 #pragma unroll
-      for (int rs = 0; rs < NRS; ++rs) {
-        i32x4 aw[CH];
+      for (int rs = 0; rs < NRS; ++rs)
 #pragma unroll
-        for (int ci = 0; ci < CH; ++ci) aw[ci] = *reinterpret_cast<const i32x4*>(&w_limb[wave][ci][rs][col][quad * 16]);
-        // LEAN: every channel block's MFMA is issued before the first sum is
-        // read, so no MFMA result is waited for right after its issue.
-        constexpr int NPV = LEAN ? NCB : 1;
-        i32x4 pvs[NPV];
+        for (int ci = 0; ci < CH; ++ci)
+          aw[rs][ci] = *reinterpret_cast<const i32x4*>(&w_limb[wave][ci][rs][col][quad * 16]);
+      // Each channel block's V is read once and serves every row set. LEAN:
+      // every channel block's MFMA is issued before the first sum is read, so
+      // no MFMA result is waited for right after its issue.
+      constexpr int NPV = LEAN ? NCB : 1;
+      i32x4 pvs[NPV];
 #pragma unroll
-        for (int m = 0; m < NCB; ++m) {
-          i32x4 pv = i32x4{0, 0, 0, 0};
+      for (int m = 0; m < NCB; ++m) {
+        i32x4 pv[NRS];
 #pragma unroll
-          for (int ci = 0; ci < CH; ++ci) {
-            if (ci >= ncur) continue;
-            uint8_t* p0 = &v_stage[ci][wave][tr_row * VROW + vchunk(tr_row, m) * 16 + tr_col];
-            uint8_t* p1 = &v_stage[ci][wave][(tr_row + 8) * VROW + vchunk(tr_row + 8, m) * 16 + tr_col];
-            const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p0);
-            const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p1);
-            pv = mfma(aw[ci], i32x4{lo[0], lo[1], hi[0], hi[1]}, pv);
-          }
-          if constexpr (LEAN) pvs[m] = pv;
-          else o_acc[rs][m] = fmaf(o_acc[rs][m], corr[rs], wscale[rs] * limb_sum(pv));
+        for (int rs = 0; rs < NRS; ++rs) pv[rs] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ci = 0; ci < CH; ++ci) {
+          if (ci >= ncur) continue;
+          uint8_t* p0 = &v_stage[ci][wave][tr_row * VROW + vchunk(tr_row, m) * 16 + tr_col];
+          uint8_t* p1 = &v_stage[ci][wave][(tr_row + 8) * VROW + vchunk(tr_row + 8, m) * 16 + tr_col];
+          const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p0);
+          const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p1);
+          const i32x4 vb = i32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int rs = 0; rs < NRS; ++rs) pv[rs] = mfma(aw[rs][ci], vb, pv[rs]);
         }
         if constexpr (LEAN) {
+          pvs[m] = pv[0];
+        } else {
 #pragma unroll
-          for (int m = 0; m < NCB; ++m) o_acc[rs][m] = fmaf(o_acc[rs][m], corr[rs], wscale[rs] * limb_sum(pvs[m]));
+          for (int rs = 0; rs < NRS; ++rs) o_acc[rs][m] = fmaf(o_acc[rs][m], corr[rs], wscale[rs] * limb_sum(pv[rs]));
         }
+      }
+      if constexpr (LEAN) {
+#pragma unroll
+        for (int m = 0; m < NCB; ++m) o_acc[0][m] = fmaf(o_acc[0][m], corr[0], wscale[0] * limb_sum(pvs[m]));
       }
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -762,6 +771,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((
   if (app && s == 0 && g == 0 && tid == 0) {
     a.stash[b] = L_old;
     a.stash[c.batch + b] = c.num_seen[b];
+  }
+  // Control words of a later in-place eviction in the same step: cleared
+  // last, after every load this workgroup waits for.
+  if (a.zero_count) {
+    const long long nthreads = (long long)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+    const long long flat =
+        ((long long)(blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    for (long long i = flat; i < a.zero_count; i += nthreads) a.zero_words[i] = 0;
   }
 }
 

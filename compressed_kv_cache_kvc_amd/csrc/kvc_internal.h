@@ -82,6 +82,10 @@ struct AttnLaunch {
   int tier_parts;    // TP: fp16-tier partial states per (sequence, query head), after the S splits
   int parts;         // S + TP: partial states per query head in part_o / part_ml
   float qk_log2;     // log2(e) / sqrt(head_dim)
+  // Words the split kernel sets to zero (NULL: none): the control words of an
+  // in-place eviction later in the same decode step.
+  int32_t* zero_words;
+  int zero_count;
 };
 // Logit slots per query head: the tiles of all splits.
 __host__ __device__ inline long long attn_span(const AttnLaunch& a) {
@@ -123,12 +127,53 @@ struct EvictArgs {
   float* out;
   int num_q_heads, splits;
   long long span;
+  // In-place eviction (dst is the source cache; NULL: out of place): control
+  // words, zero on entry (ticket, per-row and per-chunk flags, then per-row
+  // first moved slot), and whether a selection kernel already wrote the keep
+  // list (the workgroups then only move rows).
+  int32_t* ip;
+  int ip_chunks;      // moving workgroups per row
+  int ip_passes;      // passes per moving workgroup
+  int ip_preselected;
 };
 constexpr int kEvictMaxMergeHeads = 4;  // query heads per KV head
 constexpr int kEvictMaxSplits = 1024;
 bool evict_fits_one_launch(int max_len, int n_sink, int n_recent);
 bool evict_can_merge(int num_q_heads, int num_kv_heads, int splits);
 hipError_t launch_evict(const EvictArgs& a, hipStream_t st);
+// In-place eviction. A moving workgroup (kEvictThreads threads, one 16-byte
+// access each per pass and row part) takes the kept entries of `passes`
+// times evict_inplace_rows_per_pass consecutive destination slots.
+// Control words: a ticket, a flag per row, a flag per (row, chunk), the
+// row's first kInplaceMaxEvicted evicted slots, then its first moved slot;
+// all but the last `rows` words must be zero when it starts.
+constexpr int kEvictThreads = 1024;
+constexpr int kInplaceMinPasses = 4;
+// Passes of codes held in registers: 10 for 128-byte rows; fewer for shorter
+// rows, whose passes cover more entries and so more scales, positions,
+// scores and logits per thread.
+__host__ __device__ constexpr int kInplaceMaxPasses(int row_bytes) {
+  return row_bytes >= 128 ? 10 : row_bytes >= 64 ? 8 : 4;
+}
+// Rows with at most this many evicted slots are moved by workgroups that load
+// their rows before the selection is known.
+constexpr int kInplaceMaxEvicted = 64;
+inline int evict_inplace_rows_per_pass(const kvc_cache_t& c) {
+  const int rb = k_row_bytes(c) > v_row_bytes(c) ? k_row_bytes(c) : v_row_bytes(c);
+  return kEvictThreads * 16 / rb;
+}
+// Control words for any pass count and any budget up to `budget`.
+inline size_t evict_inplace_words_bound(const kvc_cache_t& c, int budget) {
+  const size_t rows = (size_t)c.batch * c.num_kv_heads;
+  const size_t chunk = (size_t)kInplaceMinPasses * evict_inplace_rows_per_pass(c);
+  return 1 + rows + rows * (((size_t)budget + chunk - 1) / chunk) + rows * kInplaceMaxEvicted + rows;
+}
+// The in-place launch merges the attention splits for up to 8 query heads per
+// KV head.
+inline bool evict_inplace_can_merge(int num_q_heads, int num_kv_heads, int splits) {
+  return num_q_heads / num_kv_heads <= 8 && (long long)splits <= kEvictMaxSplits;
+}
+hipError_t launch_evict_inplace(const EvictArgs& a, hipStream_t st);
 
 hipError_t launch_compact(const kvc_cache_t& src, const float* src_score, const uint8_t* mask,
                           const kvc_cache_t& dst, float* dst_score, int32_t* counts, int chunks,

@@ -26,8 +26,10 @@ __device__ __forceinline__ float part_weight(float m_part, float m_total) {
 }
 
 // Split states of one head as a wave holds them: lane l has splits
-// l + 64 r, r < kStatRegs (m = -inf and l = 0 past S); splits past 64 *
-// kStatRegs are read again by split_stats.
+// l + 64 r, r < kStatRegs, as loaded (a clamped split past S; split_stats
+// masks them); splits past 64 * kStatRegs are read again by split_stats.
+// Nothing here uses the loaded values, so a caller's later loads are not held
+// behind these.
 constexpr int kStatRegs = 4;
 struct SplitML {
   float m[kStatRegs], l[kStatRegs];
@@ -38,10 +40,9 @@ __device__ __forceinline__ SplitML load_split_ml(const float* ml, int S) {
   SplitML r;
 #pragma unroll
   for (int q = 0; q < kStatRegs; ++q) {
-    const int sp = lane + 64 * q;
-    const float m = ml[2 * min(sp, S - 1)], l = ml[2 * min(sp, S - 1) + 1];  // unconditional loads
-    r.m[q] = sp < S ? m : -INFINITY;
-    r.l[q] = sp < S ? l : 0.f;
+    const int sp = min(lane + 64 * q, S - 1);
+    r.m[q] = ml[2 * sp];
+    r.l[q] = ml[2 * sp + 1];
   }
   return r;
 }
@@ -51,9 +52,16 @@ __device__ __forceinline__ SplitML load_split_ml(const float* ml, int S) {
 // over the splits: the global max m and 1/l (0 for an empty head); fac[s] (may
 // be NULL) receives each split's output weight exp2(m_s - m) / l. Each lane
 // accumulates its splits in increasing order; padded entries add exactly 0.
-__device__ __forceinline__ void split_stats(const SplitML& r, const float* ml, int S, float* fac, float& m_out,
+__device__ __forceinline__ void split_stats(const SplitML& raw, const float* ml, int S, float* fac, float& m_out,
                                             float& inv_out) {
   const int lane = threadIdx.x & 63;
+  SplitML r;  // m = -inf and l = 0 past S
+#pragma unroll
+  for (int q = 0; q < kStatRegs; ++q) {
+    const bool in = lane + 64 * q < S;
+    r.m[q] = in ? raw.m[q] : -INFINITY;
+    r.l[q] = in ? raw.l[q] : 0.f;
+  }
   float m = -INFINITY;
 #pragma unroll
   for (int q = 0; q < kStatRegs; ++q) m = fmaxf(m, r.m[q]);

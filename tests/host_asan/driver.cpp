@@ -152,6 +152,27 @@ static void test_eviction() {
                                 (int32_t*)kidx, &d, (float*)dscore, 8191, nullptr) == KVC_OK);
   CHECK(kvc_decode_step_noalloc(&s, kn, vn, q, Hq, (float*)out, (float*)score, budget, 4, 1024, (uint8_t*)mask,
                                 (int32_t*)kidx, &d, (float*)dscore, 9000, nullptr) == KVC_ERR_CAPACITY);
+  // In place (the cache is its own destination): one launch after the split
+  // when the rows fit it, else the merge and selection kernels first.
+  int n0 = kvc_stub_launches;
+  CHECK(kvc_decode_step(&s, kn, vn, q, Hq, (float*)out, (float*)score, budget, 4, 1024, (uint8_t*)mask,
+                        (int32_t*)kidx, &s, (float*)score, 8191, fake(), need, nullptr) == KVC_OK);
+  CHECK(kvc_stub_launches == n0 + 2);
+  n0 = kvc_stub_launches;
+  kvc_cache_t big = cache(8, B, H, 128, 12000);
+  const size_t need_long = kvc_decode_attn_workspace_bytes(&big, Hq, 11000, 1);
+  void *bscore = fake(), *bmask = fake();
+  CHECK(kvc_decode_step(&big, kn, vn, q, Hq, (float*)out, (float*)bscore, budget, 4, 1024, (uint8_t*)bmask,
+                        (int32_t*)kidx, &big, (float*)bscore, 10999, fake(), need_long, nullptr) == KVC_OK);
+  CHECK(kvc_stub_launches == n0 + 3);
+  CHECK(kvc_decode_step_noalloc(&s, kn, vn, q, Hq, (float*)out, (float*)score, budget, 4, 1024, (uint8_t*)mask,
+                                (int32_t*)kidx, &s, (float*)score, 8191, nullptr) == KVC_OK);
+  kvc_cache_t part = s;
+  part.v_codes = d.v_codes;  // shares only some buffers with the cache
+  n0 = kvc_stub_launches;
+  CHECK(kvc_decode_step(&s, kn, vn, q, Hq, (float*)out, (float*)score, budget, 4, 1024, (uint8_t*)mask,
+                        (int32_t*)kidx, &part, (float*)score, 8191, fake(), need, nullptr) == KVC_ERR_INVALID_ARG);
+  CHECK(kvc_stub_launches == n0);
   // Block eviction on a paged cache.
   kvc_cache_t p = cache(8, 3, 4, 128, 512), pd;
   p.block_size = 16;

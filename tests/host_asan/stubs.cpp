@@ -38,6 +38,7 @@ bool evict_can_merge(int num_q_heads, int num_kv_heads, int splits) {
   return num_q_heads / num_kv_heads <= kEvictMaxMergeHeads && splits <= kEvictMaxSplits;
 }
 hipError_t launch_evict(const EvictArgs&, hipStream_t) { return launched(); }
+hipError_t launch_evict_inplace(const EvictArgs&, hipStream_t) { return launched(); }
 hipError_t launch_compact(const kvc_cache_t&, const float*, const uint8_t*, const kvc_cache_t&, float*, int32_t*, int,
                           hipStream_t) {
   return launched();

@@ -277,6 +277,17 @@ def test_compact_validation():
     assert step(d_=bad) == INVALID
     assert step(w=0x1100000) == INVALID               # workspace overlaps dst codes
     assert step(s_=paged) == UNSUPPORTED
+    # In place (dst = the cache): every dst buffer must be the cache's and the
+    # kept scores the step's scores; the keep outputs overlap no cache buffer.
+    # (Only refusals here: a valid call would enqueue kernels.)
+    assert step(d_=src, dsc=0x4100000) == INVALID     # kept scores elsewhere
+    half = desc(k_codes=0x100000, v_codes=0x1200000, k_scale=0x300000, v_scale=0x400000,
+                positions=0x500000, lengths=0x600000, num_seen=0x600100)
+    assert step(d_=half, dsc=0x4000000) == INVALID    # dst shares the K codes only
+    assert step(d_=src, dsc=0x4000000, idx=0x100000 + 64) == INVALID     # keep list inside the K codes
+    assert step(d_=src, dsc=0x4000000, mask=0x4000000) == INVALID        # mask over the scores
+    assert step(d_=src, dsc=0x4000000, idx=0x5000000, mask=0x5000000) == INVALID  # list and mask overlap
+    assert step(d_=src, dsc=0x4000000, w=0x300000) == INVALID            # workspace overlaps the scales
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 512) >= 4 * 1 * 4
     assert lib.kvc_compact_workspace_bytes(ctypes.byref(src), 2048) == 0   # beyond capacity
 
@@ -408,10 +419,21 @@ def _a256(n):
     return (n + 255) // 256 * 256
 
 
-def _attn_ws(B, Hq, D, P, span):
+def _ip_words(B, H, D, bits, cap):
+    """Control words of an in-place eviction to any budget up to the capacity:
+    a ticket, a flag per row and per (row, chunk), a first moved slot and 64
+    evicted slots per row; a chunk is 4 passes of 1024 * 16 / row-bytes rows."""
+    chunk = 4 * (1024 * 16 // (D * bits // 8))
+    rows = B * H
+    return 1 + rows + rows * -(-cap // chunk) + rows + rows * 64
+
+
+def _attn_ws(B, Hq, D, P, span, H=1, bits=8, cap=0):
     """Workspace of one attention call: split partials o [B][Hq][P][D], their
-    (m, l), spilled logits [B][Hq][span], the two per-sequence stash words."""
-    return _a256(B * Hq * P * D * 4) + _a256(B * Hq * P * 2 * 4) + _a256(B * Hq * span * 4) + _a256(2 * B * 4)
+    (m, l), spilled logits [B][Hq][span], the two per-sequence stash words,
+    and (with H2O) the in-place eviction's control words."""
+    return (_a256(B * Hq * P * D * 4) + _a256(B * Hq * P * 2 * 4) + _a256(B * Hq * span * 4) + _a256(2 * B * 4)
+            + _a256(_ip_words(B, H, D, bits, cap) * 4))
 
 
 @pytest.mark.parametrize("name,B,H,Hq,D,cap,hint,tiers,P,span", [
@@ -430,10 +452,11 @@ def test_attention_workspace_follows_the_split_geometry(name, B, H, Hq, D, cap, 
              k_recent16=0x8200000, v_recent16=0x8300000) if tiers[0] or tiers[1] else {}
     d = desc(batch=B, num_kv_heads=H, head_dim=D, capacity=cap, **T)
     got = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), Hq, hint, 1)
-    assert got == _attn_ws(B, Hq, D, P, span), (name, got, _attn_ws(B, Hq, D, P, span))
-    # without H2O there is no logit spill
+    want = _attn_ws(B, Hq, D, P, span, H, d.bits, cap)
+    assert got == want, (name, got, want)
+    # without H2O there is no logit spill and no eviction follows
     got0 = lib.kvc_decode_attn_workspace_bytes(ctypes.byref(d), Hq, hint, 0)
-    assert got0 == got - _a256(B * Hq * span * 4), name
+    assert got0 == got - _a256(B * Hq * span * 4) - _a256(_ip_words(B, H, D, d.bits, cap) * 4), name
 
 
 def test_decode_step_noalloc_validation():

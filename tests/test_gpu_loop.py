@@ -64,3 +64,45 @@ def test_decode_step_loop_llama7b_full_size():
     # a correct keep-set) must stay rare.
     print(f"{ambiguous} of {candidates} candidates within the threshold band", flush=True)
     assert ambiguous <= candidates // 100, (ambiguous, candidates)
+
+
+def test_decode_step_in_place_loop_qwen_full_size():
+    """The GQA stream's decode loop in place at full size: 8 sequences, 28
+    query / 4 KV heads, 32767 prefilled tokens; each kvc_decode_step names the
+    cache as its own destination. Step 0 evicts 32768 -> 8192 (the selection
+    kernel, then the in-place moves); the next steps run the steady state
+    (8193 -> 8192, one launch that merges, selects and moves). Each step is
+    checked against the oracle as above."""
+    steps = 4
+    w = get("qwen_gqa_stream").scaled(steps=steps)
+    d = draw(w)
+    B, Hq, H, D, L, bits = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.context, w.bits
+    budget, S, R = w.budget, w.n_sink, w.n_recent
+    print(f"[loop in place] Qwen GQA stream, {steps} decode steps, budget {budget}", flush=True)
+    gc = kvc.KVCache(B, H, D, L, bits)
+    score = gc.score_buffer()
+    ref = oracle.RefCache(B, H, D, L, bits)
+    kvc.kvc_quant_append(gc, dev(d["k"][:, :, :L - 1]), dev(d["v"][:, :, :L - 1]), h2o_score=score)
+    ref.append(d["k"][:, :, :L - 1], d["v"][:, :, :L - 1])
+    kidx = torch.zeros((B, H, budget), dtype=torch.int32, device="cuda")
+    mask = torch.zeros((B, H, L), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    ambiguous = candidates = 0
+    for i in range(steps):
+        mask.zero_()
+        kvc.kvc_decode_step(gc, dev(d["step_k"][i]), dev(d["step_v"][i]), dev(d["step_q"][i]), out, score, budget,
+                            S, R, kidx, gc, score, keep_mask=mask, max_len_hint=int(ref.lengths.max()))
+        ref.append(d["step_k"][i], d["step_v"][i])
+        ro, _ = ref.attend(d["step_q"][i])
+        candidates += B * H * (int(ref.lengths.max()) - S - R)
+        torch.cuda.synchronize()
+        err = assert_out_close(host(out), ro)
+        m = host(mask)
+        ambiguous += assert_keep_equivalent(m, ref.score, ref.lengths, budget, S, R)
+        ref.compact(m[:, :, :L].astype(bool))
+        assert_codes_equal(gc, ref)
+        rel = assert_scores_close(host(score), ref.score, ref.lengths)
+        print(f"step {i}: length {int(ref.lengths[0])}, max-abs out err {err:.2e}, score rel err {rel:.2e}",
+              flush=True)
+    print(f"{ambiguous} of {candidates} candidates within the threshold band", flush=True)
+    assert ambiguous <= candidates // 100, (ambiguous, candidates)

@@ -464,6 +464,63 @@ def test_decode_step_bit_exact(hq, hkv, bits, D, lens, budget, S, R, with_mask):
     _oracle_step_check(w, d, lens, cap, seed, budget, S, R, oB, dB, sB, kB, mB if with_mask else None)
 
 
+@pytest.mark.parametrize("hq,hkv,bits,D,lens,budget,S,R,with_mask", [
+    (28, 4, 8, 128, [1000, 1000, 990], 1000, 4, 256, True),      # GQA 7: one token evicted, one row within budget
+    (28, 4, 8, 128, [1002, 1040, 999], 1000, 4, 256, True),      # 3 evicted (repeated minimum), 41 (radix), none
+    (4, 2, 4, 128, [701, 700, 650], 700, 4, 64, False),          # INT4, GQA 2: 2 and 1 evicted
+    (8, 1, 8, 128, [5000, 5000], 5000, 4, 2048, True),           # GQA 8, ten chunks of 512 rows per row
+    (4, 4, 8, 128, [2999, 1000, 500], 1000, 4, 100, True),       # MHA, most tokens evicted
+    (4, 2, 4, 128, [2000, 1999, 100], 700, 4, 64, False),        # INT4, GQA 2, no mask
+    (8, 4, 8, 64, [1500, 1400, 1300], 500, 0, 64, True),         # D = 64, no sinks
+    (4, 4, 8, 128, [1200, 1100, 1000], 1028, 4, 1024, True),     # no heavy hitters
+    (4, 4, 8, 128, [800, 700, 600], 600, 4, 0, True),            # no recent window
+    (32, 2, 8, 128, [2000, 1500, 1000], 600, 4, 64, True),       # GQA 16: merge kernel, then the in-place launch
+    (4, 4, 8, 64, [20000, 19000, 100], 5000, 4, 256, True),      # long rows: selection kernel, then the moves
+    # 72 rows of 4 workgroups each: more workgroups than CUs
+    (32, 8, 8, 128, [1200, 300, 1100, 499, 800, 1000, 200, 1300, 650], 1100, 4, 64, True),
+])
+def test_decode_step_in_place(hq, hkv, bits, D, lens, budget, S, R, with_mask):
+    """kvc_decode_step with the cache as its own destination: the kept tokens
+    move down in place. Output, keep list, mask, codes, scales, positions,
+    lengths, token counts and kept scores equal those of the out-of-place step
+    bit for bit, and the oracle's decode step."""
+    print(f"[step in place] hq={hq} hkv={hkv} bits={bits} D={D} lens={lens} budget={budget} R={R}", flush=True)
+    w = get("tiny_mha").scaled(context=max(lens) + 1, batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                               head_dim=D, bits=bits)
+    cap, seed = max(lens) + 1 + 11, budget + hq + 1
+    d, ((gA, sA), (gB, sB)) = _step_caches(w, lens, cap, seed=seed)
+    B, H, Lmax = len(lens), hkv, max(lens)
+    knew, vnew, q = dev(d["k"][:, :, Lmax:Lmax + 1]), dev(d["v"][:, :, Lmax:Lmax + 1]), dev(d["q"])
+    res = []
+    for gc, sc, in_place in ((gA, sA, False), (gB, sB, True)):
+        dst, dsc = (gc, sc) if in_place else (make_gpu_cache(w, cap), None)
+        if dsc is None:
+            dsc = dst.score_buffer()
+        kidx = torch.full((B, H, budget), -5, dtype=torch.int32, device="cuda")
+        mask = torch.full((B, H, cap), 7, dtype=torch.uint8, device="cuda") if with_mask else None
+        out = torch.empty((B, hq, D), dtype=torch.float32, device="cuda")
+        kvc.kvc_decode_step(gc, knew, vnew, q, out, sc, budget, S, R, kidx, dst, dsc, keep_mask=mask,
+                            max_len_hint=Lmax)
+        res.append((out, dst, dsc, kidx, mask))
+    torch.cuda.synchronize()
+    (oA, dA, dsA, kA, mA), (oB, dB, dsB, kB, mB) = res
+    assert torch.equal(oA, oB)
+    assert torch.equal(kA, kB)
+    if with_mask:
+        assert torch.equal(mA, mB)
+    new_len = host(dA.lengths)
+    assert host(dB.lengths).tolist() == new_len.tolist() == [min(n + 1, budget) for n in lens]
+    assert torch.equal(dA.num_seen, dB.num_seen)
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "positions"):
+        a, b = host(getattr(dA, name)), host(getattr(dB, name))
+        for i in range(B):
+            assert np.array_equal(a[i, :, :new_len[i]], b[i, :, :new_len[i]]), (name, i)
+    a, b = host(dsA), host(dsB)
+    for i in range(B):
+        assert np.array_equal(a[i, :, :new_len[i]].view(np.uint32), b[i, :, :new_len[i]].view(np.uint32)), i
+    _oracle_step_check(w, d, lens, cap, seed, budget, S, R, oB, dB, dsB, kB, mB if with_mask else None)
+
+
 def test_decode_step_llama7b_full_size():
     """The benchmarked step at full size (8191 cached tokens + the new one,
     32 heads, keep 2457): kvc_decode_step equals the two calls bit for bit."""
