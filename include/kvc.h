@@ -13,7 +13,8 @@
  *                     (kvc_compact_gather: from the keep list instead;
  *                     kvc_h2o_evict: selection and compaction in one call)
  *   kvc_decode_step   the whole step (append, attention, H2O, eviction) in
- *                     one call of two launches
+ *                     one call of two launches, into another cache or in
+ *                     place
  * and a host-side paged block pool (kvc_pool_*) that yields block tables.
  *
  * Conventions shared by every call:
@@ -389,9 +390,27 @@ int32_t kvc_h2o_evict(const kvc_cache_t* src, const float* h2o_score, int32_t bu
  * bounds the lengths before the append; the workspace is that of
  * kvc_append_decode_attn (kvc_decode_attn_workspace_bytes(cache, num_q_heads,
  * max_len_hint + 1, 1)) and must not overlap any cache buffer.
+ *
+ * In place: `dst` may describe `cache` itself (every buffer the same, and
+ * dst_score == h2o_score). The kept tokens then keep their order and move
+ * down to their rank inside the cache, so only those past the first evicted
+ * slot are rewritten (a decode loop that evicts one token per step moves
+ * about half a row instead of copying all of it; tutorial section 2.2's
+ * sorted keep, applied where the tokens are). Output, keep_index, keep_mask,
+ * lengths, num_seen and, below the new length, codes, scales, positions and
+ * scores equal those of the same step into a separate dst bit for bit; slots
+ * at or past the new length hold stale tokens. Launches: the split kernel,
+ * then one in-place eviction kernel that merges the splits (up to 8 query
+ * heads per KV head), selects and moves; with more query heads the merge
+ * kernel runs first, and with more than 8192 candidates the selection kernel
+ * too. Its workgroups order their reads and writes of the cache through flags
+ * in the workspace, so the workspace must not be shared with a concurrent
+ * call.
  * Errors: those of kvc_append_decode_attn and kvc_h2o_evict (with
  * max_len_hint + 1 as the eviction's hint), and INVALID_ARG for a NULL
- * h2o_score or dst_score.
+ * h2o_score or dst_score, a dst that shares some but not all of the cache's
+ * buffers, an in-place dst_score other than h2o_score, or a keep_index or
+ * keep_mask that overlaps a cache buffer, the scores or each other.
  */
 int32_t kvc_decode_step(const kvc_cache_t* cache, const void* k_new, const void* v_new, const void* q,
                         int32_t num_q_heads, float* out, float* h2o_score, int32_t budget,
