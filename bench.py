@@ -58,8 +58,10 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-TRAFFIC_SHA256 = None   # sources the counters were taken on (None: no measurement yet)
-TRAFFIC_BYTES = None
+# FETCH_SIZE 33,913.2 KiB x 1.9993 + WRITE_SIZE 1,308.03 KiB per launch
+# on the LLaMA-7B layer, with the copy calibration above.
+TRAFFIC_SHA256 = "3cdf8214245394af950e94c3b94ec337ca3cd81d005ffcfcae68cce40a0d885c"
+TRAFFIC_BYTES = 70769290
 
 
 def attention_traffic():
@@ -73,6 +75,8 @@ def traffic_sources_sha256():
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
 HBM_PEAK_GBPS = 8000.0
 LAYERS = 32
 
@@ -490,6 +494,58 @@ def secondary_attention(kvc, torch, reps=16):
     return res
 
 
+def kernel_case(kvc, torch, name, reps=16):
+    """16 eager launches of one case of the GQA stream's steady state (8
+    sequences, 28 query / 4 KV heads, 8193 tokens, H2O on) over 8 rotated
+    caches, for a profiler's kernel trace and counters: `qwen_attention` is
+    kvc_decode_attn (split, merge); `qwen_step_in_place` is kvc_decode_step
+    with the cache as its own destination (split, in-place eviction)."""
+    from workloads import get
+    w = get("qwen_gqa_stream")
+    B, Hq, H, D, Lk, n_bufs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.budget, 8
+    L = Lk + 1
+    lengths = torch.zeros((n_bufs, B), dtype=torch.int32, device="cuda")
+    seen = torch.zeros((n_bufs, B), dtype=torch.int32, device="cuda")
+    caches, scores = [], []
+    for i in range(n_bufs):
+        c = kvc.KVCache(B, H, D, L, w.bits)
+        c.lengths, c.num_seen = lengths[i], seen[i]
+        c.desc = c._make_desc()
+        n = L if name == "qwen_attention" else Lk
+        kv = torch.randn((2, B, H, n, D), device="cuda").half()
+        kvc.kvc_quant_append(c, kv[0], kv[1], max_len_hint=0)
+        del kv
+        caches.append(c)
+        scores.append(c.score_buffer())
+    q = torch.randn((B, Hq, D), device="cuda").half()
+    knew, vnew = torch.randn((B, H, 1, D), device="cuda").half(), torch.randn((B, H, 1, D), device="cuda").half()
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    kidx = torch.empty((B, H, Lk), dtype=torch.int32, device="cuda")
+    ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(caches[0], Hq, L, True), dtype=torch.uint8, device="cuda")
+
+    def launch(i):
+        c, sc = caches[i % n_bufs], scores[i % n_bufs]
+        if name == "qwen_attention":
+            kvc.kvc_decode_attn(c, q, out, h2o_score=sc, max_len_hint=L, workspace=ws)
+        else:
+            if i % n_bufs == 0:
+                lengths.fill_(Lk)
+                seen.fill_(Lk)
+            kvc.kvc_decode_step(c, knew, vnew, q, out, sc, Lk, w.n_sink, w.n_recent, kidx, c, sc, max_len_hint=Lk,
+                                workspace=ws)
+
+    for i in range(n_bufs):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"kernel_case": name, "launches": reps, "us_per_call": round(e0.elapsed_time(e1) * 1e3 / reps, 2)}
+
+
 def _graph_time(torch, fn, stream, reps, before=None):
     """Capture fn() once, then time `reps` replays with events on `stream`
     (before() runs eagerly, untimed, ahead of each replay); returns the mean
@@ -655,6 +711,9 @@ def main(argv=None):
     ap.add_argument("--legs-only", action="store_true",
                     help="instead of the benchmark, run only the configured workloads' other legs (prefill append, "
                          "GQA stream loop, 70B INT4 step) and print them as one JSON line")
+    ap.add_argument("--kernel-case", choices=("qwen_attention", "qwen_step_in_place"), default=None,
+                    help="instead of the benchmark, run 16 launches of one GQA-stream case (8 rotated caches of "
+                         "8193 tokens) for a profiler, and print their mean time")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the benchmark, run 8 plain device-to-device copies of this many MiB "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -662,7 +721,7 @@ def main(argv=None):
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence and KV head with no communication; see DESIGN.md).",
+              "(the path shards by sequence and KV head with no communication between GPUs).",
               file=sys.stderr)
         return 2
 
@@ -673,6 +732,9 @@ def main(argv=None):
     from workloads import draw, get
 
     torch.cuda.set_device(0)
+    if args.kernel_case:
+        print(json.dumps(kernel_case(kvc, torch, args.kernel_case)))
+        return 0
     if args.legs_only:
         print(json.dumps({"config_legs": config_legs(kvc, torch)}))
         return 0

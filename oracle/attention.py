@@ -15,7 +15,7 @@ Sources:
 * Eviction-and-reuse survey (大模型推理 KV 缓存智能驱逐与复用策略), §6: with GQA
   several query heads share one KV head.
 
-Readings (listed in the design doc): every cached token is attended (the query is
+Readings: every cached token is attended (the query is
 the newest token, so no mask applies); no positional transform is applied to
 the cached keys; query head h reads KV head h // (Hq / Hkv).
 

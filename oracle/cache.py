@@ -9,7 +9,7 @@ cache with H2O accumulation (§3.4 of the report), then, when the length exceeds
 the budget, selection and compaction ("KV Cache optimization techniques"
 tutorial, §2.2: append, then evict when over the limit).
 
-Readings (listed in the design doc): a freshly appended slot starts with score 0 and
+Readings: a freshly appended slot starts with score 0 and
 receives the current query's probability in the same step; a slot's position
 is the running count of tokens the sequence has seen.
 """

@@ -16,7 +16,7 @@ Sources:
   tokens are permanent attention sinks; the window holds the most recent tokens;
   a token is a sink or in the window, not both.
 
-Readings (listed in DESIGN.md):
+Readings:
 * Scores are kept per (sequence, KV head); a KV head's score sums the
   probabilities of the query heads that read it.
 * Keep-set = sinks [0, n_sink) + recent [L - n_recent, L) + the k = budget -

@@ -7,7 +7,7 @@ K of every token stays on the GPU and is used to score the query; the full
 V is kept in fp16, hot rows on the GPU and cold rows in host memory, and only
 the V rows of the top-k scored tokens are fetched to form the output.
 
-Readings (listed in DESIGN.md):
+Readings:
 * The scores are the cache's ordinary attention logits, s_i = q . K_i /
   sqrt(D) for every cached token, with K_i the key as that attention reads it:
   code_i * scale_i, or the fp16 row on a cache's fp16 tiers.

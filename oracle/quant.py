@@ -15,7 +15,7 @@ Sources:
 * Same tutorial, section "KV Cache的挑战": bytes per token of KV cache are
   2 x layers x heads x head_dim x bytes per element.
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
 * No epsilon is added to the scale; an all-zero row gets scale 0 and codes 0.
 * The scale is an fp32 number: the correctly rounded fp32 quotient amax/qmax.
 * Each code is round-half-to-even of the correctly rounded fp32 quotient

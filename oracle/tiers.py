@@ -11,7 +11,7 @@ Sources:
   same page's strategy table names this mode "int4_hybrid" (recent fp16,
   distant INT4).
 
-Readings (listed in DESIGN.md):
+Readings:
 * The sink tier is the first ``n_sink16`` slots of a row, the recent tier the
   last ``n_recent16`` slots; a slot in both (a row shorter than the two
   together) belongs to the sink tier, so the recent tier takes the last
