@@ -41,7 +41,9 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
   __shared__ unsigned mm_tmp[32];
   __shared__ int sel[4];
   __shared__ unsigned small[64];
-  __shared__ __align__(16) unsigned stage_lds[REG ? NT * KPT : 1];
+  // Register path: the staged keys. Memory path: one tile of the output pass.
+  __shared__ __align__(16) unsigned stage_lds[NT * KPT];
+  __shared__ int tile_tot[2];
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const long long rowoff = ((long long)b * c.num_kv_heads + g) * c.capacity;
   const float* row = score + rowoff;
@@ -166,35 +168,7 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
   }
   // Candidates: rank the threshold ties in slot order; with a gather list,
   // also count the candidates above T before this thread.
-  int ties = 0, above = 0;
-  if (REG) {
-    // Unused slots hold key 0, never equal to or above T.
-#pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-      ties += any_heavy & (key[q] == T);
-      above += any_heavy & (key[q] > T);
-    }
-  } else {
-    for_own([&](int, unsigned u) {
-      ties += any_heavy & (u == T);
-      above += any_heavy & (u > T);
-    });
-  }
-  // Both prefix counts at once when every count fits 16 bits (ties in the
-  // low half); longer rows scan them separately.
-  int tie_rank, above_before;
-  if (n < 65536) {
-    const int packed = ties | (above << 16);
-    const int before = block_inclusive_scan<NT>(packed, scan_tmp) - packed;
-    tie_rank = before & 0xFFFF;
-    above_before = before >> 16;
-  } else {
-    tie_rank = block_inclusive_scan<NT>(ties, scan_tmp) - ties;
-    above_before = block_inclusive_scan<NT>(above, scan_tmp) - above;
-  }
-  // Kept before this thread = candidates above T before it + ties kept before it.
-  int out = above_before + min(tie_rank, k);
-  for_own([&](int i, unsigned u) {
+  auto decide = [&](int i, unsigned u, int& tie_rank, int& out) {
     uint8_t keepb = 0;
     if (any_heavy) {
       if (u > T) {
@@ -206,7 +180,76 @@ __global__ __launch_bounds__(NT) void select_kernel(kvc_cache_t c, const float* 
     }
     if (m) m[i] = keepb;
     if (kidx && keepb) kidx[lo + out++] = i;
-  });
+  };
+  if (REG) {
+    // Unused slots hold key 0, never equal to or above T; every count fits
+    // 16 bits, so one packed scan gives both prefix counts.
+    int ties = 0, above = 0;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      ties += any_heavy & (key[q] == T);
+      above += any_heavy & (key[q] > T);
+    }
+    const int packed = ties | (above << 16);
+    const int before = block_inclusive_scan<NT>(packed, scan_tmp) - packed;
+    int tie_rank = before & 0xFFFF;
+    // Kept before this thread = candidates above T before it + ties kept before it.
+    int out = (before >> 16) + min(tie_rank, k);
+    for_own([&](int i, unsigned u) { decide(i, u, tie_rank, out); });
+  } else {
+    // Memory path: the candidates in tiles of NT * KPT slots, in order. Each
+    // tile is loaded coalesced into LDS, then every thread takes KPT
+    // consecutive slots of it (so that slot order is tile, thread, key) and
+    // the tile's prefix counts come from one packed block scan, on top of
+    // the counts of the tiles before it. (Reading a thread's own range
+    // straight from memory would touch 64 cache lines per load.)
+    constexpr int TILE = NT * KPT;
+    int run_ties = 0, run_above = 0;  // uniform: counts of the tiles before
+    // The next tile's keys load while this one is processed.
+    float nxt[KPT];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) nxt[j] = row[lo + min(t0 + tid + j * NT, n - 1)];
+    };
+    load_tile(0);
+    for (int t0 = 0; t0 < n; t0 += TILE) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) stage_lds[tid + j * NT] = t0 + tid + j * NT < n ? order_key(nxt[j]) : 0u;
+      if (t0 + TILE < n) load_tile(t0 + TILE);
+      __syncthreads();
+      unsigned kk[KPT];
+#pragma unroll
+      for (int q = 0; q < KPT; q += 4) {
+        const uint4 w = *reinterpret_cast<const uint4*>(stage_lds + tid * KPT + q);
+        kk[q] = w.x;
+        kk[q + 1] = w.y;
+        kk[q + 2] = w.z;
+        kk[q + 3] = w.w;
+      }
+      const int cnt_t = min(max(n - t0 - tid * KPT, 0), KPT);
+      int ties = 0, above = 0;
+#pragma unroll
+      for (int q = 0; q < KPT; ++q) {
+        ties += any_heavy & (q < cnt_t) & (kk[q] == T);
+        above += any_heavy & (q < cnt_t) & (kk[q] > T);
+      }
+      const int packed = ties | (above << 16);  // a tile's counts fit 16 bits
+      const int incl = block_inclusive_scan<NT>(packed, scan_tmp);
+      if (tid == NT - 1) {
+        tile_tot[0] = incl & 0xFFFF;
+        tile_tot[1] = incl >> 16;
+      }
+      const int before = incl - packed;
+      int tie_rank = run_ties + (before & 0xFFFF);
+      int out = run_above + (before >> 16) + min(tie_rank, k);
+#pragma unroll
+      for (int q = 0; q < KPT; ++q)
+        if (q < cnt_t) decide(lo + t0 + tid * KPT + q, kk[q], tie_rank, out);
+      __syncthreads();  // the tile's totals are written; LDS is free for the next tile
+      run_ties += tile_tot[0];
+      run_above += tile_tot[1];
+    }
+  }
 }
 
 }  // namespace
