@@ -13,8 +13,9 @@
 //    Rows of the A operand are (head, limb) pairs, the B operand is 16 tokens
 //    x 64 codes read straight from HBM, and the integer sums are exact, so
 //    the only roundings are the final combination of the four limb sums;
-//  * p . V: the weights w_i = p_i * vscale_i of a 64-token block are split the
-//    same way (exponent from the block maximum), and V, staged in LDS, is read
+//  * p . V: the weights w_i = p_i * vscale_i of a 64-token block are split
+//    into four limbs the same way (exponent from the block maximum; being
+//    non-negative, as the base-128 digits of one integer), and V, staged in LDS, is read
 //    transposed (ds_read_b64_tr_b8) so that each lane holds 16 tokens of one
 //    channel, the layout of the B operand.
 // INT4 codes are widened to bytes holding code + 8; the +8 is taken out of
@@ -130,6 +131,19 @@ __device__ __forceinline__ void to_limbs(float y, int* l) {
     l[k] = (int)a;
     y = (y - a) * 128.f;
   }
+}
+
+// The same for a non-negative y (< 64), given as y * 2^21: the limbs are the
+// base-128 digits of n = RNE(y * 2^21), a0 = n >> 21 (at most 64) and a1..a3
+// in [0, 127]. Their weighted sum n / 2^21 equals to_limbs' (which also
+// rounds y to the nearest multiple of 2^-21, ties to even), in 6 operations
+// instead of 16; only the split of n into digits differs.
+__device__ __forceinline__ void to_limbs_nonneg(float y21, int* l) {
+  const unsigned n = (unsigned)rintf(y21);
+  l[0] = (int)(n >> 21);
+  l[1] = (int)((n >> 14) & 127u);
+  l[2] = (int)((n >> 7) & 127u);
+  l[3] = (int)(n & 127u);
 }
 
 // Exponent E with max * 2^E in [32, 64): then every scaled value is below 64
@@ -284,6 +298,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((
   // order) does not wait for V. Rows of contiguous caches are tokens; paged
   // rows come from the block's four 16-token pages.
   auto issue = [&](Regs& r, int it, int vs) {
+    // INT8 V: the lane-dependent offsets are recomputed at every issue (a few
+    // adds) rather than kept live across the block loop, where at 8 heads per
+    // pass they would be spilled to scratch.
+    int lane = threadIdx.x & 63;
+    if constexpr (VBITS == 8) asm volatile("" : "+v"(lane));
+    const int quad = lane >> 4, col = lane & 15;
     unsigned pb[4];
     const int t0 = block_t0(it);
     if (PAGED) {
@@ -563,6 +583,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((
     // block's P.V, so the wait for the V loads does not also wait for them.
     auto spill = [&](int it, const float* sv) {
       if (a.logits == nullptr) return;
+      int lane = threadIdx.x & 63;  // recomputed addresses, as in issue
+      if constexpr (VBITS == 8) asm volatile("" : "+v"(lane));
+      const int quad = lane >> 4, col = lane & 15;
       const int t0 = block_t0(it);
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
@@ -637,7 +660,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((
             if ((GP >= 8 ? cc % NRS : 0) != rs) continue;
             const int j = 4 * cc + quad, h = j % GP, tok = 16 * (j / GP) + col;
             int lm[4];
-            to_limbs(ldexpf(wv[ci][cc], E), lm);
+            to_limbs_nonneg(ldexpf(wv[ci][cc], E + 21), lm);  // weights are >= 0
 #pragma unroll
             for (int k = 0; k < 4; ++k) w_limb[wave][ci][rs][4 * (h & 3) + k][tok] = (int8_t)lm[k];
           }
