@@ -70,8 +70,9 @@ __global__ __launch_bounds__(1024) void quant_append_seq_kernel(kvc_cache_t c, c
 // bytes, so one wave instruction loads 64 / (D/8) consecutive rows (1 KB,
 // contiguous); each wave keeps U such loads in flight. The max-abs is a DPP
 // reduction over the row's lanes; each lane then quantizes its 8 values with
-// the same correctly rounded divisions and rounding as quant_row.h (the codes
-// are identical whichever kernel writes them) and stores them with one 8-byte
+// correctly rounded quotients (one division per row, then three operations
+// per value) and the rounding of quant_row.h (the codes are identical
+// whichever kernel writes them) and stores them with one 8-byte
 // (INT8) or 4-byte (INT4) store. The lengths advance in a second launch once
 // every row has read them.
 template <int D>
@@ -128,10 +129,19 @@ __global__ __launch_bounds__(256) void quant_append_bulk_kernel(kvc_cache_t c, c
       const int bits = kv ? VBITS : KBITS;
       const float qmax = bits == 8 ? 127.f : 7.f, qmin = bits == 8 ? -127.f : -8.f;
       const float sc = __fdiv_rn(amax, qmax);
+      // The row's quotients v / sc, correctly rounded, by Markstein's
+      // correction of a product with the correctly rounded reciprocal: with
+      // y = RN(1 / sc), q0 = RN(v y) and r = v - q0 sc (exact, by fma),
+      // RN(q0 + r y) = RN(v / sc). tests/test_quotient_sequence.py checks this
+      // for every fp16 v and every fp16 max-abs >= |v|, at both code widths,
+      // so the codes equal those of quant_row.h's divisions.
+      const float y = __fdiv_rn(1.f, sc);
       int code[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float q = sc == 0.f ? 0.f : rintf(__fdiv_rn(v[i], sc));
+        const float q0 = __fmul_rn(v[i], y);
+        const float q1 = fmaf(fmaf(-q0, sc, v[i]), y, q0);
+        const float q = sc == 0.f ? 0.f : rintf(q1);
         code[i] = (int)fminf(fmaxf(q, qmin), qmax);
       }
       const int L0 = c.lengths[b];

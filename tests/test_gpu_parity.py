@@ -93,6 +93,33 @@ def test_quant_zero_rows_and_halfway_cases():
         assert_codes_equal(gc, ref)
 
 
+def test_quant_bulk_halfway_cases():
+    """The same exact-half quotients through the prefill-sized bulk kernel
+    (4 heads x 64 tokens: 512 rows per sequence), for INT8 (max-abs 127:
+    x / scale lands on .5) and INT4 (max-abs 7), between rows of random
+    values, zero rows and rows whose max-abs is an fp16 subnormal."""
+    w = get("tiny_mha").scaled(context=64)
+    rng = np.random.default_rng(77)
+    k = rng.standard_normal((1, 4, 64, 64)).astype(np.float16)
+    halves = np.array([2.5, 3.5, -2.5, -3.5, 126.5, 0.5, -0.5, 1.5, 6.5, -6.5, 100.5], np.float16)
+    for t in range(0, 64, 4):
+        k[0, t % 4, t, :] = 0
+        k[0, t % 4, t, 0] = 127.0
+        k[0, t % 4, t, 1:12] = halves
+        k[0, (t + 1) % 4, t + 1, :] = 0
+        k[0, (t + 1) % 4, t + 1, 0] = 7.0
+        k[0, (t + 1) % 4, t + 1, 1:7] = np.array([2.5, -2.5, 0.5, 3.5, -6.5, 1.5], np.float16)
+        k[0, (t + 2) % 4, t + 2, :] = 0
+        k[0, (t + 3) % 4, t + 3, :] = (np.arange(64) - 32).astype(np.float16) * np.float16(2.0 ** -24)
+    v = -k[:, :, ::-1].copy()
+    d = {"k": k, "v": v}
+    for bits in (8, 4):
+        print(f"[quant bulk halves] bits={bits}", flush=True)
+        gc, ref, _ = prefill_both(w, d, capacity=64, bits=bits)
+        torch.cuda.synchronize()
+        assert_codes_equal(gc, ref)
+
+
 # ---------------------------------------------------------------- attention --
 
 @pytest.mark.parametrize("bits", [8, 4])
