@@ -323,6 +323,9 @@ int32_t prepare_attn(const kvc_cache_t* cache, const void* k_new, const void* v_
   a->qk_log2 = (float)(1.4426950408889634 / sqrt((double)cache->head_dim));
   a->zero_words = nullptr;
   a->zero_count = 0;
+  // One tier part, one query head per KV head and a contiguous cache (the
+  // split kernel variant that holds the tier code): the split kernel computes it.
+  a->fold_tier = g.tier_parts == 1 && num_q_heads == cache->num_kv_heads && cache->block_size == 0;
   return KVC_OK;
 }
 

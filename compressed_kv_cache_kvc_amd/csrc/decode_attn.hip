@@ -196,7 +196,11 @@ __device__ __forceinline__ unsigned sel4(const unsigned* v, int i) {
 //
 // KBITS and VBITS: the K and V code widths (8 or 4), set apart so a cache can
 // hold K and V at different precisions.
-template <int KBITS, int VBITS, int D, int GP, bool PAGED, int NW>
+//
+// FOLD (one-head contiguous kernel only): the first split's workgroups also
+// compute a one-part fp16 tier (AttnLaunch::fold_tier); a separate instance,
+// so the kernel without tiers keeps its code and registers.
+template <int KBITS, int VBITS, int D, int GP, bool PAGED, int NW, bool FOLD = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((
     amdgpu_waves_per_eu(NW == 8 ? 4 : (kChunk<GP, PAGED, NW> == 2 || kLean<GP, PAGED, NW>) ? 2 : GP <= 2 ? 3 : 2)))
     void attn_split_kernel(AttnLaunch a) {
@@ -791,6 +795,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((
     }
     if (hp + GP < G) __syncthreads();  // the next pass rewrites the LDS this one read
   }
+  // A one-part fp16 tier: the first split's workgroup adds it after its own
+  // work (tiers.h; a workgroup of this kernel's waves runs it as two working
+  // waves and idle ones, all reaching its barriers). Its exchange area is the
+  // staging area, free now: every DMA into it has been waited for, and the
+  // barrier below orders the last reads of it before the first writes.
+  // Only in the one-head contiguous kernel, which has registers to spare at
+  // two waves per SIMD: elsewhere the tier code's registers would raise the
+  // kernel's (those launches keep the tier kernel).
+  static_assert(!FOLD || LEAN, "the tier is folded into the one-head contiguous kernel only");
+  if constexpr (FOLD) if (s == 0) {
+    constexpr int TGT = 1;  // the tier launch's query heads per pass at one head
+    static_assert(TGT * D * 4 <= CH * NW * 64 * VROW, "the tier's exchange fits the staging area");
+    __shared__ float tier_ml[2 * TGT];
+    __syncthreads();
+    tier::tier_parts<D, TGT>(a, 0, reinterpret_cast<float*>(&v_stage[0][0][0]), tier_ml);
+  }
   if (app && s == 0 && g == 0 && tid == 0) {
     a.stash[b] = L_old;
     a.stash[c.batch + b] = c.num_seen[b];
@@ -930,6 +950,13 @@ __global__ __launch_bounds__(128) void attn_tier_kernel(AttnLaunch a) {
 template <int KBITS, int VBITS, int D, int GP, bool PAGED>
 hipError_t launch_split(const AttnLaunch& a, hipStream_t st) {
   constexpr int NW = kSplitWaves<GP>;
+  if constexpr (kLean<GP, PAGED, NW>) {
+    if (a.fold_tier) {
+      hipLaunchKernelGGL((attn_split_kernel<KBITS, VBITS, D, GP, PAGED, NW, true>),
+                         dim3(a.splits, a.c.num_kv_heads, a.c.batch), dim3(64 * NW), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_split_kernel<KBITS, VBITS, D, GP, PAGED, NW>), dim3(a.splits, a.c.num_kv_heads, a.c.batch),
                      dim3(64 * NW), 0, st, a);
   return hipGetLastError();
@@ -955,13 +982,17 @@ hipError_t launch_dim(const AttnLaunch& a, int G, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t st) {
+hipError_t launch_attn_split(const AttnLaunch& a0, hipStream_t st) {
+  // The tier is folded only where the one-head contiguous kernel has the
+  // folding instance (four waves per workgroup); otherwise the tier kernel runs.
+  AttnLaunch a = a0;
+  a.fold_tier = a0.fold_tier && kLean<1, false, kSplitWaves<1>>;
   const int G = a.num_q_heads / a.c.num_kv_heads;
   const int vb = vbits_of(a.c);
   hipError_t e;
   if (a.c.bits == 8) e = vb == 8 ? launch_dim<8, 8>(a, G, st) : launch_dim<8, 4>(a, G, st);
   else e = vb == 8 ? launch_dim<4, 8>(a, G, st) : launch_dim<4, 4>(a, G, st);
-  if (e != hipSuccess || a.tier_parts <= 0) return e;
+  if (e != hipSuccess || a.tier_parts <= 0 || a.fold_tier) return e;
   // The fp16 tiers: one two-wave workgroup per part, right after the splits.
   const dim3 grid(a.tier_parts, a.c.num_kv_heads, a.c.batch);
   const int gt = G == 1 ? 1 : G == 2 ? 2 : 4;

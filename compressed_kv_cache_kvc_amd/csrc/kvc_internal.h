@@ -86,6 +86,11 @@ struct AttnLaunch {
   // in-place eviction later in the same decode step.
   int32_t* zero_words;
   int zero_count;
+  // Set when the tiers make one part (at most kTierTokens tier tokens, e.g.
+  // the sinks alone), each KV head serves one query head and the cache is
+  // contiguous: the first split's workgroups compute it at their end, and no
+  // tier launch follows.
+  int fold_tier;
 };
 // Logit slots per query head: the tiles of all splits.
 __host__ __device__ inline long long attn_span(const AttnLaunch& a) {

@@ -235,25 +235,29 @@ def test_int4_hybrid_llama7b_full_size(path):
     print(f"max-abs out err {err:.2e}, worst score rel err {rel:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("hq,R16", [(8, 64), (4, 0)])  # (4, 0): one head per KV head, sinks only (folded tier)
 @pytest.mark.parametrize("L", [1, 3, 4, 5, 66])
-def test_tier_short_rows_fused_append(L):
+def test_tier_short_rows_fused_append(L, hq, R16):
     """The fused append + attention when the appended token is itself a sink
     (L <= fp16_sinks = 4) or the row is just past the sinks: the new token's
-    rows come from k_new / v_new and go to the tiers in the same call."""
-    w = _workload(8, 8, 4, 128, L, 2)
+    rows come from k_new / v_new and go to the tiers in the same call. With
+    one query head per KV head and the sinks alone, the tier is a single part
+    that the split kernel computes itself."""
+    print(f"[tier short fused] L={L} hq={hq} R16={R16}", flush=True)
+    w = _workload(8, hq, 4, 128, L, 2)
     d = draw(w)
-    gc = _tiered(w, L + 4, 0, 4, 64)
+    gc = _tiered(w, L + 4, 0, 4, R16)
     score = gc.score_buffer()
-    ref = oracle.RefCache(w.batch, 4, 128, L + 4, 8, fp16_sinks=4, fp16_recent=64)
+    ref = oracle.RefCache(w.batch, 4, 128, L + 4, 8, fp16_sinks=4, fp16_recent=R16)
     if L > 1:
         kvc.kvc_quant_append(gc, dev(d["k"][:, :, :L - 1]), dev(d["v"][:, :, :L - 1]), h2o_score=score)
         ref.append(d["k"][:, :, :L - 1], d["v"][:, :, :L - 1])
-    out = torch.empty((w.batch, 8, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.batch, hq, 128), dtype=torch.float32, device="cuda")
     kvc.kvc_append_decode_attn(gc, dev(d["k"][:, :, L - 1:L]), dev(d["v"][:, :, L - 1:L]), dev(d["q"]), out,
                                h2o_score=score)
     ref.append(d["k"][:, :, L - 1:L], d["v"][:, :, L - 1:L])
     ro, _ = ref.attend(d["q"])
     torch.cuda.synchronize()
-    _check_tier_rows(gc, ref, 4, 64)
+    _check_tier_rows(gc, ref, 4, R16)
     assert_out_close(host(out), ro)
     assert_scores_close(host(score), ref.score, ref.lengths)
