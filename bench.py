@@ -58,10 +58,10 @@ TRAFFIC_SOURCES = ("compressed_kv_cache_kvc_amd/csrc/decode_attn.hip",
                    "compressed_kv_cache_kvc_amd/csrc/merge.h",
                    "compressed_kv_cache_kvc_amd/csrc/tiers.h",
                    "compressed_kv_cache_kvc_amd/csrc/api.hip")
-# FETCH_SIZE 33,918.5 KiB x 1.9993 + WRITE_SIZE 1,308.06 KiB per launch
+# FETCH_SIZE 33,915.7 KiB x 1.9993 + WRITE_SIZE 1,308.09 KiB per launch
 # on the LLaMA-7B layer, with the copy calibration above.
-TRAFFIC_SHA256 = "2352414f109b96c9ddd279f02865b1c13d4cd4f4c4ebcecf3d933fd9ade46ade"
-TRAFFIC_BYTES = 70780171
+TRAFFIC_SHA256 = "5807953937d734d32ac098c75ee72e66f4ecd0b5b2b23c1981bfdca1919e3702"
+TRAFFIC_BYTES = 70774469
 
 
 def attention_traffic():
