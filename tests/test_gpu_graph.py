@@ -5,8 +5,9 @@ once, its inputs restored by ordinary (eager) copies before every replay, and
 each of three replays must reproduce the eager call's outputs and cache
 state bit for bit: the one-call decode step (split kernel, then the
 eviction kernel with the merge), the fused append + attention on a tiered
-INT4 cache (split, tier and merge kernels), and on a paged cache the
-attention with H2O and the block eviction.
+INT4 cache (split, tier and merge kernels) and on a plain INT8 cache (also
+replayed three times in a row), and on a paged cache the attention with H2O
+and the block eviction.
 """
 import numpy as np
 import pytest
@@ -127,6 +128,59 @@ def test_tiered_append_attention_graph_replays(hq, hkv):
     outputs = {"out": out, "score": score, **{"cache." + n: t for n, t in _state(gc).items()}}
     _replays_match(call, restore, outputs)
     assert np.isfinite(out.cpu().numpy()).all()
+
+
+def test_append_attention_graph_replays_in_a_row():
+    """The append + attention at one query head per KV head captured once:
+    replays after a restore equal the eager call, and three replays in a row
+    equal three eager calls (the lengths advance once per replay)."""
+    P, hq = 900, 8
+    print("[graph] append + attention, replays in a row", flush=True)
+    w = _workload(8, hq, hq, P)
+    d = draw(w)
+    B, D, cap = w.batch, 128, P + 8
+    gc = kvc.KVCache(B, hq, D, cap, 8)
+    score = gc.score_buffer()
+    kvc.kvc_quant_append(gc, dev(d["k"][:, :, :P]), dev(d["v"][:, :, :P]), h2o_score=score)
+    torch.cuda.synchronize()
+    saved = {n: t.clone() for n, t in _state(gc).items()}
+    saved_score = score.clone()
+    out = torch.empty((B, hq, D), dtype=torch.float32, device="cuda")
+    knew, vnew, q = dev(d["step_k"][0]), dev(d["step_v"][0]), dev(d["step_q"][0])
+    ws = torch.empty(kvc.kvc_decode_attn_workspace_bytes(gc, hq, P + 4, True), dtype=torch.uint8, device="cuda")
+
+    def call():
+        kvc.kvc_append_decode_attn(gc, knew, vnew, q, out, h2o_score=score, max_len_hint=P + 2, workspace=ws)
+
+    def restore():
+        for n, t in _state(gc).items():
+            t.copy_(saved[n])
+        score.copy_(saved_score)
+        out.zero_()
+
+    outputs = {"out": out, "score": score, **{"cache." + n: t for n, t in _state(gc).items()}}
+    _replays_match(call, restore, outputs)
+
+    # Three in a row, eager, then as replays of one captured call.
+    restore()
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ref = {k: t.clone() for k, t in outputs.items()}
+    assert ref["cache.lengths"].tolist() == [P + 3] * B
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    restore()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    for k, t in outputs.items():
+        assert torch.equal(t, ref[k]), f"three replays: {k} differs from three eager calls"
+    del g
 
 
 def test_paged_attention_and_block_evict_graph_replays():

@@ -290,11 +290,18 @@ def test_append_decode_attn_bit_exact(hq, hkv, bits, D, lens, h2o, cap_extra):
 
 
 @pytest.mark.parametrize("append", [False, True])
-def test_split_then_merge_equals_one_call(append):
+@pytest.mark.parametrize("B,H,Hq,L", [
+    (2, 4, 8, 1500),   # GQA 2
+    (2, 4, 4, 1500),   # one query head per KV head
+    (1, 1, 1, 70001),  # one row of 274 splits (more than 4 x 64 split states per head)
+    (3, 2, 2, 5),      # one split per row
+])
+def test_split_then_merge_equals_one_call(append, B, H, Hq, L):
     """kvc_decode_attn_split + kvc_decode_attn_merge equal kvc_decode_attn
     (or, with the new token, kvc_append_decode_attn) bit for bit: output,
     scores and every cache buffer."""
-    B, H, Hq, D, L = 2, 4, 8, 128, 1500
+    D = 128
+    print(f"[attn] split + merge vs one call B={B} H={H} Hq={Hq} L={L} append={append}", flush=True)
     w = get("tiny_mha").scaled(context=L + 1, batch=B, num_q_heads=Hq, num_kv_heads=H, head_dim=D, bits=8)
     d = draw(w)
     runs = []
@@ -321,6 +328,61 @@ def test_split_then_merge_equals_one_call(append):
     assert torch.equal(oa, ob)
     _assert_same_cache(ga, gb, sa, sb)
     assert host(gb.lengths).tolist() == [L + int(append)] * B
+
+
+def test_attention_consecutive_steps_on_one_workspace():
+    """Several decode steps (with and without a new token) of the one-call
+    attention on one workspace that starts as arbitrary bytes: each step's
+    output, scores and cache (lengths and counts included) equal the split
+    and merge calls' bit for bit, and the last step matches the oracle."""
+    B, H, D, lens = 3, 4, 128, [700, 1, 0]
+    print(f"[attn] consecutive steps on one workspace B={B} H={H} lens={lens}", flush=True)
+    steps = 4
+    Lmax = max(lens)
+    w = get("tiny_mha").scaled(context=Lmax + steps, batch=B, num_q_heads=H, num_kv_heads=H, head_dim=D, bits=8)
+    d = draw(w)
+    cap = Lmax + steps + 3
+    rng = np.random.default_rng(3)
+    sc = (rng.random((B, H, cap)) * 0.1).astype(np.float32)
+    pair = []
+    for _ in range(2):
+        gc = make_gpu_cache(w, cap, 8)
+        kvc.kvc_quant_append(gc, dev(d["k"][:, :, :Lmax]), dev(d["v"][:, :, :Lmax]))
+        gc.lengths.copy_(dev(np.array(lens, np.int32)))
+        gc.num_seen.copy_(dev(np.array(lens, np.int32) + 5))
+        pair.append((gc, dev(sc)))
+    (gA, sA), (gB, sB) = pair
+    ref = oracle.RefCache(B, H, D, cap, 8)
+    ref.append(d["k"][:, :, :Lmax], d["v"][:, :, :Lmax])
+    ref.lengths[:] = lens
+    ref.num_seen[:] = np.array(lens) + 5
+    ref.score[:] = sc
+    nbytes = kvc.kvc_decode_attn_workspace_bytes(gB, H, cap, True)
+    wsA = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    wsB = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    q = dev(d["q"])
+    for i in range(steps):
+        hint = Lmax + i
+        kn, vn = dev(d["k"][:, :, Lmax + i:Lmax + i + 1]), dev(d["v"][:, :, Lmax + i:Lmax + i + 1])
+        outA = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+        outB = torch.empty_like(outA)
+        append = i != 2  # step 2 attends without a new token
+        kvc.kvc_decode_attn_split(gA, q, wsA, k_new=kn if append else None, v_new=vn if append else None,
+                                  h2o_score=sA, max_len_hint=hint)
+        kvc.kvc_decode_attn_merge(gA, H, outA, wsA, appended=append, h2o_score=sA, max_len_hint=hint)
+        if append:
+            kvc.kvc_append_decode_attn(gB, kn, vn, q, outB, h2o_score=sB, max_len_hint=hint, workspace=wsB)
+            ref.append(d["k"][:, :, Lmax + i:Lmax + i + 1], d["v"][:, :, Lmax + i:Lmax + i + 1])
+        else:
+            kvc.kvc_decode_attn(gB, q, outB, h2o_score=sB, max_len_hint=hint, workspace=wsB)
+        ro, _ = ref.attend(d["q"], h2o=True)
+        torch.cuda.synchronize()
+        assert torch.equal(outA, outB), f"step {i}"
+        _assert_same_cache(gA, gB, sA, sB)
+    assert host(gB.lengths).tolist() == [n + steps - 1 for n in lens]
+    assert_out_close(host(outB), ro)
+    assert_codes_equal(gB, ref)
+    assert_scores_close(host(sB), ref.score, ref.lengths)
 
 
 def test_append_decode_attn_paged():
