@@ -93,26 +93,37 @@ __global__ __launch_bounds__(256) void quant_append_bulk_kernel(kvc_cache_t c, c
   constexpr int RPI = 64 / LPR;  // rows per wave instruction
   constexpr int U = 4;           // loads in flight per wave
   const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
-  const long long rows = 2 * tokens;  // K rows [0, tokens), V rows [tokens, 2 tokens)
-  const long long nwaves = (long long)gridDim.x * 4;
-  const int H = c.num_kv_heads;
-  for (long long r0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (RPI * U); r0 < rows;
-       r0 += nwaves * RPI * U) {
+  // Row indices in 32 bits (the launcher takes this kernel only for fewer
+  // than 2^31 rows): K rows [0, tokens), V rows [tokens, 2 tokens).
+  const unsigned ntok = (unsigned)tokens, rows = 2u * ntok, nn = (unsigned)n_new, H = (unsigned)c.num_kv_heads;
+  const unsigned nwaves = gridDim.x * 4u;
+  for (unsigned r0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (RPI * U); r0 < rows; r0 += nwaves * (RPI * U)) {
+    // The rows' values, then their sequences' lengths and counts (clamped
+    // rows, so every load is unconditional and all are in flight together).
     uint4 x[U];
+    unsigned rtu[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const long long r = min(r0 + u * RPI + sub, rows - 1);
-      const bool kv = r >= tokens;
-      x[u] = *reinterpret_cast<const uint4*>((kv ? vn : kn) + (kv ? r - tokens : r) * D + part * 8);
+      const unsigned r = min(r0 + u * RPI + sub, rows - 1);
+      rtu[u] = r >= ntok ? r - ntok : r;  // (b, h, t) flattened
+      x[u] = *reinterpret_cast<const uint4*>((r >= ntok ? vn : kn) + (size_t)rtu[u] * D + part * 8);
+    }
+    int len0[U], seen0[U], tt[U], hh[U], bb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const unsigned bh = rtu[u] / nn;
+      tt[u] = (int)(rtu[u] - bh * nn);
+      bb[u] = (int)(bh / H);
+      hh[u] = (int)(bh - (unsigned)bb[u] * H);
+      len0[u] = c.lengths[bb[u]];
+      seen0[u] = c.num_seen[bb[u]];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const long long r = r0 + u * RPI + sub;
-      const bool valid = r < rows, kv = r >= tokens;
-      const long long rt = kv ? r - tokens : r;  // (b, h, t) flattened
-      const int t = (int)(rt % n_new);
-      const long long bh = rt / n_new;
-      const int h = (int)(bh % H), b = (int)(bh / H);
+      const unsigned r = r0 + u * RPI + sub;
+      const bool valid = r < rows, kv = r >= ntok;
+      const int t = tt[u], h = hh[u], b = bb[u];
+      const long long bh = (long long)b * H + h;
       const __half2* hv = reinterpret_cast<const __half2*>(&x[u]);
       float v[8];
 #pragma unroll
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(256) void quant_append_bulk_kernel(kvc_cache_t c, c
         const float q = sc == 0.f ? 0.f : rintf(q1);
         code[i] = (int)fminf(fmaxf(q, qmin), qmax);
       }
-      const int L0 = c.lengths[b];
+      const int L0 = len0[u];
       const long long row = cache_row(c, b, h, L0 + t);
       if (row < 0) continue;
       if (bits == 8) {
@@ -166,7 +177,7 @@ __global__ __launch_bounds__(256) void quant_append_bulk_kernel(kvc_cache_t c, c
       if (part == 0) {
         (kv ? c.v_scale : c.k_scale)[row] = sc;
         if (!kv) {
-          if (c.positions) c.positions[row] = c.num_seen[b] + t;
+          if (c.positions) c.positions[row] = seen0[u] + t;
           if (score) score[bh * c.capacity + L0 + t] = 0.f;
         }
       }
@@ -175,7 +186,7 @@ __global__ __launch_bounds__(256) void quant_append_bulk_kernel(kvc_cache_t c, c
 }
 
 // Prefill-sized appends whose inputs or codes are not aligned for the bulk
-// kernel: four rows per workgroup, one wave per row.
+// kernel, or of 2^31 rows or more: four rows per workgroup, one wave per row.
 template <int KBITS, int VBITS, int D>
 __global__ __launch_bounds__(256) void quant_append_rows_kernel(kvc_cache_t c, const __half* __restrict__ kn,
                                                                 const __half* __restrict__ vn, int n_new,
@@ -223,16 +234,16 @@ hipError_t launch_bits(const kvc_cache_t& c, const __half* kn, const __half* vn,
   }
   const long long tokens = (long long)c.batch * c.num_kv_heads * n_new;
   const uintptr_t align = (uintptr_t)kn | (uintptr_t)vn | (uintptr_t)c.k_codes | (uintptr_t)c.v_codes;
-  if (align % 16) {
+  if (align % 16 || 2 * tokens >= (1LL << 31)) {
     const long long total = rows_per_seq * c.batch;
     hipLaunchKernelGGL((quant_append_rows_kernel<KBITS, VBITS, D>), dim3((unsigned)((total + 3) / 4)), dim3(256), 0,
                        st, c, kn, vn, n_new, score, total);
   } else {
-    // The bulk kernel: about 8 workgroups of 4 waves per CU, grid-stride
-    // over the rows.
+    // The bulk kernel: one pass of U loads per wave (2^31 rows make at most
+    // 2^25 workgroups), so that no wave's loads wait behind its own earlier
+    // stores, which gfx9 counts with them.
     const long long rows_per_wg = 4LL * (64 / (D / 8)) * 4;
-    const long long blocks = std::max(1LL, std::min((2 * tokens + rows_per_wg - 1) / rows_per_wg,
-                                                     8LL * device_cus()));
+    const long long blocks = std::max(1LL, (2 * tokens + rows_per_wg - 1) / rows_per_wg);
     hipLaunchKernelGGL((quant_append_bulk_kernel<KBITS, VBITS, D>), dim3((unsigned)blocks), dim3(256), 0, st, c, kn,
                        vn, n_new, score, tokens);
   }
