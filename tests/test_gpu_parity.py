@@ -50,10 +50,11 @@ def test_quant_append_bit_exact(name, bits, L):
 @pytest.mark.parametrize("bits,v_bits,D", [(8, 8, 128), (4, 4, 128), (8, 4, 64), (4, 8, 128)])
 def test_quant_append_bulk_edges(aligned, bits, v_bits, D):
     """Prefill-sized appends: 3 KV heads x 47 tokens per sequence (141 K rows,
-    so a wave instruction straddles the last K and first V rows), appended at
-    different lengths per sequence (one after a short first append); inputs
-    offset by one fp16 element take the per-row kernel. Codes, scales and
-    positions bit-exact against the oracle."""
+    so a wave instruction straddles the last K and first V rows), appended
+    after a short first append at different lengths and counts per sequence
+    (13 and 6 tokens, seen 13 and 9); inputs offset by one fp16 element take
+    the per-row kernel. Codes, scales, positions, lengths and counts
+    bit-exact against the oracle."""
     print(f"[quant bulk] aligned={aligned} bits={bits} v_bits={v_bits} D={D}", flush=True)
     w = get("tiny_mha").scaled(context=60, batch=2, num_q_heads=3, num_kv_heads=3, head_dim=D, bits=bits)
     d = draw(w)
@@ -62,6 +63,11 @@ def test_quant_append_bulk_edges(aligned, bits, v_bits, D):
     k0, v0 = d["k"][:, :, :13], d["v"][:, :, :13]
     kvc.kvc_quant_append(gc, dev(k0), dev(v0))
     ref.append(k0, v0)
+    # Sequence 1 continues from 6 tokens (its later slots are overwritten).
+    gc.lengths.copy_(dev(np.array([13, 6], np.int32)))
+    gc.num_seen.copy_(dev(np.array([13, 9], np.int32)))
+    ref.lengths[:] = [13, 6]
+    ref.num_seen[:] = [13, 9]
     k1, v1 = d["k"][:, :, 13:60], d["v"][:, :, 13:60]
     if aligned:
         kd, vd = dev(k1), dev(v1)
@@ -76,7 +82,8 @@ def test_quant_append_bulk_edges(aligned, bits, v_bits, D):
     ref.append(k1, v1)
     torch.cuda.synchronize()
     assert_codes_equal(gc, ref)
-    assert host(gc.num_seen).tolist() == [60, 60]
+    assert host(gc.lengths).tolist() == [60, 53]
+    assert host(gc.num_seen).tolist() == [60, 56]
 
 
 def test_quant_zero_rows_and_halfway_cases():
