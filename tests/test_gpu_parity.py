@@ -636,10 +636,13 @@ def test_decode_step_llama7b_full_size():
 
 @pytest.mark.parametrize("L,budget,S,R", [(512, 128, 4, 64), (3000, 1000, 4, 100), (9000, 2457, 4, 1024),
                                           (100, 100, 4, 10), (99, 100, 4, 10), (300, 20, 10, 10),
-                                          (5000, 5000 - 1, 4, 2048), (20000, 5000, 4, 256)])
+                                          (5000, 5000 - 1, 4, 2048), (20000, 5000, 4, 256),
+                                          (30000, 23000, 4, 256), (40000, 12000, 4, 1024)])
 def test_select_bit_exact_on_shared_scores(L, budget, S, R):
     """Same fp32 scores on both sides: the keep masks must be identical,
-    including ties (broken toward the lower slot)."""
+    including ties (broken toward the lower slot). Rows of more than 8192
+    candidates take the memory path (keys re-read on every digit pass);
+    30000 / 23000 puts the k-th key of row 0 in the 0.5 tie class."""
     rng = np.random.default_rng(L + budget)
     B, H = 2, 3
     sc = rng.random((B, H, L)).astype(np.float32) * 3
