@@ -17,9 +17,9 @@
 //    keys fall in the same bin then collide in groups of at most 64 / COPIES
 //    instead of 64;
 //  * the bin holding the k-th key comes from a block-wide suffix scan; once
-//    that bin holds at most 64 keys, they are gathered into LDS and one wave
-//    ranks them directly (each lane counts the keys above and equal to its
-//    own), which ends the search without further passes.
+//    that bin holds at most 64 keys, they are gathered into LDS and ranked
+//    directly (every key's count of keys above and equal to it, spread over
+//    the whole workgroup), which ends the search without further passes.
 #pragma once
 
 #include "kvc_internal.h"
@@ -160,19 +160,30 @@ __device__ __forceinline__ unsigned radix_threshold_range(ForKeys for_keys, int&
         if ((u & pmask) == T) small[atomicAdd(&sel[3], 1)] = u;
       });
       __syncthreads();
+      // Every wave ranks: NT / 64 adjacent threads per gathered key, each
+      // comparing it with 64 / (NT / 64) of the others, then a sum over the
+      // key's threads. Equal keys write the same result.
+      constexpr int TPK = NT / 64, JPT = 64 / TPK;
+      static_assert(TPK >= 1 && TPK <= 64 && TPK * JPT == 64, "NT");
       const int n_small = sel[2];
-      if (tid < 64) {
-        const unsigned u = small[min(tid, n_small - 1)];
-        int gt = 0, eq = 0;
-        for (int j = 0; j < n_small; ++j) {
-          const unsigned w = small[j];
-          gt += w > u;
-          eq += w == u;
-        }
-        if (tid < n_small && gt < k && k <= gt + eq) {
-          sel[0] = (int)u;
-          sel[1] = k - gt;
-        }
+      const int ki = tid / TPK, part = tid % TPK;
+      const unsigned u = small[min(ki, n_small - 1)];
+      int gt = 0, eq = 0;
+#pragma unroll
+      for (int q = 0; q < JPT; ++q) {
+        const int j = part * JPT + q;
+        const unsigned w = small[min(j, n_small - 1)];
+        gt += (j < n_small) & (w > u);
+        eq += (j < n_small) & (w == u);
+      }
+#pragma unroll
+      for (int o = 1; o < TPK; o <<= 1) {
+        gt += __shfl_xor(gt, o);
+        eq += __shfl_xor(eq, o);
+      }
+      if (part == 0 && ki < n_small && gt < k && k <= gt + eq) {
+        sel[0] = (int)u;
+        sel[1] = k - gt;
       }
       __syncthreads();
       k = sel[1];
