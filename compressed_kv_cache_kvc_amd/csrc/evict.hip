@@ -434,23 +434,33 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
   int out = (before >> 16) + min(tie_rank, k);  // kept candidates before this thread
   // Kept candidates into LDS in rank order (the heavy list); mask bytes of
   // the threads [p*NT/parts, (p+1)*NT/parts).
+  // The decisions take no branch per key (keys past cnt are 0, below T);
+  // the mask bytes go out four to a store where the slots are 4-byte aligned.
   int* heavy = reinterpret_cast<int*>(stage_lds);
   const bool my_threads = m && (tid >> (kLog2NT - log2_parts)) == p;
+  unsigned keep_bytes[KPT / 4];
+#pragma unroll
+  for (int w = 0; w < KPT / 4; ++w) keep_bytes[w] = 0u;
 #pragma unroll
   for (int q = 0; q < KPT; ++q) {
-    if (q < cnt) {
-      const unsigned u = key[q];
-      int keepb = 0;
-      if (any_heavy) {
-        if (u > T) {
-          keepb = 1;
-        } else if (u == T) {
-          keepb = tie_rank < k;
-          ++tie_rank;
-        }
+    const unsigned u = key[q];
+    const bool tie = any_heavy && u == T;
+    const bool keepb = (any_heavy && u > T) || (tie && tie_rank < k);
+    tie_rank += tie;
+    keep_bytes[q / 4] |= (unsigned)keepb << (8 * (q % 4));
+    if (keepb) heavy[min(out, NT * KPT - 1)] = i0 + q;
+    out += keepb;
+  }
+  if (my_threads) {
+#pragma unroll
+    for (int w = 0; w < KPT / 4; ++w) {
+      if (4 * w + 4 <= cnt && ((uintptr_t)(m + i0 + 4 * w) & 3u) == 0u) {
+        *reinterpret_cast<unsigned*>(m + i0 + 4 * w) = keep_bytes[w];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * w + e < cnt) m[i0 + 4 * w + e] = (uint8_t)(keep_bytes[w] >> (8 * e));
       }
-      if (my_threads) m[i0 + q] = (uint8_t)keepb;
-      if (keepb) heavy[min(out++, NT * KPT - 1)] = i0 + q;
     }
   }
   __syncthreads();
