@@ -356,12 +356,14 @@ __global__ __launch_bounds__(kNT) void evict_kernel(EvictArgs e) {
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     float s = sv[j];
-    if (MERGE && n_sink + tid + j * NT < L_h2o) {
+    if (MERGE) {
+      // Computed for every slot (clamped loads, so the logits are some
+      // row's), kept only below L_h2o: a select, not a branch per key.
       float add = 0.f;
 #pragma unroll
       for (int h = 0; h < GL; ++h)
         if (h < G) add = merge::h2o_add(add, lgv[j][h], mstat[2 * h], mstat[2 * h + 1]);
-      s = s + add;
+      s = n_sink + tid + j * NT < L_h2o ? s + add : s;
     }
     v[j] = radix::order_key(s);
   }
